@@ -1,0 +1,240 @@
+"""Python binding of libcgs, the cache-guided selective FFN for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libcgs.so``.  PyTorch supplies device memory (tensors) and the
+current stream; it computes nothing here.  If the library has not been built
+the import succeeds but every call raises, so no path silently falls back.
+
+Entry points mirror ``include/cgs.h``: ``ctx_select``, ``ctx_ffn_recompute``,
+``act_build_mask``, ``act_ffn_masked``, ``ref_rebuild_dense`` and the
+``residual_rmsnorm`` glue.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcgs.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "cgs.h")
+
+CGS_BF16, CGS_F32 = 0, 1
+CGS_SCORE_REL_RMS, CGS_SCORE_COSINE = 0, 1
+CGS_MASK_TOPK, CGS_MASK_COVERAGE = 0, 1
+CGS_DOWN_DF, CGS_DOWN_FD = 0, 1
+
+_KIND = {"rel_rms": CGS_SCORE_REL_RMS, "cosine": CGS_SCORE_COSINE}
+_MODE = {"topk": CGS_MASK_TOPK, "coverage": CGS_MASK_COVERAGE}
+_LAYOUT = {"df": CGS_DOWN_DF, "fd": CGS_DOWN_FD}
+
+
+class CgsError(RuntimeError):
+    pass
+
+
+class _Ffn(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("ff", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("down_layout", ctypes.c_int32), ("w_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
+
+
+_lib = None
+_vp, _i, _sz, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+_SIGS = {
+    "cgs_ratio_to_count": (_i, [_d, _i]),
+    "cgs_status_str": (ctypes.c_char_p, [_i]),
+    "cgs_version": (_i, []),
+    "cgs_ctx_select_workspace": (_sz, [_i, _i]),
+    "ctx_select": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "cgs_ctx_ffn_recompute_workspace": (_sz, [_i, _i, _i, _i, _i]),
+    "ctx_ffn_recompute": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp]),
+    "cgs_act_build_mask_workspace": (_sz, [_i, _i, _i, _i]),
+    "act_build_mask": (_i, [_vp, _i, _i, _vp, _i, _i, _d, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "cgs_act_ffn_masked_workspace": (_sz, [_i, _i, _i, _i]),
+    "act_ffn_masked": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "cgs_ref_rebuild_dense_workspace": (_sz, [_i, _i, _i, _i, _i]),
+    "ref_rebuild_dense": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
+    "cgs_residual_rmsnorm": (_i, [_vp, _vp, _i, _vp, _i, _i, _vp, _i, _vp]),
+}
+
+
+def lib():
+    """The loaded libcgs (raises CgsError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CgsError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise CgsError(f"{what}: {lib().cgs_status_str(status).decode()} (status {status})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return CGS_BF16
+    if t.dtype == torch.float32:
+        return CGS_F32
+    raise CgsError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise CgsError("tensors must be contiguous device tensors")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+_ws_cache: dict = {}
+
+
+def workspace(nbytes: int, device, tag: str = "default") -> torch.Tensor:
+    """A cached device workspace of at least nbytes for (device, tag)."""
+    key = (str(device), tag)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+@dataclass
+class FFN:
+    """Device weights of one GeGLU FFN: w_gate, w_up [ff][d]; w_down [d][ff]
+    (``layout='df'``) or neuron-major [ff][d] (``'fd'``)."""
+    w_gate: torch.Tensor
+    w_up: torch.Tensor
+    w_down: torch.Tensor
+    layout: str = "df"
+
+    @property
+    def d(self) -> int:
+        return self.w_gate.shape[1]
+
+    @property
+    def ff(self) -> int:
+        return self.w_gate.shape[0]
+
+    def cstruct(self) -> _Ffn:
+        dt = _dtype_code(self.w_gate)
+        for t in (self.w_up, self.w_down):
+            if _dtype_code(t) != dt:
+                raise CgsError("FFN weights must share one dtype")
+        return _Ffn(self.d, self.ff, dt, _LAYOUT[self.layout], _ptr(self.w_gate),
+                    _ptr(self.w_up), _ptr(self.w_down))
+
+
+def ratio_to_count(rho: float, n: int) -> int:
+    return int(lib().cgs_ratio_to_count(float(rho), int(n)))
+
+
+def ctx_select(x, x_ref, k: int, kind: str = "rel_rms", idx_out=None, key_out=None,
+               ws=None, stream=None):
+    """Top-k token indices (ascending int32) by the Eq. 2 drift score."""
+    P, d = x.shape
+    if idx_out is None:
+        idx_out = torch.empty(k, dtype=torch.int32, device=x.device)
+    nbytes = lib().cgs_ctx_select_workspace(P, d)
+    ws = workspace(nbytes, x.device, "select") if ws is None else ws
+    _check(lib().ctx_select(_ptr(x), _ptr(x_ref), P, d, _dtype_code(x), int(k), _KIND[kind],
+                            _ptr(idx_out), _ptr(key_out), _ptr(ws), ws.numel(), _stream(stream)),
+           "ctx_select")
+    return idx_out
+
+
+def ctx_ffn_recompute(w: FFN, x, y_ref, idx, y_out=None, ws=None, stream=None):
+    """Eq. 3: F(x) on the rows idx, the reference outputs elsewhere."""
+    P, d = x.shape
+    k = int(idx.numel())
+    if y_out is None:
+        y_out = torch.empty_like(y_ref)
+    c = w.cstruct()
+    nbytes = lib().cgs_ctx_ffn_recompute_workspace(k, P, d, w.ff, c.dtype)
+    ws = workspace(nbytes, x.device, "ctx") if ws is None else ws
+    _check(lib().ctx_ffn_recompute(ctypes.byref(c), _ptr(x), _ptr(y_ref), _ptr(idx), k, P,
+                                   _ptr(y_out), _ptr(ws), ws.numel(), _stream(stream)),
+           "ctx_ffn_recompute")
+    return y_out
+
+
+def act_build_mask(h_ref, w: FFN, mode: str = "topk", K: int = 0, coverage: float = 0.0,
+                   mask_out=None, idx_out=None, count_out=None, ws=None, stream=None):
+    """Group mask from the reference steps' activations h_ref [T][ff][S] (fp32).
+    Returns (mask words uint64 as int64 tensor, idx int32 [ff], count int32 [1])."""
+    T, ff, S = h_ref.shape
+    dev = h_ref.device
+    if mask_out is None:
+        mask_out = torch.empty((ff + 63) // 64, dtype=torch.int64, device=dev)
+    if idx_out is None:
+        idx_out = torch.empty(ff, dtype=torch.int32, device=dev)
+    if count_out is None:
+        count_out = torch.empty(1, dtype=torch.int32, device=dev)
+    c = w.cstruct()
+    nbytes = lib().cgs_act_build_mask_workspace(T, S, ff, w.d)
+    ws = workspace(nbytes, dev, "mask") if ws is None else ws
+    _check(lib().act_build_mask(_ptr(h_ref), T, S, ctypes.byref(c), _MODE[mode], int(K),
+                                float(coverage), _ptr(mask_out), _ptr(idx_out), _ptr(count_out),
+                                _ptr(ws), ws.numel(), _stream(stream)), "act_build_mask")
+    return mask_out, idx_out, count_out
+
+
+def act_ffn_masked(w: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=None, y_f32_out=None,
+                   h_out=None, ws=None, stream=None):
+    """Eq. 4 masked update of a dense anchor (dense anchor step when idx covers
+    every neuron and no anchors are given)."""
+    S, d = x.shape
+    K = int(idx.numel())
+    if y_out is None:
+        y_out = torch.empty_like(x)
+    c = w.cstruct()
+    nbytes = lib().cgs_act_ffn_masked_workspace(S, K, d, w.ff)
+    ws = workspace(nbytes, x.device, "act") if ws is None else ws
+    _check(lib().act_ffn_masked(ctypes.byref(c), _ptr(x), S, _ptr(idx), K, _ptr(y_anchor),
+                                _ptr(h_anchor), _ptr(y_out), _ptr(y_f32_out), _ptr(h_out),
+                                _ptr(ws), ws.numel(), _stream(stream)), "act_ffn_masked")
+    return y_out
+
+
+def ref_rebuild_dense(layers, r0, x_ref_out=None, y_ref_out=None, ws=None, stream=None):
+    """Dense rebuild of an entry: returns (x_ref [L][P][d], y_ref [L][P][d])."""
+    L = len(layers)
+    P, d = r0.shape
+    if x_ref_out is None:
+        x_ref_out = torch.empty((L, P, d), dtype=r0.dtype, device=r0.device)
+    if y_ref_out is None:
+        y_ref_out = torch.empty((L, P, d), dtype=r0.dtype, device=r0.device)
+    arr = (_Ffn * L)(*[w.cstruct() for w in layers])
+    c0 = arr[0]
+    nbytes = lib().cgs_ref_rebuild_dense_workspace(L, P, d, c0.ff, c0.dtype)
+    ws = workspace(nbytes, r0.device, "rebuild") if ws is None else ws
+    _check(lib().ref_rebuild_dense(arr, L, _ptr(r0), P, _ptr(x_ref_out), _ptr(y_ref_out),
+                                   _ptr(ws), ws.numel(), _stream(stream)), "ref_rebuild_dense")
+    return x_ref_out, y_ref_out
+
+
+def residual_rmsnorm(r, y=None, bias=None, x_out=None, stream=None):
+    """r += y + bias (in place, fp32); x_out = RMSNorm(r) (eps 1e-6, no scale)."""
+    M, d = r.shape
+    ydt = _dtype_code(y) if y is not None else CGS_BF16
+    odt = _dtype_code(x_out) if x_out is not None else CGS_BF16
+    _check(lib().cgs_residual_rmsnorm(_ptr(r), _ptr(y), ydt, _ptr(bias), M, d, _ptr(x_out), odt,
+                                      _stream(stream)), "cgs_residual_rmsnorm")
+    return x_out

@@ -1,0 +1,190 @@
+// Block-wide exact selection over 64-bit ordered keys, one workgroup of
+// kSelThreads threads.  Larger keys rank first; equal keys rank by ascending
+// index, so every key set has exactly one top-k set.
+//
+// The top k is found by an 8-pass radix descent over the key bytes (most
+// significant first), which yields the k-th largest key value T and how many
+// elements equal to T are still needed; a final pass in index order emits
+// every element with key > T and the first `need` elements with key == T, in
+// ascending index order.  All work is integer, so the result does not depend
+// on thread scheduling.
+#pragma once
+
+#include "common.hpp"
+
+namespace cgs {
+
+constexpr int kSelThreads = 1024;
+
+struct SelShared {
+  uint32_t hist[256];
+  unsigned long long hsum[256];
+  long long scan[kSelThreads / kWave];
+  uint64_t digit;
+  long long above_cnt;
+  long long above_sum;
+  long long tie_z;
+  int need;
+};
+
+// Threshold of the top k: returns T (the k-th largest key) and sets *need to
+// the number of elements equal to T that belong to the top k (>= 1).
+// Requires 1 <= k <= n.
+template <class KeyFn>
+__device__ uint64_t block_topk_threshold(KeyFn key_of, int n, int k, int* need, SelShared& sm) {
+  uint64_t prefix = 0, pmask = 0;
+  long long remaining = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int b = threadIdx.x; b < 256; b += blockDim.x) sm.hist[b] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      uint64_t kv = key_of(i);
+      if ((kv & pmask) == prefix) atomicAdd(&sm.hist[(kv >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      const int lane = threadIdx.x;
+      // lane owns bins 4*lane .. 4*lane+3; count of all bins above this lane's
+      long long c = 0;
+      for (int j = 0; j < 4; ++j) c += sm.hist[4 * lane + j];
+      // suffix sum over higher lanes: scan in reversed lane order
+      long long rev = c;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        long long u = __shfl_down(rev, o, kWave);
+        if (lane + o < kWave) rev += u;
+      }
+      long long above = rev - c;  // elements in bins of higher lanes
+      for (int j = 3; j >= 0; --j) {
+        long long h = sm.hist[4 * lane + j];
+        if (above < remaining && remaining <= above + h) {
+          sm.digit = static_cast<uint64_t>(4 * lane + j);
+          sm.above_cnt = above;
+        }
+        above += h;
+      }
+    }
+    __syncthreads();
+    prefix |= sm.digit << shift;
+    pmask |= 0xffull << shift;
+    remaining -= sm.above_cnt;
+    __syncthreads();
+  }
+  *need = static_cast<int>(remaining);
+  return prefix;
+}
+
+// Emit, in ascending index order, every i with key > T and the first `need`
+// indices with key == T: emit(i, position).  Returns the number emitted.
+template <class KeyFn, class EmitFn>
+__device__ int block_emit_selected(KeyFn key_of, int n, uint64_t T, int need, EmitFn emit,
+                                   SelShared& sm) {
+  const int chunk = (n + blockDim.x - 1) / blockDim.x;
+  const int lo = min(n, static_cast<int>(threadIdx.x) * chunk);
+  const int hi = min(n, lo + chunk);
+  long long eq = 0;
+  for (int i = lo; i < hi; ++i) eq += (key_of(i) == T);
+  long long tot;
+  long long eq_before = block_exclusive_scan(eq, sm.scan, &tot);
+  long long cnt = 0;
+  {
+    long long e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+      uint64_t kv = key_of(i);
+      bool s = kv > T;
+      if (kv == T) { s = e < need; ++e; }
+      cnt += s;
+    }
+  }
+  long long pos = block_exclusive_scan(cnt, sm.scan, &tot);
+  {
+    long long e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+      uint64_t kv = key_of(i);
+      bool s = kv > T;
+      if (kv == T) { s = e < need; ++e; }
+      if (s) emit(i, static_cast<int>(pos++));
+    }
+  }
+  return static_cast<int>(tot);
+}
+
+// Top k in ascending index order: emit(i, position) for each chosen i.
+template <class KeyFn, class EmitFn>
+__device__ int block_topk(KeyFn key_of, int n, int k, EmitFn emit, SelShared& sm) {
+  if (k <= 0) return 0;
+  if (k >= n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) emit(i, i);
+    return n;
+  }
+  int need = 0;
+  uint64_t T = block_topk_threshold(key_of, n, k, &need, sm);
+  return block_emit_selected(key_of, n, T, need, emit, sm);
+}
+
+// Coverage cut: with elements ordered by (key desc, index asc) and weights
+// z_of(i) >= 0, the shortest prefix whose weight sum S satisfies
+// fl64(S) >= thr.  Emits that prefix in ascending index order and returns its
+// length.  Requires thr <= fl64(sum of all weights) (sum < 2^63).
+template <class KeyFn, class ZFn, class EmitFn>
+__device__ int block_coverage_cut(KeyFn key_of, ZFn z_of, int n, double thr, EmitFn emit,
+                                  SelShared& sm) {
+  if (n <= 0 || !(thr > 0.0)) return 0;  // fl64(0) >= thr
+  uint64_t prefix = 0, pmask = 0;
+  long long before_sum = 0;  // weight of all elements ranked above the candidates
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int b = threadIdx.x; b < 256; b += blockDim.x) { sm.hist[b] = 0; sm.hsum[b] = 0; }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      uint64_t kv = key_of(i);
+      if ((kv & pmask) == prefix) {
+        const int b = static_cast<int>((kv >> shift) & 255u);
+        atomicAdd(&sm.hsum[b], static_cast<unsigned long long>(z_of(i)));
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      const int lane = threadIdx.x;
+      long long c = 0;
+      for (int j = 0; j < 4; ++j) c += static_cast<long long>(sm.hsum[4 * lane + j]);
+      long long rev = c;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        long long u = __shfl_down(rev, o, kWave);
+        if (lane + o < kWave) rev += u;
+      }
+      long long above = before_sum + (rev - c);
+      // the first bucket (from the top) whose inclusive cumulative weight reaches thr
+      for (int j = 3; j >= 0; --j) {
+        long long h = static_cast<long long>(sm.hsum[4 * lane + j]);
+        if (!(static_cast<double>(above) >= thr) && static_cast<double>(above + h) >= thr) {
+          sm.digit = static_cast<uint64_t>(4 * lane + j);
+          sm.above_sum = above;
+        }
+        above += h;
+      }
+    }
+    __syncthreads();
+    prefix |= sm.digit << shift;
+    pmask |= 0xffull << shift;
+    before_sum = sm.above_sum;
+    __syncthreads();
+  }
+  // Elements with key == prefix share one weight zT (the weight is a function
+  // of the key); take ties in index order until the cumulative weight
+  // reaches thr.
+  for (int i = threadIdx.x; i < n; i += blockDim.x)
+    if (key_of(i) == prefix) sm.tie_z = z_of(i);  // every writer stores the same value
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const long long zT = sm.tie_z;
+    int j = 1;
+    while (j < n && !(static_cast<double>(before_sum + j * zT) >= thr)) ++j;
+    sm.need = j;
+  }
+  __syncthreads();
+  const int need = sm.need;
+  return block_emit_selected(key_of, n, prefix, need, emit, sm);
+}
+
+}  // namespace cgs

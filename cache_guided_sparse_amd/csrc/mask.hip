@@ -1,0 +1,190 @@
+// Action Cache group-shared neuron mask (rMuscle §3.4 Eq. 1 and §5).
+//
+// contrib_kernel: one wavefront per neuron n.  In fixed point
+//   A[t,n] = sum_r rint(2^24 |h_ref[t,n,r]|),  B[n] = sum_j rint(2^40 w_nj^2)
+// are exact int64 sums (order-free), nrm = sqrt(fl64(B)) is correctly
+// rounded, c[t,n] = fl64(A) nrm and s[n] = fl64(sum_t A) nrm.  The kernel
+// stores the 64-bit order-preserving images of c and s and the value of s.
+//
+// mask_select_kernel: one workgroup of 1024 threads.
+//   TOPK      (§5) for every reference step t, the top K of c[t,:] joins a
+//             union; the mask is the top K of the union by s.
+//   COVERAGE  (§3.4 coverage) z_n = rint(s_n 2^-e) with e = ilogb(max s) - Q,
+//             Q = 61 - ceil(log2 ff); the mask is the shortest prefix of the
+//             (s desc, n asc) order with fl64(sum z) >= fl64(tau fl64(sum_all z)).
+// Selections are exact radix selects; ties go to the lower neuron index.
+//
+// Compiled with -ffp-contract=off: every float64 operation is separately
+// rounded.
+#include <algorithm>
+
+#include "block_select.hpp"
+#include "common.hpp"
+
+namespace cgs {
+namespace {
+
+constexpr double kTwo24 = 16777216.0;      // 2^24
+constexpr double kTwo40 = 1099511627776.0; // 2^40
+
+template <typename T>
+__global__ __launch_bounds__(256) void contrib_kernel(const float* __restrict__ h, int T_steps,
+                                                      int S, const T* __restrict__ wd, int d, int ff,
+                                                      uint64_t* __restrict__ ckey,
+                                                      uint64_t* __restrict__ skey,
+                                                      double* __restrict__ sval) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= ff) return;
+  long long b = 0;
+  const T* wr = wd + static_cast<size_t>(n) * d;
+  for (int j = lane; j < d; j += 64) {
+    const double w = static_cast<double>(Elem<T>::to_f32(wr[j]));
+    b += static_cast<long long>(rint((w * w) * kTwo40));
+  }
+  b = wave_sum(b);
+  const double nrm = __dsqrt_rn(static_cast<double>(b));
+  long long atot = 0;
+  for (int t = 0; t < T_steps; ++t) {
+    const float* hr = h + (static_cast<size_t>(t) * ff + n) * S;
+    long long a = 0;
+    for (int r = lane; r < S; r += 64)
+      a += static_cast<long long>(rint(fabs(static_cast<double>(hr[r])) * kTwo24));
+    a = wave_sum(a);
+    atot += a;
+    if (lane == 0) ckey[static_cast<size_t>(t) * ff + n] = ordered_key(static_cast<double>(a) * nrm);
+  }
+  if (lane == 0) {
+    const double sv = static_cast<double>(atot) * nrm;
+    sval[n] = sv;
+    skey[n] = ordered_key(sv);
+  }
+}
+
+struct MaskShared {
+  SelShared sel;
+  double dred[kSelThreads / kWave];
+  long long lred[kSelThreads / kWave];
+};
+
+__global__ __launch_bounds__(kSelThreads) void mask_select_kernel(
+    const uint64_t* __restrict__ ckey, const uint64_t* __restrict__ skey,
+    const double* __restrict__ sval, int T_steps, int ff, int mode, int K, double coverage,
+    int q_bits, uint32_t* __restrict__ uni, uint32_t* __restrict__ flag,
+    uint64_t* __restrict__ mask_out, int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out) {
+  __shared__ MaskShared sm;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  for (int i = tid; i < ff; i += blockDim.x) { uni[i] = 0; flag[i] = 0; }
+  __syncthreads();
+  auto emit = [&](int i, int pos) { idx_out[pos] = i; flag[i] = 1; };
+  int count = 0;
+  if (mode == CGS_MASK_TOPK) {
+    if (K > 0) {
+      for (int t = 0; t < T_steps; ++t) {
+        const uint64_t* ck = ckey + static_cast<size_t>(t) * ff;
+        block_topk([&](int i) { return ck[i]; }, ff, K, [&](int i, int) { uni[i] = 1; }, sm.sel);
+        __syncthreads();
+      }
+      count = block_topk([&](int i) { return uni[i] ? skey[i] : 0ull; }, ff, K, emit, sm.sel);
+    }
+  } else {
+    double m = 0.0;
+    for (int i = tid; i < ff; i += blockDim.x) m = fmax(m, sval[i]);
+    m = wave_max(m);
+    if (lane == 0) sm.dred[wid] = m;
+    __syncthreads();
+    double smax = 0.0;
+    for (int w = 0; w < static_cast<int>(blockDim.x / kWave); ++w) smax = fmax(smax, sm.dred[w]);
+    if (smax > 0.0) {
+      const int e = ilogb(smax) - q_bits;
+      auto z_of = [&](int i) { return static_cast<long long>(rint(ldexp(sval[i], -e))); };
+      long long zs = 0;
+      for (int i = tid; i < ff; i += blockDim.x) zs += z_of(i);
+      zs = wave_sum(zs);
+      if (lane == 0) sm.lred[wid] = zs;
+      __syncthreads();
+      long long Z = 0;
+      for (int w = 0; w < static_cast<int>(blockDim.x / kWave); ++w) Z += sm.lred[w];
+      const double thr = coverage * static_cast<double>(Z);
+      count = block_coverage_cut([&](int i) { return skey[i]; }, z_of, ff, thr, emit, sm.sel);
+    }
+  }
+  __syncthreads();
+  for (int i = count + tid; i < ff; i += blockDim.x) idx_out[i] = -1;
+  const int words = (ff + 63) / 64;
+  for (int wdx = tid; wdx < words; wdx += blockDim.x) {
+    uint64_t bits = 0;
+    for (int b = 0; b < 64 && wdx * 64 + b < ff; ++b)
+      if (flag[wdx * 64 + b]) bits |= 1ull << b;
+    mask_out[wdx] = bits;
+  }
+  if (tid == 0) *count_out = count;
+}
+
+struct MaskWs {
+  uint64_t* ckey;
+  uint64_t* skey;
+  double* sval;
+  uint32_t* uni;
+  uint32_t* flag;
+  size_t bytes;
+};
+
+MaskWs carve_mask(void* ws, int T, int ff) {
+  Carve cv(ws);
+  MaskWs m{};
+  m.ckey = cv.take<uint64_t>(static_cast<size_t>(T) * ff);
+  m.skey = cv.take<uint64_t>(ff);
+  m.sval = cv.take<double>(ff);
+  m.uni = cv.take<uint32_t>(ff);
+  m.flag = cv.take<uint32_t>(ff);
+  m.bytes = cv.bytes();
+  return m;
+}
+
+int bit_length(unsigned v) {
+  int b = 0;
+  while (v) { ++b; v >>= 1; }
+  return b;
+}
+
+}  // namespace
+}  // namespace cgs
+
+using namespace cgs;
+
+extern "C" size_t cgs_act_build_mask_workspace(int T, int S, int ff, int d) {
+  (void)S; (void)d;
+  if (T <= 0 || ff <= 0) return 0;
+  return carve_mask(nullptr, T, ff).bytes;
+}
+
+extern "C" int act_build_mask(const float* h_ref, int T, int S, const cgs_ffn* w, int mode, int K,
+                              double coverage, uint64_t* mask_out, int32_t* idx_out,
+                              int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!h_ref || !w || !w->w_down || !valid_dtype(w->dtype) || w->down_layout != CGS_DOWN_FD ||
+      !mask_out || !idx_out || !count_out)
+    return CGS_ERR_ARG;
+  if (mode != CGS_MASK_TOPK && mode != CGS_MASK_COVERAGE) return CGS_ERR_ARG;
+  const int ff = w->ff, d = w->d;
+  if (T <= 0 || S <= 0 || ff <= 0 || d <= 0 || d > 4096 || ff > 65536 ||
+      static_cast<long long>(S) * T > (1 << 14))
+    return CGS_ERR_SHAPE;
+  if (mode == CGS_MASK_TOPK && (K < 0 || K > ff)) return CGS_ERR_SHAPE;
+  if (mode == CGS_MASK_COVERAGE && !(coverage >= 0.0 && coverage <= 1.0)) return CGS_ERR_SHAPE;
+  if (!ws || ws_bytes < cgs_act_build_mask_workspace(T, S, ff, d)) return CGS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const MaskWs m = carve_mask(ws, T, ff);
+  const dim3 grid((ff + 3) / 4), block(256);
+  if (w->dtype == CGS_BF16)
+    hipLaunchKernelGGL((contrib_kernel<uint16_t>), grid, block, 0, s, h_ref, T, S,
+                       static_cast<const uint16_t*>(w->w_down), d, ff, m.ckey, m.skey, m.sval);
+  else
+    hipLaunchKernelGGL((contrib_kernel<float>), grid, block, 0, s, h_ref, T, S,
+                       static_cast<const float*>(w->w_down), d, ff, m.ckey, m.skey, m.sval);
+  if (!launch_ok()) return CGS_ERR_LAUNCH;
+  const int q_bits = 61 - bit_length(static_cast<unsigned>(ff - 1));
+  hipLaunchKernelGGL(mask_select_kernel, dim3(1), dim3(kSelThreads), 0, s, m.ckey, m.skey, m.sval,
+                     T, ff, mode, K, coverage, q_bits, m.uni, m.flag, mask_out, idx_out, count_out);
+  return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
+}

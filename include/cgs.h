@@ -1,0 +1,204 @@
+/*
+ * cgs.h — C ABI of the cache-guided selective FFN for AMD Instinct MI355X (gfx950).
+ *
+ * The method is rMuscle (Zhou, Li, Chen, Gu, "rMuscle: Robotic Muscle Memory
+ * for Efficient Vision-Language-Action Model Inference"):
+ *   - Context Cache (§4.1, Eq. 2 and Eq. 3): rank visual tokens by the drift of
+ *     their FFN input from a cached reference input, recompute the FFN only for
+ *     the top ceil(rho_p P) tokens and scatter the results into the cached
+ *     reference outputs;
+ *   - Action Cache (§3.4 Eq. 1, §4.1 Eq. 4, §5): build a group-shared neuron
+ *     mask from contribution scores, then update a dense anchor's output with
+ *     the masked neurons only, reading only their weight rows;
+ *   - reference rebuild (§4.2, asynchronous online reconstruction): a dense
+ *     prefill that expands a compact entry into per-layer FFN inputs/outputs.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller; row-major; bf16
+ *     values are passed as their uint16 bit pattern.  Nothing is freed or kept.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues kernels on it: no host synchronisation, no device allocation.
+ *     Results are valid once the stream reaches that point.
+ *   - `ws`/`ws_bytes` is a caller-owned device workspace of at least the size
+ *     returned by the matching cgs_*_workspace() query; its contents need not
+ *     be initialised and are clobbered.  Calls that run concurrently need
+ *     distinct workspaces and outputs.
+ *   - Errors that the host can see (null pointers, bad sizes, counts out of
+ *     range, unsupported dtype/layout, workspace too small) return a status
+ *     code before anything is launched.  A failed launch returns
+ *     CGS_ERR_LAUNCH.  Preconditions on device data (index lists ascending
+ *     and unique, value ranges of the fixed-point scores) are the caller's.
+ *   - Layout of an FFN: w_gate, w_up are [ff][d]; w_down is [d][ff]
+ *     (CGS_DOWN_DF, the Context Cache path and the rebuild) or neuron-major
+ *     [ff][d] (CGS_DOWN_FD, the Action Cache path, so that a neuron's down
+ *     weights are one contiguous row).
+ */
+#ifndef CGS_H
+#define CGS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CGS_OK = 0,
+  CGS_ERR_ARG = 1,          /* null pointer or invalid enum value */
+  CGS_ERR_SHAPE = 2,        /* size or count out of range */
+  CGS_ERR_WORKSPACE = 3,    /* ws too small or null while needed */
+  CGS_ERR_UNSUPPORTED = 4,  /* dtype / layout / size this build does not handle */
+  CGS_ERR_LAUNCH = 5        /* a kernel launch failed */
+} cgs_status;
+
+typedef enum { CGS_BF16 = 0, CGS_F32 = 1 } cgs_dtype;
+
+/* Token score kind: CGS_SCORE_REL_RMS is Eq. 2 of §4.1 (relative RMS drift);
+ * CGS_SCORE_COSINE ranks by cosine distance between x and x_ref instead. */
+typedef enum { CGS_SCORE_REL_RMS = 0, CGS_SCORE_COSINE = 1 } cgs_score_kind;
+
+/* Mask rule: CGS_MASK_TOPK is §5's rule (top K per step, union over the
+ * group, top K of the union by summed contribution); CGS_MASK_COVERAGE keeps
+ * the top-ranked neurons until `coverage` of the total contribution (§3.4). */
+typedef enum { CGS_MASK_TOPK = 0, CGS_MASK_COVERAGE = 1 } cgs_mask_mode;
+
+typedef enum { CGS_DOWN_DF = 0, CGS_DOWN_FD = 1 } cgs_down_layout;
+
+/* One GeGLU FFN layer: y = (gelu_tanh(x W_gate^T) * (x W_up^T)) W_down. */
+typedef struct {
+  int32_t d;            /* model width */
+  int32_t ff;           /* hidden neurons (H in §3.4) */
+  int32_t dtype;        /* cgs_dtype of weights and activations */
+  int32_t down_layout;  /* cgs_down_layout of w_down */
+  const void* w_gate;   /* [ff][d] */
+  const void* w_up;     /* [ff][d] */
+  const void* w_down;   /* [d][ff] (DF) or [ff][d] (FD) */
+} cgs_ffn;
+
+/* ---- host helpers ------------------------------------------------------ */
+
+/* ceil(rho * n) as in §4.1 (ceil(rho_p P) tokens) and §5 (K = ceil(rho_n H)),
+ * computed as ceil(rho*n - 1e-9) and clamped to [0, n]. */
+int cgs_ratio_to_count(double rho, int n);
+
+/* Static string for a cgs_status value. */
+const char* cgs_status_str(int status);
+
+/* ABI version (major*100 + minor). */
+int cgs_version(void);
+
+/* ---- Context Cache ----------------------------------------------------- */
+
+/* Workspace bytes for ctx_select with P tokens. */
+size_t cgs_ctx_select_workspace(int P, int d);
+
+/* §4.1, Eq. 2 + the selected set P_l(rho_p): score every token of x against
+ * x_ref and return the k highest-scoring token indices.
+ *   x, x_ref : [P][d] dtype, the current FFN input after RMSNorm and the
+ *              cached reference input of the same layer.
+ *   k        : number of tokens to select, 0 <= k <= P (cgs_ratio_to_count).
+ *   kind     : cgs_score_kind.
+ *   idx_out  : [k] int32, selected token indices in ascending order; ties in
+ *              score go to the lower index.
+ *   key_out  : [P] double or NULL; the score key of every token (rel-RMS:
+ *              d_p^2 in the fixed-point form below; cosine: 1 - cos|cos|).
+ * Scores are exact functions of the inputs: per-element float64 terms are
+ * rounded to int64 at 2^-24 and summed as integers, and the key is
+ * fl64(Sd) / fl64(max(Sx, E)), E = max(1, ceil(d 2^24 / 10^12)).  Requires
+ * |x|, |x_ref| <= 2^12 and d <= 4096.  P <= 65536. */
+int ctx_select(const void* x, const void* x_ref, int P, int d, int dtype, int k, int kind,
+               int32_t* idx_out, double* key_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for ctx_ffn_recompute with k selected rows. */
+size_t cgs_ctx_ffn_recompute_workspace(int k, int P, int d, int ff, int dtype);
+
+/* §4.1, Eq. 3: y_out[p] = F(x[p]) for p in idx, y_out[p] = y_ref[p] otherwise.
+ *   w      : FFN with down_layout CGS_DOWN_DF.
+ *   x      : [P][d] current FFN inputs; y_ref: [P][d] cached reference outputs.
+ *   idx    : [k] int32, ascending, unique, in [0, P) (the selected visual
+ *            tokens plus any always-recomputed rows the caller adds).
+ *   y_out  : [P][d] dtype, must not alias y_ref or x.
+ * Unselected rows are copied bit for bit.  k = 0 is a pure copy; k = P is
+ * the dense FFN.  The hidden activation is rounded to dtype before the down
+ * projection; products accumulate in fp32. */
+int ctx_ffn_recompute(const cgs_ffn* w, const void* x, const void* y_ref, const int32_t* idx,
+                      int k, int P, void* y_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Action Cache ------------------------------------------------------ */
+
+/* Workspace bytes for act_build_mask. */
+size_t cgs_act_build_mask_workspace(int T, int S, int ff, int d);
+
+/* §3.4 Eq. 1 and §5: group-shared neuron mask of one layer.
+ *   h_ref     : [T][ff][S] float, post-GeGLU activations of the group's T
+ *               reference denoising steps (S action tokens).
+ *   w         : FFN with down_layout CGS_DOWN_FD (only w_down is read).
+ *   mode      : cgs_mask_mode; K (TOPK, 0 <= K <= ff) or coverage (COVERAGE,
+ *               0 <= coverage <= 1).
+ *   mask_out  : [ceil(ff/64)] uint64; bit n%64 of word n/64 set iff n kept.
+ *   idx_out   : [ff] int32; kept neurons ascending, then -1 up to ff.
+ *   count_out : [1] int32 (device), number of kept neurons.
+ * Scores: A[t,n] = sum_r rint(2^24 |h|), B[n] = sum_j rint(2^40 w^2) (int64),
+ * nrm = sqrt(fl64(B)), c[t,n] = fl64(A) nrm, s[n] = fl64(sum_t A) nrm.
+ * TOPK: union over t of the top K of c[t,:], then the top K of the union by
+ * s (ties to the lower index).  COVERAGE: with z = rint(s 2^-e), e =
+ * ilogb(max s) - (61 - ceil(log2 ff)), the shortest prefix of neurons in
+ * (s desc, n asc) order with fl64(sum z) >= fl64(coverage fl64(sum_all z)).
+ * Requires |h| < 2^24, S*T <= 2^14, |w| < 2^5, d <= 4096, ff <= 65536. */
+int act_build_mask(const float* h_ref, int T, int S, const cgs_ffn* w, int mode, int K,
+                   double coverage, uint64_t* mask_out, int32_t* idx_out, int32_t* count_out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for act_ffn_masked with S tokens and K masked neurons. */
+size_t cgs_act_ffn_masked_workspace(int S, int K, int d, int ff);
+
+/* §4.1, Eq. 4: y = y_anchor + (h^M - h_anchor^M) W_down[M] for the mask M.
+ *   w          : FFN with down_layout CGS_DOWN_FD.
+ *   x          : [S][d] dtype, the FFN input after RMSNorm.
+ *   idx        : [K] int32 mask, ascending, unique, in [0, ff).
+ *   y_anchor   : [S][d] float or NULL (NULL = 0: a plain masked FFN).
+ *   h_anchor   : [ff][S] float or NULL (NULL = 0); only rows idx are read.
+ *   y_out      : [S][d] dtype.
+ *   y_f32_out  : [S][d] float or NULL; the same result before rounding.
+ *   h_out      : [ff][S] float or NULL; rows idx receive h^M, other rows
+ *                are not written.
+ * With idx = 0..ff-1 and NULL anchors this is the dense anchor step; its
+ * y_f32_out / h_out are the anchor state of later steps.  Only rows idx of
+ * w_gate, w_up and w_down are read.  The delta h - h_anchor is rounded to
+ * dtype before the down projection.  K = 0 gives y = y_anchor (or 0). */
+int act_ffn_masked(const cgs_ffn* w, const void* x, int S, const int32_t* idx, int K,
+                   const float* y_anchor, const float* h_anchor, void* y_out, float* y_f32_out,
+                   float* h_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Reference rebuild ------------------------------------------------- */
+
+/* Workspace bytes for ref_rebuild_dense. */
+size_t cgs_ref_rebuild_dense_workspace(int L, int P, int d, int ff, int dtype);
+
+/* §4.2, asynchronous online reconstruction: dense prefill of a compact entry.
+ *   layers    : HOST array of L FFNs (down_layout CGS_DOWN_DF), same d/ff/dtype.
+ *   r0        : [P][d] dtype, the entry's compact input (residual stream).
+ *   x_ref_out : [L][P][d] dtype, xbar_l = RMSNorm(r_l) (no learned scale,
+ *               eps 1e-6) rounded to dtype.
+ *   y_ref_out : [L][P][d] dtype, ybar_l = F_l(xbar_l).
+ * r_{l+1} = r_l + ybar_l with r kept in fp32. */
+int ref_rebuild_dense(const cgs_ffn* layers, int L, const void* r0, int P, void* x_ref_out,
+                      void* y_ref_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Inter-layer glue -------------------------------------------------- */
+
+/* Residual add and RMSNorm between FFN layers (the glue of a layer stack,
+ * not part of the selective FFN itself):
+ *   r[m] += (y ? y[m] : 0) + (bias ? bias : 0);  x_out[m] = RMSNorm(r[m]).
+ *   r     : [M][d] float, updated in place (may be NULL only if y and bias
+ *           are NULL, then x_out is normalised from r_in instead).
+ *   y     : [M][d] y_dtype or NULL; bias: [d] float or NULL.
+ *   x_out : [M][d] out_dtype or NULL.  RMSNorm eps is 1e-6, no scale. */
+int cgs_residual_rmsnorm(float* r, const void* y, int y_dtype, const float* bias, int M, int d,
+                         void* x_out, int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CGS_H */

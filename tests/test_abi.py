@@ -1,0 +1,110 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before launching anything (no GPU needed)."""
+import ctypes
+import re
+
+import numpy as np
+import pytest
+
+import cache_guided_sparse_amd as cgs
+import oracle as O
+
+
+def _declared_functions():
+    src = open(cgs.HEADER_PATH).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\**([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared_functions()
+    for n in ("ctx_select", "ctx_ffn_recompute", "act_build_mask", "act_ffn_masked",
+              "ref_rebuild_dense"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = cgs.lib()
+    names = _declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(cgs._SIGS)
+
+
+def test_ratio_to_count_matches_oracle():
+    for rho in np.linspace(0, 1, 101):
+        for n in (0, 1, 10, 64, 100, 768, 1024, 4096, 16384):
+            assert cgs.ratio_to_count(rho, n) == O.ratio_to_count(rho, n), (rho, n)
+    assert cgs.ratio_to_count(0.07, 100) == 7
+    assert cgs.ratio_to_count(2.0, 10) == 10 and cgs.ratio_to_count(-1.0, 10) == 0
+
+
+def test_status_strings_and_version():
+    L = cgs.lib()
+    assert L.cgs_status_str(0) == b"ok"
+    assert L.cgs_status_str(3) == b"workspace too small"
+    assert L.cgs_status_str(99) == b"unknown status"
+    assert L.cgs_version() >= 100
+
+
+def test_workspace_queries():
+    L = cgs.lib()
+    assert L.cgs_ctx_select_workspace(768, 2048) >= 768 * 8
+    big = L.cgs_ctx_ffn_recompute_workspace(231, 768, 2048, 16384, 0)
+    assert big >= 231 * 16384 * 2 + 231 * 2048 * 4
+    assert L.cgs_ctx_ffn_recompute_workspace(0, 768, 2048, 16384, 0) > 0
+    assert L.cgs_ctx_ffn_recompute_workspace(231, 768, 2000, 16384, 0) == 0  # unsupported d
+    assert L.cgs_act_ffn_masked_workspace(50, 1229, 1024, 4096) >= 64 * 1248 * 2
+    assert L.cgs_act_build_mask_workspace(4, 50, 4096, 1024) >= 4 * 4096 * 8
+    assert L.cgs_ref_rebuild_dense_workspace(17, 768, 2048, 16384, 0) >= 768 * 2048 * 4
+
+
+def _ffn(d=256, ff=1024, dtype=0, layout=0, null=False):
+    p = None if null else 0x1000
+    return cgs._Ffn(d, ff, dtype, layout, p, p, p)
+
+
+def test_host_validation_without_launch():
+    """Bad arguments return a status before anything reaches the GPU."""
+    L = cgs.lib()
+    buf = ctypes.c_void_p(0x1000)
+    # ctx_select: bad dtype / kind / k / d
+    assert L.ctx_select(buf, buf, 8, 16, 7, 1, 0, buf, None, buf, 1 << 20, None) == 1
+    assert L.ctx_select(buf, buf, 8, 16, 0, 1, 5, buf, None, buf, 1 << 20, None) == 1
+    assert L.ctx_select(buf, buf, 8, 16, 0, 9, 0, buf, None, buf, 1 << 20, None) == 2
+    assert L.ctx_select(buf, buf, 8, 8192, 0, 1, 0, buf, None, buf, 1 << 20, None) == 2
+    assert L.ctx_select(None, buf, 8, 16, 0, 1, 0, buf, None, buf, 1 << 20, None) == 1
+    assert L.ctx_select(buf, buf, 8, 16, 0, 1, 0, buf, None, buf, 8, None) == 3
+    assert L.ctx_select(buf, buf, 0, 16, 0, 0, 0, None, None, None, 0, None) == 0
+    # ctx_ffn_recompute: wrong layout, null weights, unsupported d, k > P, aliasing
+    w = _ffn()
+    assert L.ctx_ffn_recompute(ctypes.byref(_ffn(layout=1)), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), buf, 1 << 30, None) == 1
+    assert L.ctx_ffn_recompute(ctypes.byref(_ffn(null=True)), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), buf, 1 << 30, None) == 1
+    assert L.ctx_ffn_recompute(ctypes.byref(_ffn(d=200)), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), buf, 1 << 30, None) == 4
+    assert L.ctx_ffn_recompute(ctypes.byref(w), buf, buf, buf, 9, 8, ctypes.c_void_p(0x2000), buf, 1 << 30, None) == 2
+    assert L.ctx_ffn_recompute(ctypes.byref(w), buf, ctypes.c_void_p(0x2000), buf, 1, 8, ctypes.c_void_p(0x2000), buf, 1 << 30, None) == 1
+    assert L.ctx_ffn_recompute(ctypes.byref(w), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), buf, 16, None) == 3
+    # act_ffn_masked: wrong layout, K > ff
+    wf = _ffn(layout=1)
+    assert L.act_ffn_masked(ctypes.byref(w), buf, 4, buf, 1, None, None, buf, None, None, buf, 1 << 30, None) == 1
+    assert L.act_ffn_masked(ctypes.byref(wf), buf, 4, buf, 2000, None, None, buf, None, None, buf, 1 << 30, None) == 2
+    assert L.act_ffn_masked(ctypes.byref(wf), buf, 4, buf, 10, None, None, buf, None, None, buf, 4, None) == 3
+    # act_build_mask: bad mode, K, coverage, S*T too large
+    assert L.act_build_mask(buf, 2, 8, ctypes.byref(wf), 9, 4, 0.0, buf, buf, buf, buf, 1 << 30, None) == 1
+    assert L.act_build_mask(buf, 2, 8, ctypes.byref(wf), 0, 5000, 0.0, buf, buf, buf, buf, 1 << 30, None) == 2
+    assert L.act_build_mask(buf, 2, 8, ctypes.byref(wf), 1, 0, 1.5, buf, buf, buf, buf, 1 << 30, None) == 2
+    assert L.act_build_mask(buf, 1 << 10, 64, ctypes.byref(wf), 0, 4, 0.0, buf, buf, buf, buf, 1 << 30, None) == 2
+    # ref_rebuild_dense: mismatched layers
+    arr = (cgs._Ffn * 2)(_ffn(), _ffn(ff=2048))
+    assert L.ref_rebuild_dense(arr, 2, buf, 8, buf, buf, buf, 1 << 30, None) == 2
+    assert L.ref_rebuild_dense(arr, 0, buf, 8, buf, buf, buf, 1 << 30, None) == 2
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(cgs, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(cgs, "_lib", None)
+    with pytest.raises(cgs.CgsError):
+        cgs.lib()

@@ -1,0 +1,99 @@
+"""GPU parity of ctx_ffn_recompute (rMuscle §4.1, Eq. 3): recomputed rows within
+1e-2 x RMS of the oracle, every other row bit-identical to the cached output."""
+import numpy as np
+import pytest
+import torch
+
+import cache_guided_sparse_amd as cgs
+import oracle as O
+from cgs_inputs import ctx_layer_inputs, ffn_weights, random_bf16, rng
+from gpu_helpers import assert_close, bits, dev, ffn_dev, say, to_dev, values
+
+pytestmark = pytest.mark.gpu
+
+
+def _recompute(w, x, y_ref, idx):
+    dt = w["dtype"]
+    W = ffn_dev(w)
+    y = cgs.ctx_ffn_recompute(W, to_dev(x, dt), to_dev(y_ref, dt),
+                              torch.from_numpy(np.asarray(idx, dtype=np.int32)).to(dev()))
+    torch.cuda.synchronize()
+    return y
+
+
+def _check_full(w, x, y_ref, idx):
+    y = _recompute(w, x, y_ref, idx)
+    y_o, rec = O.ctx_ffn_recompute(w, x, y_ref, idx)
+    assert_close(values(y)[rec], y_o[rec], "recomputed rows", out=w["dtype"])
+    assert np.array_equal(bits(y)[~rec], np.asarray(y_ref)[~rec]), "copied rows differ"
+    return y
+
+
+@pytest.mark.parametrize("rho", [0.0, 0.25, 1.0])
+def test_tiny_fp32(rho):
+    say("ctx tiny fp32", rho)
+    P, d, ff = 64, 256, 1024
+    inp = ctx_layer_inputs(0, 0, P, d, 16, 1.0, 0.02, dtype="f32")
+    w = ffn_weights(0, 0, d, ff, dtype="f32")
+    y_ref = O.ffn_geglu(O.decode(inp["x_ref"], "f32"), w).astype(np.float32)
+    idx, _ = O.ctx_select(inp["x"], inp["x_ref"], O.ratio_to_count(rho, P), "f32")
+    _check_full(w, inp["x"], y_ref, idx)
+
+
+@pytest.mark.parametrize("k", [0, 1, 37, 64, 65, 129, 200, 300])
+def test_ragged_bf16(k):
+    """k spans the 64/128/256-row tiles, several M tiles and a ragged tail."""
+    say("ctx ragged", k)
+    P, d, ff = 300, 256, 512
+    w = ffn_weights(1, 0, d, ff)
+    x = random_bf16(1, 0, "x", (P, d))
+    y_ref = random_bf16(1, 0, "y_ref", (P, d))
+    idx = np.sort(rng(1, k, "perm").permutation(P)[:k]).astype(np.int32)
+    _check_full(w, x, y_ref, idx)
+
+
+def test_dense_equals_rebuild_layer():
+    """k = P is the dense FFN: equal to one rebuild layer's output at the same input."""
+    say("ctx dense vs rebuild")
+    P, d, ff = 96, 256, 512
+    w = ffn_weights(2, 0, d, ff)
+    r0 = random_bf16(2, 0, "r0", (P, d))
+    W = ffn_dev(w)
+    xo, yo = cgs.ref_rebuild_dense([W], to_dev(r0))
+    y = cgs.ctx_ffn_recompute(W, xo[0], torch.zeros_like(xo[0]),
+                              torch.arange(P, dtype=torch.int32, device=dev()))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(y), bits(yo[0]))
+
+
+@pytest.mark.parametrize("rho", [0.1, 0.3, 1.0])
+def test_full_layer_sampled(rho):
+    """One VLM layer at full size (768 x 2048, ff 16384), the configuration the
+    benchmark times; the oracle computes a sample of recomputed rows one by one
+    and every copied row is checked bit for bit."""
+    say("ctx full layer", rho)
+    P, d, ff = 768, 2048, 16384
+    inp = ctx_layer_inputs(1, 0, P, d, 231, 1.3333, 0.1752)
+    w = ffn_weights(1, 0, d, ff)
+    y_ref = random_bf16(1, 0, "y_ref", (P, d))
+    k = O.ratio_to_count(rho, P)
+    idx, _ = O.ctx_select(inp["x"], inp["x_ref"], k)
+    y = _recompute(w, inp["x"], y_ref, idx)
+    yb = bits(y)
+    rec = np.zeros(P, dtype=bool)
+    rec[idx] = True
+    assert np.array_equal(yb[~rec], y_ref[~rec])
+    sample = idx[np.linspace(0, len(idx) - 1, 12).astype(int)]
+    y_o = O.ffn_geglu(O.decode(inp["x"], "bf16")[sample], w)
+    assert_close(O.decode(yb[sample], "bf16"), y_o, "sampled recomputed rows", out="bf16")
+
+
+def test_deterministic_repeats():
+    P, d, ff = 300, 256, 512
+    w = ffn_weights(3, 0, d, ff)
+    x = random_bf16(3, 0, "x", (P, d))
+    y_ref = random_bf16(3, 0, "y_ref", (P, d))
+    idx = np.arange(0, P, 2, dtype=np.int32)
+    a = bits(_recompute(w, x, y_ref, idx))
+    b = bits(_recompute(w, x, y_ref, idx))
+    assert np.array_equal(a, b)

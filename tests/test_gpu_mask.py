@@ -1,0 +1,93 @@
+"""GPU parity of act_build_mask (rMuscle §3.4 Eq. 1, §5): mask words, index list
+and count must equal the oracle's bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import cache_guided_sparse_amd as cgs
+import oracle as O
+from cgs_inputs import ffn_weights, rng, synthetic_h_ref
+from gpu_helpers import dev, ffn_dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_mask(h, w, mode, K=0, cov=0.0):
+    W = ffn_dev(w)
+    m, idx, cnt = cgs.act_build_mask(to_dev(np.ascontiguousarray(h, dtype=np.float32), "f32"), W,
+                                     mode, K=K, coverage=cov)
+    torch.cuda.synchronize()
+    return m.cpu().numpy().view(np.uint64), idx.cpu().numpy(), int(cnt.item())
+
+
+def _check(h, w, mode, K=0, cov=0.0):
+    gm, gi, gc = _gpu_mask(h, w, mode, K, cov)
+    oi, om = O.act_build_mask(h, w, mode, K=K, coverage=cov)
+    ff = w["ff"]
+    assert gc == len(oi), f"count {gc} != {len(oi)}"
+    assert np.array_equal(gi[:gc], oi), "mask indices differ"
+    assert np.all(gi[gc:] == -1)
+    assert np.array_equal(gm, om), "mask words differ"
+    assert gm.size == (ff + 63) // 64
+    return gc
+
+
+def _setup(seed, T, ff, S, d, sigma=1.5, dtype="bf16"):
+    w = ffn_weights(seed, 0, d, ff, dtype=dtype, down_layout="fd", down_lognormal_sigma=sigma)
+    h = synthetic_h_ref(seed, 0, T, ff, S, neuron_sigma=0.5)
+    return w, h
+
+
+@pytest.mark.parametrize("T", [1, 2, 4])
+@pytest.mark.parametrize("rho", [0.0, 0.001, 0.2, 0.3, 0.5, 1.0])
+def test_topk_expert_size(T, rho):
+    """Expert of 4096 neurons, d 1024, 50 action tokens, T reference steps."""
+    say("mask topk", T, rho)
+    w, h = _setup(20, T, 4096, 50, 1024)
+    _check(h, w, "topk", K=O.ratio_to_count(rho, 4096))
+
+
+@pytest.mark.parametrize("cov", [0.0, 0.3, 0.5, 0.844, 0.99, 1.0])
+def test_coverage_expert_size(cov):
+    say("mask coverage", cov)
+    w, h = _setup(21, 4, 4096, 50, 1024)
+    n = _check(h, w, "coverage", cov=cov)
+    if cov == 0.844:
+        say("  coverage 0.844 keeps", n, "of 4096")
+
+
+@pytest.mark.parametrize("ff,d,S,T", [(1000, 128, 7, 3), (64, 128, 1, 1), (1, 128, 5, 2), (5000, 256, 33, 2)])
+def test_ragged(ff, d, S, T):
+    say("mask ragged", ff, d, S, T)
+    w, h = _setup(22, T, ff, S, d)
+    for K in sorted({0, 1, ff // 3, ff}):
+        _check(h, w, "topk", K=K)
+    for cov in (0.25, 0.844, 1.0):
+        _check(h, w, "coverage", cov=cov)
+
+
+def test_ties_and_zeros():
+    """Duplicated neurons (equal scores) and all-zero activations."""
+    say("mask ties")
+    ff, d, S, T = 512, 128, 8, 2
+    w, h = _setup(23, T, ff, S, d, sigma=0.0)
+    g = rng(23, 0, "misc")
+    src = g.integers(0, 16, ff)
+    wd = w["w_down"].copy()
+    wd[:] = wd[src]
+    w = dict(w, w_down=wd)
+    h = np.ascontiguousarray(h[:, src, :])
+    for K in (1, 7, 32, 100, 511):
+        _check(h, w, "topk", K=K)
+    for cov in (0.1, 0.5, 0.9):
+        _check(h, w, "coverage", cov=cov)
+    hz = np.zeros_like(h)
+    _check(hz, w, "topk", K=10)
+    assert _check(hz, w, "coverage", cov=0.5) == 0
+
+
+def test_fp32_weights():
+    say("mask fp32")
+    w, h = _setup(24, 2, 1024, 16, 256, dtype="f32")
+    _check(h, w, "topk", K=256)
+    _check(h, w, "coverage", cov=0.844)
