@@ -1,0 +1,389 @@
+#!/usr/bin/env python3
+"""Benchmark of the cache-guided selective FFN on one MI355X.
+
+One step is one policy-call slice of rMuscle (Zhou et al.), every row of the
+hot path once, with all inputs resident in HBM:
+  * Context Cache prefill (§4.1, Eq. 2/3): 17 VLM FFN layers, 768 visual tokens
+    (3 views x 256 patches), d 2048, ff 16384, bf16; per layer the input drift
+    score picks ceil(0.3 x 768) = 231 tokens, their FFN rows are recomputed and
+    scattered into the cached reference outputs; residual + RMSNorm between
+    layers;
+  * Action Cache denoise (§4.1, Eq. 4): action expert of 18 layers, d 1024,
+    ff 4096, 50 action tokens, 4 denoising steps in one group: step 0 is the
+    dense anchor, steps 1-3 update it with the group mask (coverage 0.844 of
+    the contribution score);
+  * group mask construction (§5) for the 18 expert layers from the reference
+    run's activations (offline on the pages, timed here);
+  * one dense rebuild of a reference entry (§4.2): the 17-layer prefill of the
+    entry 16 calls ahead, into the slot the current call just used (a
+    16-entry sliding working set).
+Prints one JSON line.  Synthetic seeded data of the pages' shapes; the
+weights are random (no trained model is involved).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Context-Cache prefill FFN ms & Action-Cache denoise FFN GB/s; % of roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+
+# workload
+P, D, FF, L_VLM, RHO_P = 768, 2048, 16384, 17, 0.3
+S, DE, FFE, L_EXP, STEPS, COVERAGE = 50, 1024, 4096, 18, 4, 0.844
+SLOTS, RING = 16, 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def site_work(site: str, k: int, K_masked: list) -> tuple:
+    """Algorithmic (flops, bytes) of one launch of a timing site."""
+    if site == "ctx.glu":
+        return 2.0 * k * D * 2 * FF, 2 * FF * D * 2 + k * D * 2 + k * FF * 2
+    if site == "ctx.down":
+        return 2.0 * k * FF * D, D * FF * 2 + k * FF * 2 + k * D * 2
+    if site == "rebuild.glu":
+        return 2.0 * P * D * 2 * FF, 2 * FF * D * 2 + P * D * 2 + P * FF * 2
+    if site == "rebuild.down":
+        return 2.0 * P * FF * D, D * FF * 2 + P * FF * 2 + P * D * 2
+    if site == "act.glu.dense":
+        return 2.0 * S * DE * 2 * FFE, 2 * FFE * DE * 2 + S * DE * 2 + FFE * S * 4
+    if site == "act.down.dense":
+        return 2.0 * S * FFE * DE, FFE * DE * 2 + S * FFE * 2 + S * DE * 4
+    if site == "act.glu.masked":
+        Km = sum(K_masked) / len(K_masked)
+        return 2.0 * S * DE * 2 * Km, 2 * Km * DE * 2 + S * DE * 2 + Km * S * 4 + 4 * Km
+    if site == "act.down.masked":
+        Km = sum(K_masked) / len(K_masked)
+        return 2.0 * S * Km * DE, Km * DE * 2 + S * Km * 2 + S * DE * 4 + 4 * Km
+    return None
+
+
+class World:
+    """Device-resident synthetic state of the benchmark."""
+
+    def __init__(self, dev, seed=1234):
+        import torch
+        import cache_guided_sparse_amd as cgs
+        self.cgs = cgs
+        self.dev = dev
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+
+        def randn(*shape, std=1.0):
+            return torch.randn(*shape, device=dev, generator=g, dtype=torch.float32) * std
+
+        bf = torch.bfloat16
+        t0 = time.time()
+        # VLM FFN layers (Context Cache path, W_down [d][ff])
+        self.vlm = [cgs.FFN(randn(FF, D, std=0.02).to(bf), randn(FF, D, std=0.02).to(bf),
+                            randn(D, FF, std=0.02).to(bf), "df") for _ in range(L_VLM)]
+        # compact entries (reference residual inputs) and current-call inputs
+        self.compact = randn(RING, P, D).to(bf)
+        sig = torch.full((RING, P, 1), 0.1752, device=dev)
+        for i in range(RING):
+            perm = torch.randperm(P, device=dev, generator=g)[: math.ceil(RHO_P * P - 1e-9)]
+            sig[i, perm] = 1.3333
+        self.current = (self.compact.float() + randn(RING, P, D) * sig).contiguous()
+        # expanded working set: SLOTS entries of (xbar, ybar) per layer
+        self.xbar = torch.empty(SLOTS, L_VLM, P, D, dtype=bf, device=dev)
+        self.ybar = torch.empty_like(self.xbar)
+        for e in range(SLOTS):
+            cgs.ref_rebuild_dense(self.vlm, self.compact[e], self.xbar[e], self.ybar[e])
+        # action expert (Action Cache path, neuron-major W_down with log-normal row scale)
+        self.exp = []
+        for _ in range(L_EXP):
+            scale = torch.exp(1.5 * randn(FFE, 1))
+            self.exp.append(cgs.FFN(randn(FFE, DE, std=0.02).to(bf), randn(FFE, DE, std=0.02).to(bf),
+                                    (randn(FFE, DE, std=0.02) * scale).to(bf), "fd"))
+        self.a0 = randn(S, DE).contiguous()
+        half = DE // 2
+        freqs = torch.exp(-math.log(10000.0) * torch.arange(half, device=dev, dtype=torch.float64) / half)
+        temb = []
+        for t in range(STEPS + 1):
+            ang = 1000.0 * (1.0 - t / STEPS) * freqs
+            temb.append(torch.cat([torch.sin(ang), torch.cos(ang)]).float())
+        self.temb0 = temb[0].contiguous()
+        self.dtemb = [(temb[t + 1] - temb[t]).contiguous() for t in range(STEPS)]
+        # buffers
+        self.k = cgs.ratio_to_count(RHO_P, P)
+        self.r = torch.empty(P, D, dtype=torch.float32, device=dev)
+        self.x = torch.empty(P, D, dtype=bf, device=dev)
+        self.y = torch.empty(P, D, dtype=bf, device=dev)
+        self.idx = torch.empty(self.k, dtype=torch.int32, device=dev)
+        self.ra = torch.empty(S, DE, dtype=torch.float32, device=dev)
+        self.xa = torch.empty(S, DE, dtype=bf, device=dev)
+        self.ya = torch.empty(S, DE, dtype=bf, device=dev)
+        self.y_anc = torch.empty(L_EXP, S, DE, dtype=torch.float32, device=dev)
+        self.h_anc = torch.empty(L_EXP, FFE, S, dtype=torch.float32, device=dev)
+        self.full = torch.arange(FFE, dtype=torch.int32, device=dev)
+        # reference denoise run (a0 perturbed, cosine ~0.95) -> h_ref -> group masks
+        self.h_ref = torch.empty(L_EXP, STEPS, FFE, S, dtype=torch.float32, device=dev)
+        a_ref = (self.a0 + 0.33 * randn(S, DE)).contiguous()
+        self._denoise_dense(a_ref, self.h_ref)
+        self.mask_words = torch.empty(L_EXP, (FFE + 63) // 64, dtype=torch.int64, device=dev)
+        self.mask_idx = torch.empty(L_EXP, FFE, dtype=torch.int32, device=dev)
+        self.mask_cnt = torch.empty(L_EXP, 1, dtype=torch.int32, device=dev)
+        self.build_masks(self.mask_words, self.mask_idx, self.mask_cnt)
+        torch.cuda.synchronize()
+        self.K = [int(c) for c in self.mask_cnt.view(-1).tolist()]
+        self.masks = [self.mask_idx[l, : self.K[l]].contiguous() for l in range(L_EXP)]
+        # second set of outputs for the timed mask build
+        self.mw2 = torch.empty_like(self.mask_words)
+        self.mi2 = torch.empty_like(self.mask_idx)
+        self.mc2 = torch.empty_like(self.mask_cnt)
+        log(f"setup {time.time() - t0:.1f}s; masked neurons per layer {min(self.K)}..{max(self.K)} "
+            f"of {FFE} (mean {sum(self.K) / len(self.K) / FFE:.3f})")
+
+    def _denoise_dense(self, a, h_store):
+        cgs = self.cgs
+        cgs.residual_rmsnorm(self.ra, r_in=a, bias=self.temb0, x_out=self.xa)
+        for t in range(STEPS):
+            for l in range(L_EXP):
+                cgs.act_ffn_masked(self.exp[l], self.xa, self.full, y_out=self.ya, h_out=h_store[l, t])
+                cgs.residual_rmsnorm(self.ra, y=self.ya, bias=self.dtemb[t] if l == L_EXP - 1 else None,
+                                     x_out=self.xa)
+
+    def build_masks(self, words, idx, cnt):
+        for l in range(L_EXP):
+            self.cgs.act_build_mask(self.h_ref[l], self.exp[l], "coverage", coverage=COVERAGE,
+                                    mask_out=words[l], idx_out=idx[l], count_out=cnt[l])
+
+    # --- one policy call -------------------------------------------------------
+    def ctx_prefill(self, i):
+        cgs = self.cgs
+        e = i % SLOTS
+        cgs.residual_rmsnorm(self.r, r_in=self.current[i % RING], x_out=self.x)
+        for l in range(L_VLM):
+            cgs.ctx_select(self.x, self.xbar[e, l], self.k, idx_out=self.idx)
+            cgs.ctx_ffn_recompute(self.vlm[l], self.x, self.ybar[e, l], self.idx, y_out=self.y)
+            cgs.residual_rmsnorm(self.r, y=self.y, x_out=self.x if l + 1 < L_VLM else None)
+
+    def act_anchor(self):
+        cgs = self.cgs
+        cgs.residual_rmsnorm(self.ra, r_in=self.a0, bias=self.temb0, x_out=self.xa)
+        for l in range(L_EXP):
+            cgs.act_ffn_masked(self.exp[l], self.xa, self.full, y_out=self.ya,
+                               y_f32_out=self.y_anc[l], h_out=self.h_anc[l])
+            cgs.residual_rmsnorm(self.ra, y=self.ya, bias=self.dtemb[0] if l == L_EXP - 1 else None,
+                                 x_out=self.xa)
+
+    def act_masked(self):
+        cgs = self.cgs
+        for t in range(1, STEPS):
+            for l in range(L_EXP):
+                cgs.act_ffn_masked(self.exp[l], self.xa, self.masks[l], y_anchor=self.y_anc[l],
+                                   h_anchor=self.h_anc[l], y_out=self.ya)
+                cgs.residual_rmsnorm(self.ra, y=self.ya,
+                                     bias=self.dtemb[t] if l == L_EXP - 1 else None, x_out=self.xa)
+
+    def rebuild(self, i):
+        e = i % SLOTS
+        self.cgs.ref_rebuild_dense(self.vlm, self.compact[(i + SLOTS) % RING], self.xbar[e], self.ybar[e])
+
+
+def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
+    """The oracle, timed on the host cores over a bounded sample of the step:
+    one context layer (select + recompute of 231 rows), one dense anchor
+    layer, one masked layer, one mask build and one dense rebuild layer, each
+    timed `reps` times (mean), scaled to the step's 17 / 18 / 54 / 18 / 17
+    layer counts."""
+    import numpy as np
+    import oracle as O
+    from cgs_inputs import act_tokens, ctx_layer_inputs, ffn_weights, random_bf16, synthetic_h_ref
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=None)
+    except Exception:
+        pass
+    cores = threads or len(os.sched_getaffinity(0))
+    w = ffn_weights(7, 0, D, FF)
+    inp = ctx_layer_inputs(7, 0, P, D, 231, 1.3333, 0.1752)
+    y_ref = random_bf16(7, 0, "y_ref", (P, D))
+    we = ffn_weights(7, 1, DE, FFE, down_layout="fd", down_lognormal_sigma=1.5)
+    t_ = act_tokens(7, 1, S, DE, noise_sigma=0.33)
+    h = synthetic_h_ref(7, 1, STEPS, FFE, S)
+    r0 = random_bf16(7, 0, "r0", (P, D))
+    k = O.ratio_to_count(RHO_P, P)
+    m = np.sort(np.random.default_rng(0).permutation(FFE)[:k_masked_mean]).astype(np.int32)
+    tm = {"ctx_layer": 0.0, "anchor_layer": 0.0, "masked_layer": 0.0, "mask_layer": 0.0,
+          "rebuild_layer": 0.0}
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        idx, _ = O.ctx_select(inp["x"], inp["x_ref"], k)
+        O.ctx_ffn_recompute(w, inp["x"], y_ref, idx)
+        tm["ctx_layer"] += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        ya, ha = O.act_ffn_masked(we, t_["x_pert"], np.arange(FFE))
+        tm["anchor_layer"] += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.act_ffn_masked(we, t_["x"], m, ya.astype(np.float32), ha.astype(np.float32))
+        tm["masked_layer"] += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.act_build_mask(h, we, "coverage", coverage=COVERAGE)
+        tm["mask_layer"] += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.rebuild_dense([w], r0)
+        tm["rebuild_layer"] += time.perf_counter() - t0
+    total = sum(tm.values())
+    tm = {k_: v / reps for k_, v in tm.items()}
+    per_step = (L_VLM * tm["ctx_layer"] + L_EXP * tm["anchor_layer"]
+                + (STEPS - 1) * L_EXP * tm["masked_layer"] + L_EXP * tm["mask_layer"]
+                + L_VLM * tm["rebuild_layer"])
+    return {"value": round(per_step * 1e3, 1), "unit": "ms", "cores": cores, "kind": "oracle",
+            "sample": (f"one layer of each row, timed {reps} times on the host (mean) and scaled to the step: "
+                       "17 x (ctx select + 231-row recompute) + 18 x dense anchor + 54 x masked "
+                       "+ 18 x mask build + 17 x dense rebuild layer; NumPy float64"),
+            "sample_seconds": round(total, 2),
+            "per_layer_ms": {k_: round(v * 1e3, 2) for k_, v in tm.items()}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this workload runs on a single MI355X "
+              "(see the sharding notes); rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("steps must be >= 1 and warmup >= 0")
+
+    import torch
+    import cache_guided_sparse_amd as cgs
+    cgs.lib()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    w = World(dev)
+
+    phases = ["ctx_prefill", "act_anchor", "act_masked", "mask_build", "rebuild"]
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        w.ctx_prefill(i)
+        if ev is not None:
+            ev[1].record()
+        w.act_anchor()
+        if ev is not None:
+            ev[2].record()
+        w.act_masked()
+        if ev is not None:
+            ev[3].record()
+        w.build_masks(w.mw2, w.mi2, w.mc2)
+        if ev is not None:
+            ev[4].record()
+        w.rebuild(i)
+        if ev is not None:
+            ev[5].record()
+
+    # warmup; the first half also times every kernel site to find the dominant one
+    n_prof = max(1, args.warmup // 2)
+    cgs.profile_start("", 800 * n_prof + 64)
+    for i in range(n_prof):
+        step(i)
+    cgs.profile_stop()
+    torch.cuda.synchronize()
+    sites = {}
+    for s in ("ctx.score", "ctx.topk", "ctx.glu", "ctx.down", "ctx.finish", "rebuild.norm",
+              "rebuild.glu", "rebuild.down", "rebuild.finish", "act.glu.dense", "act.down.dense",
+              "act.glu.masked", "act.down.masked", "act.finish", "mask.contrib", "mask.select",
+              "glue.rmsnorm"):
+        t, n = cgs.profile_result(s)
+        if n:
+            sites[s] = {"launches_per_step": n / n_prof, "mean_us": round(1e3 * t / n, 2),
+                        "ms_per_step": round(t / n_prof, 4)}
+    dom = max((s for s in sites if site_work(s, w.k, w.K)), key=lambda s: sites[s]["ms_per_step"])
+    for i in range(n_prof, args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, the dominant kernel bracketed by HIP events
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    cgs.profile_start(dom, args.steps * 64 + 64)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        step(args.warmup + j, evs[j])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    cgs.profile_stop()
+    dom_ms, dom_n = cgs.profile_result(dom)
+    ms_per_step = 1e3 * elapsed / args.steps
+    ph = {p: sum(evs[j][q].elapsed_time(evs[j][q + 1]) for j in range(args.steps)) / args.steps
+          for q, p in enumerate(phases)}
+
+    flops, byts = site_work(dom, w.k, w.K)
+    dom_s = dom_ms / 1e3 / dom_n
+    mfma = flops / byts > RIDGE
+    achieved = (flops / dom_s / 1e12) if mfma else (byts / dom_s / 1e9)
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBPS
+    roofline = {"bound": "mfma" if mfma else "hbm", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s" if mfma else "GB/s", "frac": round(achieved / peak, 4),
+                "traffic": None, "kernel": dom, "mean_us": round(dom_s * 1e6, 2),
+                "launches": dom_n, "flops_per_launch": flops, "bytes_per_launch": byts}
+
+    # Action Cache masked step: algorithmic bytes over its measured time (FFN + glue)
+    Km = w.K
+    masked_bytes = sum(K * DE * 2 * 3 + S * DE * 2 + S * DE * 4 + K * S * 4 + S * DE * 2 + K * 4
+                       for K in Km)
+    masked_step_ms = ph["act_masked"] / (STEPS - 1)
+    k_ffn_ms = (sites.get("act.glu.masked", {}).get("ms_per_step", 0)
+                + sites.get("act.down.masked", {}).get("ms_per_step", 0)
+                + sites.get("act.finish", {}).get("ms_per_step", 0) * (STEPS - 1) / STEPS) / (STEPS - 1)
+    ctx_flops = L_VLM * (2.0 * w.k * D * 2 * FF + 2.0 * w.k * FF * D)
+    ctx_bytes = L_VLM * (3 * FF * D * 2 + 2 * w.k * D * 2 + w.k * FF * 4 + 2 * P * D * 2)
+    ctx_roof_ms = 1e3 * max(ctx_flops / (PEAK_BF16_TFLOPS * 1e12), ctx_bytes / (PEAK_HBM_GBPS * 1e9))
+    out = {
+        "metric": METRIC, "value": round(ms_per_step, 4), "unit": "ms", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": ("policy-call slice: 17-layer Context Cache prefill (768 tokens, d 2048, "
+                                "ff 16384, rho_p 0.3) + 4-step Action Cache denoise (18 layers, d 1024, "
+                                "ff 4096, 50 tokens, coverage 0.844, anchor step 0) + group mask build "
+                                "+ one 17-layer dense entry rebuild; 16-entry working set"),
+                   "tokens": P, "rho_p": RHO_P, "k": w.k, "coverage": COVERAGE,
+                   "masked_neurons_mean": round(sum(Km) / len(Km), 1)},
+        "roofline": roofline,
+        "breakdown_ms": {p: round(v, 4) for p, v in ph.items()},
+        "ctx_prefill": {"ms": round(ph["ctx_prefill"], 4), "tflops": round(ctx_flops / ph["ctx_prefill"] / 1e9, 1),
+                        "roofline_ms": round(ctx_roof_ms, 4),
+                        "frac_of_roofline": round(ctx_roof_ms / ph["ctx_prefill"], 4),
+                        "mfma_frac": round(ctx_flops / ph["ctx_prefill"] / 1e9 / PEAK_BF16_TFLOPS, 4)},
+        "act_masked_step": {"ms": round(masked_step_ms, 4), "bytes": masked_bytes,
+                            "GBps": round(masked_bytes / masked_step_ms / 1e6, 1),
+                            "hbm_frac": round(masked_bytes / masked_step_ms / 1e6 / PEAK_HBM_GBPS, 4),
+                            "ffn_kernels_ms": round(k_ffn_ms, 4),
+                            "note": "18 masked layers incl. residual/RMSNorm glue; MALL-warm"},
+        "rebuild_ms_per_entry": round(ph["rebuild"], 4),
+        "kernel_sites": sites,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        out["cpu_baseline"] = cpu_baseline(int(round(sum(Km) / len(Km))))
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

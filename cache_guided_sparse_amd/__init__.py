@@ -57,7 +57,11 @@ _SIGS = {
     "act_ffn_masked": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cgs_ref_rebuild_dense_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "ref_rebuild_dense": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
-    "cgs_residual_rmsnorm": (_i, [_vp, _vp, _i, _vp, _i, _i, _vp, _i, _vp]),
+    "cgs_residual_rmsnorm": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _vp, _i, _vp]),
+    "cgs_profile_start": (_i, [ctypes.c_char_p, _i]),
+    "cgs_profile_stop": (_i, []),
+    "cgs_profile_result": (_i, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_int)]),
 }
 
 
@@ -230,11 +234,30 @@ def ref_rebuild_dense(layers, r0, x_ref_out=None, y_ref_out=None, ws=None, strea
     return x_ref_out, y_ref_out
 
 
-def residual_rmsnorm(r, y=None, bias=None, x_out=None, stream=None):
-    """r += y + bias (in place, fp32); x_out = RMSNorm(r) (eps 1e-6, no scale)."""
+def residual_rmsnorm(r, y=None, bias=None, x_out=None, r_in=None, stream=None):
+    """r = (r_in or r) + y + bias (fp32); x_out = RMSNorm(r) (eps 1e-6, no scale)."""
     M, d = r.shape
     ydt = _dtype_code(y) if y is not None else CGS_BF16
     odt = _dtype_code(x_out) if x_out is not None else CGS_BF16
-    _check(lib().cgs_residual_rmsnorm(_ptr(r), _ptr(y), ydt, _ptr(bias), M, d, _ptr(x_out), odt,
-                                      _stream(stream)), "cgs_residual_rmsnorm")
+    _check(lib().cgs_residual_rmsnorm(_ptr(r), _ptr(r_in), _ptr(y), ydt, _ptr(bias), M, d,
+                                      _ptr(x_out), odt, _stream(stream)), "cgs_residual_rmsnorm")
     return x_out
+
+
+def profile_start(site_filter: str, max_launches: int = 4096):
+    """Time every launch whose site name contains site_filter with HIP events."""
+    _check(lib().cgs_profile_start(site_filter.encode(), int(max_launches)), "cgs_profile_start")
+
+
+def profile_stop():
+    _check(lib().cgs_profile_stop(), "cgs_profile_stop")
+
+
+def profile_result(site: str | None = None):
+    """(summed kernel milliseconds, launches) of the recorded launches whose site
+    contains ``site`` (None = all)."""
+    t = ctypes.c_double(0.0)
+    n = ctypes.c_int(0)
+    _check(lib().cgs_profile_result(None if site is None else site.encode(), ctypes.byref(t),
+                                    ctypes.byref(n)), "cgs_profile_result")
+    return t.value, n.value

@@ -21,6 +21,7 @@
 
 #include "common.hpp"
 #include "mfma.hpp"
+#include "profile.hpp"
 
 namespace cgs {
 namespace {
@@ -219,10 +220,14 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
   T* D = cv.take<T>(p.d_elems);
   float* part = cv.take<float>(std::max<size_t>(p.part_elems, 1));
   if (K > 0) {
+    {
+    ProfScope ps(K == w.ff ? "act.glu.dense" : "act.glu.masked", s);
     hipLaunchKernelGGL((masked_glu_kernel<T>), dim3(p.K_pad / kNB, p.S_pad / kTok), dim3(kThreads), 0, s,
                        x, S, w.d, idx, K, p.K_pad, static_cast<const T*>(w.w_gate),
                        static_cast<const T*>(w.w_up), ha, h_out, D);
+    }
     if (!launch_ok()) return CGS_ERR_LAUNCH;
+    ProfScope ps(K == w.ff ? "act.down.dense" : "act.down.masked", s);
     hipLaunchKernelGGL((masked_down_kernel<T>), dim3(w.d / kCols, p.splits, p.S_pad / kTok), dim3(kThreads),
                        0, s, D, S, p.K_pad, idx, K, static_cast<const T*>(w.w_down), w.d,
                        p.steps_per_split, part);
@@ -230,6 +235,7 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
   }
   const size_t n = static_cast<size_t>(S) * w.d;
   const int blocks = static_cast<int>(std::min<size_t>((n + kThreads - 1) / kThreads, 1024));
+  ProfScope ps("act.finish", s);
   hipLaunchKernelGGL((masked_finish_kernel<T>), dim3(blocks), dim3(kThreads), 0, s, part,
                      K > 0 ? p.splits : 0, S, w.d, ya, y_out, y_f32);
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;

@@ -28,6 +28,7 @@
 
 #include "common.hpp"
 #include "mfma.hpp"
+#include "profile.hpp"
 
 namespace cgs {
 namespace {
@@ -55,7 +56,7 @@ template <typename T> struct GemmArgs {
   size_t split_stride;
 };
 
-template <typename T, int BM, bool GLU>
+template <typename T, int BM, bool GLU, bool GATHER>
 __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(GemmArgs<T> g) {
   constexpr int E = 16 / sizeof(T);        // elements per 16-byte chunk
   constexpr int BK = 128 / sizeof(T);      // elements per K tile
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(GemmArgs<T> g) {
   for (int i = 0; i < A_CH; ++i) {
     const int r = (tid + kThreads * i) / 8;
     const int m = m0 + r;
-    a_src[i] = (m < g.M) ? (g.a_rows ? g.a_rows[m] : m) : -1;
+    a_src[i] = (m < g.M) ? (GATHER ? g.a_rows[m] : m) : -1;
   }
   const T* b_src[B_CH];
 #pragma unroll
@@ -304,30 +305,32 @@ FfnPlan plan_ffn(int M, int d, int ff, int dtype) {
   return p;
 }
 
-template <typename T, int BM, bool GLU>
-void launch_gemm_bm(const GemmArgs<T>& g, hipStream_t s) {
+template <typename T, int BM, bool GLU, bool GATHER>
+void launch_gemm_bm(const GemmArgs<T>& g, const char* site, hipStream_t s) {
   const int nb = g.n_tiles * g.m_tiles * g.splits;
-  hipLaunchKernelGGL((ffn_gemm_kernel<T, BM, GLU>), dim3(nb), dim3(kThreads), 0, s, g);
+  ProfScope ps(site, s);
+  hipLaunchKernelGGL((ffn_gemm_kernel<T, BM, GLU, GATHER>), dim3(nb), dim3(kThreads), 0, s, g);
 }
 
-template <typename T, bool GLU>
-void launch_gemm(int bm, const GemmArgs<T>& g, hipStream_t s) {
-  if (bm == 64) launch_gemm_bm<T, 64, GLU>(g, s);
-  else if (bm == 128) launch_gemm_bm<T, 128, GLU>(g, s);
-  else launch_gemm_bm<T, 256, GLU>(g, s);
+template <typename T, bool GLU, bool GATHER>
+void launch_gemm(int bm, const GemmArgs<T>& g, const char* site, hipStream_t s) {
+  if (bm == 64) launch_gemm_bm<T, 64, GLU, GATHER>(g, site, s);
+  else if (bm == 128) launch_gemm_bm<T, 128, GLU, GATHER>(g, site, s);
+  else launch_gemm_bm<T, 256, GLU, GATHER>(g, site, s);
 }
 
 // Gate/up + GeGLU then split-K down for M rows (gathered through a_rows).
 template <typename T>
 void launch_ffn_core(const cgs_ffn& w, const T* A, const int32_t* a_rows, int M, const FfnPlan& p,
-                     T* H, float* part, hipStream_t s) {
+                     T* H, float* part, const char* glu_site, const char* down_site, hipStream_t s) {
   GemmArgs<T> g{};
   g.A = A; g.lda = w.d; g.a_rows = a_rows; g.M = M;
   g.B0 = static_cast<const T*>(w.w_gate); g.B1 = static_cast<const T*>(w.w_up); g.ldb = w.d;
   g.K = w.d; g.k_per_split = w.d;
   g.n_tiles = p.glu_ntiles; g.m_tiles = p.m_tiles; g.splits = 1;
   g.H = H; g.ldh = w.ff;
-  launch_gemm<T, true>(p.bm, g, s);
+  if (a_rows) launch_gemm<T, true, true>(p.bm, g, glu_site, s);
+  else launch_gemm<T, true, false>(p.bm, g, glu_site, s);
 
   GemmArgs<T> q{};
   q.A = H; q.lda = w.ff; q.a_rows = nullptr; q.M = M;
@@ -335,7 +338,7 @@ void launch_ffn_core(const cgs_ffn& w, const T* A, const int32_t* a_rows, int M,
   q.K = w.ff; q.k_per_split = p.k_per_split;
   q.n_tiles = p.down_ntiles; q.m_tiles = p.m_tiles; q.splits = p.splits;
   q.C = part; q.ldc = w.d; q.split_stride = static_cast<size_t>(M) * w.d;
-  launch_gemm<T, false>(p.bm, q, s);
+  launch_gemm<T, false, false>(p.bm, q, down_site, s);
 }
 
 bool ffn_ok(const cgs_ffn* w, int layout) {
@@ -351,11 +354,14 @@ int ctx_recompute_t(const cgs_ffn& w, const T* x, const T* y_ref, const int32_t*
   T* H = cv.take<T>(p.h_elems);
   float* part = cv.take<float>(p.part_elems);
   if (k > 0) {
-    launch_ffn_core<T>(w, x, idx, k, p, H, part, s);
+    launch_ffn_core<T>(w, x, idx, k, p, H, part, "ctx.glu", "ctx.down", s);
     if (!launch_ok()) return CGS_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kThreads), 0, s, part, p.splits,
-                     static_cast<size_t>(k) * w.d, w.d, true, idx, k, y_ref, y_out, nullptr, nullptr);
+  {
+    ProfScope ps("ctx.finish", s);
+    hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kThreads), 0, s, part, p.splits,
+                       static_cast<size_t>(k) * w.d, w.d, true, idx, k, y_ref, y_out, nullptr, nullptr);
+  }
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
 }
 
@@ -368,11 +374,16 @@ int rebuild_t(const cgs_ffn* layers, int L, const T* r0, int P, T* xo, T* yo, vo
   T* H = cv.take<T>(p.h_elems);
   float* part = cv.take<float>(p.part_elems);
   const size_t lay = static_cast<size_t>(P) * w0.d;
-  hipLaunchKernelGGL((residual_rmsnorm_kernel<T, T, T>), dim3(P), dim3(kThreads), 0, s, r0, r,
-                     static_cast<const T*>(nullptr), static_cast<const float*>(nullptr), w0.d, xo);
+  {
+    ProfScope ps("rebuild.norm", s);
+    hipLaunchKernelGGL((residual_rmsnorm_kernel<T, T, T>), dim3(P), dim3(kThreads), 0, s, r0, r,
+                       static_cast<const T*>(nullptr), static_cast<const float*>(nullptr), w0.d, xo);
+  }
   if (!launch_ok()) return CGS_ERR_LAUNCH;
   for (int l = 0; l < L; ++l) {
-    launch_ffn_core<T>(layers[l], xo + l * lay, nullptr, P, p, H, part, s);
+    launch_ffn_core<T>(layers[l], xo + l * lay, nullptr, P, p, H, part, "rebuild.glu",
+                       "rebuild.down", s);
+    ProfScope ps("rebuild.finish", s);
     hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kThreads), 0, s, part, p.splits, lay,
                        w0.d, false, static_cast<const int32_t*>(nullptr), P, static_cast<const T*>(nullptr),
                        yo + l * lay, r, (l + 1 < L) ? xo + (l + 1) * lay : static_cast<T*>(nullptr));
@@ -448,26 +459,27 @@ extern "C" int ref_rebuild_dense(const cgs_ffn* layers, int L, const void* r0, i
                           static_cast<float*>(y_ref_out), ws, s);
 }
 
-extern "C" int cgs_residual_rmsnorm(float* r, const void* y, int y_dtype, const float* bias, int M,
-                                    int d, void* x_out, int out_dtype, void* stream) {
+extern "C" int cgs_residual_rmsnorm(float* r, const float* r_in, const void* y, int y_dtype,
+                                    const float* bias, int M, int d, void* x_out, int out_dtype,
+                                    void* stream) {
   if (!r || (y && !valid_dtype(y_dtype)) || (x_out && !valid_dtype(out_dtype))) return CGS_ERR_ARG;
   if (M < 0 || d <= 0) return CGS_ERR_SHAPE;
   if (M == 0) return CGS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const float* nf = nullptr;
   const dim3 grid(M), block(kThreads);
+  ProfScope ps("glue.rmsnorm", s);
   if (y_dtype == CGS_BF16 || !y) {
     auto* yy = static_cast<const uint16_t*>(y);
     if (out_dtype == CGS_BF16)
-      hipLaunchKernelGGL((residual_rmsnorm_kernel<float, uint16_t, uint16_t>), grid, block, 0, s, nf, r, yy, bias, d, static_cast<uint16_t*>(x_out));
+      hipLaunchKernelGGL((residual_rmsnorm_kernel<float, uint16_t, uint16_t>), grid, block, 0, s, r_in, r, yy, bias, d, static_cast<uint16_t*>(x_out));
     else
-      hipLaunchKernelGGL((residual_rmsnorm_kernel<float, uint16_t, float>), grid, block, 0, s, nf, r, yy, bias, d, static_cast<float*>(x_out));
+      hipLaunchKernelGGL((residual_rmsnorm_kernel<float, uint16_t, float>), grid, block, 0, s, r_in, r, yy, bias, d, static_cast<float*>(x_out));
   } else {
     auto* yy = static_cast<const float*>(y);
     if (out_dtype == CGS_BF16)
-      hipLaunchKernelGGL((residual_rmsnorm_kernel<float, float, uint16_t>), grid, block, 0, s, nf, r, yy, bias, d, static_cast<uint16_t*>(x_out));
+      hipLaunchKernelGGL((residual_rmsnorm_kernel<float, float, uint16_t>), grid, block, 0, s, r_in, r, yy, bias, d, static_cast<uint16_t*>(x_out));
     else
-      hipLaunchKernelGGL((residual_rmsnorm_kernel<float, float, float>), grid, block, 0, s, nf, r, yy, bias, d, static_cast<float*>(x_out));
+      hipLaunchKernelGGL((residual_rmsnorm_kernel<float, float, float>), grid, block, 0, s, r_in, r, yy, bias, d, static_cast<float*>(x_out));
   }
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
 }

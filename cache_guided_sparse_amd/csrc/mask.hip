@@ -20,6 +20,7 @@
 
 #include "block_select.hpp"
 #include "common.hpp"
+#include "profile.hpp"
 
 namespace cgs {
 namespace {
@@ -176,14 +177,18 @@ extern "C" int act_build_mask(const float* h_ref, int T, int S, const cgs_ffn* w
   hipStream_t s = static_cast<hipStream_t>(stream);
   const MaskWs m = carve_mask(ws, T, ff);
   const dim3 grid((ff + 3) / 4), block(256);
+  {
+  ProfScope ps("mask.contrib", s);
   if (w->dtype == CGS_BF16)
     hipLaunchKernelGGL((contrib_kernel<uint16_t>), grid, block, 0, s, h_ref, T, S,
                        static_cast<const uint16_t*>(w->w_down), d, ff, m.ckey, m.skey, m.sval);
   else
     hipLaunchKernelGGL((contrib_kernel<float>), grid, block, 0, s, h_ref, T, S,
                        static_cast<const float*>(w->w_down), d, ff, m.ckey, m.skey, m.sval);
+  }
   if (!launch_ok()) return CGS_ERR_LAUNCH;
   const int q_bits = 61 - bit_length(static_cast<unsigned>(ff - 1));
+  ProfScope ps("mask.select", s);
   hipLaunchKernelGGL(mask_select_kernel, dim3(1), dim3(kSelThreads), 0, s, m.ckey, m.skey, m.sval,
                      T, ff, mode, K, coverage, q_bits, m.uni, m.flag, mask_out, idx_out, count_out);
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;

@@ -14,6 +14,7 @@
 // operation below is a separate, correctly rounded IEEE operation.
 #include "block_select.hpp"
 #include "common.hpp"
+#include "profile.hpp"
 
 namespace cgs {
 namespace {
@@ -135,6 +136,8 @@ extern "C" int ctx_select(const void* x, const void* x_ref, int P, int d, int dt
   const bool vec = (d % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(x_ref) % 16 == 0) && ((static_cast<size_t>(d) * eb) % 16 == 0);
   const dim3 grid((P + 3) / 4), block(256);
+  {
+  ProfScope ps("ctx.score", s);
   if (dtype == CGS_BF16) {
     auto* a = static_cast<const uint16_t*>(x);
     auto* b = static_cast<const uint16_t*>(x_ref);
@@ -150,8 +153,10 @@ extern "C" int ctx_select(const void* x, const void* x_ref, int P, int d, int dt
     else
       hipLaunchKernelGGL((score_kernel<float, false>), grid, block, 0, s, a, b, P, d, floor_e, okeys, key_out, vec);
   }
+  }
   if (!launch_ok()) return CGS_ERR_LAUNCH;
   if (k > 0) {
+    ProfScope ps("ctx.topk", s);
     hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(kSelThreads), 0, s, okeys, P, k, idx_out);
     if (!launch_ok()) return CGS_ERR_LAUNCH;
   }

@@ -190,13 +190,37 @@ int ref_rebuild_dense(const cgs_ffn* layers, int L, const void* r0, int P, void*
 
 /* Residual add and RMSNorm between FFN layers (the glue of a layer stack,
  * not part of the selective FFN itself):
- *   r[m] += (y ? y[m] : 0) + (bias ? bias : 0);  x_out[m] = RMSNorm(r[m]).
- *   r     : [M][d] float, updated in place (may be NULL only if y and bias
- *           are NULL, then x_out is normalised from r_in instead).
+ *   r[m] = (r_in ? r_in[m] : r[m]) + (y ? y[m] : 0) + (bias ? bias : 0);
+ *   x_out[m] = RMSNorm(r[m]) (eps 1e-6, no learned scale).
+ *   r     : [M][d] float, written (read too when r_in is NULL); required.
+ *   r_in  : [M][d] float or NULL, a separate source for the residual.
  *   y     : [M][d] y_dtype or NULL; bias: [d] float or NULL.
- *   x_out : [M][d] out_dtype or NULL.  RMSNorm eps is 1e-6, no scale. */
-int cgs_residual_rmsnorm(float* r, const void* y, int y_dtype, const float* bias, int M, int d,
-                         void* x_out, int out_dtype, void* stream);
+ *   x_out : [M][d] out_dtype or NULL. */
+int cgs_residual_rmsnorm(float* r, const float* r_in, const void* y, int y_dtype,
+                         const float* bias, int M, int d, void* x_out, int out_dtype,
+                         void* stream);
+
+/* ---- Kernel timing (benchmarks) ----------------------------------------- */
+
+/* Start timing every kernel launch whose site name contains `site_filter`
+ * ("" = all).  Site names: "ctx.score", "ctx.topk", "ctx.glu", "ctx.down",
+ * "ctx.finish", "rebuild.norm", "rebuild.glu", "rebuild.down",
+ * "rebuild.finish", "act.glu.dense", "act.glu.masked", "act.down.dense",
+ * "act.down.masked", "act.finish", "mask.contrib", "mask.select",
+ * "glue.rmsnorm".  Each matching launch is bracketed by two HIP events
+ * recorded on its stream; at most max_launches are kept, later ones are
+ * counted as overflow.  Process-wide host state: start, launch and query
+ * from one thread, and not while a stream is being captured. */
+int cgs_profile_start(const char* site_filter, int max_launches);
+
+/* Stop recording (the recorded launches stay queryable). */
+int cgs_profile_stop(void);
+
+/* Wait for the recorded events of the launches whose site contains `site`
+ * (NULL = all) and return their summed kernel time in milliseconds and their
+ * number.  Returns CGS_ERR_SHAPE if launches overflowed the buffer (the sums
+ * cover the kept ones). */
+int cgs_profile_result(const char* site, double* total_ms, int* launches);
 
 #ifdef __cplusplus
 }
