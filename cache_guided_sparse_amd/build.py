@@ -19,7 +19,7 @@ SOURCES = ["select.hip", "ffn.hip", "act.hip", "mask.hip", "api.cpp", "profile.c
 FLAGS = [
     "-O3", "-fPIC", "-std=c++17", "--offload-arch=gfx950", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-Wno-inline-asm",
 ]
 
 

@@ -3,217 +3,135 @@
 //   ctx_ffn_recompute  rMuscle §4.1, Eq. 3: recompute the FFN for the
 //                      selected rows only and scatter them into a copy of the
 //                      cached reference outputs.
-//   ref_rebuild_dense  §4.2: dense prefill of a compact entry into per-layer
-//                      reference inputs/outputs.
+//   ref_rebuild_dense  §4.2 (asynchronous online reconstruction): dense
+//                      prefill of a compact entry into per-layer reference
+//                      inputs and outputs.
 //   cgs_residual_rmsnorm  residual add + RMSNorm glue between layers.
 //
-// One GEMM kernel serves both projections.  Both operands are K-contiguous
-// (x rows / h rows against weight rows), so a wavefront's MFMA fragments are
-// 16-byte vectors straight out of LDS:
-//   * gate/up (GLU mode): a workgroup owns 64 neurons; its B tile stacks their
-//     64 gate rows over their 64 up rows, so each wave holds the gate and up
-//     accumulators of the same (row, neuron) in the same lane and applies
-//     gelu_tanh(g) * u in registers before one rounded store of h;
-//   * down: split-K over ff, fp32 partials, reduced in a fixed order by the
-//     row-finish kernel, which also scatters into the output (selected rows)
-//     or copies the reference bits (unselected rows), or adds the residual
-//     and normalises the next layer's input (rebuild).
-// A rows can be gathered through an index list (the selected tokens), so the
-// selected rows are never copied into a compact buffer.  Tiles are K-steps of
-// 128 bytes staged through LDS with a padded 144-byte row pitch (conflict-free
-// 16-byte fragment reads), double-buffered through registers.  Workgroups are
-// renumbered so that consecutive logical tiles, which share A and B slices,
-// land on the same XCD (hardware deals workgroups round-robin over 8 XCDs).
+// Both projections run on the GEMM core of gemm.hpp (LDS-DMA pipelined bf16
+// MFMA).  Gate/up fuses gelu_tanh(g) * u into its epilogue and stores h
+// rounded to the activation type; the down projection splits K (ff) and
+// writes fp32 partials, which the row-finish kernel sums in a fixed split
+// order.  The finish scatters the selected rows into the output and copies
+// the reference bits of the others (Context Cache), or adds the residual and
+// normalises the next layer's input (rebuild).  Selected rows are gathered
+// straight from x through the index list, never copied.
+//
+// Tile choice by the number of rows M (the selected tokens k, or P for the
+// rebuild), all with 8 waves except the smallest:
+//   M <= 64   64 x 128, 4 waves, 4 LDS stages
+//   M <= 128  128 x 128, 4 stages
+//   M <= 256  256 x 128, 3 stages (the 231-row Context Cache layer: one M tile,
+//             ff/64 = 256 workgroups stream every weight row once)
+//   M > 256   192 x 256, 2 stages (bf16 with d % 256 == 0: the 768-row rebuild
+//             is 4 x 128 gate/up tiles and 4 x 8 x 8 down tiles, two and one
+//             rounds of 256 workgroups); else 256 x 128.
 #include <algorithm>
 
 #include "common.hpp"
-#include "mfma.hpp"
+#include "gemm.hpp"
 #include "profile.hpp"
 
 namespace cgs {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kPitch = 144;  // LDS bytes per 128-byte tile row
-constexpr int kBRows = 128;  // B rows per tile
-constexpr int kXcds = 8;
+constexpr int kRowThreads = 256;
 
-template <typename T> struct GemmArgs {
-  const T* A;              // [*][lda]; row r of the tile is a_rows[m0+r] or m0+r
-  int lda;
-  const int32_t* a_rows;   // gather list (NULL = identity)
-  int M;                   // rows of the problem
-  const T* B0;             // GLU: gate [ff][ldb]; else W [N][ldb]
-  const T* B1;             // GLU: up [ff][ldb]
-  int ldb;
-  int K;
-  int k_per_split;
-  int n_tiles, m_tiles, splits;
-  T* H;                    // GLU output [M][ldh]
-  int ldh;
-  float* C;                // partial output [splits][M][ldc]
-  int ldc;
-  size_t split_stride;
-};
+// Tile configurations <BM, WM, WN, NT, STAGES> (BN = 16 NT WN).
+using CfgS = GemmCfg<64, 2, 2, 4, 4>;    //  64 x 128, 4 waves
+using CfgM = GemmCfg<128, 4, 2, 4, 4>;   // 128 x 128, 8 waves
+using CfgL = GemmCfg<256, 4, 2, 4, 3>;   // 256 x 128, 8 waves
+using CfgX = GemmCfg<192, 2, 4, 4, 2>;   // 192 x 256, 8 waves
+enum TileId { kTileS = 0, kTileM = 1, kTileL = 2, kTileX = 3 };
 
-template <typename T, int BM, bool GLU, bool GATHER>
-__global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(GemmArgs<T> g) {
-  constexpr int E = 16 / sizeof(T);        // elements per 16-byte chunk
-  constexpr int BK = 128 / sizeof(T);      // elements per K tile
-  constexpr int KS = BK / 32;              // 32-wide MFMA K steps per tile (bf16: 2, f32: 1)
-  constexpr int MT = BM / 32;              // 16-row MFMA tiles per wave (2x2 waves)
-  constexpr int A_CH = BM * 8 / kThreads;  // 16-byte A chunks per thread per tile
-  constexpr int B_CH = kBRows * 8 / kThreads;
-  constexpr int STAGE = (BM + kBRows) * kPitch;
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+template <typename Cfg, typename T, bool GLU, bool GATHER>
+void launch_cfg(const GemmArgs<T>& g, const char* site, hipStream_t s) {
+  ProfScope ps(site, s);
+  hipLaunchKernelGGL((gemm_kernel<T, Cfg::kBM, Cfg::kWM, Cfg::kWN, Cfg::kNT, Cfg::kStages, GLU, GATHER>),
+                     dim3(g.n_tiles * g.m_tiles * g.splits), dim3(Cfg::kThreads), 0, s, g);
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // XCD-aware renumbering of the workgroup
-  const int nb = g.n_tiles * g.m_tiles * g.splits;
-  int logical = blockIdx.x;
-  if (nb % kXcds == 0) logical = (blockIdx.x % kXcds) * (nb / kXcds) + blockIdx.x / kXcds;
-  const int mtile = logical % g.m_tiles;
-  const int ntile = (logical / g.m_tiles) % g.n_tiles;
-  const int split = logical / (g.m_tiles * g.n_tiles);
-  const int m0 = mtile * BM;
-  const int k_begin = split * g.k_per_split;
-  const int k_end = min(g.K, k_begin + g.k_per_split);
-  const int nk = (k_end - k_begin) / BK;
-
-  // Source rows for this thread's A chunks (-1: past M, zero-filled)
-  int a_src[A_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int r = (tid + kThreads * i) / 8;
-    const int m = m0 + r;
-    a_src[i] = (m < g.M) ? (GATHER ? g.a_rows[m] : m) : -1;
-  }
-  const T* b_src[B_CH];
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int r = (tid + kThreads * i) / 8;
-    if (GLU) {
-      const int n = ntile * 64 + (r & 63);
-      b_src[i] = (r < 64 ? g.B0 : g.B1) + static_cast<size_t>(n) * g.ldb;
-    } else {
-      b_src[i] = g.B0 + static_cast<size_t>(ntile * kBRows + r) * g.ldb;
-    }
-  }
-  const int chunk = tid & 7;
-
-  f32x4_t acc[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  int brow[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
-    brow[nt] = GLU ? ((nt < 2) ? wn * 32 + nt * 16 : 64 + wn * 32 + (nt - 2) * 16) : wn * 64 + nt * 16;
-
-  u32x4_t ra[A_CH], rb[B_CH];
-  // global -> registers for K tile kt
-#define CGS_LOAD_TILE(kt)                                                                      \
-  {                                                                                            \
-    const int k0_ = k_begin + (kt) * BK + chunk * E;                                           \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) ra[i] =                                   \
-        a_src[i] >= 0 ? *reinterpret_cast<const u32x4_t*>(g.A + static_cast<size_t>(a_src[i]) * \
-                                                             g.lda + k0_)                      \
-                      : u32x4_t{0u, 0u, 0u, 0u};                                               \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[i] =                                   \
-        *reinterpret_cast<const u32x4_t*>(b_src[i] + k0_);                                     \
-  }
-  // registers -> LDS stage buf
-#define CGS_STORE_TILE(buf)                                                                    \
-  {                                                                                            \
-    char* as_ = lds + (buf) * STAGE;                                                           \
-    char* bs_ = as_ + BM * kPitch;                                                             \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4_t*>(              \
-        as_ + ((tid + kThreads * i) / 8) * kPitch + chunk * 16) = ra[i];                       \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) *reinterpret_cast<u32x4_t*>(              \
-        bs_ + ((tid + kThreads * i) / 8) * kPitch + chunk * 16) = rb[i];                       \
-  }
-  if (nk > 0) {
-    CGS_LOAD_TILE(0);
-    CGS_STORE_TILE(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) CGS_LOAD_TILE(kt + 1);
-    const char* as = lds + (kt & 1) * STAGE;
-    const char* bs = as + BM * kPitch;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int off = ks * 32 * static_cast<int>(sizeof(T)) + (lane >> 4) * Frag<T>::kBytes;
-      Frag<T> af[MT], bfr[4];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        af[mt].load(as + (wm * (BM / 2) + mt * 16 + (lane & 15)) * kPitch + off);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) bfr[nt].load(bs + (brow[nt] + (lane & 15)) * kPitch + off);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mma(af[mt], bfr[nt], acc[mt][nt]);
-    }
-    if (kt + 1 < nk) CGS_STORE_TILE((kt + 1) & 1);
-    __syncthreads();
-  }
-#undef CGS_LOAD_TILE
-#undef CGS_STORE_TILE
-
-  // Epilogue
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = m0 + wm * (BM / 2) + mt * 16 + 4 * (lane >> 4) + v;
-      if (row >= g.M) continue;
-      if (GLU) {
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int col = ntile * 64 + wn * 32 + nt * 16 + (lane & 15);
-          const float h = gelu_tanh(acc[mt][nt][v]) * acc[mt][nt + 2][v];
-          g.H[static_cast<size_t>(row) * g.ldh + col] = Elem<T>::from_f32(h);
-        }
-      } else {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int col = ntile * kBRows + wn * 64 + nt * 16 + (lane & 15);
-          g.C[split * g.split_stride + static_cast<size_t>(row) * g.ldc + col] = acc[mt][nt][v];
-        }
-      }
-    }
+template <typename T, bool GLU, bool GATHER>
+void launch_tile(int tile, const GemmArgs<T>& g, const char* site, hipStream_t s) {
+  switch (tile) {
+    case kTileS: launch_cfg<CfgS, T, GLU, GATHER>(g, site, s); break;
+    case kTileM: launch_cfg<CfgM, T, GLU, GATHER>(g, site, s); break;
+    case kTileL: launch_cfg<CfgL, T, GLU, GATHER>(g, site, s); break;
+    default:
+      if constexpr (sizeof(T) == 2) launch_cfg<CfgX, T, GLU, GATHER>(g, site, s);
+      break;
   }
 }
 
-// Block-wide float sum (256 threads).
-__device__ __forceinline__ float block_sum256(float v, float* red) {
+// Eight consecutive elements of a row as fp32 (16 bytes of bf16, 32 of fp32).
+template <typename T> struct Vec8Io;
+template <> struct Vec8Io<uint16_t> {
+  static __device__ __forceinline__ void load(const uint16_t* p, float* v) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const float* v) {
+    u32x4_t u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    *reinterpret_cast<u32x4_t*>(p) = u;
+  }
+  static __device__ __forceinline__ void round(float* v) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32(f32_to_bf16(v[i]));
+  }
+  static __device__ __forceinline__ void copy(const uint16_t* src, uint16_t* dst) {
+    *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+  }
+};
+template <> struct Vec8Io<float> {
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0], b = reinterpret_cast<const f32x4_t*>(p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+    reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+  }
+  static __device__ __forceinline__ void round(float*) {}
+  static __device__ __forceinline__ void copy(const float* src, float* dst) {
+    reinterpret_cast<f32x4_t*>(dst)[0] = reinterpret_cast<const f32x4_t*>(src)[0];
+    reinterpret_cast<f32x4_t*>(dst)[1] = reinterpret_cast<const f32x4_t*>(src)[1];
+  }
+};
+
+// Block-wide float sum (kRowThreads threads).
+__device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
-  const float t = red[0] + red[1] + red[2] + red[3];
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < kRowThreads / 64; ++w) t += red[w];
   __syncthreads();
   return t;
 }
 
-// One workgroup per output row p.
-//   selected (p in idx[0..k) when scatter, every row otherwise): y_out[p] = round(sum over splits of
-//     the partials of row i, in split order); optionally r[p] += y_out[p] and
-//     x_next[p] = RMSNorm(r[p]).
+// One workgroup per output row p; each thread owns runs of 8 elements.
+//   selected (p = idx[i] when scattering, every row otherwise): y_out[p] =
+//     round(sum over splits of the partials of row i, in split order);
+//     optionally r[p] += y_out[p] and x_next[p] = RMSNorm(r[p]);
 //   unselected: y_out[p] = y_ref[p], bit for bit.
+// The selected position of p is found by a binary search over the ascending
+// index list (wave-uniform loads).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void row_finish_kernel(
+__global__ __launch_bounds__(kRowThreads) void row_finish_kernel(
     const float* __restrict__ part, int splits, size_t split_stride, int d, bool scatter,
     const int32_t* __restrict__ idx, int k, const T* __restrict__ y_ref, T* __restrict__ y_out,
     float* __restrict__ resid, T* __restrict__ x_next) {
-  __shared__ float red[4];
+  __shared__ float red[kRowThreads / 64];
   const int p = blockIdx.x;
   int i = p;
   bool sel = true;
@@ -221,63 +139,92 @@ __global__ __launch_bounds__(kThreads) void row_finish_kernel(
     int lo = 0, hi = k;  // first position with idx[pos] >= p
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (idx[mid] < p) lo = mid + 1; else hi = mid;
+      if (__builtin_amdgcn_readfirstlane(idx[mid]) < p) lo = mid + 1; else hi = mid;
     }
     i = lo;
     sel = (lo < k) && (idx[lo] == p);
   }
   const size_t ro = static_cast<size_t>(p) * d;
   if (!sel) {
-    for (int c = threadIdx.x; c < d; c += kThreads) y_out[ro + c] = y_ref[ro + c];
+    for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) Vec8Io<T>::copy(y_ref + ro + c, y_out + ro + c);
     return;
   }
   const size_t io = static_cast<size_t>(i) * d;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += kThreads) {
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += part[s * split_stride + io + c];
-    const T yb = Elem<T>::from_f32(v);
-    y_out[ro + c] = yb;
+  for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) {
+    float v[8], t[8];
+    Vec8Io<float>::load(part + io + c, v);
+    for (int sp = 1; sp < splits; ++sp) {
+      Vec8Io<float>::load(part + sp * split_stride + io + c, t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += t[e];
+    }
+    Vec8Io<T>::store(y_out + ro + c, v);
     if (resid) {
-      const float r = resid[ro + c] + Elem<T>::to_f32(yb);
-      resid[ro + c] = r;
-      ss += r * r;
+      Vec8Io<T>::round(v);
+      float r[8];
+      Vec8Io<float>::load(resid + ro + c, r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { r[e] += v[e]; ss += r[e] * r[e]; }
+      Vec8Io<float>::store(resid + ro + c, r);
     }
   }
   if (resid && x_next) {
-    const float tot = block_sum256(ss, red);
+    const float tot = block_sum(ss, red);
     const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + 1e-6f);
-    for (int c = threadIdx.x; c < d; c += kThreads) x_next[ro + c] = Elem<T>::from_f32(resid[ro + c] * inv);
+    for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) {
+      float r[8];
+      Vec8Io<float>::load(resid + ro + c, r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] *= inv;
+      Vec8Io<T>::store(x_next + ro + c, r);
+    }
   }
 }
 
 // r[m] = (r_src ? decode(r_src[m]) : r[m]) + (y ? decode(y[m]) : 0) + (bias ? bias : 0);
 // x_out[m] = RMSNorm(r[m]).  One workgroup per row.
 template <typename TS, typename TY, typename TO>
-__global__ __launch_bounds__(kThreads) void residual_rmsnorm_kernel(
+__global__ __launch_bounds__(kRowThreads) void residual_rmsnorm_kernel(
     const TS* __restrict__ r_src, float* __restrict__ r, const TY* __restrict__ y,
     const float* __restrict__ bias, int d, TO* __restrict__ x_out) {
-  __shared__ float red[4];
+  __shared__ float red[kRowThreads / 64];
   const size_t ro = static_cast<size_t>(blockIdx.x) * d;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < d; c += kThreads) {
-    float v = r_src ? Elem<TS>::to_f32(r_src[ro + c]) : r[ro + c];
-    if (y) v += Elem<TY>::to_f32(y[ro + c]);
-    if (bias) v += bias[c];
-    r[ro + c] = v;
-    ss += v * v;
+  for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) {
+    float v[8], t[8];
+    if (r_src) Vec8Io<TS>::load(r_src + ro + c, v); else Vec8Io<float>::load(r + ro + c, v);
+    if (y) {
+      Vec8Io<TY>::load(y + ro + c, t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += t[e];
+    }
+    if (bias) {
+      Vec8Io<float>::load(bias + c, t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += t[e];
+    }
+    Vec8Io<float>::store(r + ro + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
   }
   if (!x_out) return;
-  const float tot = block_sum256(ss, red);
+  const float tot = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + 1e-6f);
-  for (int c = threadIdx.x; c < d; c += kThreads) x_out[ro + c] = Elem<TO>::from_f32(r[ro + c] * inv);
+  for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) {
+    float v[8];
+    Vec8Io<float>::load(r + ro + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= inv;
+    Vec8Io<TO>::store(x_out + ro + c, v);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Host planning
 // ---------------------------------------------------------------------------
 struct FfnPlan {
-  int bm, m_tiles, glu_ntiles, down_ntiles, splits, k_per_split;
+  int tile, bm, bn, m_tiles, glu_ntiles, down_ntiles, splits, k_per_split;
   size_t h_elems, part_elems;
 };
 
@@ -289,13 +236,18 @@ bool ffn_shape_ok(int d, int ff, int dtype) {
 FfnPlan plan_ffn(int M, int d, int ff, int dtype) {
   FfnPlan p{};
   const int bk = 128 / elem_bytes(dtype);
-  p.bm = M <= 64 ? 64 : (M <= 128 ? 128 : 256);
+  if (M <= 64) { p.tile = kTileS; p.bm = CfgS::kBM; p.bn = CfgS::kBN; }
+  else if (M <= 128) { p.tile = kTileM; p.bm = CfgM::kBM; p.bn = CfgM::kBN; }
+  else if (M <= 256 || dtype != CGS_BF16 || d % CfgX::kBN != 0 || ff % (CfgX::kBN / 2) != 0) {
+    p.tile = kTileL; p.bm = CfgL::kBM; p.bn = CfgL::kBN;
+  } else { p.tile = kTileX; p.bm = CfgX::kBM; p.bn = CfgX::kBN; }
   p.m_tiles = std::max(1, (M + p.bm - 1) / p.bm);
-  p.glu_ntiles = ff / 64;
-  p.down_ntiles = d / kBRows;
+  p.glu_ntiles = ff / (p.bn / 2);
+  p.down_ntiles = d / p.bn;
+  // split K of the down projection so that about 256 workgroups run
   const int base = p.down_ntiles * p.m_tiles;
   const int max_splits = std::max(1, ff / (8 * bk));
-  int splits = std::min(max_splits, std::max(1, (256 + base - 1) / base));
+  const int splits = std::min(max_splits, std::max(1, (256 + base - 1) / base));
   const int kt = ff / bk;                                 // K tiles in total
   const int tiles_per = (kt + splits - 1) / splits;
   p.k_per_split = tiles_per * bk;
@@ -303,20 +255,6 @@ FfnPlan plan_ffn(int M, int d, int ff, int dtype) {
   p.h_elems = static_cast<size_t>(M) * ff;
   p.part_elems = static_cast<size_t>(p.splits) * M * d;
   return p;
-}
-
-template <typename T, int BM, bool GLU, bool GATHER>
-void launch_gemm_bm(const GemmArgs<T>& g, const char* site, hipStream_t s) {
-  const int nb = g.n_tiles * g.m_tiles * g.splits;
-  ProfScope ps(site, s);
-  hipLaunchKernelGGL((ffn_gemm_kernel<T, BM, GLU, GATHER>), dim3(nb), dim3(kThreads), 0, s, g);
-}
-
-template <typename T, bool GLU, bool GATHER>
-void launch_gemm(int bm, const GemmArgs<T>& g, const char* site, hipStream_t s) {
-  if (bm == 64) launch_gemm_bm<T, 64, GLU, GATHER>(g, site, s);
-  else if (bm == 128) launch_gemm_bm<T, 128, GLU, GATHER>(g, site, s);
-  else launch_gemm_bm<T, 256, GLU, GATHER>(g, site, s);
 }
 
 // Gate/up + GeGLU then split-K down for M rows (gathered through a_rows).
@@ -329,8 +267,8 @@ void launch_ffn_core(const cgs_ffn& w, const T* A, const int32_t* a_rows, int M,
   g.K = w.d; g.k_per_split = w.d;
   g.n_tiles = p.glu_ntiles; g.m_tiles = p.m_tiles; g.splits = 1;
   g.H = H; g.ldh = w.ff;
-  if (a_rows) launch_gemm<T, true, true>(p.bm, g, glu_site, s);
-  else launch_gemm<T, true, false>(p.bm, g, glu_site, s);
+  if (a_rows) launch_tile<T, true, true>(p.tile, g, glu_site, s);
+  else launch_tile<T, true, false>(p.tile, g, glu_site, s);
 
   GemmArgs<T> q{};
   q.A = H; q.lda = w.ff; q.a_rows = nullptr; q.M = M;
@@ -338,7 +276,7 @@ void launch_ffn_core(const cgs_ffn& w, const T* A, const int32_t* a_rows, int M,
   q.K = w.ff; q.k_per_split = p.k_per_split;
   q.n_tiles = p.down_ntiles; q.m_tiles = p.m_tiles; q.splits = p.splits;
   q.C = part; q.ldc = w.d; q.split_stride = static_cast<size_t>(M) * w.d;
-  launch_gemm<T, false, false>(p.bm, q, down_site, s);
+  launch_tile<T, false, false>(p.tile, q, down_site, s);
 }
 
 bool ffn_ok(const cgs_ffn* w, int layout) {
@@ -359,7 +297,7 @@ int ctx_recompute_t(const cgs_ffn& w, const T* x, const T* y_ref, const int32_t*
   }
   {
     ProfScope ps("ctx.finish", s);
-    hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kThreads), 0, s, part, p.splits,
+    hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kRowThreads), 0, s, part, p.splits,
                        static_cast<size_t>(k) * w.d, w.d, true, idx, k, y_ref, y_out, nullptr, nullptr);
   }
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
@@ -376,7 +314,7 @@ int rebuild_t(const cgs_ffn* layers, int L, const T* r0, int P, T* xo, T* yo, vo
   const size_t lay = static_cast<size_t>(P) * w0.d;
   {
     ProfScope ps("rebuild.norm", s);
-    hipLaunchKernelGGL((residual_rmsnorm_kernel<T, T, T>), dim3(P), dim3(kThreads), 0, s, r0, r,
+    hipLaunchKernelGGL((residual_rmsnorm_kernel<T, T, T>), dim3(P), dim3(kRowThreads), 0, s, r0, r,
                        static_cast<const T*>(nullptr), static_cast<const float*>(nullptr), w0.d, xo);
   }
   if (!launch_ok()) return CGS_ERR_LAUNCH;
@@ -384,7 +322,7 @@ int rebuild_t(const cgs_ffn* layers, int L, const T* r0, int P, T* xo, T* yo, vo
     launch_ffn_core<T>(layers[l], xo + l * lay, nullptr, P, p, H, part, "rebuild.glu",
                        "rebuild.down", s);
     ProfScope ps("rebuild.finish", s);
-    hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kThreads), 0, s, part, p.splits, lay,
+    hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kRowThreads), 0, s, part, p.splits, lay,
                        w0.d, false, static_cast<const int32_t*>(nullptr), P, static_cast<const T*>(nullptr),
                        yo + l * lay, r, (l + 1 < L) ? xo + (l + 1) * lay : static_cast<T*>(nullptr));
     if (!launch_ok()) return CGS_ERR_LAUNCH;
@@ -466,7 +404,8 @@ extern "C" int cgs_residual_rmsnorm(float* r, const float* r_in, const void* y, 
   if (M < 0 || d <= 0) return CGS_ERR_SHAPE;
   if (M == 0) return CGS_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(M), block(kThreads);
+  if (d % 8 != 0) return CGS_ERR_UNSUPPORTED;
+  const dim3 grid(M), block(kRowThreads);
   ProfScope ps("glue.rmsnorm", s);
   if (y_dtype == CGS_BF16 || !y) {
     auto* yy = static_cast<const uint16_t*>(y);

@@ -1,0 +1,268 @@
+// MFMA GEMM core shared by the Context Cache recompute and the dense rebuild.
+//
+// C = A B^T with both operands K-contiguous (activation rows against weight
+// rows), bf16 (or fp32) MFMA 16x16 with fp32 accumulation:
+//   * GLU mode: the B tile stacks BN/2 gate rows over the same BN/2 up rows,
+//     so a lane holds the gate and up accumulators of one (row, neuron) and
+//     the epilogue stores h = gelu_tanh(g) * u rounded once;
+//   * plain mode: fp32 partial sums of one K split, [split][M][ldc].
+// A rows may be gathered through an index list (the selected tokens).
+//
+// Data movement (gfx950): K tiles of 128 bytes per row travel global -> LDS
+// by LDS DMA (global_load_lds_dwordx4, 1 KB per wavefront instruction), a
+// STAGES-deep ring, one workgroup barrier per K tile.  A tile row is 8 chunks
+// of 16 bytes; chunk c of row r sits at physical chunk c ^ (r & 7), so the
+// 16-byte MFMA fragment reads of 8 consecutive rows fall in 8 distinct bank
+// groups.  The waves form a WM x WN grid; each owns (BM/WM) x 16 NT of the tile.
+#pragma once
+
+#include "common.hpp"
+#include "mfma.hpp"
+
+namespace cgs {
+
+constexpr int kXcds = 8;
+
+template <typename T> struct GemmArgs {
+  const T* A;              // [*][lda]; row r of the tile is a_rows[m0+r] or m0+r
+  int lda;
+  const int32_t* a_rows;   // gather list (NULL = identity)
+  int M;                   // rows of the problem
+  const T* B0;             // GLU: gate [ff][ldb]; else W [N][ldb]
+  const T* B1;             // GLU: up [ff][ldb]
+  int ldb;
+  int K;
+  int k_per_split;
+  int n_tiles, m_tiles, splits;
+  T* H;                    // GLU output [M][ldh]
+  int ldh;
+  float* C;                // partial output [splits][M][ldc]
+  int ldc;
+  size_t split_stride;
+};
+
+// LDS byte address (M0 / ds offset) of a __shared__ location.
+typedef __attribute__((address_space(3))) char lds_char_t;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char_t*)p));
+}
+
+// One 1 KB global -> LDS transfer of a wavefront: lane i copies the 16 bytes
+// at gbase + voff to LDS byte lds + 16 i.  Issued as inline assembly so that
+// the only wait for it is the explicit vmcnt of wait_vm_barrier (the compiler
+// would otherwise wait for every outstanding transfer before each LDS read).
+// Nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma_1k(uint32_t lds, const void* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's global loads are outstanding and its
+// LDS reads are done, then barrier the workgroup: a K tile whose transfers
+// every wave has waited for is visible to all, and a stage every wave has
+// finished reading may be refilled.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int STAGES, int LPW>
+__device__ __forceinline__ void wait_tile(int ahead) {
+  if constexpr (STAGES >= 4) {
+    if (ahead >= 2) { wait_vm_barrier<2 * LPW>(); return; }
+  }
+  if constexpr (STAGES >= 3) {
+    if (ahead >= 1) { wait_vm_barrier<LPW>(); return; }
+  }
+  wait_vm_barrier<0>();
+}
+
+template <int BM, int WM, int WN, int NT, int STAGES>
+struct GemmCfg {
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kBN = 16 * NT * WN;            // B rows per tile
+  static constexpr int kStage = (BM + kBN) * 128;     // LDS bytes per stage
+  static constexpr int kLds = STAGES * kStage;
+  static constexpr int kBM = BM, kWM = WM, kWN = WN, kNT = NT, kStages = STAGES;
+};
+
+template <typename T, int BM, int WM, int WN, int NT, int STAGES, bool GLU, bool GATHER>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> g) {
+  using Cfg = GemmCfg<BM, WM, WN, NT, STAGES>;
+  static_assert(!GLU || NT % 2 == 0, "GLU pairs gate and up tiles");
+  constexpr int NW = Cfg::kWaves;
+  constexpr int BN = Cfg::kBN;
+  constexpr int BK = 128 / static_cast<int>(sizeof(T));  // elements per K tile
+  constexpr int KS = BK / 32;                            // 32-wide K steps per tile
+  constexpr int FC = Frag<T>::kBytes / 16;               // 16-byte chunks per fragment
+  constexpr int WTM = BM / WM;                           // wave tile rows
+  constexpr int MT = WTM / 16;                           // MFMA row tiles per wave
+  constexpr int A_DMA = BM / 8, B_DMA = BN / 8;          // 1 KB transfers per stage
+  static_assert((A_DMA + B_DMA) % NW == 0, "transfers must split evenly over the waves");
+  constexpr int LPW = (A_DMA + B_DMA) / NW;              // transfers per wave per stage
+  constexpr int STAGE = Cfg::kStage;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::kLds];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  // Workgroups are dealt round-robin over the 8 XCDs; renumber them so that
+  // consecutive logical tiles (same B tile, neighbouring A tiles) share an XCD
+  // and its L2.
+  const int nb = g.n_tiles * g.m_tiles * g.splits;
+  int logical = blockIdx.x;
+  if (nb % kXcds == 0) logical = (blockIdx.x % kXcds) * (nb / kXcds) + blockIdx.x / kXcds;
+  const int mtile = logical % g.m_tiles;
+  const int ntile = (logical / g.m_tiles) % g.n_tiles;
+  const int split = logical / (g.m_tiles * g.n_tiles);
+  const int m0 = mtile * BM;
+  const int k_begin = split * g.k_per_split;
+  const int k_end = min(g.K, k_begin + g.k_per_split);
+  const int nk = (k_end - k_begin) / BK;
+
+  // Transfer j (0 <= j < A_DMA + B_DMA) of a stage covers tile rows 8j'..8j'+7
+  // of A (j' = j) or of B (j' = j - A_DMA); lane l fills physical chunk l & 7
+  // of row 8j' + (l >> 3) with logical chunk (l & 7) ^ (l >> 3).  Wave w owns
+  // transfers w, w + NW, w + 2 NW, ...
+  const int sub = lane >> 3;
+  const uint32_t cbyte = static_cast<uint32_t>(((lane & 7) ^ sub) * 16);
+  const uint32_t kbyte0 = static_cast<uint32_t>(k_begin) * sizeof(T);
+  uint32_t off[LPW];
+  const T* base[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int j = wave + NW * i;
+    if (j < A_DMA) {
+      int m = min(m0 + 8 * j + sub, g.M - 1);  // rows past M repeat the last row; results dropped
+      if (GATHER) m = g.a_rows[m];
+      base[i] = g.A;
+      off[i] = static_cast<uint32_t>(m) * static_cast<uint32_t>(g.lda) * sizeof(T) + kbyte0 + cbyte;
+    } else {
+      const int r8 = 8 * (j - A_DMA);  // first B tile row of the transfer (wave-uniform)
+      const int r = r8 + sub;
+      int n;
+      if (GLU) {
+        n = ntile * (BN / 2) + (r % (BN / 2));
+        base[i] = (r8 < BN / 2) ? g.B0 : g.B1;
+      } else {
+        n = ntile * BN + r;
+        base[i] = g.B0;
+      }
+      off[i] = static_cast<uint32_t>(n) * static_cast<uint32_t>(g.ldb) * sizeof(T) + kbyte0 + cbyte;
+    }
+  }
+  const uint32_t lds0 = lds_addr(lds);
+
+  auto issue = [&](int kt) {
+    const uint32_t st = lds0 + (kt % STAGES) * STAGE;
+    const uint32_t kb = static_cast<uint32_t>(kt) * 128u;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) dma_1k(st + (wave + NW * i) * 1024, base[i], off[i] + kb);
+  };
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // B tile rows of this wave's NT 16-column MFMA tiles.  GLU: NT/2 gate tiles
+  // and the NT/2 up tiles of the same 8 NT neurons.
+  int brow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    brow[nt] = GLU ? ((nt < NT / 2) ? wn * 8 * NT + nt * 16 : BN / 2 + wn * 8 * NT + (nt - NT / 2) * 16)
+                   : wn * 16 * NT + nt * 16;
+  const int arow0 = wm * WTM + (lane & 15);
+  const int swz = lane & 7;
+  const int grp = lane >> 4;
+
+  // Fragment reads of K step ks of the tile at `as`: four B tiles, MT A tiles.
+  auto load = [&](const char* as, int ks, Frag<T> (&af)[MT], Frag<T> (&bf)[NT]) {
+    const char* bs = as + BM * 128;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const char* rowp = bs + (brow[nt] + (lane & 15)) * 128;
+#pragma unroll
+      for (int q = 0; q < FC; ++q)
+        bf[nt].chunk(q) = *reinterpret_cast<const u32x4_t*>(rowp + (((ks * 4 + grp) * FC + q) ^ swz) * 16);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const char* rowp = as + (arow0 + mt * 16) * 128;
+#pragma unroll
+      for (int q = 0; q < FC; ++q)
+        af[mt].chunk(q) = *reinterpret_cast<const u32x4_t*>(rowp + (((ks * 4 + grp) * FC + q) ^ swz) * 16);
+    }
+  };
+
+  // Pipeline: tiles 0 .. STAGES-1 are in flight before the loop.  The
+  // fragments of the next K step are read before the MFMAs of the current
+  // one; at the last K step of tile t the workgroup waits for tile t+1 (all
+  // waves have then also finished reading tile t, whose stage takes tile
+  // t + STAGES).
+  if (nk > 0) {
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+      if (p < nk) issue(p);
+    wait_tile<STAGES, LPW>(min(STAGES - 2, nk - 1));
+    if (STAGES - 1 < nk) issue(STAGES - 1);
+  }
+  Frag<T> ca[MT], cb[NT];
+  if (nk > 0) load(lds, 0, ca, cb);
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* as = lds + (kt % STAGES) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      Frag<T> na[MT], nb_[NT];
+      if (ks + 1 < KS) {
+        load(as, ks + 1, na, nb_);
+      } else if (kt + 1 < nk) {
+        wait_tile<STAGES, LPW>(min(STAGES - 2, nk - 2 - kt));
+        if (kt + STAGES < nk) issue(kt + STAGES);
+        load(lds + ((kt + 1) % STAGES) * STAGE, 0, na, nb_);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mma(ca[mt], cb[nt], acc[mt][nt]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) ca[mt] = na[mt];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) cb[nt] = nb_[nt];
+    }
+  }
+
+  // Epilogue: lane holds rows 4 (lane >> 4) + v of column lane & 15 of each
+  // 16 x 16 tile.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = m0 + wm * WTM + mt * 16 + 4 * (lane >> 4) + v;
+      if (row >= g.M) continue;
+      if (GLU) {
+#pragma unroll
+        for (int nt = 0; nt < NT / 2; ++nt) {
+          const int col = ntile * (BN / 2) + wn * 8 * NT + nt * 16 + (lane & 15);
+          const float h = gelu_tanh(acc[mt][nt][v]) * acc[mt][nt + NT / 2][v];
+          g.H[static_cast<size_t>(row) * g.ldh + col] = Elem<T>::from_f32(h);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int col = ntile * BN + wn * 16 * NT + nt * 16 + (lane & 15);
+          g.C[split * g.split_stride + static_cast<size_t>(row) * g.ldc + col] = acc[mt][nt][v];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace cgs

@@ -20,6 +20,7 @@ template <> struct Frag<uint16_t> {
   static constexpr int kBytes = 16;
   __device__ __forceinline__ void load(const void* p) { u = *reinterpret_cast<const u32x4_t*>(p); }
   __device__ __forceinline__ void zero() { u = u32x4_t{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ u32x4_t& chunk(int) { return u; }
 };
 
 template <> struct Frag<float> {
@@ -30,6 +31,7 @@ template <> struct Frag<float> {
     hi = reinterpret_cast<const u32x4_t*>(p)[1];
   }
   __device__ __forceinline__ void zero() { lo = hi = u32x4_t{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ u32x4_t& chunk(int q) { return q ? hi : lo; }
 };
 
 __device__ __forceinline__ f32x4_t mma(const Frag<uint16_t>& a, const Frag<uint16_t>& b, f32x4_t c) {
@@ -47,9 +49,12 @@ __device__ __forceinline__ f32x4_t mma(const Frag<float>& a, const Frag<float>& 
   return c;
 }
 
+// GELU, tanh form (Hendrycks & Gimpel): 0.5 g (1 + tanh(z)), z = sqrt(2/pi)(g +
+// 0.044715 g^3), evaluated as g / (1 + exp(-2z)) with the hardware exp2 and
+// reciprocal (relative error ~1e-6; saturates correctly for large |g|).
 __device__ __forceinline__ float gelu_tanh(float g) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * g * (1.0f + tanhf(k0 * (g + 0.044715f * g * g * g)));
+  const float m2z = -1.5957691216057308f * (g + 0.044715f * g * g * g);  // -2z
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(m2z));
 }
 
 }  // namespace cgs
