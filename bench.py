@@ -144,6 +144,7 @@ class World:
         self.mw2 = torch.empty_like(self.mask_words)
         self.mi2 = torch.empty_like(self.mask_idx)
         self.mc2 = torch.empty_like(self.mask_cnt)
+        self.g_ctx, self.g_anchor, self.g_masked, self.g_mask = [], None, None, None
         log(f"setup {time.time() - t0:.1f}s; masked neurons per layer {min(self.K)}..{max(self.K)} "
             f"of {FFE} (mean {sum(self.K) / len(self.K) / FFE:.3f})")
 
@@ -162,36 +163,73 @@ class World:
                                     mask_out=words[l], idx_out=idx[l], count_out=cnt[l])
 
     # --- one policy call -------------------------------------------------------
-    def ctx_prefill(self, i):
+    # Between layers the residual add and the RMSNorm of the next layer's input
+    # run inside each layer's finish kernel (the ``glue`` argument).
+    def ctx_layers(self, e):
         cgs = self.cgs
-        e = i % SLOTS
-        cgs.residual_rmsnorm(self.r, r_in=self.current[i % RING], x_out=self.x)
         for l in range(L_VLM):
             cgs.ctx_select(self.x, self.xbar[e, l], self.k, idx_out=self.idx)
-            cgs.ctx_ffn_recompute(self.vlm[l], self.x, self.ybar[e, l], self.idx, y_out=self.y)
-            cgs.residual_rmsnorm(self.r, y=self.y, x_out=self.x if l + 1 < L_VLM else None)
+            cgs.ctx_ffn_recompute(self.vlm[l], self.x, self.ybar[e, l], self.idx, y_out=self.y,
+                                  glue=(self.r, None, self.x if l + 1 < L_VLM else None))
 
-    def act_anchor(self):
+    def ctx_prefill(self, i):
+        e = i % SLOTS
+        self.cgs.residual_rmsnorm(self.r, r_in=self.current[i % RING], x_out=self.x)
+        if self.g_ctx:
+            self.g_ctx[e].replay()
+        else:
+            self.ctx_layers(e)
+
+    def _anchor(self):
         cgs = self.cgs
         cgs.residual_rmsnorm(self.ra, r_in=self.a0, bias=self.temb0, x_out=self.xa)
         for l in range(L_EXP):
             cgs.act_ffn_masked(self.exp[l], self.xa, self.full, y_out=self.ya,
-                               y_f32_out=self.y_anc[l], h_out=self.h_anc[l])
-            cgs.residual_rmsnorm(self.ra, y=self.ya, bias=self.dtemb[0] if l == L_EXP - 1 else None,
-                                 x_out=self.xa)
+                               y_f32_out=self.y_anc[l], h_out=self.h_anc[l],
+                               glue=(self.ra, self.dtemb[0] if l == L_EXP - 1 else None, self.xa))
 
-    def act_masked(self):
+    def _masked(self):
         cgs = self.cgs
         for t in range(1, STEPS):
             for l in range(L_EXP):
                 cgs.act_ffn_masked(self.exp[l], self.xa, self.masks[l], y_anchor=self.y_anc[l],
-                                   h_anchor=self.h_anc[l], y_out=self.ya)
-                cgs.residual_rmsnorm(self.ra, y=self.ya,
-                                     bias=self.dtemb[t] if l == L_EXP - 1 else None, x_out=self.xa)
+                                   h_anchor=self.h_anc[l], y_out=self.ya,
+                                   glue=(self.ra, self.dtemb[t] if l == L_EXP - 1 else None, self.xa))
+
+    def _mask_build(self):
+        self.build_masks(self.mw2, self.mi2, self.mc2)
+
+    def act_anchor(self):
+        self.g_anchor.replay() if self.g_anchor else self._anchor()
+
+    def act_masked(self):
+        self.g_masked.replay() if self.g_masked else self._masked()
+
+    def mask_build(self):
+        self.g_mask.replay() if self.g_mask else self._mask_build()
 
     def rebuild(self, i):
         e = i % SLOTS
         self.cgs.ref_rebuild_dense(self.vlm, self.compact[(i + SLOTS) % RING], self.xbar[e], self.ybar[e])
+
+    def capture(self):
+        """HIP graphs of the launch-bound phases (fixed buffers): the 17 context
+        layers of each working-set slot, the anchor step, the three masked steps
+        and the mask build.  The rebuild (long kernels) and each call's first
+        RMSNorm stay eager."""
+        import torch
+        torch.cuda.synchronize()
+
+        def cap(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            return g
+        self.g_ctx = [cap(lambda e=e: self.ctx_layers(e)) for e in range(SLOTS)]
+        self.g_anchor = cap(self._anchor)
+        self.g_masked = cap(self._masked)
+        self.g_mask = cap(self._mask_build)
+        torch.cuda.synchronize()
 
 
 def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
@@ -257,6 +295,8 @@ def main():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graphs", action="store_true",
+                    help="launch every kernel eagerly instead of replaying HIP graphs")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -286,7 +326,7 @@ def main():
         w.act_masked()
         if ev is not None:
             ev[3].record()
-        w.build_masks(w.mw2, w.mi2, w.mc2)
+        w.mask_build()
         if ev is not None:
             ev[4].record()
         w.rebuild(i)
@@ -310,7 +350,9 @@ def main():
             sites[s] = {"launches_per_step": n / n_prof, "mean_us": round(1e3 * t / n, 2),
                         "ms_per_step": round(t / n_prof, 4)}
     dom = max((s for s in sites if site_work(s, w.k, w.K)), key=lambda s: sites[s]["ms_per_step"])
-    for i in range(n_prof, args.warmup):
+    if not args.no_graphs:
+        w.capture()
+    for i in range(n_prof, max(args.warmup, n_prof + 1)):
         step(i)
     torch.cuda.synchronize()
 
@@ -360,6 +402,7 @@ def main():
                                 "ff 4096, 50 tokens, coverage 0.844, anchor step 0) + group mask build "
                                 "+ one 17-layer dense entry rebuild; 16-entry working set"),
                    "tokens": P, "rho_p": RHO_P, "k": w.k, "coverage": COVERAGE,
+                   "hip_graphs": not args.no_graphs,
                    "masked_neurons_mean": round(sum(Km) / len(Km), 1)},
         "roofline": roofline,
         "breakdown_ms": {p: round(v, 4) for p, v in ph.items()},

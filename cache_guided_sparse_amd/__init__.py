@@ -35,6 +35,20 @@ class CgsError(RuntimeError):
     pass
 
 
+class _Glue(ctypes.Structure):
+    _fields_ = [("r", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("x_next", ctypes.c_void_p)]
+
+
+def _glue(glue):
+    """Optional (r, bias, x_next) residual/RMSNorm glue -> cgs_glue pointer or None."""
+    if glue is None:
+        return None
+    r, bias, x_next = glue
+    if r is None or r.dtype != torch.float32:
+        raise CgsError("glue residual r must be a float32 device tensor")
+    return ctypes.byref(_Glue(_ptr(r), _ptr(bias), _ptr(x_next)))
+
+
 class _Ffn(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("ff", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("down_layout", ctypes.c_int32), ("w_gate", ctypes.c_void_p),
@@ -50,11 +64,11 @@ _SIGS = {
     "cgs_ctx_select_workspace": (_sz, [_i, _i]),
     "ctx_select": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "cgs_ctx_ffn_recompute_workspace": (_sz, [_i, _i, _i, _i, _i]),
-    "ctx_ffn_recompute": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp]),
+    "ctx_ffn_recompute": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "cgs_act_build_mask_workspace": (_sz, [_i, _i, _i, _i]),
     "act_build_mask": (_i, [_vp, _i, _i, _vp, _i, _i, _d, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cgs_act_ffn_masked_workspace": (_sz, [_i, _i, _i, _i]),
-    "act_ffn_masked": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "act_ffn_masked": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cgs_ref_rebuild_dense_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "ref_rebuild_dense": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
     "cgs_residual_rmsnorm": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _vp, _i, _vp]),
@@ -164,8 +178,9 @@ def ctx_select(x, x_ref, k: int, kind: str = "rel_rms", idx_out=None, key_out=No
     return idx_out
 
 
-def ctx_ffn_recompute(w: FFN, x, y_ref, idx, y_out=None, ws=None, stream=None):
-    """Eq. 3: F(x) on the rows idx, the reference outputs elsewhere."""
+def ctx_ffn_recompute(w: FFN, x, y_ref, idx, y_out=None, glue=None, ws=None, stream=None):
+    """Eq. 3: F(x) on the rows idx, the reference outputs elsewhere.  ``glue`` =
+    (r, bias, x_next) applies r += y (+ bias), x_next = RMSNorm(r) per row."""
     P, d = x.shape
     k = int(idx.numel())
     if y_out is None:
@@ -174,7 +189,7 @@ def ctx_ffn_recompute(w: FFN, x, y_ref, idx, y_out=None, ws=None, stream=None):
     nbytes = lib().cgs_ctx_ffn_recompute_workspace(k, P, d, w.ff, c.dtype)
     ws = workspace(nbytes, x.device, "ctx") if ws is None else ws
     _check(lib().ctx_ffn_recompute(ctypes.byref(c), _ptr(x), _ptr(y_ref), _ptr(idx), k, P,
-                                   _ptr(y_out), _ptr(ws), ws.numel(), _stream(stream)),
+                                   _ptr(y_out), _glue(glue), _ptr(ws), ws.numel(), _stream(stream)),
            "ctx_ffn_recompute")
     return y_out
 
@@ -201,9 +216,9 @@ def act_build_mask(h_ref, w: FFN, mode: str = "topk", K: int = 0, coverage: floa
 
 
 def act_ffn_masked(w: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=None, y_f32_out=None,
-                   h_out=None, ws=None, stream=None):
+                   h_out=None, glue=None, ws=None, stream=None):
     """Eq. 4 masked update of a dense anchor (dense anchor step when idx covers
-    every neuron and no anchors are given)."""
+    every neuron and no anchors are given).  ``glue`` = (r, bias, x_next)."""
     S, d = x.shape
     K = int(idx.numel())
     if y_out is None:
@@ -213,7 +228,7 @@ def act_ffn_masked(w: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=None, y_f
     ws = workspace(nbytes, x.device, "act") if ws is None else ws
     _check(lib().act_ffn_masked(ctypes.byref(c), _ptr(x), S, _ptr(idx), K, _ptr(y_anchor),
                                 _ptr(h_anchor), _ptr(y_out), _ptr(y_f32_out), _ptr(h_out),
-                                _ptr(ws), ws.numel(), _stream(stream)), "act_ffn_masked")
+                                _glue(glue), _ptr(ws), ws.numel(), _stream(stream)), "act_ffn_masked")
     return y_out
 
 

@@ -3,99 +3,136 @@
 //
 // Only the mask's rows of W_gate, W_up and the neuron-major W_down are read;
 // each is a contiguous d-element row, so every weight access is a coalesced
-// row segment.
+// row segment.  The path is memory- and latency-bound (a masked layer of the
+// 18-layer expert moves ~7.5 MB), so every kernel puts all of its weight
+// loads in flight before it computes:
 //
-//   masked_glu_kernel  (phase 1) a workgroup owns 16 mask positions and 64
-//       tokens; its four waves split d into quarters and each computes the
-//       gate and up products of its quarter with MFMA, fragments loaded
-//       straight from global memory (x rows and gathered weight rows); the
-//       quarters are summed in LDS in a fixed order.  Fused epilogue: h, the
-//       optional h_out rows, and the anchor delta rounded to the activation
-//       type, stored token-major [S_pad][K_pad] as the next GEMM's A operand.
-//   masked_down_kernel (phase 2) a workgroup owns 64 output columns, 64
-//       tokens and a contiguous range of mask positions (split-K); it gathers
-//       32 down rows x 64 columns per step into LDS and reads them transposed
-//       as MFMA B fragments.  fp32 partials per split.
-//   masked_finish_kernel sums the partials in split order and adds y_a.
+//   act_glu_kernel    a workgroup owns 16 mask positions and TT tokens; its
+//       four waves split d into quarters.  Each wave issues all of its
+//       gathered gate/up fragments and its x fragments of a chunk at once,
+//       then runs the MFMAs; the quarters are summed in LDS in a fixed order.
+//       Epilogue: h (optionally stored to the neuron-major h_out rows) and the
+//       anchor delta h - h_a rounded to the activation type, stored
+//       token-major [S_pad][K_pad] as the next GEMM's A operand (zero past K).
+//   act_down_kernel   a workgroup owns 64 output columns, 64 tokens and a
+//       contiguous range of at most kMaxSteps x 32 mask positions (split-K).
+//       All of its gathered W_down row segments go global -> LDS by LDS DMA
+//       up front; B fragments are read transposed (column-major) out of LDS.
+//       fp32 partials per split.
+//   act_finish_kernel sums the partials in split order, adds y_a, stores y
+//       (and its fp32 value), and optionally applies the residual/RMSNorm glue.
 #include <algorithm>
 
 #include "common.hpp"
-#include "mfma.hpp"
+#include "gemm.hpp"
+#include "glue.hpp"
 #include "profile.hpp"
 
 namespace cgs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kNB = 16;      // mask positions per phase-1 workgroup
-constexpr int kTok = 64;     // tokens per workgroup (4 waves x 16)
-constexpr int kStep = 32;    // mask positions per phase-2 K step
-constexpr int kCols = 64;    // output columns per phase-2 workgroup
+constexpr int kNB = 16;        // mask positions per GLU workgroup
+constexpr int kChunk = 8;      // 32-wide K steps per load batch of a GLU wave
+constexpr int kStep = 32;      // mask positions per down K step
+constexpr int kCols = 64;      // output columns per down workgroup
+constexpr int kTokDown = 64;   // tokens per down workgroup (4 waves x 16)
+constexpr int kMaxSteps = 8;   // K steps per down workgroup (LDS: 8 x 32 rows)
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void masked_glu_kernel(
+template <typename T, int MTW>
+__global__ __launch_bounds__(kThreads) void act_glu_kernel(
     const T* __restrict__ x, int S, int d, const int32_t* __restrict__ idx, int K, int K_pad,
     const T* __restrict__ wg, const T* __restrict__ wu, const float* __restrict__ h_anchor,
     float* __restrict__ h_out, T* __restrict__ D) {
+  constexpr int TT = 16 * MTW;  // tokens per workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i0 = blockIdx.x * kNB;
-  const int s0 = blockIdx.y * kTok;
+  const int s0 = blockIdx.y * TT;
   const int r = lane & 15, grp = lane >> 4;
   const int dq = d / 4;
 
   const int i_lane = i0 + r;
   const bool nvalid = i_lane < K;
   const size_t wrow = nvalid ? static_cast<size_t>(idx[i_lane]) * d : 0;
-  const T* xrow[4];
-  bool tvalid[4];
+
+  // Epilogue elements of this thread: e = tid + 256 j -> (token e / 16, mask
+  // position e % 16).  Their neuron rows and anchor activations are fetched
+  // now, so that the wait for them overlaps the weight loads below.
+  constexpr int EPT = TT * kNB / kThreads;
+  size_t hn[EPT];
+  bool ev[EPT];
+  float ha[EPT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + kThreads * j;
+    const int i = i0 + e % kNB, sg = s0 + e / kNB;
+    ev[j] = i < K && sg < S;
+    hn[j] = ev[j] ? static_cast<size_t>(idx[i]) * S + sg : 0;
+    ha[j] = (ev[j] && h_anchor) ? h_anchor[hn[j]] : 0.f;
+  }
+  const T* xrow[MTW];
+  bool tvalid[MTW];
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt) {
     const int s = s0 + mt * 16 + r;
     tvalid[mt] = s < S;
     xrow[mt] = x + static_cast<size_t>(tvalid[mt] ? s : 0) * d;
   }
 
-  f32x4_t ag[4], au[4];
+  f32x4_t ag[MTW], au[MTW];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) ag[mt] = au[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int k = wave * dq; k < (wave + 1) * dq; k += 32) {
-    const int kk = k + grp * 8;
-    Frag<T> bg, bu;
-    if (nvalid) { bg.load(wg + wrow + kk); bu.load(wu + wrow + kk); } else { bg.zero(); bu.zero(); }
+  for (int mt = 0; mt < MTW; ++mt) ag[mt] = au[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int kb = wave * dq, ke = kb + dq;
+  for (int k0 = kb; k0 < ke; k0 += kChunk * 32) {
+    Frag<T> bg[kChunk], bu[kChunk], a[kChunk][MTW];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      Frag<T> a;
-      if (tvalid[mt]) a.load(xrow[mt] + kk); else a.zero();
-      ag[mt] = mma(a, bg, ag[mt]);
-      au[mt] = mma(a, bu, au[mt]);
+    for (int c = 0; c < kChunk; ++c) {
+      const int kk = k0 + c * 32 + grp * 8;
+      const bool kv = k0 + c * 32 < ke;
+      if (nvalid && kv) { bg[c].load(wg + wrow + kk); bu[c].load(wu + wrow + kk); }
+      else { bg[c].zero(); bu[c].zero(); }
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+        if (tvalid[mt] && kv) a[c][mt].load(xrow[mt] + kk); else a[c][mt].zero();
+      }
     }
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c)
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+        ag[mt] = mma(a[c][mt], bg[c], ag[mt]);
+        au[mt] = mma(a[c][mt], bu[c], au[mt]);
+      }
   }
   // Lane holds rows (tokens) mt*16 + 4*grp + v of column (mask position) r.
-  __shared__ float part[4][2][kTok][kNB];
+  __shared__ float part[4][2][TT][kNB];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       part[wave][0][mt * 16 + 4 * grp + v][r] = ag[mt][v];
       part[wave][1][mt * 16 + 4 * grp + v][r] = au[mt][v];
     }
   __syncthreads();
-  for (int e = tid; e < kTok * kNB; e += kThreads) {
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + kThreads * j;
     const int s = e / kNB, c = e % kNB;
     const float gsum = part[0][0][s][c] + part[1][0][s][c] + part[2][0][s][c] + part[3][0][s][c];
     const float usum = part[0][1][s][c] + part[1][1][s][c] + part[2][1][s][c] + part[3][1][s][c];
     const int i = i0 + c, sg = s0 + s;
     float delta = 0.f;
-    if (i < K && sg < S) {
-      const size_t hn = static_cast<size_t>(idx[i]) * S + sg;
+    if (ev[j]) {
       const float h = gelu_tanh(gsum) * usum;
-      if (h_out) h_out[hn] = h;
-      delta = h_anchor ? h - h_anchor[hn] : h;
+      if (h_out) h_out[hn[j]] = h;
+      delta = h - ha[j];
     }
     if (i < K_pad) D[static_cast<size_t>(sg) * K_pad + i] = Elem<T>::from_f32(delta);
   }
 }
 
+// B fragment of a 16x16x32 MFMA read column-major out of a [32 rows][pitch]
+// LDS tile: lane (col, grp) takes the 8 rows grp*8 .. grp*8+7 of its column.
 template <typename T>
 __device__ __forceinline__ void gather_b_frag(const char* tile, int pitch, int col, int grp, Frag<T>& f);
 
@@ -124,47 +161,68 @@ __device__ __forceinline__ void gather_b_frag<float>(const char* tile, int pitch
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void masked_down_kernel(
+__global__ __launch_bounds__(kThreads) void act_down_kernel(
     const T* __restrict__ D, int S, int K_pad, const int32_t* __restrict__ idx, int K,
     const T* __restrict__ wd, int d, int steps_per_split, float* __restrict__ part) {
-  constexpr int RB = kCols * sizeof(T);          // bytes of a row segment
-  constexpr int PITCH = RB + 8;                  // padded LDS pitch
-  constexpr int CH = RB / 8;                     // 8-byte chunks per row segment
-  __shared__ __attribute__((aligned(16))) char tile[kStep * PITCH];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int RB = kCols * static_cast<int>(sizeof(T));  // bytes of a row segment (128 / 256)
+  constexpr int RPD = 1024 / RB;                           // rows per 1 KB DMA transfer
+  constexpr int DPS = kStep / RPD;                         // transfers per K step
+  __shared__ __attribute__((aligned(1024))) char tile[kMaxSteps * kStep * RB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, grp = lane >> 4;
   const int j0 = blockIdx.x * kCols;
   const int split = blockIdx.y;
-  const int s0 = blockIdx.z * kTok;
+  const int s0 = blockIdx.z * kTokDown;
   const int st_begin = split * steps_per_split;
-  const int st_end = min(K_pad / kStep, st_begin + steps_per_split);
-  const int srow = s0 + wave * 16 + r;           // token row of this lane's A fragment
+  const int nst = min(K_pad / kStep, st_begin + steps_per_split) - st_begin;
+
+  // Every row segment of this workgroup's mask range, global -> LDS.  Rows
+  // past K read the last mask row (their D entries are zero).  All index
+  // loads are issued before the first transfer, so no wait for an index
+  // also waits for an earlier transfer.
+  constexpr int QMAX = kMaxSteps * DPS / 4;  // transfers per wave, at most
+  const uint32_t lds0 = lds_addr(tile);
+  const int lrow = lane / (RB / 16), lchunk = lane % (RB / 16);
+  const int nq = nst * DPS;
+  int src[QMAX];
+#pragma unroll
+  for (int t = 0; t < QMAX; ++t) {
+    const int q = wave + 4 * t;
+    const int i = min(st_begin * kStep + q * RPD + lrow, K - 1);
+    src[t] = (q < nq) ? idx[i] : 0;
+  }
+#pragma unroll
+  for (int t = 0; t < QMAX; ++t) {
+    const int q = wave + 4 * t;
+    if (q < nq)
+      dma_1k(lds0 + q * 1024, wd,
+             static_cast<uint32_t>(src[t]) * static_cast<uint32_t>(d) * sizeof(T) +
+                 static_cast<uint32_t>(j0) * sizeof(T) + lchunk * 16);
+  }
+  // A fragments (the deltas of this lane's token row) of every K step.
+  const int srow = s0 + wave * 16 + r;  // token row of this lane's A fragment
+  Frag<T> a[kMaxSteps];
+#pragma unroll
+  for (int st = 0; st < kMaxSteps; ++st) {
+    if (st < nst) a[st].load(D + static_cast<size_t>(srow) * K_pad + (st_begin + st) * kStep + grp * 8);
+    else a[st].zero();
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
   f32x4_t acc[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int st = st_begin; st < st_end; ++st) {
-    const int i0 = st * kStep;
-    for (int q = tid; q < kStep * CH; q += kThreads) {
-      const int rr = q / CH, c = q % CH;
-      u32x2_t v = u32x2_t{0u, 0u};
-      if (i0 + rr < K) {
-        const char* src = reinterpret_cast<const char*>(wd + static_cast<size_t>(idx[i0 + rr]) * d + j0);
-        v = *reinterpret_cast<const u32x2_t*>(src + c * 8);
-      }
-      *reinterpret_cast<u32x2_t*>(tile + rr * PITCH + c * 8) = v;
-    }
-    __syncthreads();
-    Frag<T> a;
-    a.load(D + static_cast<size_t>(srow) * K_pad + i0 + grp * 8);
+#pragma unroll
+  for (int st = 0; st < kMaxSteps; ++st) {
+    if (st >= nst) break;
+    const char* tl = tile + st * kStep * RB;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       Frag<T> b;
-      gather_b_frag<T>(tile, PITCH, nt * 16 + r, grp, b);
-      acc[nt] = mma(a, b, acc[nt]);
+      gather_b_frag<T>(tl, RB, nt * 16 + r, grp, b);
+      acc[nt] = mma(a[st], b, acc[nt]);
     }
-    __syncthreads();
   }
   const size_t so = static_cast<size_t>(split) * S * d;
 #pragma unroll
@@ -176,33 +234,46 @@ __global__ __launch_bounds__(kThreads) void masked_down_kernel(
     }
 }
 
+// One workgroup per token row: y = y_a + sum over splits (split order), then
+// the optional residual/RMSNorm glue on the rounded y.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void masked_finish_kernel(
+__global__ __launch_bounds__(kThreads) void act_finish_kernel(
     const float* __restrict__ part, int splits, int S, int d, const float* __restrict__ y_anchor,
-    T* __restrict__ y_out, float* __restrict__ y_f32) {
+    T* __restrict__ y_out, float* __restrict__ y_f32, GlueArgs<T> glue) {
+  __shared__ float red[kThreads / 64];
+  const int s = blockIdx.x;
+  const size_t ro = static_cast<size_t>(s) * d;
   const size_t n = static_cast<size_t>(S) * d;
-  for (size_t e = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; e < n;
-       e += static_cast<size_t>(gridDim.x) * kThreads) {
-    float v = 0.f;
-    for (int s = 0; s < splits; ++s) v += part[s * n + e];
-    if (y_anchor) v = y_anchor[e] + v;
-    if (y_f32) y_f32[e] = v;
-    y_out[e] = Elem<T>::from_f32(v);
+  float ss = 0.f;
+  for (int c = threadIdx.x * 8; c < d; c += kThreads * 8) {
+    float v[8];
+    if (y_anchor) Row8<float>::load(y_anchor + ro + c, v);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    add_splits(part + ro + c, n, splits, v);
+    if (y_f32) Row8<float>::store(y_f32 + ro + c, v);
+    Row8<T>::store(y_out + ro + c, v);
+    if (glue.r) ss += glue_add(glue, ro, c, v);
   }
+  if (glue.r && glue.x_next) glue_norm(glue, ro, d, ss, red);
 }
 
 struct ActPlan {
-  int K_pad, S_pad, splits, steps_per_split;
+  int K_pad, S_pad, tt, splits, steps_per_split;
   size_t d_elems, part_elems;
 };
 
 ActPlan plan_act(int S, int K, int d) {
   ActPlan p{};
   p.K_pad = (K + kStep - 1) / kStep * kStep;
-  p.S_pad = (S + kTok - 1) / kTok * kTok;
+  p.tt = S <= 16 ? 16 : 32;  // tokens per GLU workgroup
+  p.S_pad = (S + kTokDown - 1) / kTokDown * kTokDown;
   const int steps = p.K_pad / kStep;
-  const int base = (d / kCols) * (p.S_pad / kTok);
+  const int base = (d / kCols) * (p.S_pad / kTokDown);
   int splits = std::max(1, std::min(std::max(steps, 1), (256 + base - 1) / std::max(base, 1)));
+  splits = std::max(splits, (steps + kMaxSteps - 1) / kMaxSteps);
   p.steps_per_split = std::max(1, (steps + splits - 1) / splits);
   p.splits = steps > 0 ? (steps + p.steps_per_split - 1) / p.steps_per_split : 0;
   p.d_elems = static_cast<size_t>(p.S_pad) * p.K_pad;
@@ -214,30 +285,33 @@ bool act_shape_ok(int d, int ff) { return d > 0 && ff > 0 && d % 128 == 0; }
 
 template <typename T>
 int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const float* ya,
-          const float* ha, T* y_out, float* y_f32, float* h_out, void* ws, hipStream_t s) {
+          const float* ha, T* y_out, float* y_f32, float* h_out, const cgs_glue* gl, void* ws,
+          hipStream_t s) {
   const ActPlan p = plan_act(S, K, w.d);
   Carve cv(ws);
   T* D = cv.take<T>(p.d_elems);
   float* part = cv.take<float>(std::max<size_t>(p.part_elems, 1));
   if (K > 0) {
     {
-    ProfScope ps(K == w.ff ? "act.glu.dense" : "act.glu.masked", s);
-    hipLaunchKernelGGL((masked_glu_kernel<T>), dim3(p.K_pad / kNB, p.S_pad / kTok), dim3(kThreads), 0, s,
-                       x, S, w.d, idx, K, p.K_pad, static_cast<const T*>(w.w_gate),
-                       static_cast<const T*>(w.w_up), ha, h_out, D);
+      ProfScope ps(K == w.ff ? "act.glu.dense" : "act.glu.masked", s);
+      const dim3 grid((p.K_pad + kNB - 1) / kNB, (p.S_pad + p.tt - 1) / p.tt);
+      if (p.tt == 16)
+        hipLaunchKernelGGL((act_glu_kernel<T, 1>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K, p.K_pad,
+                           static_cast<const T*>(w.w_gate), static_cast<const T*>(w.w_up), ha, h_out, D);
+      else
+        hipLaunchKernelGGL((act_glu_kernel<T, 2>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K, p.K_pad,
+                           static_cast<const T*>(w.w_gate), static_cast<const T*>(w.w_up), ha, h_out, D);
     }
     if (!launch_ok()) return CGS_ERR_LAUNCH;
     ProfScope ps(K == w.ff ? "act.down.dense" : "act.down.masked", s);
-    hipLaunchKernelGGL((masked_down_kernel<T>), dim3(w.d / kCols, p.splits, p.S_pad / kTok), dim3(kThreads),
+    hipLaunchKernelGGL((act_down_kernel<T>), dim3(w.d / kCols, p.splits, p.S_pad / kTokDown), dim3(kThreads),
                        0, s, D, S, p.K_pad, idx, K, static_cast<const T*>(w.w_down), w.d,
                        p.steps_per_split, part);
     if (!launch_ok()) return CGS_ERR_LAUNCH;
   }
-  const size_t n = static_cast<size_t>(S) * w.d;
-  const int blocks = static_cast<int>(std::min<size_t>((n + kThreads - 1) / kThreads, 1024));
   ProfScope ps("act.finish", s);
-  hipLaunchKernelGGL((masked_finish_kernel<T>), dim3(blocks), dim3(kThreads), 0, s, part,
-                     K > 0 ? p.splits : 0, S, w.d, ya, y_out, y_f32);
+  hipLaunchKernelGGL((act_finish_kernel<T>), dim3(S), dim3(kThreads), 0, s, part, K > 0 ? p.splits : 0,
+                     S, w.d, ya, y_out, y_f32, make_glue<T>(gl));
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
 }
 
@@ -257,10 +331,10 @@ extern "C" size_t cgs_act_ffn_masked_workspace(int S, int K, int d, int ff) {
 
 extern "C" int act_ffn_masked(const cgs_ffn* w, const void* x, int S, const int32_t* idx, int K,
                               const float* y_anchor, const float* h_anchor, void* y_out,
-                              float* y_f32_out, float* h_out, void* ws, size_t ws_bytes,
-                              void* stream) {
+                              float* y_f32_out, float* h_out, const cgs_glue* glue, void* ws,
+                              size_t ws_bytes, void* stream) {
   if (!w || !w->w_gate || !w->w_up || !w->w_down || !valid_dtype(w->dtype) ||
-      w->down_layout != CGS_DOWN_FD || !x || !y_out || (K > 0 && !idx))
+      w->down_layout != CGS_DOWN_FD || !x || !y_out || (K > 0 && !idx) || !glue_ok(glue))
     return CGS_ERR_ARG;
   if (!act_shape_ok(w->d, w->ff)) return CGS_ERR_UNSUPPORTED;
   if (S < 0 || K < 0 || K > w->ff) return CGS_ERR_SHAPE;
@@ -269,7 +343,7 @@ extern "C" int act_ffn_masked(const cgs_ffn* w, const void* x, int S, const int3
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w->dtype == CGS_BF16)
     return act_t<uint16_t>(*w, static_cast<const uint16_t*>(x), S, idx, K, y_anchor, h_anchor,
-                           static_cast<uint16_t*>(y_out), y_f32_out, h_out, ws, s);
+                           static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s);
   return act_t<float>(*w, static_cast<const float*>(x), S, idx, K, y_anchor, h_anchor,
-                      static_cast<float*>(y_out), y_f32_out, h_out, ws, s);
+                      static_cast<float*>(y_out), y_f32_out, h_out, glue, ws, s);
 }

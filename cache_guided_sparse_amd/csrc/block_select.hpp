@@ -187,4 +187,180 @@ __device__ int block_coverage_cut(KeyFn key_of, ZFn z_of, int n, double thr, Emi
   return block_emit_selected(key_of, n, prefix, need, emit, sm);
 }
 
+// ---------------------------------------------------------------------------
+// Register-cached variant for n <= R * blockDim.x: every thread loads the keys
+// (and, for the coverage cut, the weights) of its contiguous index chunk once;
+// all radix passes and the emit pass then work on registers.  Same results as
+// the functions above.
+// ---------------------------------------------------------------------------
+template <int R> struct SelChunk {
+  int lo = 0, cnt = 0;
+  uint64_t key[R];
+  long long z[R];
+};
+
+// Chunk bounds of this thread and its keys key_of(lo + j).
+template <int R, class KeyFn>
+__device__ __forceinline__ void chunk_load(SelChunk<R>& c, int n, KeyFn key_of) {
+  const int chunk = (n + static_cast<int>(blockDim.x) - 1) / static_cast<int>(blockDim.x);
+  c.lo = min(n, static_cast<int>(threadIdx.x) * chunk);
+  c.cnt = min(n, c.lo + chunk) - c.lo;
+#pragma unroll
+  for (int j = 0; j < R; ++j) c.key[j] = (j < c.cnt) ? key_of(c.lo + j) : 0ull;
+}
+
+struct SelShared2 {
+  uint32_t hist[2][256];
+  unsigned long long hsum[2][256];
+  unsigned long long scan[kSelThreads / kWave];
+  uint64_t digit[2];
+  long long above[2];
+  int need;
+  long long tie_z;
+};
+
+// One radix pass over the candidates (key & pmask) == prefix: the digit at
+// `shift` whose bucket holds the rank-`remaining` element (counting from the
+// top), and the count of candidates in higher buckets.  hist[b] must be zero
+// on entry; hist[b ^ 1] is cleared here for the next pass.
+template <int R>
+__device__ __forceinline__ void chunk_pass(const SelChunk<R>& c, uint64_t prefix, uint64_t pmask,
+                                           int shift, long long remaining, int b, SelShared2& sm) {
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    if (j < c.cnt && (c.key[j] & pmask) == prefix) atomicAdd(&sm.hist[b][(c.key[j] >> shift) & 255u], 1u);
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    long long cs = 0;
+    for (int j = 0; j < 4; ++j) cs += sm.hist[b][4 * lane + j];
+    long long rev = cs;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const long long u = __shfl_down(rev, o, kWave);
+      if (lane + o < kWave) rev += u;
+    }
+    long long above = rev - cs;
+    for (int j = 3; j >= 0; --j) {
+      const long long h = sm.hist[b][4 * lane + j];
+      if (above < remaining && remaining <= above + h) {
+        sm.digit[b] = static_cast<uint64_t>(4 * lane + j);
+        sm.above[b] = above;
+      }
+      above += h;
+    }
+  } else {
+    for (int q = static_cast<int>(threadIdx.x) - kWave; q < 256; q += static_cast<int>(blockDim.x) - kWave)
+      sm.hist[b ^ 1][q] = 0;
+  }
+  __syncthreads();
+}
+
+// Emit, in ascending index order, every element with key > T and the first
+// `need` elements with key == T: emit(i, position, j) with j the register slot.
+template <int R, class EmitFn>
+__device__ __forceinline__ int chunk_emit(const SelChunk<R>& c, uint64_t T, int need, EmitFn emit,
+                                          SelShared2& sm) {
+  unsigned long long gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    if (j < c.cnt) { gt += c.key[j] > T; eq += c.key[j] == T; }
+  // one scan of (gt << 32 | eq): counts before this thread's chunk
+  unsigned long long tot;
+  const unsigned long long before = block_exclusive_scan((gt << 32) | eq, sm.scan, &tot);
+  const long long gt_before = static_cast<long long>(before >> 32);
+  long long e = static_cast<long long>(before & 0xffffffffull);
+  long long pos = gt_before + min(e, static_cast<long long>(need));
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    if (j >= c.cnt) continue;
+    bool s = c.key[j] > T;
+    if (c.key[j] == T) { s = e < need; ++e; }
+    if (s) emit(c.lo + j, static_cast<int>(pos++), j);
+  }
+  return static_cast<int>(tot >> 32) + need;
+}
+
+// Top k (1 <= k) of the cached keys in ascending index order.
+template <int R, class EmitFn>
+__device__ int chunk_topk(const SelChunk<R>& c, int n, int k, EmitFn emit, SelShared2& sm) {
+  if (k <= 0) return 0;
+  if (k >= n) {
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (j < c.cnt) emit(c.lo + j, c.lo + j, j);
+    return n;
+  }
+  for (int q = threadIdx.x; q < 256; q += blockDim.x) sm.hist[0][q] = 0;
+  __syncthreads();
+  uint64_t prefix = 0, pmask = 0;
+  long long remaining = k;
+  int b = 0;
+  for (int shift = 56; shift >= 0; shift -= 8, b ^= 1) {
+    chunk_pass(c, prefix, pmask, shift, remaining, b, sm);
+    prefix |= sm.digit[b] << shift;
+    pmask |= 0xffull << shift;
+    remaining -= sm.above[b];
+  }
+  return chunk_emit(c, prefix, static_cast<int>(remaining), emit, sm);
+}
+
+// Coverage cut over the cached keys and weights c.z (see block_coverage_cut).
+template <int R, class EmitFn>
+__device__ int chunk_coverage_cut(const SelChunk<R>& c, int n, double thr, EmitFn emit, SelShared2& sm) {
+  if (n <= 0 || !(thr > 0.0)) return 0;
+  for (int q = threadIdx.x; q < 256; q += blockDim.x) sm.hsum[0][q] = 0;
+  __syncthreads();
+  uint64_t prefix = 0, pmask = 0;
+  long long before_sum = 0;
+  int b = 0;
+  for (int shift = 56; shift >= 0; shift -= 8, b ^= 1) {
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (j < c.cnt && (c.key[j] & pmask) == prefix)
+        atomicAdd(&sm.hsum[b][(c.key[j] >> shift) & 255u], static_cast<unsigned long long>(c.z[j]));
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      const int lane = threadIdx.x;
+      long long cs = 0;
+      for (int j = 0; j < 4; ++j) cs += static_cast<long long>(sm.hsum[b][4 * lane + j]);
+      long long rev = cs;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const long long u = __shfl_down(rev, o, kWave);
+        if (lane + o < kWave) rev += u;
+      }
+      long long above = before_sum + (rev - cs);
+      for (int j = 3; j >= 0; --j) {
+        const long long h = static_cast<long long>(sm.hsum[b][4 * lane + j]);
+        if (!(static_cast<double>(above) >= thr) && static_cast<double>(above + h) >= thr) {
+          sm.digit[b] = static_cast<uint64_t>(4 * lane + j);
+          sm.above[b] = above;
+        }
+        above += h;
+      }
+    } else {
+      for (int q = static_cast<int>(threadIdx.x) - kWave; q < 256; q += static_cast<int>(blockDim.x) - kWave)
+        sm.hsum[b ^ 1][q] = 0;
+    }
+    __syncthreads();
+    prefix |= sm.digit[b] << shift;
+    pmask |= 0xffull << shift;
+    before_sum = sm.above[b];
+  }
+  // ties share one weight; take them in index order until thr is reached
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    if (j < c.cnt && c.key[j] == prefix) sm.tie_z = c.z[j];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const long long zT = sm.tie_z;
+    int j = 1;
+    while (j < n && !(static_cast<double>(before_sum + j * zT) >= thr)) ++j;
+    sm.need = j;
+  }
+  __syncthreads();
+  return chunk_emit(c, prefix, sm.need, emit, sm);
+}
+
 }  // namespace cgs

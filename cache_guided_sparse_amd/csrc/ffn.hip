@@ -30,6 +30,7 @@
 
 #include "common.hpp"
 #include "gemm.hpp"
+#include "glue.hpp"
 #include "profile.hpp"
 
 namespace cgs {
@@ -63,74 +64,19 @@ void launch_tile(int tile, const GemmArgs<T>& g, const char* site, hipStream_t s
   }
 }
 
-// Eight consecutive elements of a row as fp32 (16 bytes of bf16, 32 of fp32).
-template <typename T> struct Vec8Io;
-template <> struct Vec8Io<uint16_t> {
-  static __device__ __forceinline__ void load(const uint16_t* p, float* v) {
-    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(u[i] << 16);
-      v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-    }
-  }
-  static __device__ __forceinline__ void store(uint16_t* p, const float* v) {
-    u32x4_t u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      u[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
-    *reinterpret_cast<u32x4_t*>(p) = u;
-  }
-  static __device__ __forceinline__ void round(float* v) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32(f32_to_bf16(v[i]));
-  }
-  static __device__ __forceinline__ void copy(const uint16_t* src, uint16_t* dst) {
-    *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
-  }
-};
-template <> struct Vec8Io<float> {
-  static __device__ __forceinline__ void load(const float* p, float* v) {
-    const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0], b = reinterpret_cast<const f32x4_t*>(p)[1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
-  }
-  static __device__ __forceinline__ void store(float* p, const float* v) {
-    reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
-    reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
-  }
-  static __device__ __forceinline__ void round(float*) {}
-  static __device__ __forceinline__ void copy(const float* src, float* dst) {
-    reinterpret_cast<f32x4_t*>(dst)[0] = reinterpret_cast<const f32x4_t*>(src)[0];
-    reinterpret_cast<f32x4_t*>(dst)[1] = reinterpret_cast<const f32x4_t*>(src)[1];
-  }
-};
-
-// Block-wide float sum (kRowThreads threads).
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int w = 0; w < kRowThreads / 64; ++w) t += red[w];
-  __syncthreads();
-  return t;
-}
-
 // One workgroup per output row p; each thread owns runs of 8 elements.
 //   selected (p = idx[i] when scattering, every row otherwise): y_out[p] =
 //     round(sum over splits of the partials of row i, in split order);
-//     optionally r[p] += y_out[p] and x_next[p] = RMSNorm(r[p]);
-//   unselected: y_out[p] = y_ref[p], bit for bit.
+//   unselected: y_out[p] = y_ref[p], bit for bit;
+//   then the optional glue on the row's output (r += y (+ bias), x_next =
+//   RMSNorm(r)).
 // The selected position of p is found by a binary search over the ascending
 // index list (wave-uniform loads).
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void row_finish_kernel(
     const float* __restrict__ part, int splits, size_t split_stride, int d, bool scatter,
     const int32_t* __restrict__ idx, int k, const T* __restrict__ y_ref, T* __restrict__ y_out,
-    float* __restrict__ resid, T* __restrict__ x_next) {
+    GlueArgs<T> glue) {
   __shared__ float red[kRowThreads / 64];
   const int p = blockIdx.x;
   int i = p;
@@ -145,41 +91,22 @@ __global__ __launch_bounds__(kRowThreads) void row_finish_kernel(
     sel = (lo < k) && (idx[lo] == p);
   }
   const size_t ro = static_cast<size_t>(p) * d;
-  if (!sel) {
-    for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) Vec8Io<T>::copy(y_ref + ro + c, y_out + ro + c);
-    return;
-  }
   const size_t io = static_cast<size_t>(i) * d;
   float ss = 0.f;
   for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) {
-    float v[8], t[8];
-    Vec8Io<float>::load(part + io + c, v);
-    for (int sp = 1; sp < splits; ++sp) {
-      Vec8Io<float>::load(part + sp * split_stride + io + c, t);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] += t[e];
+    float v[8];
+    if (!sel) {
+      Row8<T>::copy(y_ref + ro + c, y_out + ro + c);
+      if (!glue.r) continue;
+      Row8<T>::load(y_ref + ro + c, v);
+    } else {
+      Row8<float>::load(part + io + c, v);
+      add_splits(part + split_stride + io + c, split_stride, splits - 1, v);
+      Row8<T>::store(y_out + ro + c, v);
     }
-    Vec8Io<T>::store(y_out + ro + c, v);
-    if (resid) {
-      Vec8Io<T>::round(v);
-      float r[8];
-      Vec8Io<float>::load(resid + ro + c, r);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { r[e] += v[e]; ss += r[e] * r[e]; }
-      Vec8Io<float>::store(resid + ro + c, r);
-    }
+    if (glue.r) ss += glue_add(glue, ro, c, v);
   }
-  if (resid && x_next) {
-    const float tot = block_sum(ss, red);
-    const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + 1e-6f);
-    for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) {
-      float r[8];
-      Vec8Io<float>::load(resid + ro + c, r);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] *= inv;
-      Vec8Io<T>::store(x_next + ro + c, r);
-    }
-  }
+  if (glue.r && glue.x_next) glue_norm_t<T, kRowThreads>(glue, ro, d, ss, red);
 }
 
 // r[m] = (r_src ? decode(r_src[m]) : r[m]) + (y ? decode(y[m]) : 0) + (bias ? bias : 0);
@@ -193,30 +120,30 @@ __global__ __launch_bounds__(kRowThreads) void residual_rmsnorm_kernel(
   float ss = 0.f;
   for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) {
     float v[8], t[8];
-    if (r_src) Vec8Io<TS>::load(r_src + ro + c, v); else Vec8Io<float>::load(r + ro + c, v);
+    if (r_src) Row8<TS>::load(r_src + ro + c, v); else Row8<float>::load(r + ro + c, v);
     if (y) {
-      Vec8Io<TY>::load(y + ro + c, t);
+      Row8<TY>::load(y + ro + c, t);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] += t[e];
     }
     if (bias) {
-      Vec8Io<float>::load(bias + c, t);
+      Row8<float>::load(bias + c, t);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] += t[e];
     }
-    Vec8Io<float>::store(r + ro + c, v);
+    Row8<float>::store(r + ro + c, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
   }
   if (!x_out) return;
-  const float tot = block_sum(ss, red);
+  const float tot = block_sum<kRowThreads>(ss, red);
   const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + 1e-6f);
   for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) {
     float v[8];
-    Vec8Io<float>::load(r + ro + c, v);
+    Row8<float>::load(r + ro + c, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] *= inv;
-    Vec8Io<TO>::store(x_out + ro + c, v);
+    Row8<TO>::store(x_out + ro + c, v);
   }
 }
 
@@ -286,7 +213,7 @@ bool ffn_ok(const cgs_ffn* w, int layout) {
 
 template <typename T>
 int ctx_recompute_t(const cgs_ffn& w, const T* x, const T* y_ref, const int32_t* idx, int k, int P,
-                    T* y_out, void* ws, hipStream_t s) {
+                    T* y_out, const cgs_glue* gl, void* ws, hipStream_t s) {
   const FfnPlan p = plan_ffn(std::max(k, 1), w.d, w.ff, w.dtype);
   Carve cv(ws);
   T* H = cv.take<T>(p.h_elems);
@@ -298,7 +225,7 @@ int ctx_recompute_t(const cgs_ffn& w, const T* x, const T* y_ref, const int32_t*
   {
     ProfScope ps("ctx.finish", s);
     hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kRowThreads), 0, s, part, p.splits,
-                       static_cast<size_t>(k) * w.d, w.d, true, idx, k, y_ref, y_out, nullptr, nullptr);
+                       static_cast<size_t>(k) * w.d, w.d, true, idx, k, y_ref, y_out, make_glue<T>(gl));
   }
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
 }
@@ -324,7 +251,8 @@ int rebuild_t(const cgs_ffn* layers, int L, const T* r0, int P, T* xo, T* yo, vo
     ProfScope ps("rebuild.finish", s);
     hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kRowThreads), 0, s, part, p.splits, lay,
                        w0.d, false, static_cast<const int32_t*>(nullptr), P, static_cast<const T*>(nullptr),
-                       yo + l * lay, r, (l + 1 < L) ? xo + (l + 1) * lay : static_cast<T*>(nullptr));
+                       yo + l * lay,
+                       GlueArgs<T>{r, nullptr, (l + 1 < L) ? xo + (l + 1) * lay : static_cast<T*>(nullptr)});
     if (!launch_ok()) return CGS_ERR_LAUNCH;
   }
   return CGS_OK;
@@ -346,9 +274,10 @@ extern "C" size_t cgs_ctx_ffn_recompute_workspace(int k, int P, int d, int ff, i
 }
 
 extern "C" int ctx_ffn_recompute(const cgs_ffn* w, const void* x, const void* y_ref,
-                                 const int32_t* idx, int k, int P, void* y_out, void* ws,
-                                 size_t ws_bytes, void* stream) {
-  if (!ffn_ok(w, CGS_DOWN_DF) || !x || !y_ref || !y_out || (k > 0 && !idx)) return CGS_ERR_ARG;
+                                 const int32_t* idx, int k, int P, void* y_out,
+                                 const cgs_glue* glue, void* ws, size_t ws_bytes, void* stream) {
+  if (!ffn_ok(w, CGS_DOWN_DF) || !x || !y_ref || !y_out || (k > 0 && !idx) || !glue_ok(glue))
+    return CGS_ERR_ARG;
   if (!ffn_shape_ok(w->d, w->ff, w->dtype)) return CGS_ERR_UNSUPPORTED;
   if (P < 0 || k < 0 || k > P) return CGS_ERR_SHAPE;
   if (P == 0) return CGS_OK;
@@ -359,9 +288,9 @@ extern "C" int ctx_ffn_recompute(const cgs_ffn* w, const void* x, const void* y_
   if (w->dtype == CGS_BF16)
     return ctx_recompute_t<uint16_t>(*w, static_cast<const uint16_t*>(x),
                                      static_cast<const uint16_t*>(y_ref), idx, k, P,
-                                     static_cast<uint16_t*>(y_out), ws, s);
+                                     static_cast<uint16_t*>(y_out), glue, ws, s);
   return ctx_recompute_t<float>(*w, static_cast<const float*>(x), static_cast<const float*>(y_ref),
-                                idx, k, P, static_cast<float*>(y_out), ws, s);
+                                idx, k, P, static_cast<float*>(y_out), glue, ws, s);
 }
 
 extern "C" size_t cgs_ref_rebuild_dense_workspace(int L, int P, int d, int ff, int dtype) {

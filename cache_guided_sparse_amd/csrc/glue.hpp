@@ -1,0 +1,147 @@
+// Row helpers shared by the finish kernels: 8-element row runs and the
+// residual / RMSNorm glue between FFN layers (cgs_glue in cgs.h).
+//
+// Glue, per row, after the FFN output y of the row is final:
+//   r += round(y) (+ bias),  x_next = RMSNorm(r) = r / sqrt(mean(r^2) + 1e-6),
+// where round() is the rounding of y to the activation type (the residual
+// stream adds the value the layer actually emits) and r stays fp32.
+#pragma once
+
+#include "common.hpp"
+
+namespace cgs {
+
+// Eight consecutive elements of a row as fp32 (16 bytes of bf16, 32 of fp32).
+template <typename T> struct Row8;
+template <> struct Row8<uint16_t> {
+  static __device__ __forceinline__ void load(const uint16_t* p, float* v) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const float* v) {
+    u32x4_t u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    *reinterpret_cast<u32x4_t*>(p) = u;
+  }
+  static __device__ __forceinline__ void round(float* v) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = bf16_to_f32(f32_to_bf16(v[i]));
+  }
+  static __device__ __forceinline__ void copy(const uint16_t* src, uint16_t* dst) {
+    *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+  }
+};
+template <> struct Row8<float> {
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0], b = reinterpret_cast<const f32x4_t*>(p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{v[0], v[1], v[2], v[3]};
+    reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{v[4], v[5], v[6], v[7]};
+  }
+  static __device__ __forceinline__ void round(float*) {}
+  static __device__ __forceinline__ void copy(const float* src, float* dst) {
+    reinterpret_cast<f32x4_t*>(dst)[0] = reinterpret_cast<const f32x4_t*>(src)[0];
+    reinterpret_cast<f32x4_t*>(dst)[1] = reinterpret_cast<const f32x4_t*>(src)[1];
+  }
+};
+
+// Sum over the threads of a workgroup of NT threads (NT/64 wave partials in
+// `red`, summed in wave order).  Contains barriers: call from every thread.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// v += part[sp * stride .. +8] for sp = 0 .. splits-1, added in split order;
+// the loads of up to 8 splits are in flight at once.
+__device__ __forceinline__ void add_splits(const float* part, size_t stride, int splits, float* v) {
+  constexpr int B = 8;
+  for (int s0 = 0; s0 < splits; s0 += B) {
+    float t[B][8];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (s0 + b < splits) Row8<float>::load(part + (s0 + b) * stride, t[b]);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (s0 + b < splits) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += t[b][e];
+      }
+    }
+  }
+}
+
+template <typename T> struct GlueArgs {
+  float* r;            // [rows][d] residual stream (NULL: no glue)
+  const float* bias;   // [d] or NULL
+  T* x_next;           // [rows][d] or NULL
+};
+
+inline bool glue_ok(const cgs_glue* g) { return !g || g->r; }
+
+template <typename T>
+inline GlueArgs<T> make_glue(const cgs_glue* g) {
+  GlueArgs<T> a{nullptr, nullptr, nullptr};
+  if (g) { a.r = g->r; a.bias = g->bias; a.x_next = static_cast<T*>(g->x_next); }
+  return a;
+}
+
+// r[ro + c .. +8] += round(v) (+ bias[c .. +8]); returns the sum of squares of
+// the updated r values.
+template <typename T>
+__device__ __forceinline__ float glue_add(const GlueArgs<T>& g, size_t ro, int c, float* v) {
+  Row8<T>::round(v);
+  float rr[8], b[8];
+  Row8<float>::load(g.r + ro + c, rr);
+  if (g.bias) Row8<float>::load(g.bias + c, b);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    rr[e] += v[e];
+    if (g.bias) rr[e] += b[e];
+    ss += rr[e] * rr[e];
+  }
+  Row8<float>::store(g.r + ro + c, rr);
+  return ss;
+}
+
+// x_next[row] = RMSNorm(r[row]) for the runs c = 8 threadIdx.x + 8 NT j that
+// this thread updated with glue_add; `ss` is its partial sum of squares.
+template <typename T, int NT>
+__device__ __forceinline__ void glue_norm_t(const GlueArgs<T>& g, size_t ro, int d, float ss, float* red) {
+  const float tot = block_sum<NT>(ss, red);
+  const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + 1e-6f);
+  for (int c = threadIdx.x * 8; c < d; c += NT * 8) {
+    float rr[8];
+    Row8<float>::load(g.r + ro + c, rr);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rr[e] *= inv;
+    Row8<T>::store(g.x_next + ro + c, rr);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void glue_norm(const GlueArgs<T>& g, size_t ro, int d, float ss, float* red) {
+  glue_norm_t<T, 256>(g, ro, d, ss, red);
+}
+
+}  // namespace cgs

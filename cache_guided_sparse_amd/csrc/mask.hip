@@ -64,9 +64,36 @@ __global__ __launch_bounds__(256) void contrib_kernel(const float* __restrict__ 
 
 struct MaskShared {
   SelShared sel;
+  SelShared2 sel2;
   double dred[kSelThreads / kWave];
   long long lred[kSelThreads / kWave];
 };
+
+constexpr int kChunkR = 4;  // neurons per thread in the register-cached path (ff <= 4096)
+
+// Largest sval over the block (sval >= 0), then the coverage threshold pieces:
+// e = ilogb(max) - q_bits, z_n = rint(sval_n 2^-e), Z = sum z.
+__device__ __forceinline__ double block_max_d(double m, MaskShared& sm) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  m = wave_max(m);
+  if (lane == 0) sm.dred[wid] = m;
+  __syncthreads();
+  double r = 0.0;
+  for (int w = 0; w < static_cast<int>(blockDim.x / kWave); ++w) r = fmax(r, sm.dred[w]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ long long block_sum_ll(long long v, MaskShared& sm) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_sum(v);
+  if (lane == 0) sm.lred[wid] = v;
+  __syncthreads();
+  long long r = 0;
+  for (int w = 0; w < static_cast<int>(blockDim.x / kWave); ++w) r += sm.lred[w];
+  __syncthreads();
+  return r;
+}
 
 __global__ __launch_bounds__(kSelThreads) void mask_select_kernel(
     const uint64_t* __restrict__ ckey, const uint64_t* __restrict__ skey,
@@ -74,11 +101,71 @@ __global__ __launch_bounds__(kSelThreads) void mask_select_kernel(
     int q_bits, uint32_t* __restrict__ uni, uint32_t* __restrict__ flag,
     uint64_t* __restrict__ mask_out, int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out) {
   __shared__ MaskShared sm;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ uint32_t bm[kSelThreads * kChunkR / 32];  // mask bits of the cached path
+  const int tid = threadIdx.x;
+  int count = 0;
+  const bool cached = ff <= kSelThreads * kChunkR;
+  if (cached) {
+    // Register-cached path: every thread owns a contiguous chunk of <= 4 neurons.
+    for (int q = tid; q < kSelThreads * kChunkR / 32; q += blockDim.x) bm[q] = 0;
+    __syncthreads();
+    SelChunk<kChunkR> c;
+    auto emit = [&](int i, int pos, int) {
+      idx_out[pos] = i;
+      atomicOr(&bm[i >> 5], 1u << (i & 31));
+    };
+    if (mode == CGS_MASK_TOPK) {
+      if (K > 0) {
+        uint32_t in_union = 0;
+        for (int t = 0; t < T_steps; ++t) {
+          const uint64_t* ck = ckey + static_cast<size_t>(t) * ff;
+          chunk_load(c, ff, [&](int i) { return ck[i]; });
+          chunk_topk(c, ff, K, [&](int, int, int j) { in_union |= 1u << j; }, sm.sel2);
+          __syncthreads();
+        }
+        chunk_load(c, ff, [&](int i) { return skey[i]; });
+#pragma unroll
+        for (int j = 0; j < kChunkR; ++j)
+          if (!((in_union >> j) & 1u)) c.key[j] = 0ull;
+        count = chunk_topk(c, ff, K, emit, sm.sel2);
+      }
+    } else {
+      chunk_load(c, ff, [&](int i) { return skey[i]; });
+      double sv[kChunkR];
+      double m = 0.0;
+#pragma unroll
+      for (int j = 0; j < kChunkR; ++j) {
+        sv[j] = (j < c.cnt) ? sval[c.lo + j] : 0.0;
+        m = fmax(m, sv[j]);
+      }
+      const double smax = block_max_d(m, sm);
+      if (smax > 0.0) {
+        const int e = ilogb(smax) - q_bits;
+        long long zs = 0;
+#pragma unroll
+        for (int j = 0; j < kChunkR; ++j) {
+          c.z[j] = (j < c.cnt) ? static_cast<long long>(rint(ldexp(sv[j], -e))) : 0;
+          zs += c.z[j];
+        }
+        const long long Z = block_sum_ll(zs, sm);
+        const double thr = coverage * static_cast<double>(Z);
+        count = chunk_coverage_cut(c, ff, thr, emit, sm.sel2);
+      }
+    }
+    __syncthreads();
+    for (int i = count + tid; i < ff; i += blockDim.x) idx_out[i] = -1;
+    const int words = (ff + 63) / 64;
+    for (int wdx = tid; wdx < words; wdx += blockDim.x)
+      mask_out[wdx] = static_cast<uint64_t>(bm[2 * wdx]) | (static_cast<uint64_t>(bm[2 * wdx + 1]) << 32);
+    if (tid == 0) *count_out = count;
+    return;
+  }
+
+  // General path (ff > 4096): keys re-read from global memory on every pass.
+  const int lane = tid & 63, wid = tid >> 6;
   for (int i = tid; i < ff; i += blockDim.x) { uni[i] = 0; flag[i] = 0; }
   __syncthreads();
   auto emit = [&](int i, int pos) { idx_out[pos] = i; flag[i] = 1; };
-  int count = 0;
   if (mode == CGS_MASK_TOPK) {
     if (K > 0) {
       for (int t = 0; t < T_steps; ++t) {

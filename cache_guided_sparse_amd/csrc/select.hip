@@ -70,12 +70,21 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ x,
     }
   };
   if (vec) {
-    for (int j = lane * 8; j < d; j += kWave * 8) {
-      double a[8], b[8];
-      Vec8<T>::load(xp + j, a);
-      Vec8<T>::load(rp + j, b);
+    // four 8-element runs per lane in flight at once (d = 2048 bf16: one batch)
+    for (int j0 = lane * 8; j0 < d; j0 += 4 * kWave * 8) {
+      double a[4][8], b[4][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) accum(a[i], b[i]);
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + q * kWave * 8;
+        if (j < d) { Vec8<T>::load(xp + j, a[q]); Vec8<T>::load(rp + j, b[q]); }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (j0 + q * kWave * 8 < d) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) accum(a[q][i], b[q][i]);
+        }
+      }
     }
   } else {
     for (int j = lane; j < d; j += kWave)
@@ -104,6 +113,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const uint64_t* __res
                                                            int P, int k,
                                                            int32_t* __restrict__ idx_out) {
   __shared__ SelShared sm;
+  __shared__ SelShared2 sm2;
+  if (P <= 4 * kSelThreads) {  // keys cached in registers, 4 per thread
+    SelChunk<4> c;
+    chunk_load(c, P, [&](int i) { return okeys[i]; });
+    chunk_topk(c, P, k, [&](int i, int pos, int) { idx_out[pos] = i; }, sm2);
+    return;
+  }
   block_topk([&](int i) { return okeys[i]; }, P, k,
              [&](int i, int pos) { idx_out[pos] = i; }, sm);
 }

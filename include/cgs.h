@@ -76,6 +76,18 @@ typedef struct {
   const void* w_down;   /* [d][ff] (DF) or [ff][d] (FD) */
 } cgs_ffn;
 
+/* Optional residual / RMSNorm glue applied by a finish kernel to each output
+ * row y once it is final (the glue between stacked FFN layers, fused so that
+ * it costs no extra pass):
+ *   r[row] += round(y[row]) (+ bias),   x_next[row] = RMSNorm(r[row]),
+ * with round() the rounding of y to the FFN dtype, RMSNorm(v) = v /
+ * sqrt(mean(v^2) + 1e-6) (no learned scale), r fp32.  Pass NULL for none. */
+typedef struct {
+  float* r;            /* [rows][d] fp32 residual stream, updated in place; required */
+  const float* bias;   /* [d] fp32 added to r after y, or NULL */
+  void* x_next;        /* [rows][d] in the FFN dtype, or NULL */
+} cgs_glue;
+
 /* ---- host helpers ------------------------------------------------------ */
 
 /* ceil(rho * n) as in §4.1 (ceil(rho_p P) tokens) and §5 (K = ceil(rho_n H)),
@@ -119,11 +131,15 @@ size_t cgs_ctx_ffn_recompute_workspace(int k, int P, int d, int ff, int dtype);
  *   idx    : [k] int32, ascending, unique, in [0, P) (the selected visual
  *            tokens plus any always-recomputed rows the caller adds).
  *   y_out  : [P][d] dtype, must not alias y_ref or x.
+ *   glue   : NULL or the residual/RMSNorm glue applied to every row of y_out
+ *            (rows [P][d]); glue->r non-NULL.
  * Unselected rows are copied bit for bit.  k = 0 is a pure copy; k = P is
  * the dense FFN.  The hidden activation is rounded to dtype before the down
- * projection; products accumulate in fp32. */
+ * projection; products accumulate in fp32.  Row pointers must be 16-byte
+ * aligned (d % 128 == 0 does it for aligned bases). */
 int ctx_ffn_recompute(const cgs_ffn* w, const void* x, const void* y_ref, const int32_t* idx,
-                      int k, int P, void* y_out, void* ws, size_t ws_bytes, void* stream);
+                      int k, int P, void* y_out, const cgs_glue* glue, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /* ---- Action Cache ------------------------------------------------------ */
 
@@ -163,13 +179,14 @@ size_t cgs_act_ffn_masked_workspace(int S, int K, int d, int ff);
  *   y_f32_out  : [S][d] float or NULL; the same result before rounding.
  *   h_out      : [ff][S] float or NULL; rows idx receive h^M, other rows
  *                are not written.
+ *   glue       : NULL or the residual/RMSNorm glue applied to y (rows [S][d]).
  * With idx = 0..ff-1 and NULL anchors this is the dense anchor step; its
  * y_f32_out / h_out are the anchor state of later steps.  Only rows idx of
  * w_gate, w_up and w_down are read.  The delta h - h_anchor is rounded to
  * dtype before the down projection.  K = 0 gives y = y_anchor (or 0). */
 int act_ffn_masked(const cgs_ffn* w, const void* x, int S, const int32_t* idx, int K,
                    const float* y_anchor, const float* h_anchor, void* y_out, float* y_f32_out,
-                   float* h_out, void* ws, size_t ws_bytes, void* stream);
+                   float* h_out, const cgs_glue* glue, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- Reference rebuild ------------------------------------------------- */
 
@@ -186,7 +203,7 @@ size_t cgs_ref_rebuild_dense_workspace(int L, int P, int d, int ff, int dtype);
 int ref_rebuild_dense(const cgs_ffn* layers, int L, const void* r0, int P, void* x_ref_out,
                       void* y_ref_out, void* ws, size_t ws_bytes, void* stream);
 
-/* ---- Inter-layer glue -------------------------------------------------- */
+/* ---- Inter-layer glue (standalone) -------------------------------------- */
 
 /* Residual add and RMSNorm between FFN layers (the glue of a layer stack,
  * not part of the selective FFN itself):
@@ -195,7 +212,8 @@ int ref_rebuild_dense(const cgs_ffn* layers, int L, const void* r0, int P, void*
  *   r     : [M][d] float, written (read too when r_in is NULL); required.
  *   r_in  : [M][d] float or NULL, a separate source for the residual.
  *   y     : [M][d] y_dtype or NULL; bias: [d] float or NULL.
- *   x_out : [M][d] out_dtype or NULL. */
+ *   x_out : [M][d] out_dtype or NULL.
+ * Requires d % 8 == 0 and 16-byte aligned rows. */
 int cgs_residual_rmsnorm(float* r, const float* r_in, const void* y, int y_dtype,
                          const float* bias, int M, int d, void* x_out, int out_dtype,
                          void* stream);

@@ -81,17 +81,21 @@ def test_host_validation_without_launch():
     assert L.ctx_select(buf, buf, 0, 16, 0, 0, 0, None, None, None, 0, None) == 0
     # ctx_ffn_recompute: wrong layout, null weights, unsupported d, k > P, aliasing
     w = _ffn()
-    assert L.ctx_ffn_recompute(ctypes.byref(_ffn(layout=1)), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), buf, 1 << 30, None) == 1
-    assert L.ctx_ffn_recompute(ctypes.byref(_ffn(null=True)), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), buf, 1 << 30, None) == 1
-    assert L.ctx_ffn_recompute(ctypes.byref(_ffn(d=200)), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), buf, 1 << 30, None) == 4
-    assert L.ctx_ffn_recompute(ctypes.byref(w), buf, buf, buf, 9, 8, ctypes.c_void_p(0x2000), buf, 1 << 30, None) == 2
-    assert L.ctx_ffn_recompute(ctypes.byref(w), buf, ctypes.c_void_p(0x2000), buf, 1, 8, ctypes.c_void_p(0x2000), buf, 1 << 30, None) == 1
-    assert L.ctx_ffn_recompute(ctypes.byref(w), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), buf, 16, None) == 3
+    assert L.ctx_ffn_recompute(ctypes.byref(_ffn(layout=1)), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), None, buf, 1 << 30, None) == 1
+    assert L.ctx_ffn_recompute(ctypes.byref(_ffn(null=True)), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), None, buf, 1 << 30, None) == 1
+    assert L.ctx_ffn_recompute(ctypes.byref(_ffn(d=200)), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), None, buf, 1 << 30, None) == 4
+    assert L.ctx_ffn_recompute(ctypes.byref(w), buf, buf, buf, 9, 8, ctypes.c_void_p(0x2000), None, buf, 1 << 30, None) == 2
+    assert L.ctx_ffn_recompute(ctypes.byref(w), buf, ctypes.c_void_p(0x2000), buf, 1, 8, ctypes.c_void_p(0x2000), None, buf, 1 << 30, None) == 1
+    assert L.ctx_ffn_recompute(ctypes.byref(w), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), None, buf, 16, None) == 3
     # act_ffn_masked: wrong layout, K > ff
     wf = _ffn(layout=1)
-    assert L.act_ffn_masked(ctypes.byref(w), buf, 4, buf, 1, None, None, buf, None, None, buf, 1 << 30, None) == 1
-    assert L.act_ffn_masked(ctypes.byref(wf), buf, 4, buf, 2000, None, None, buf, None, None, buf, 1 << 30, None) == 2
-    assert L.act_ffn_masked(ctypes.byref(wf), buf, 4, buf, 10, None, None, buf, None, None, buf, 4, None) == 3
+    assert L.act_ffn_masked(ctypes.byref(w), buf, 4, buf, 1, None, None, buf, None, None, None, buf, 1 << 30, None) == 1
+    assert L.act_ffn_masked(ctypes.byref(wf), buf, 4, buf, 2000, None, None, buf, None, None, None, buf, 1 << 30, None) == 2
+    assert L.act_ffn_masked(ctypes.byref(wf), buf, 4, buf, 10, None, None, buf, None, None, None, buf, 4, None) == 3
+    # glue without a residual buffer
+    g = cgs._Glue(None, None, None)
+    assert L.act_ffn_masked(ctypes.byref(wf), buf, 4, buf, 10, None, None, buf, None, None, ctypes.byref(g), buf, 1 << 30, None) == 1
+    assert L.ctx_ffn_recompute(ctypes.byref(w), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), ctypes.byref(g), buf, 1 << 30, None) == 1
     # act_build_mask: bad mode, K, coverage, S*T too large
     assert L.act_build_mask(buf, 2, 8, ctypes.byref(wf), 9, 4, 0.0, buf, buf, buf, buf, 1 << 30, None) == 1
     assert L.act_build_mask(buf, 2, 8, ctypes.byref(wf), 0, 5000, 0.0, buf, buf, buf, buf, 1 << 30, None) == 2

@@ -104,3 +104,29 @@ def test_deterministic_repeats():
     a = values(_masked(w, x, idx)[1])
     b = values(_masked(w, x, idx)[1])
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("S,d,ff,rho", [(50, 1024, 4096, 0.3), (16, 256, 1024, 1.0)])
+def test_fused_glue(S, d, ff, rho):
+    """The finish kernel's residual/RMSNorm glue: r += bf16(y) + bias and
+    x_next = RMSNorm(r), checked on the GPU's own y (teacher forcing) against
+    the oracle's RMSNorm; y itself against the oracle's Eq. 4."""
+    say("act glue", S, d, ff, rho)
+    w, x, xa = _setup(15, S, d, ff)
+    ya, ha = O.act_ffn_masked(w, xa, np.arange(ff))
+    ya32, ha32 = ya.astype(np.float32), ha.astype(np.float32)
+    K = O.ratio_to_count(rho, ff)
+    idx = np.sort(rng(15, K, "perm").permutation(ff)[:K]).astype(np.int32)
+    g = rng(15, 1, "misc")
+    r0 = g.standard_normal((S, d)).astype(np.float32)
+    bias = g.standard_normal(d).astype(np.float32)
+    r = to_dev(r0, "f32")
+    xn = torch.empty(S, d, dtype=torch.bfloat16, device=dev())
+    y = cgs.act_ffn_masked(ffn_dev(w), to_dev(x), _idx_dev(idx), y_anchor=to_dev(ya32, "f32"),
+                           h_anchor=to_dev(ha32, "f32"), glue=(r, to_dev(bias, "f32"), xn))
+    torch.cuda.synchronize()
+    y_o, _ = O.act_ffn_masked(w, x, idx, ya32, ha32)
+    assert_close(values(y), y_o, "y", out="bf16")
+    r_exp = r0.astype(np.float64) + values(y) + bias.astype(np.float64)
+    assert_close(values(r), r_exp, "residual")
+    assert_close(values(xn), O.rms_norm(r_exp), "x_next", out="bf16")

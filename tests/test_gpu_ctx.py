@@ -97,3 +97,26 @@ def test_deterministic_repeats():
     a = bits(_recompute(w, x, y_ref, idx))
     b = bits(_recompute(w, x, y_ref, idx))
     assert np.array_equal(a, b)
+
+
+def test_fused_glue():
+    """Residual/RMSNorm glue in the finish kernel on all P rows (recomputed and
+    copied), checked on the GPU's own y against the oracle's RMSNorm."""
+    say("ctx glue")
+    P, d, ff = 300, 256, 512
+    inp = ctx_layer_inputs(21, 0, P, d, 90, 1.3333, 0.1752)
+    w = ffn_weights(21, 0, d, ff)
+    y_ref = random_bf16(21, 0, "y_ref", (P, d))
+    idx, _ = O.ctx_select(inp["x"], inp["x_ref"], 90)
+    r0 = rng(21, 1, "misc").standard_normal((P, d)).astype(np.float32)
+    r = to_dev(r0, "f32")
+    xn = torch.empty(P, d, dtype=torch.bfloat16, device=dev())
+    y = cgs.ctx_ffn_recompute(ffn_dev(w), to_dev(inp["x"]), to_dev(y_ref),
+                              torch.from_numpy(idx).to(dev()), glue=(r, None, xn))
+    torch.cuda.synchronize()
+    y_o, rec = O.ctx_ffn_recompute(w, inp["x"], y_ref, idx)
+    assert_close(values(y)[rec], y_o[rec], "recomputed rows", out="bf16")
+    assert np.array_equal(bits(y)[~rec], y_ref[~rec])
+    r_exp = r0.astype(np.float64) + values(y)
+    assert_close(values(r), r_exp, "residual")
+    assert_close(values(xn), O.rms_norm(r_exp), "x_next", out="bf16")
