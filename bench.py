@@ -48,6 +48,32 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _source_hash(files) -> str:
+    """First 16 hex digits of the sha256 of the kernel's source files, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "cache_guided_sparse_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(site: str):
+    """HBM bytes per launch of a timing site from the PMC record under profiles/
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel calibration), or
+    (None, None) if there is none or the kernel's sources changed since."""
+    import glob
+    for fn in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(fn) as fh:
+            for line in fh:
+                if not line.startswith("traffic-json:"):
+                    continue
+                tj = json.loads(line[len("traffic-json:"):])
+                if tj.get("kernel") == site and tj.get("source_sha256_16") == _source_hash(tj["source_files"]):
+                    return tj["traffic_bytes_per_launch"], os.path.basename(fn)
+    return None, None
+
+
 def site_work(site: str, k: int, K_masked: list) -> tuple:
     """Algorithmic (flops, bytes) of one launch of a timing site."""
     if site == "ctx.glu":
@@ -376,10 +402,13 @@ def main():
     mfma = flops / byts > RIDGE
     achieved = (flops / dom_s / 1e12) if mfma else (byts / dom_s / 1e9)
     peak = PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBPS
+    traffic, traffic_src = stored_traffic(dom)
     roofline = {"bound": "mfma" if mfma else "hbm", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s" if mfma else "GB/s", "frac": round(achieved / peak, 4),
-                "traffic": None, "kernel": dom, "mean_us": round(dom_s * 1e6, 2),
-                "launches": dom_n, "flops_per_launch": flops, "bytes_per_launch": byts}
+                "traffic": traffic, "kernel": dom, "mean_us": round(dom_s * 1e6, 2),
+                "launches": dom_n, "flops_per_launch": flops, "bytes_per_launch": byts,
+                "traffic_source": traffic_src,
+                "traffic_over_algorithmic": round(traffic / byts, 3) if traffic else None}
 
     # Action Cache masked step: algorithmic bytes over its measured time (FFN + glue)
     Km = w.K

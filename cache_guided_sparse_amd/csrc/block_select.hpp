@@ -193,6 +193,25 @@ __device__ int block_coverage_cut(KeyFn key_of, ZFn z_of, int n, double thr, Emi
 // all radix passes and the emit pass then work on registers.  Same results as
 // the functions above.
 // ---------------------------------------------------------------------------
+// hist[bin] += val for every lane with `valid`.  Radix passes over keys of
+// similar magnitude put most lanes of a wave in one bin; when every valid lane
+// of the wave agrees on the bin, one lane adds the wave's sum (integer sums:
+// the same result as one add per lane).
+template <typename V>
+__device__ __forceinline__ void hist_add(V* hist, uint32_t bin, bool valid, V val) {
+  const uint64_t act = __ballot(valid);
+  if (act == 0) return;
+  const uint32_t lead = __builtin_amdgcn_readfirstlane(valid ? bin : 0xffffffffu);
+  const uint32_t first = lead != 0xffffffffu ? lead : static_cast<uint32_t>(__shfl(static_cast<int>(bin), __builtin_ctzll(act), kWave));
+  const bool same = __ballot(valid && bin != first) == 0;
+  if (same) {
+    V tot = wave_sum(valid ? val : V(0));
+    if ((threadIdx.x & (kWave - 1)) == static_cast<unsigned>(__builtin_ctzll(act))) atomicAdd(&hist[first], tot);
+  } else if (valid) {
+    atomicAdd(&hist[bin], val);
+  }
+}
+
 template <int R> struct SelChunk {
   int lo = 0, cnt = 0;
   uint64_t key[R];
@@ -227,8 +246,10 @@ template <int R>
 __device__ __forceinline__ void chunk_pass(const SelChunk<R>& c, uint64_t prefix, uint64_t pmask,
                                            int shift, long long remaining, int b, SelShared2& sm) {
 #pragma unroll
-  for (int j = 0; j < R; ++j)
-    if (j < c.cnt && (c.key[j] & pmask) == prefix) atomicAdd(&sm.hist[b][(c.key[j] >> shift) & 255u], 1u);
+  for (int j = 0; j < R; ++j) {
+    const bool v = j < c.cnt && (c.key[j] & pmask) == prefix;
+    hist_add(sm.hist[b], static_cast<uint32_t>((c.key[j] >> shift) & 255u), v, 1u);
+  }
   __syncthreads();
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
@@ -316,9 +337,11 @@ __device__ int chunk_coverage_cut(const SelChunk<R>& c, int n, double thr, EmitF
   int b = 0;
   for (int shift = 56; shift >= 0; shift -= 8, b ^= 1) {
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-      if (j < c.cnt && (c.key[j] & pmask) == prefix)
-        atomicAdd(&sm.hsum[b][(c.key[j] >> shift) & 255u], static_cast<unsigned long long>(c.z[j]));
+    for (int j = 0; j < R; ++j) {
+      const bool v = j < c.cnt && (c.key[j] & pmask) == prefix;
+      hist_add(sm.hsum[b], static_cast<uint32_t>((c.key[j] >> shift) & 255u), v,
+               static_cast<unsigned long long>(v ? c.z[j] : 0));
+    }
     __syncthreads();
     if (threadIdx.x < kWave) {
       const int lane = threadIdx.x;

@@ -19,12 +19,13 @@
 //
 // Tile choice by the number of rows M (the selected tokens k, or P for the
 // rebuild), all with 8 waves except the smallest:
-//   M <= 64   64 x 128, 4 waves, 4 LDS stages
-//   M <= 128  128 x 128, 4 stages
-//   M <= 256  256 x 128, 3 stages (the 231-row Context Cache layer: one M tile,
-//             ff/64 = 256 workgroups stream every weight row once)
-//   M > 256   192 x 256, 2 stages (bf16 with d % 256 == 0: the 768-row rebuild
-//             is 4 x 128 gate/up tiles and 4 x 8 x 8 down tiles, two and one
+//   M <= 64   64 x 128, 4 waves
+//   M <= 128  128 x 128
+//   M <= 256  256 x 128 (the 231-row Context Cache layer: one M tile, ff/64 =
+//             256 workgroups stream every weight row once, 4 weight tiles
+//             in flight per workgroup)
+//   M > 256   192 x 256 (bf16 with d % 256 == 0: the 768-row rebuild is
+//             4 x 128 gate/up tiles and 4 x 8 x 8 down tiles, two and one
 //             rounds of 256 workgroups); else 256 x 128.
 #include <algorithm>
 
@@ -37,18 +38,21 @@ namespace cgs {
 namespace {
 
 constexpr int kRowThreads = 256;
+constexpr int kFinishIdxLds = 4096;  // index lists up to this length are searched in LDS
 
-// Tile configurations <BM, WM, WN, NT, STAGES> (BN = 16 NT WN).
-using CfgS = GemmCfg<64, 2, 2, 4, 4>;    //  64 x 128, 4 waves
-using CfgM = GemmCfg<128, 4, 2, 4, 4>;   // 128 x 128, 8 waves
-using CfgL = GemmCfg<256, 4, 2, 4, 3>;   // 256 x 128, 8 waves
-using CfgX = GemmCfg<192, 2, 4, 4, 2>;   // 192 x 256, 8 waves
+// Tile configurations <BM, WM, WN, NT, SA, SB> (BN = 16 NT WN; A and B ring
+// depths).  The weight (B) ring runs deeper: on the selective path the
+// weights stream from HBM while the gathered rows (A) hit L2.
+using CfgS = GemmCfg<64, 2, 2, 4, 2, 4>;    //  64 x 128, 4 waves,  80 KB LDS
+using CfgM = GemmCfg<128, 4, 2, 4, 2, 4>;   // 128 x 128, 8 waves,  96 KB
+using CfgL = GemmCfg<256, 4, 2, 4, 2, 5>;   // 256 x 128, 8 waves, 144 KB
+using CfgX = GemmCfg<192, 2, 4, 4, 2, 3>;   // 192 x 256, 8 waves, 144 KB
 enum TileId { kTileS = 0, kTileM = 1, kTileL = 2, kTileX = 3 };
 
 template <typename Cfg, typename T, bool GLU, bool GATHER>
 void launch_cfg(const GemmArgs<T>& g, const char* site, hipStream_t s) {
   ProfScope ps(site, s);
-  hipLaunchKernelGGL((gemm_kernel<T, Cfg::kBM, Cfg::kWM, Cfg::kWN, Cfg::kNT, Cfg::kStages, GLU, GATHER>),
+  hipLaunchKernelGGL((gemm_kernel<T, Cfg::kBM, Cfg::kWM, Cfg::kWN, Cfg::kNT, Cfg::kSA, Cfg::kSB, GLU, GATHER>),
                      dim3(g.n_tiles * g.m_tiles * g.splits), dim3(Cfg::kThreads), 0, s, g);
 }
 
@@ -78,17 +82,29 @@ __global__ __launch_bounds__(kRowThreads) void row_finish_kernel(
     const int32_t* __restrict__ idx, int k, const T* __restrict__ y_ref, T* __restrict__ y_out,
     GlueArgs<T> glue) {
   __shared__ float red[kRowThreads / 64];
+  __shared__ int32_t sidx[kFinishIdxLds];
   const int p = blockIdx.x;
   int i = p;
   bool sel = true;
   if (scatter) {
-    int lo = 0, hi = k;  // first position with idx[pos] >= p
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (__builtin_amdgcn_readfirstlane(idx[mid]) < p) lo = mid + 1; else hi = mid;
+    // first position with idx[pos] >= p; the list is staged in LDS when it fits
+    int lo = 0, hi = k;
+    if (k <= kFinishIdxLds) {
+      for (int q = threadIdx.x; q < k; q += kRowThreads) sidx[q] = idx[q];
+      __syncthreads();
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sidx[mid] < p) lo = mid + 1; else hi = mid;
+      }
+      sel = (lo < k) && (sidx[lo] == p);
+    } else {
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (__builtin_amdgcn_readfirstlane(idx[mid]) < p) lo = mid + 1; else hi = mid;
+      }
+      sel = (lo < k) && (idx[lo] == p);
     }
     i = lo;
-    sel = (lo < k) && (idx[lo] == p);
   }
   const size_t ro = static_cast<size_t>(p) * d;
   const size_t io = static_cast<size_t>(i) * d;

@@ -9,8 +9,9 @@
 // A rows may be gathered through an index list (the selected tokens).
 //
 // Data movement (gfx950): K tiles of 128 bytes per row travel global -> LDS
-// by LDS DMA (global_load_lds_dwordx4, 1 KB per wavefront instruction), a
-// STAGES-deep ring, one workgroup barrier per K tile.  A tile row is 8 chunks
+// by LDS DMA (global_load_lds_dwordx4, 1 KB per wavefront instruction) into
+// two rings (A tiles SA deep, B tiles SB deep; half of the waves load each
+// operand), one workgroup barrier per K tile.  A tile row is 8 chunks
 // of 16 bytes; chunk c of row r sits at physical chunk c ^ (r & 7), so the
 // 16-byte MFMA fragment reads of 8 consecutive rows fall in 8 distinct bank
 // groups.  The waves form a WM x WN grid; each owns (BM/WM) x 16 NT of the tile.
@@ -69,48 +70,60 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int STAGES, int LPW>
+// Wait for the K tile whose transfers were followed by `ahead` more tiles of
+// LPW transfers each (0 <= ahead <= MAXA), then barrier (wait_vm_barrier).
+template <int LPW, int MAXA>
 __device__ __forceinline__ void wait_tile(int ahead) {
-  if constexpr (STAGES >= 4) {
-    if (ahead >= 2) { wait_vm_barrier<2 * LPW>(); return; }
-  }
-  if constexpr (STAGES >= 3) {
-    if (ahead >= 1) { wait_vm_barrier<LPW>(); return; }
-  }
+  if constexpr (MAXA >= 4) { if (ahead >= 4) { wait_vm_barrier<4 * LPW>(); return; } }
+  if constexpr (MAXA >= 3) { if (ahead == 3) { wait_vm_barrier<3 * LPW>(); return; } }
+  if constexpr (MAXA >= 2) { if (ahead == 2) { wait_vm_barrier<2 * LPW>(); return; } }
+  if constexpr (MAXA >= 1) { if (ahead == 1) { wait_vm_barrier<LPW>(); return; } }
   wait_vm_barrier<0>();
 }
 
-template <int BM, int WM, int WN, int NT, int STAGES>
+// Tile configuration: BM x BN workgroup tile (BN = 16 NT WN), WM x WN waves,
+// SA-deep LDS ring for A tiles and SB-deep ring for B tiles.
+template <int BM, int WM, int WN, int NT, int SA, int SB>
 struct GemmCfg {
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kBN = 16 * NT * WN;            // B rows per tile
-  static constexpr int kStage = (BM + kBN) * 128;     // LDS bytes per stage
-  static constexpr int kLds = STAGES * kStage;
-  static constexpr int kBM = BM, kWM = WM, kWN = WN, kNT = NT, kStages = STAGES;
+  static constexpr int kBN = 16 * NT * WN;                       // B rows per tile
+  static constexpr int kLds = SA * BM * 128 + SB * kBN * 128;    // LDS bytes
+  static constexpr int kBM = BM, kWM = WM, kWN = WN, kNT = NT, kSA = SA, kSB = SB;
 };
 
-template <typename T, int BM, int WM, int WN, int NT, int STAGES, bool GLU, bool GATHER>
+// Loader roles: waves 0 .. NW/2-1 move A tiles, waves NW/2 .. NW-1 move B
+// tiles.  Each wave's vmcnt then counts transfers of one operand only, so the
+// B (weight) ring can run SB-1 tiles ahead while the A ring runs SA-1 ahead:
+// a wave waiting for tile t waits for exactly the transfers of its operand
+// issued up to tile t.
+template <typename T, int BM, int WM, int WN, int NT, int SA, int SB, bool GLU, bool GATHER>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> g) {
-  using Cfg = GemmCfg<BM, WM, WN, NT, STAGES>;
+  using Cfg = GemmCfg<BM, WM, WN, NT, SA, SB>;
   static_assert(!GLU || NT % 2 == 0, "GLU pairs gate and up tiles");
+  static_assert(SA >= 2 && SB >= 2 && SA <= 6 && SB <= 6, "ring depth");
   constexpr int NW = Cfg::kWaves;
+  static_assert(NW % 2 == 0, "two loader roles");
+  constexpr int HW = NW / 2;                             // waves per loader role
   constexpr int BN = Cfg::kBN;
   constexpr int BK = 128 / static_cast<int>(sizeof(T));  // elements per K tile
   constexpr int KS = BK / 32;                            // 32-wide K steps per tile
   constexpr int FC = Frag<T>::kBytes / 16;               // 16-byte chunks per fragment
   constexpr int WTM = BM / WM;                           // wave tile rows
   constexpr int MT = WTM / 16;                           // MFMA row tiles per wave
-  constexpr int A_DMA = BM / 8, B_DMA = BN / 8;          // 1 KB transfers per stage
-  static_assert((A_DMA + B_DMA) % NW == 0, "transfers must split evenly over the waves");
-  constexpr int LPW = (A_DMA + B_DMA) / NW;              // transfers per wave per stage
-  constexpr int STAGE = Cfg::kStage;
+  constexpr int A_DMA = BM / 8, B_DMA = BN / 8;          // 1 KB transfers per tile
+  static_assert(A_DMA % HW == 0 && B_DMA % HW == 0, "transfers must split evenly");
+  constexpr int LPW_A = A_DMA / HW, LPW_B = B_DMA / HW;  // transfers per loader wave per tile
+  constexpr int LPW_M = LPW_A > LPW_B ? LPW_A : LPW_B;
+  constexpr int A_RING = 0, B_RING = SA * BM * 128;      // LDS byte offsets of the rings
   __shared__ __attribute__((aligned(1024))) char lds[Cfg::kLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  const bool role_a = wave < HW;
+  const int wr = role_a ? wave : wave - HW;  // index within the role
 
   // Workgroups are dealt round-robin over the 8 XCDs; renumber them so that
   // consecutive logical tiles (same B tile, neighbouring A tiles) share an XCD
@@ -126,25 +139,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> g) {
   const int k_end = min(g.K, k_begin + g.k_per_split);
   const int nk = (k_end - k_begin) / BK;
 
-  // Transfer j (0 <= j < A_DMA + B_DMA) of a stage covers tile rows 8j'..8j'+7
-  // of A (j' = j) or of B (j' = j - A_DMA); lane l fills physical chunk l & 7
-  // of row 8j' + (l >> 3) with logical chunk (l & 7) ^ (l >> 3).  Wave w owns
-  // transfers w, w + NW, w + 2 NW, ...
+  // Transfer j of an A (B) tile covers tile rows 8j .. 8j+7; lane l fills
+  // physical chunk l & 7 of row 8j + (l >> 3) with logical chunk
+  // (l & 7) ^ (l >> 3).  Loader wave w of a role owns transfers w, w + HW, ...
   const int sub = lane >> 3;
   const uint32_t cbyte = static_cast<uint32_t>(((lane & 7) ^ sub) * 16);
   const uint32_t kbyte0 = static_cast<uint32_t>(k_begin) * sizeof(T);
-  uint32_t off[LPW];
-  const T* base[LPW];
+  uint32_t off[LPW_M];
+  const T* base[LPW_M];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int j = wave + NW * i;
-    if (j < A_DMA) {
-      int m = min(m0 + 8 * j + sub, g.M - 1);  // rows past M repeat the last row; results dropped
-      if (GATHER) m = g.a_rows[m];
-      base[i] = g.A;
-      off[i] = static_cast<uint32_t>(m) * static_cast<uint32_t>(g.lda) * sizeof(T) + kbyte0 + cbyte;
-    } else {
-      const int r8 = 8 * (j - A_DMA);  // first B tile row of the transfer (wave-uniform)
+  for (int i = 0; i < LPW_M; ++i) {
+    const int j = wr + HW * i;
+    off[i] = 0;
+    base[i] = g.A;
+    if (role_a) {
+      if (i < LPW_A) {
+        int m = min(m0 + 8 * j + sub, g.M - 1);  // rows past M repeat the last row; results dropped
+        if (GATHER) m = g.a_rows[m];
+        off[i] = static_cast<uint32_t>(m) * static_cast<uint32_t>(g.lda) * sizeof(T) + kbyte0 + cbyte;
+      }
+    } else if (i < LPW_B) {
+      const int r8 = 8 * j;  // first B tile row of the transfer (wave-uniform)
       const int r = r8 + sub;
       int n;
       if (GLU) {
@@ -159,11 +174,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> g) {
   }
   const uint32_t lds0 = lds_addr(lds);
 
+  // Transfers of this wave's operand for K tile kt.
   auto issue = [&](int kt) {
-    const uint32_t st = lds0 + (kt % STAGES) * STAGE;
     const uint32_t kb = static_cast<uint32_t>(kt) * 128u;
+    if (role_a) {
+      const uint32_t st = lds0 + A_RING + (kt % SA) * (BM * 128);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) dma_1k(st + (wave + NW * i) * 1024, base[i], off[i] + kb);
+      for (int i = 0; i < LPW_A; ++i) dma_1k(st + (wr + HW * i) * 1024, base[i], off[i] + kb);
+    } else {
+      const uint32_t st = lds0 + B_RING + (kt % SB) * (BN * 128);
+#pragma unroll
+      for (int i = 0; i < LPW_B; ++i) dma_1k(st + (wr + HW * i) * 1024, base[i], off[i] + kb);
+    }
+  };
+  // Wait until tile t has landed, given that tiles up to `last` were issued.
+  auto wait_for = [&](int t, int last_a, int last_b) {
+    if (role_a) wait_tile<LPW_A, SA - 1>(max(0, last_a - t));
+    else wait_tile<LPW_B, SB - 1>(max(0, last_b - t));
   };
 
   f32x4_t acc[MT][NT];
@@ -183,9 +210,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> g) {
   const int swz = lane & 7;
   const int grp = lane >> 4;
 
-  // Fragment reads of K step ks of the tile at `as`: four B tiles, MT A tiles.
-  auto load = [&](const char* as, int ks, Frag<T> (&af)[MT], Frag<T> (&bf)[NT]) {
-    const char* bs = as + BM * 128;
+  // Fragment reads of K step ks of tile kt: four B tiles, MT A tiles.
+  auto load = [&](int kt, int ks, Frag<T> (&af)[MT], Frag<T> (&bf)[NT]) {
+    const char* as = lds + A_RING + (kt % SA) * (BM * 128);
+    const char* bs = lds + B_RING + (kt % SB) * (BN * 128);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const char* rowp = bs + (brow[nt] + (lane & 15)) * 128;
@@ -202,31 +230,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> g) {
     }
   };
 
-  // Pipeline: tiles 0 .. STAGES-1 are in flight before the loop.  The
-  // fragments of the next K step are read before the MFMAs of the current
-  // one; at the last K step of tile t the workgroup waits for tile t+1 (all
-  // waves have then also finished reading tile t, whose stage takes tile
-  // t + STAGES).
+  // Pipeline: before the loop, A tiles 0 .. SA-1 and B tiles 0 .. SB-1 are
+  // in flight.  The fragments of the next K step are read before the MFMAs of
+  // the current one; at the last K step of tile t the workgroup waits for
+  // tile t+1 (all waves have then finished reading tile t, whose ring slots
+  // take A tile t + SA and B tile t + SB).
+  const int S_own = role_a ? SA : SB;
   if (nk > 0) {
-#pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p)
-      if (p < nk) issue(p);
-    wait_tile<STAGES, LPW>(min(STAGES - 2, nk - 1));
-    if (STAGES - 1 < nk) issue(STAGES - 1);
+    for (int p = 0; p < S_own - 1 && p < nk; ++p) issue(p);
+    wait_for(0, min(SA - 2, nk - 1), min(SB - 2, nk - 1));
+    if (S_own - 1 < nk) issue(S_own - 1);
   }
   Frag<T> ca[MT], cb[NT];
-  if (nk > 0) load(lds, 0, ca, cb);
+  if (nk > 0) load(0, 0, ca, cb);
   for (int kt = 0; kt < nk; ++kt) {
-    const char* as = lds + (kt % STAGES) * STAGE;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       Frag<T> na[MT], nb_[NT];
       if (ks + 1 < KS) {
-        load(as, ks + 1, na, nb_);
+        load(kt, ks + 1, na, nb_);
       } else if (kt + 1 < nk) {
-        wait_tile<STAGES, LPW>(min(STAGES - 2, nk - 2 - kt));
-        if (kt + STAGES < nk) issue(kt + STAGES);
-        load(lds + ((kt + 1) % STAGES) * STAGE, 0, na, nb_);
+        wait_for(kt + 1, min(kt + SA - 1, nk - 1), min(kt + SB - 1, nk - 1));
+        if (kt + S_own < nk) issue(kt + S_own);
+        load(kt + 1, 0, na, nb_);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
