@@ -193,19 +193,36 @@ __device__ int block_coverage_cut(KeyFn key_of, ZFn z_of, int n, double thr, Emi
 // all radix passes and the emit pass then work on registers.  Same results as
 // the functions above.
 // ---------------------------------------------------------------------------
-// hist[bin] += val for every lane with `valid`.  Radix passes over keys of
-// similar magnitude put most lanes of a wave in one bin; when every valid lane
-// of the wave agrees on the bin, one lane adds the wave's sum (integer sums:
-// the same result as one add per lane).
-template <typename V>
-__device__ __forceinline__ void hist_add(V* hist, uint32_t bin, bool valid, V val) {
+// hist[bin] += 1 (hist_count) or += val (hist_sum) for every lane with
+// `valid`.  Radix passes over keys of similar magnitude put most lanes of a
+// wave in one bin; when every valid lane of the wave agrees on the bin, one
+// lane adds the wave's total (integer sums: the same result as one add per
+// lane).  Wave-uniform control flow; ballots, readlane and DPP only.
+__device__ __forceinline__ bool wave_same_bin(uint32_t bin, bool valid, uint64_t act, uint32_t* first) {
+  const int fl = __builtin_ctzll(act);
+  *first = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), fl));
+  return __ballot(valid && bin != *first) == 0;
+}
+
+__device__ __forceinline__ void hist_count(uint32_t* hist, uint32_t bin, bool valid) {
   const uint64_t act = __ballot(valid);
   if (act == 0) return;
-  const uint32_t lead = __builtin_amdgcn_readfirstlane(valid ? bin : 0xffffffffu);
-  const uint32_t first = lead != 0xffffffffu ? lead : static_cast<uint32_t>(__shfl(static_cast<int>(bin), __builtin_ctzll(act), kWave));
-  const bool same = __ballot(valid && bin != first) == 0;
-  if (same) {
-    V tot = wave_sum(valid ? val : V(0));
+  uint32_t first;
+  if (wave_same_bin(bin, valid, act, &first)) {
+    if ((threadIdx.x & (kWave - 1)) == static_cast<unsigned>(__builtin_ctzll(act)))
+      atomicAdd(&hist[first], static_cast<uint32_t>(__popcll(act)));
+  } else if (valid) {
+    atomicAdd(&hist[bin], 1u);
+  }
+}
+
+__device__ __forceinline__ void hist_sum(unsigned long long* hist, uint32_t bin, bool valid,
+                                         unsigned long long val) {
+  const uint64_t act = __ballot(valid);
+  if (act == 0) return;
+  uint32_t first;
+  if (wave_same_bin(bin, valid, act, &first)) {
+    const unsigned long long tot = static_cast<unsigned long long>(wave_sum_i64(valid ? static_cast<long long>(val) : 0));
     if ((threadIdx.x & (kWave - 1)) == static_cast<unsigned>(__builtin_ctzll(act))) atomicAdd(&hist[first], tot);
   } else if (valid) {
     atomicAdd(&hist[bin], val);
@@ -228,10 +245,10 @@ __device__ __forceinline__ void chunk_load(SelChunk<R>& c, int n, KeyFn key_of) 
   for (int j = 0; j < R; ++j) c.key[j] = (j < c.cnt) ? key_of(c.lo + j) : 0ull;
 }
 
-struct SelShared2 {
+struct alignas(16) SelShared2 {
   uint32_t hist[2][256];
   unsigned long long hsum[2][256];
-  unsigned long long scan[kSelThreads / kWave];
+  uint32_t scan[kSelThreads / kWave];
   uint64_t digit[2];
   long long above[2];
   int need;
@@ -248,22 +265,19 @@ __device__ __forceinline__ void chunk_pass(const SelChunk<R>& c, uint64_t prefix
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const bool v = j < c.cnt && (c.key[j] & pmask) == prefix;
-    hist_add(sm.hist[b], static_cast<uint32_t>((c.key[j] >> shift) & 255u), v, 1u);
+    hist_count(sm.hist[b], static_cast<uint32_t>((c.key[j] >> shift) & 255u), v);
   }
   __syncthreads();
   if (threadIdx.x < kWave) {
+    // lane owns bins 4 lane .. 4 lane + 3; count of candidates in the bins of
+    // higher lanes = total - inclusive prefix (DPP scan, counts < 2^32)
     const int lane = threadIdx.x;
-    long long cs = 0;
-    for (int j = 0; j < 4; ++j) cs += sm.hist[b][4 * lane + j];
-    long long rev = cs;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const long long u = __shfl_down(rev, o, kWave);
-      if (lane + o < kWave) rev += u;
-    }
-    long long above = rev - cs;
+    const u32x4_t h4 = *reinterpret_cast<const u32x4_t*>(&sm.hist[b][4 * lane]);
+    const uint32_t cs = h4[0] + h4[1] + h4[2] + h4[3];
+    const uint32_t inc = wave_incl_scan_u32(cs);
+    long long above = static_cast<long long>(wave_last_u32(inc) - inc);
     for (int j = 3; j >= 0; --j) {
-      const long long h = sm.hist[b][4 * lane + j];
+      const long long h = h4[j];
       if (above < remaining && remaining <= above + h) {
         sm.digit[b] = static_cast<uint64_t>(4 * lane + j);
         sm.above[b] = above;
@@ -282,15 +296,16 @@ __device__ __forceinline__ void chunk_pass(const SelChunk<R>& c, uint64_t prefix
 template <int R, class EmitFn>
 __device__ __forceinline__ int chunk_emit(const SelChunk<R>& c, uint64_t T, int need, EmitFn emit,
                                           SelShared2& sm) {
-  unsigned long long gt = 0, eq = 0;
+  uint32_t gt = 0, eq = 0;
 #pragma unroll
   for (int j = 0; j < R; ++j)
     if (j < c.cnt) { gt += c.key[j] > T; eq += c.key[j] == T; }
-  // one scan of (gt << 32 | eq): counts before this thread's chunk
-  unsigned long long tot;
-  const unsigned long long before = block_exclusive_scan((gt << 32) | eq, sm.scan, &tot);
-  const long long gt_before = static_cast<long long>(before >> 32);
-  long long e = static_cast<long long>(before & 0xffffffffull);
+  // one scan of (gt << 16 | eq) (both < 2^16 for n <= R blockDim <= 4096):
+  // counts before this thread's chunk
+  uint32_t tot;
+  const uint32_t before = block_exclusive_scan_u32((gt << 16) | eq, sm.scan, &tot);
+  const long long gt_before = static_cast<long long>(before >> 16);
+  long long e = static_cast<long long>(before & 0xffffu);
   long long pos = gt_before + min(e, static_cast<long long>(need));
 #pragma unroll
   for (int j = 0; j < R; ++j) {
@@ -299,7 +314,7 @@ __device__ __forceinline__ int chunk_emit(const SelChunk<R>& c, uint64_t T, int 
     if (c.key[j] == T) { s = e < need; ++e; }
     if (s) emit(c.lo + j, static_cast<int>(pos++), j);
   }
-  return static_cast<int>(tot >> 32) + need;
+  return static_cast<int>(tot >> 16) + need;
 }
 
 // Top k (1 <= k) of the cached keys in ascending index order.
@@ -339,21 +354,16 @@ __device__ int chunk_coverage_cut(const SelChunk<R>& c, int n, double thr, EmitF
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const bool v = j < c.cnt && (c.key[j] & pmask) == prefix;
-      hist_add(sm.hsum[b], static_cast<uint32_t>((c.key[j] >> shift) & 255u), v,
+      hist_sum(sm.hsum[b], static_cast<uint32_t>((c.key[j] >> shift) & 255u), v,
                static_cast<unsigned long long>(v ? c.z[j] : 0));
     }
     __syncthreads();
     if (threadIdx.x < kWave) {
       const int lane = threadIdx.x;
-      long long cs = 0;
-      for (int j = 0; j < 4; ++j) cs += static_cast<long long>(sm.hsum[b][4 * lane + j]);
-      long long rev = cs;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const long long u = __shfl_down(rev, o, kWave);
-        if (lane + o < kWave) rev += u;
-      }
-      long long above = before_sum + (rev - cs);
+      uint64_t cs = 0;
+      for (int j = 0; j < 4; ++j) cs += sm.hsum[b][4 * lane + j];
+      const uint64_t inc = wave_incl_scan_u64(cs);
+      long long above = before_sum + static_cast<long long>(wave_last_u64(inc) - inc);
       for (int j = 3; j >= 0; --j) {
         const long long h = static_cast<long long>(sm.hsum[b][4 * lane + j]);
         if (!(static_cast<double>(above) >= thr) && static_cast<double>(above + h) >= thr) {

@@ -83,6 +83,81 @@ __device__ __forceinline__ T wave_inclusive_scan(T v) {
   return v;
 }
 
+// DPP (gfx9 data-parallel primitives) wave scans: row_shr 1/2/4/8 within rows
+// of 16 lanes, then row_bcast 15 / 31 across rows.  Lanes without a source
+// add 0.  Much cheaper than cross-lane shuffles through LDS permutes.
+#define CGS_DPP(v, ctrl, rmask) \
+  static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), ctrl, rmask, 0xf, false))
+
+// Inclusive prefix sum of a 32-bit value across the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += CGS_DPP(v, 0x111, 0xf);  // row_shr:1
+  v += CGS_DPP(v, 0x112, 0xf);  // row_shr:2
+  v += CGS_DPP(v, 0x114, 0xf);  // row_shr:4
+  v += CGS_DPP(v, 0x118, 0xf);  // row_shr:8
+  v += CGS_DPP(v, 0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+  v += CGS_DPP(v, 0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Same for a 64-bit value, carried through two 32-bit halves.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+#define CGS_DPP64_STEP(ctrl, rmask)                \
+  {                                                \
+    const uint32_t l2 = CGS_DPP(lo, ctrl, rmask);  \
+    const uint32_t h2 = CGS_DPP(hi, ctrl, rmask);  \
+    const uint32_t nl = lo + l2;                   \
+    hi = hi + h2 + (nl < lo ? 1u : 0u);            \
+    lo = nl;                                       \
+  }
+  CGS_DPP64_STEP(0x111, 0xf)
+  CGS_DPP64_STEP(0x112, 0xf)
+  CGS_DPP64_STEP(0x114, 0xf)
+  CGS_DPP64_STEP(0x118, 0xf)
+  CGS_DPP64_STEP(0x142, 0xa)
+  CGS_DPP64_STEP(0x143, 0xc)
+#undef CGS_DPP64_STEP
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t wave_last_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+__device__ __forceinline__ uint64_t wave_last_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Sum of a 64-bit integer over the 64 lanes (two's complement, exact), every
+// lane receives it.
+__device__ __forceinline__ long long wave_sum_i64(long long v) {
+  return static_cast<long long>(wave_last_u64(wave_incl_scan_u64(static_cast<uint64_t>(v))));
+}
+
+// Exclusive prefix sum of a 32-bit value over all threads of a block
+// (blockDim.x a multiple of 64, at most 1024) with DPP wave scans; `scratch`
+// holds >= 16 values in LDS.  Also returns the block total.  Contains
+// barriers: call from every thread.
+__device__ __forceinline__ uint32_t block_exclusive_scan_u32(uint32_t v, uint32_t* scratch, uint32_t* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  const uint32_t inc = wave_incl_scan_u32(v);
+  if (lane == kWave - 1) scratch[wid] = inc;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const uint32_t s = scratch[w];
+    if (w < wid) off += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + inc - v;
+}
+
 // Exclusive prefix sum over all threads of a block (blockDim.x a multiple of
 // 64, at most 1024).  `scratch` holds >= 16 values of T in LDS.  Also
 // returns the block total.  Contains barriers: call from every thread.

@@ -167,7 +167,9 @@ __global__ __launch_bounds__(kRowThreads) void residual_rmsnorm_kernel(
 // Host planning
 // ---------------------------------------------------------------------------
 struct FfnPlan {
-  int tile, bm, bn, m_tiles, glu_ntiles, down_ntiles, splits, k_per_split;
+  int tile, bm, bn, m_tiles, glu_ntiles;       // gate/up projection
+  int dtile, dbm, dbn, dm_tiles, down_ntiles;  // down projection
+  int splits, k_per_split;
   size_t h_elems, part_elems;
 };
 
@@ -176,19 +178,34 @@ bool ffn_shape_ok(int d, int ff, int dtype) {
   return d > 0 && ff > 0 && d % 128 == 0 && d % bk == 0 && ff % 64 == 0 && ff % bk == 0;
 }
 
+void pick_tile(int tile, int* bm, int* bn) {
+  switch (tile) {
+    case kTileS: *bm = CfgS::kBM; *bn = CfgS::kBN; break;
+    case kTileM: *bm = CfgM::kBM; *bn = CfgM::kBN; break;
+    case kTileL: *bm = CfgL::kBM; *bn = CfgL::kBN; break;
+    default: *bm = CfgX::kBM; *bn = CfgX::kBN; break;
+  }
+}
+
 FfnPlan plan_ffn(int M, int d, int ff, int dtype) {
   FfnPlan p{};
   const int bk = 128 / elem_bytes(dtype);
-  if (M <= 64) { p.tile = kTileS; p.bm = CfgS::kBM; p.bn = CfgS::kBN; }
-  else if (M <= 128) { p.tile = kTileM; p.bm = CfgM::kBM; p.bn = CfgM::kBN; }
-  else if (M <= 256 || dtype != CGS_BF16 || d % CfgX::kBN != 0 || ff % (CfgX::kBN / 2) != 0) {
-    p.tile = kTileL; p.bm = CfgL::kBM; p.bn = CfgL::kBN;
-  } else { p.tile = kTileX; p.bm = CfgX::kBM; p.bn = CfgX::kBN; }
+  const bool wide = dtype == CGS_BF16 && d % CfgX::kBN == 0 && ff % (CfgX::kBN / 2) == 0;
+  if (M <= 64) p.tile = kTileS;
+  else if (M <= 128) p.tile = kTileM;
+  else if (M <= 256 || !wide) p.tile = kTileL;
+  else p.tile = kTileX;
+  // Down projection: 129..256 rows use two 128-row tiles, which keeps ~256
+  // workgroups with half the K splits (half the fp32 partial traffic).
+  p.dtile = (p.tile == kTileL && M <= 256) ? kTileM : p.tile;
+  pick_tile(p.tile, &p.bm, &p.bn);
+  pick_tile(p.dtile, &p.dbm, &p.dbn);
   p.m_tiles = std::max(1, (M + p.bm - 1) / p.bm);
   p.glu_ntiles = ff / (p.bn / 2);
-  p.down_ntiles = d / p.bn;
+  p.dm_tiles = std::max(1, (M + p.dbm - 1) / p.dbm);
+  p.down_ntiles = d / p.dbn;
   // split K of the down projection so that about 256 workgroups run
-  const int base = p.down_ntiles * p.m_tiles;
+  const int base = p.down_ntiles * p.dm_tiles;
   const int max_splits = std::max(1, ff / (8 * bk));
   const int splits = std::min(max_splits, std::max(1, (256 + base - 1) / base));
   const int kt = ff / bk;                                 // K tiles in total
@@ -217,9 +234,9 @@ void launch_ffn_core(const cgs_ffn& w, const T* A, const int32_t* a_rows, int M,
   q.A = H; q.lda = w.ff; q.a_rows = nullptr; q.M = M;
   q.B0 = static_cast<const T*>(w.w_down); q.ldb = w.ff;
   q.K = w.ff; q.k_per_split = p.k_per_split;
-  q.n_tiles = p.down_ntiles; q.m_tiles = p.m_tiles; q.splits = p.splits;
+  q.n_tiles = p.down_ntiles; q.m_tiles = p.dm_tiles; q.splits = p.splits;
   q.C = part; q.ldc = w.d; q.split_stride = static_cast<size_t>(M) * w.d;
-  launch_tile<T, false, false>(p.tile, q, down_site, s);
+  launch_tile<T, false, false>(p.dtile, q, down_site, s);
 }
 
 bool ffn_ok(const cgs_ffn* w, int layout) {

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void contrib_kernel(const float* __restrict__ 
     const double w = static_cast<double>(Elem<T>::to_f32(wr[j]));
     b += static_cast<long long>(rint((w * w) * kTwo40));
   }
-  b = wave_sum(b);
+  b = wave_sum_i64(b);
   const double nrm = __dsqrt_rn(static_cast<double>(b));
   long long atot = 0;
   for (int t = 0; t < T_steps; ++t) {
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void contrib_kernel(const float* __restrict__ 
     long long a = 0;
     for (int r = lane; r < S; r += 64)
       a += static_cast<long long>(rint(fabs(static_cast<double>(hr[r])) * kTwo24));
-    a = wave_sum(a);
+    a = wave_sum_i64(a);
     atot += a;
     if (lane == 0) ckey[static_cast<size_t>(t) * ff + n] = ordered_key(static_cast<double>(a) * nrm);
   }

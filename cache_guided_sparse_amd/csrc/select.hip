@@ -90,16 +90,16 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ x,
     for (int j = lane; j < d; j += kWave)
       accum(static_cast<double>(Elem<T>::to_f32(xp[j])), static_cast<double>(Elem<T>::to_f32(rp[j])));
   }
-  sx = wave_sum(sx);
+  sx = wave_sum_i64(sx);
   double key;
   if (kCosine) {
-    sy = wave_sum(sy);
-    sxy = wave_sum(sxy);
+    sy = wave_sum_i64(sy);
+    sxy = wave_sum_i64(sxy);
     const double q = static_cast<double>(sxy);
     const double den = static_cast<double>(sx) * static_cast<double>(sy);
     key = (den == 0.0) ? 1.0 : 1.0 - (q * fabs(q)) / den;
   } else {
-    sd = wave_sum(sd);
+    sd = wave_sum_i64(sd);
     const long long den = sx > floor_e ? sx : floor_e;
     key = static_cast<double>(sd) / static_cast<double>(den);
   }
