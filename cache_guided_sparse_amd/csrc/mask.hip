@@ -28,29 +28,81 @@ namespace {
 constexpr double kTwo24 = 16777216.0;      // 2^24
 constexpr double kTwo40 = 1099511627776.0; // 2^40
 
+// Eight consecutive weights of a row as float64 (exact).
+template <typename T> struct W8;
+template <> struct W8<uint16_t> {
+  static __device__ __forceinline__ void load(const uint16_t* p, double* v) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = static_cast<double>(__uint_as_float(u[i] << 16));
+      v[2 * i + 1] = static_cast<double>(__uint_as_float(u[i] & 0xffff0000u));
+    }
+  }
+};
+template <> struct W8<float> {
+  static __device__ __forceinline__ void load(const float* p, double* v) {
+    const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0], b = reinterpret_cast<const f32x4_t*>(p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+};
+
+constexpr int kContribT = 8;  // reference steps whose activations are loaded up front
+
 template <typename T>
 __global__ __launch_bounds__(256) void contrib_kernel(const float* __restrict__ h, int T_steps,
                                                       int S, const T* __restrict__ wd, int d, int ff,
                                                       uint64_t* __restrict__ ckey,
                                                       uint64_t* __restrict__ skey,
-                                                      double* __restrict__ sval) {
+                                                      double* __restrict__ sval, bool vec) {
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= ff) return;
-  long long b = 0;
   const T* wr = wd + static_cast<size_t>(n) * d;
-  for (int j = lane; j < d; j += 64) {
-    const double w = static_cast<double>(Elem<T>::to_f32(wr[j]));
-    b += static_cast<long long>(rint((w * w) * kTwo40));
+  // The activations of up to kContribT steps (S <= 64: one per lane) are
+  // fetched before the weight row, so both loads are in flight together.
+  const bool fast_h = T_steps <= kContribT && S <= kWave;
+  float hv[kContribT];
+#pragma unroll
+  for (int t = 0; t < kContribT; ++t)
+    hv[t] = (fast_h && t < T_steps && lane < S) ? h[(static_cast<size_t>(t) * ff + n) * S + lane] : 0.f;
+  long long b = 0;
+  if (vec) {
+    for (int j0 = lane * 8; j0 < d; j0 += 4 * kWave * 8) {
+      double w[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (j0 + q * kWave * 8 < d) W8<T>::load(wr + j0 + q * kWave * 8, w[q]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (j0 + q * kWave * 8 >= d) continue;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b += static_cast<long long>(rint((w[q][i] * w[q][i]) * kTwo40));
+      }
+    }
+  } else {
+    for (int j = lane; j < d; j += kWave) {
+      const double w = static_cast<double>(Elem<T>::to_f32(wr[j]));
+      b += static_cast<long long>(rint((w * w) * kTwo40));
+    }
   }
   b = wave_sum_i64(b);
   const double nrm = __dsqrt_rn(static_cast<double>(b));
   long long atot = 0;
   for (int t = 0; t < T_steps; ++t) {
-    const float* hr = h + (static_cast<size_t>(t) * ff + n) * S;
     long long a = 0;
-    for (int r = lane; r < S; r += 64)
-      a += static_cast<long long>(rint(fabs(static_cast<double>(hr[r])) * kTwo24));
+    if (fast_h) {
+      float hvt = 0.f;
+#pragma unroll
+      for (int q = 0; q < kContribT; ++q)
+        if (q == t) hvt = hv[q];
+      a = static_cast<long long>(rint(fabs(static_cast<double>(hvt)) * kTwo24));
+    } else {
+      const float* hr = h + (static_cast<size_t>(t) * ff + n) * S;
+      for (int r = lane; r < S; r += kWave)
+        a += static_cast<long long>(rint(fabs(static_cast<double>(hr[r])) * kTwo24));
+    }
     a = wave_sum_i64(a);
     atot += a;
     if (lane == 0) ckey[static_cast<size_t>(t) * ff + n] = ordered_key(static_cast<double>(a) * nrm);
@@ -266,12 +318,15 @@ extern "C" int act_build_mask(const float* h_ref, int T, int S, const cgs_ffn* w
   const dim3 grid((ff + 3) / 4), block(256);
   {
   ProfScope ps("mask.contrib", s);
+  // 16-byte weight loads when every row starts 16-byte aligned
+  const bool vec = d % 8 == 0 && reinterpret_cast<uintptr_t>(w->w_down) % 16 == 0 &&
+                   (static_cast<size_t>(d) * elem_bytes(w->dtype)) % 16 == 0;
   if (w->dtype == CGS_BF16)
     hipLaunchKernelGGL((contrib_kernel<uint16_t>), grid, block, 0, s, h_ref, T, S,
-                       static_cast<const uint16_t*>(w->w_down), d, ff, m.ckey, m.skey, m.sval);
+                       static_cast<const uint16_t*>(w->w_down), d, ff, m.ckey, m.skey, m.sval, vec);
   else
     hipLaunchKernelGGL((contrib_kernel<float>), grid, block, 0, s, h_ref, T, S,
-                       static_cast<const float*>(w->w_down), d, ff, m.ckey, m.skey, m.sval);
+                       static_cast<const float*>(w->w_down), d, ff, m.ckey, m.skey, m.sval, vec);
   }
   if (!launch_ok()) return CGS_ERR_LAUNCH;
   const int q_bits = 61 - bit_length(static_cast<unsigned>(ff - 1));
