@@ -36,17 +36,28 @@ class CgsError(RuntimeError):
 
 
 class _Glue(ctypes.Structure):
-    _fields_ = [("r", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("x_next", ctypes.c_void_p)]
+    _fields_ = [("r", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("x_next", ctypes.c_void_p),
+                ("score_ref", ctypes.c_void_p), ("score_key", ctypes.c_void_p),
+                ("score_kind", ctypes.c_int32)]
 
 
 def _glue(glue):
-    """Optional (r, bias, x_next) residual/RMSNorm glue -> cgs_glue pointer or None."""
+    """Optional residual/RMSNorm glue -> cgs_glue pointer or None.
+
+    ``glue`` = (r, bias, x_next) or (r, bias, x_next, score_ref, score_key[, kind]):
+    r += y (+ bias), x_next = RMSNorm(r), and optionally the Eq. 2 keys of x_next
+    against score_ref into score_key (float64 [rows])."""
     if glue is None:
         return None
-    r, bias, x_next = glue
+    r, bias, x_next = glue[:3]
+    score_ref = glue[3] if len(glue) > 3 else None
+    score_key = glue[4] if len(glue) > 4 else None
+    kind = _KIND[glue[5]] if len(glue) > 5 else CGS_SCORE_REL_RMS
     if r is None or r.dtype != torch.float32:
         raise CgsError("glue residual r must be a float32 device tensor")
-    return ctypes.byref(_Glue(_ptr(r), _ptr(bias), _ptr(x_next)))
+    if score_key is not None and score_key.dtype != torch.float64:
+        raise CgsError("glue score_key must be a float64 device tensor")
+    return ctypes.byref(_Glue(_ptr(r), _ptr(bias), _ptr(x_next), _ptr(score_ref), _ptr(score_key), kind))
 
 
 class _Ffn(ctypes.Structure):
@@ -63,6 +74,7 @@ _SIGS = {
     "cgs_version": (_i, []),
     "cgs_ctx_select_workspace": (_sz, [_i, _i]),
     "ctx_select": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "ctx_select_from_keys": (_i, [_vp, _i, _i, _vp, _vp]),
     "cgs_ctx_ffn_recompute_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "ctx_ffn_recompute": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "cgs_act_build_mask_workspace": (_sz, [_i, _i, _i, _i]),
@@ -175,6 +187,16 @@ def ctx_select(x, x_ref, k: int, kind: str = "rel_rms", idx_out=None, key_out=No
     _check(lib().ctx_select(_ptr(x), _ptr(x_ref), P, d, _dtype_code(x), int(k), _KIND[kind],
                             _ptr(idx_out), _ptr(key_out), _ptr(ws), ws.numel(), _stream(stream)),
            "ctx_select")
+    return idx_out
+
+
+def ctx_select_from_keys(keys, k: int, idx_out=None, stream=None):
+    """The k highest of precomputed Eq. 2 keys (float64 [P]), indices ascending."""
+    P = int(keys.numel())
+    if idx_out is None:
+        idx_out = torch.empty(int(k), dtype=torch.int32, device=keys.device)
+    _check(lib().ctx_select_from_keys(_ptr(keys), P, int(k), _ptr(idx_out), _stream(stream)),
+           "ctx_select_from_keys")
     return idx_out
 
 

@@ -311,7 +311,7 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
   }
   ProfScope ps("act.finish", s);
   hipLaunchKernelGGL((act_finish_kernel<T>), dim3(S), dim3(kThreads), 0, s, part, K > 0 ? p.splits : 0,
-                     S, w.d, ya, y_out, y_f32, make_glue<T>(gl));
+                     S, w.d, ya, y_out, y_f32, make_glue<T>(gl, w.d));
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
 }
 

@@ -258,7 +258,7 @@ int ctx_recompute_t(const cgs_ffn& w, const T* x, const T* y_ref, const int32_t*
   {
     ProfScope ps("ctx.finish", s);
     hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kRowThreads), 0, s, part, p.splits,
-                       static_cast<size_t>(k) * w.d, w.d, true, idx, k, y_ref, y_out, make_glue<T>(gl));
+                       static_cast<size_t>(k) * w.d, w.d, true, idx, k, y_ref, y_out, make_glue<T>(gl, w.d));
   }
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
 }
@@ -285,7 +285,8 @@ int rebuild_t(const cgs_ffn* layers, int L, const T* r0, int P, T* xo, T* yo, vo
     hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kRowThreads), 0, s, part, p.splits, lay,
                        w0.d, false, static_cast<const int32_t*>(nullptr), P, static_cast<const T*>(nullptr),
                        yo + l * lay,
-                       GlueArgs<T>{r, nullptr, (l + 1 < L) ? xo + (l + 1) * lay : static_cast<T*>(nullptr)});
+                       GlueArgs<T>{r, nullptr, (l + 1 < L) ? xo + (l + 1) * lay : static_cast<T*>(nullptr),
+                                  nullptr, nullptr, 0, 0});
     if (!launch_ok()) return CGS_ERR_LAUNCH;
   }
   return CGS_OK;

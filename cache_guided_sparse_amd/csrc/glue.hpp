@@ -8,6 +8,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "score.hpp"
 
 namespace cgs {
 
@@ -91,17 +92,34 @@ __device__ __forceinline__ void add_splits(const float* part, size_t stride, int
 }
 
 template <typename T> struct GlueArgs {
-  float* r;            // [rows][d] residual stream (NULL: no glue)
-  const float* bias;   // [d] or NULL
-  T* x_next;           // [rows][d] or NULL
+  float* r;             // [rows][d] residual stream (NULL: no glue)
+  const float* bias;    // [d] or NULL
+  T* x_next;            // [rows][d] or NULL
+  const T* score_ref;   // [rows][d] or NULL: score x_next against it (Eq. 2)
+  double* score_key;    // [rows]
+  int score_kind;       // cgs_score_kind
+  long long score_floor;
 };
 
-inline bool glue_ok(const cgs_glue* g) { return !g || g->r; }
+inline bool glue_ok(const cgs_glue* g) {
+  if (!g) return true;
+  if (!g->r) return false;
+  if (g->score_key && (!g->x_next || !g->score_ref)) return false;
+  return g->score_kind == CGS_SCORE_REL_RMS || g->score_kind == CGS_SCORE_COSINE;
+}
 
 template <typename T>
-inline GlueArgs<T> make_glue(const cgs_glue* g) {
-  GlueArgs<T> a{nullptr, nullptr, nullptr};
-  if (g) { a.r = g->r; a.bias = g->bias; a.x_next = static_cast<T*>(g->x_next); }
+inline GlueArgs<T> make_glue(const cgs_glue* g, int d) {
+  GlueArgs<T> a{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
+  if (g) {
+    a.r = g->r; a.bias = g->bias; a.x_next = static_cast<T*>(g->x_next);
+    if (g->score_key) {
+      a.score_ref = static_cast<const T*>(g->score_ref);
+      a.score_key = g->score_key;
+      a.score_kind = g->score_kind;
+      a.score_floor = score_floor(d);
+    }
+  }
   return a;
 }
 
@@ -124,18 +142,58 @@ __device__ __forceinline__ float glue_add(const GlueArgs<T>& g, size_t ro, int c
   return ss;
 }
 
+// Integer sum over a workgroup of NT threads (exact, so its order is free).
+template <int NT>
+__device__ __forceinline__ long long block_sum_i64(long long v, long long* red) {
+  v = wave_sum_i64(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  long long t = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
 // x_next[row] = RMSNorm(r[row]) for the runs c = 8 threadIdx.x + 8 NT j that
-// this thread updated with glue_add; `ss` is its partial sum of squares.
+// this thread updated with glue_add; `ss` is its partial sum of squares.  With
+// a score reference, also the Eq. 2 key of the stored (rounded) x_next row
+// against it, exactly as the standalone score kernel computes it.
 template <typename T, int NT>
 __device__ __forceinline__ void glue_norm_t(const GlueArgs<T>& g, size_t ro, int d, float ss, float* red) {
   const float tot = block_sum<NT>(ss, red);
   const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + 1e-6f);
+  ScoreSums sc;
+  const bool cosine = g.score_kind == CGS_SCORE_COSINE;
   for (int c = threadIdx.x * 8; c < d; c += NT * 8) {
     float rr[8];
     Row8<float>::load(g.r + ro + c, rr);
 #pragma unroll
     for (int e = 0; e < 8; ++e) rr[e] *= inv;
     Row8<T>::store(g.x_next + ro + c, rr);
+    if (g.score_key) {
+      float xr[8];
+      Row8<T>::round(rr);
+      Row8<T>::load(g.score_ref + ro + c, xr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (cosine) sc.add<true>(static_cast<double>(rr[e]), static_cast<double>(xr[e]));
+        else sc.add<false>(static_cast<double>(rr[e]), static_cast<double>(xr[e]));
+      }
+    }
+  }
+  if (g.score_key) {
+    __shared__ long long lred[NT / 64];
+    sc.sx = block_sum_i64<NT>(sc.sx, lred);
+    if (cosine) {
+      sc.sy = block_sum_i64<NT>(sc.sy, lred);
+      sc.sxy = block_sum_i64<NT>(sc.sxy, lred);
+    } else {
+      sc.sd = block_sum_i64<NT>(sc.sd, lred);
+    }
+    if (threadIdx.x == 0)
+      g.score_key[ro / d] = cosine ? score_key<true>(sc, g.score_floor) : score_key<false>(sc, g.score_floor);
   }
 }
 

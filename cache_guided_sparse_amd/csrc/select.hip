@@ -15,11 +15,10 @@
 #include "block_select.hpp"
 #include "common.hpp"
 #include "profile.hpp"
+#include "score.hpp"
 
 namespace cgs {
 namespace {
-
-constexpr double kTwo24 = 16777216.0;  // 2^24
 
 template <typename T> struct Vec8;
 template <> struct Vec8<uint16_t> {
@@ -42,10 +41,6 @@ template <> struct Vec8<float> {
   }
 };
 
-__device__ __forceinline__ long long fixed_term(double t) {
-  return static_cast<long long>(rint(t * kTwo24));
-}
-
 template <typename T, bool kCosine>
 __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ x,
                                                     const T* __restrict__ xr, int P, int d,
@@ -57,18 +52,8 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ x,
   if (p >= P) return;
   const T* xp = x + static_cast<size_t>(p) * d;
   const T* rp = xr + static_cast<size_t>(p) * d;
-  long long sd = 0, sx = 0, sy = 0, sxy = 0;
-  auto accum = [&](double a, double b) {
-    if (kCosine) {
-      sx += fixed_term(a * a);
-      sy += fixed_term(b * b);
-      sxy += fixed_term(a * b);
-    } else {
-      const double df = a - b;
-      sd += fixed_term(df * df);
-      sx += fixed_term(a * a);
-    }
-  };
+  ScoreSums acc;
+  auto accum = [&](double a, double b) { acc.add<kCosine>(a, b); };
   if (vec) {
     // four 8-element runs per lane in flight at once (d = 2048 bf16: one batch)
     for (int j0 = lane * 8; j0 < d; j0 += 4 * kWave * 8) {
@@ -90,19 +75,14 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ x,
     for (int j = lane; j < d; j += kWave)
       accum(static_cast<double>(Elem<T>::to_f32(xp[j])), static_cast<double>(Elem<T>::to_f32(rp[j])));
   }
-  sx = wave_sum_i64(sx);
-  double key;
+  acc.sx = wave_sum_i64(acc.sx);
   if (kCosine) {
-    sy = wave_sum_i64(sy);
-    sxy = wave_sum_i64(sxy);
-    const double q = static_cast<double>(sxy);
-    const double den = static_cast<double>(sx) * static_cast<double>(sy);
-    key = (den == 0.0) ? 1.0 : 1.0 - (q * fabs(q)) / den;
+    acc.sy = wave_sum_i64(acc.sy);
+    acc.sxy = wave_sum_i64(acc.sxy);
   } else {
-    sd = wave_sum_i64(sd);
-    const long long den = sx > floor_e ? sx : floor_e;
-    key = static_cast<double>(sd) / static_cast<double>(den);
+    acc.sd = wave_sum_i64(acc.sd);
   }
+  const double key = score_key<kCosine>(acc, floor_e);
   if (lane == 0) {
     okeys[p] = ordered_key(key);
     if (key_out) key_out[p] = key;
@@ -124,10 +104,36 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const uint64_t* __res
              [&](int i, int pos) { idx_out[pos] = i; }, sm);
 }
 
+// Top k of precomputed float64 keys (the scores a finish kernel wrote).
+__global__ __launch_bounds__(kSelThreads) void topk_values_kernel(const double* __restrict__ keys,
+                                                                  int P, int k,
+                                                                  int32_t* __restrict__ idx_out) {
+  __shared__ SelShared sm;
+  __shared__ SelShared2 sm2;
+  if (P <= 4 * kSelThreads) {
+    SelChunk<4> c;
+    chunk_load(c, P, [&](int i) { return ordered_key(keys[i]); });
+    chunk_topk(c, P, k, [&](int i, int pos, int) { idx_out[pos] = i; }, sm2);
+    return;
+  }
+  block_topk([&](int i) { return ordered_key(keys[i]); }, P, k,
+             [&](int i, int pos) { idx_out[pos] = i; }, sm);
+}
+
 }  // namespace
 }  // namespace cgs
 
 using namespace cgs;
+
+extern "C" int ctx_select_from_keys(const double* keys, int P, int k, int32_t* idx_out, void* stream) {
+  if (P < 0 || k < 0 || k > P || P > 65536) return CGS_ERR_SHAPE;
+  if (P == 0 || k == 0) return CGS_OK;
+  if (!keys || !idx_out) return CGS_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ProfScope ps("ctx.topk", s);
+  hipLaunchKernelGGL(topk_values_kernel, dim3(1), dim3(kSelThreads), 0, s, keys, P, k, idx_out);
+  return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
+}
 
 extern "C" size_t cgs_ctx_select_workspace(int P, int d) {
   (void)d;
@@ -147,7 +153,7 @@ extern "C" int ctx_select(const void* x, const void* x_ref, int P, int d, int dt
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint64_t* okeys = static_cast<uint64_t*>(ws);
   // d * eps^2 in the 2^-24 fixed point, rounded up, at least 1 (eps = 1e-6)
-  const long long floor_e = std::max<long long>(1, (static_cast<long long>(d) * (1ll << 24) + 999999999999ll) / 1000000000000ll);
+  const long long floor_e = score_floor(d);
   const int eb = elem_bytes(dtype);
   const bool vec = (d % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(x_ref) % 16 == 0) && ((static_cast<size_t>(d) * eb) % 16 == 0);

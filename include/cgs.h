@@ -83,9 +83,16 @@ typedef struct {
  * with round() the rounding of y to the FFN dtype, RMSNorm(v) = v /
  * sqrt(mean(v^2) + 1e-6) (no learned scale), r fp32.  Pass NULL for none. */
 typedef struct {
-  float* r;            /* [rows][d] fp32 residual stream, updated in place; required */
-  const float* bias;   /* [d] fp32 added to r after y, or NULL */
-  void* x_next;        /* [rows][d] in the FFN dtype, or NULL */
+  float* r;              /* [rows][d] fp32 residual stream, updated in place; required */
+  const float* bias;     /* [d] fp32 added to r after y, or NULL */
+  void* x_next;          /* [rows][d] in the FFN dtype, or NULL */
+  /* Optional fusion of the next layer's token score (§4.1, Eq. 2): with
+   * score_key non-NULL (x_next and score_ref required), every row's key of
+   * x_next against score_ref is written exactly as ctx_select computes it
+   * (key_out), so the next selection is ctx_select_from_keys. */
+  const void* score_ref; /* [rows][d] in the FFN dtype: the next layer's cached input */
+  double* score_key;     /* [rows] out, or NULL */
+  int32_t score_kind;    /* cgs_score_kind */
 } cgs_glue;
 
 /* ---- host helpers ------------------------------------------------------ */
@@ -121,6 +128,12 @@ size_t cgs_ctx_select_workspace(int P, int d);
  * |x|, |x_ref| <= 2^12 and d <= 4096.  P <= 65536. */
 int ctx_select(const void* x, const void* x_ref, int P, int d, int dtype, int k, int kind,
                int32_t* idx_out, double* key_out, void* ws, size_t ws_bytes, void* stream);
+
+/* §4.1: the set P_l(rho_p) from scores already computed (the key_out of
+ * ctx_select, or the score_key of a finish kernel's glue): the k highest keys,
+ * indices ascending, ties to the lower index.  keys: [P] double (device);
+ * k <= P <= 65536.  No workspace. */
+int ctx_select_from_keys(const double* keys, int P, int k, int32_t* idx_out, void* stream);
 
 /* Workspace bytes for ctx_ffn_recompute with k selected rows. */
 size_t cgs_ctx_ffn_recompute_workspace(int k, int P, int d, int ff, int dtype);

@@ -96,6 +96,15 @@ def test_host_validation_without_launch():
     g = cgs._Glue(None, None, None)
     assert L.act_ffn_masked(ctypes.byref(wf), buf, 4, buf, 10, None, None, buf, None, None, ctypes.byref(g), buf, 1 << 30, None) == 1
     assert L.ctx_ffn_recompute(ctypes.byref(w), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), ctypes.byref(g), buf, 1 << 30, None) == 1
+    # glue score keys without x_next / score_ref, or with an unknown kind
+    for g in (cgs._Glue(buf, None, None, buf, buf, 0), cgs._Glue(buf, None, buf, None, buf, 0),
+              cgs._Glue(buf, None, buf, buf, buf, 7)):
+        assert L.ctx_ffn_recompute(ctypes.byref(w), buf, buf, buf, 1, 8, ctypes.c_void_p(0x2000), ctypes.byref(g), buf, 1 << 30, None) == 1
+    # ctx_select_from_keys: k > P, P too large, null keys; empty is a no-op
+    assert L.ctx_select_from_keys(buf, 8, 9, buf, None) == 2
+    assert L.ctx_select_from_keys(buf, 70000, 1, buf, None) == 2
+    assert L.ctx_select_from_keys(None, 8, 1, buf, None) == 1
+    assert L.ctx_select_from_keys(None, 8, 0, None, None) == 0
     # act_build_mask: bad mode, K, coverage, S*T too large
     assert L.act_build_mask(buf, 2, 8, ctypes.byref(wf), 9, 4, 0.0, buf, buf, buf, buf, 1 << 30, None) == 1
     assert L.act_build_mask(buf, 2, 8, ctypes.byref(wf), 0, 5000, 0.0, buf, buf, buf, buf, 1 << 30, None) == 2

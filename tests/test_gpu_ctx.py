@@ -120,3 +120,44 @@ def test_fused_glue():
     r_exp = r0.astype(np.float64) + values(y)
     assert_close(values(r), r_exp, "residual")
     assert_close(values(xn), O.rms_norm(r_exp), "x_next", out="bf16")
+
+
+@pytest.mark.parametrize("kind", ["rel_rms", "cosine"])
+def test_fused_next_score(kind):
+    """The finish kernel's Eq. 2 keys of x_next against the next layer's cached
+    input are bit-identical to ctx_select's keys of the same pair and to the
+    oracle's; selecting from them gives the oracle's index set."""
+    say("ctx fused score", kind)
+    P, d, ff, k = 300, 256, 512, 90
+    inp = ctx_layer_inputs(22, 0, P, d, k, 1.3333, 0.1752)
+    nxt = ctx_layer_inputs(22, 1, P, d, k, 1.3333, 0.1752)
+    w = ffn_weights(22, 0, d, ff)
+    y_ref = random_bf16(22, 0, "y_ref", (P, d))
+    idx, _ = O.ctx_select(inp["x"], inp["x_ref"], k)
+    r = to_dev(rng(22, 1, "misc").standard_normal((P, d)).astype(np.float32), "f32")
+    xn = torch.empty(P, d, dtype=torch.bfloat16, device=dev())
+    xr = to_dev(nxt["x_ref"])
+    keys = torch.full((P,), -1.0, dtype=torch.float64, device=dev())
+    cgs.ctx_ffn_recompute(ffn_dev(w), to_dev(inp["x"]), to_dev(y_ref), torch.from_numpy(idx).to(dev()),
+                          glue=(r, None, xn, xr, keys, kind))
+    sel = cgs.ctx_select_from_keys(keys, k)
+    keys2 = torch.empty(P, dtype=torch.float64, device=dev())
+    sel2 = cgs.ctx_select(xn, xr, k, kind=kind, key_out=keys2)
+    torch.cuda.synchronize()
+    assert torch.equal(keys, keys2), "fused keys differ from ctx_select's"
+    assert torch.equal(sel, sel2)
+    idx_o, keys_o = O.ctx_select(bits(xn), nxt["x_ref"], k, kind=kind)
+    assert np.array_equal(keys.cpu().numpy(), keys_o)
+    assert np.array_equal(sel.cpu().numpy(), idx_o)
+
+
+@pytest.mark.parametrize("P,k", [(1, 1), (7, 3), (1024, 1), (1024, 1024), (4096, 2731), (5000, 1667)])
+def test_select_from_keys(P, k):
+    """Top k of stored keys with ties (repeated values) to the lower index,
+    on both the one-chunk (P <= 1024) and the general path."""
+    say("select from keys", P, k)
+    g = rng(23, P, "misc")
+    keys = np.round(g.standard_normal(P), 1) + 0.0  # many equal keys, no -0.0
+    idx = cgs.ctx_select_from_keys(torch.from_numpy(keys).to(dev()), k)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), O.topk_ascending(keys, k))

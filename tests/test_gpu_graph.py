@@ -64,8 +64,9 @@ def test_act_masked_chain_graph():
     _replays_match(run, reset, [y, r, x])
 
 
-def test_ctx_chain_graph():
-    say("graph ctx chain")
+@pytest.mark.parametrize("fused_score", [False, True])
+def test_ctx_chain_graph(fused_score):
+    say("graph ctx chain", fused_score)
     P, d, ff, L, k = 300, 256, 512, 3, 90
     ws = [ffn_weights(31, l, d, ff) for l in range(L)]
     W = [ffn_dev(w) for w in ws]
@@ -76,14 +77,22 @@ def test_ctx_chain_graph():
     x = torch.empty(P, d, dtype=torch.bfloat16, device=dev())
     y = torch.empty_like(x)
     idx = torch.empty(k, dtype=torch.int32, device=dev())
+    keys = torch.empty(P, dtype=torch.float64, device=dev())
 
     def reset():
         cgs.residual_rmsnorm(r, r_in=cur.float().contiguous(), x_out=x)
 
     def run():
         for l in range(L):
-            cgs.ctx_select(x, xr[l], k, idx_out=idx)
-            cgs.ctx_ffn_recompute(W[l], x, yr[l], idx, y_out=y, glue=(r, None, x if l + 1 < L else None))
+            if l == 0 or not fused_score:
+                cgs.ctx_select(x, xr[l], k, idx_out=idx)
+            else:
+                cgs.ctx_select_from_keys(keys, k, idx_out=idx)
+            if fused_score and l + 1 < L:
+                glue = (r, None, x, xr[l + 1], keys)
+            else:
+                glue = (r, None, x if l + 1 < L else None)
+            cgs.ctx_ffn_recompute(W[l], x, yr[l], idx, y_out=y, glue=glue)
 
     _replays_match(run, reset, [y, r, x, idx])
     assert np.all(np.diff(idx.cpu().numpy()) > 0)
