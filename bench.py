@@ -328,6 +328,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graphs", action="store_true",
                     help="launch every kernel eagerly instead of replaying HIP graphs")
+    ap.add_argument("--rebuild-stream", choices=("side", "main"), default="main",
+                    help="run the entry rebuild on a side stream (overlapped) or in line")
+    ap.add_argument("--serial-steps", type=int, default=8,
+                    help="calls timed with everything on one stream, for comparison")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -344,34 +348,68 @@ def main():
     w = World(dev)
 
     phases = ["ctx_prefill", "act_anchor", "act_masked", "mask_build", "rebuild"]
+    # The rebuild of the entry 16 calls ahead runs on a side stream (default
+    # priority): it waits for the call's context prefill to release the slot,
+    # and the prefill that next uses the slot waits for the rebuild.
+    main_s = torch.cuda.current_stream()
+    side = torch.cuda.Stream(device=dev) if args.rebuild_stream == "side" else None
+    ctx_done = [torch.cuda.Event() for _ in range(SLOTS)]
+    rebuilt = [torch.cuda.Event() for _ in range(SLOTS)]
+    pending = [False] * SLOTS
 
-    def step(i, ev=None):
-        if ev is not None:
-            ev[0].record()
+    def step(i, ev=None, serial=False):
+        """One call.  ev: 7 timing events; 0-4 bracket the main-stream phases,
+        5-6 the rebuild on the stream that runs it."""
+        e = i % SLOTS
+        rec = (lambda q: ev[q].record()) if ev is not None else (lambda q: None)
+        if pending[e]:
+            main_s.wait_event(rebuilt[e])
+            pending[e] = False
+        rec(0)
         w.ctx_prefill(i)
-        if ev is not None:
-            ev[1].record()
+        rec(1)
+        if side is not None and not serial:
+            ctx_done[e].record(main_s)
+            with torch.cuda.stream(side):
+                side.wait_event(ctx_done[e])
+                rec(5)
+                w.rebuild(i)
+                rec(6)
+                rebuilt[e].record(side)
+            pending[e] = True
         w.act_anchor()
-        if ev is not None:
-            ev[2].record()
+        rec(2)
         w.act_masked()
-        if ev is not None:
-            ev[3].record()
+        rec(3)
         w.mask_build()
-        if ev is not None:
-            ev[4].record()
-        w.rebuild(i)
-        if ev is not None:
-            ev[5].record()
+        rec(4)
+        if side is None or serial:
+            rec(5)
+            w.rebuild(i)
+            rec(6)
+
+    def timed(first, n, serial=False):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for j in range(n):
+            step(first + j, evs[j], serial)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / n
+        bounds = [(0, 1), (1, 2), (2, 3), (3, 4), (5, 6)]
+        ph = {p: sum(evs[j][a].elapsed_time(evs[j][b]) for j in range(n)) / n
+              for p, (a, b) in zip(phases, bounds)}
+        crit = sorted(evs[j][0].elapsed_time(evs[j][4]) for j in range(n))
+        return 1e3 * wall, ph, crit
 
     # warmup; after one step that loads every kernel, the first half also times
-    # every kernel site to find the dominant one
-    step(0)
+    # every kernel site (one stream) to find the dominant one
+    step(0, serial=True)
     torch.cuda.synchronize()
     n_prof = max(1, args.warmup // 2)
     cgs.profile_start("", 800 * n_prof + 64)
     for i in range(1, n_prof + 1):
-        step(i)
+        step(i, serial=True)
     cgs.profile_stop()
     torch.cuda.synchronize()
     sites = {}
@@ -386,24 +424,28 @@ def main():
     dom = max((s for s in sites if site_work(s, w.k, w.K)), key=lambda s: sites[s]["ms_per_step"])
     if not args.no_graphs:
         w.capture()
-    for i in range(n_prof + 1, max(args.warmup, n_prof + 2)):
+    i = n_prof + 1
+    for _ in range(max(args.warmup - n_prof, 1)):
         step(i)
+        i += 1
     torch.cuda.synchronize()
+    # the same calls with everything on one stream, for the overlap figures
+    serial = None
+    if side is not None and args.serial_steps > 0:
+        s_ms, s_ph, s_crit = timed(i, args.serial_steps, serial=True)
+        i += args.serial_steps
+        serial = {"ms_per_step": round(s_ms, 4), "breakdown_ms": {p: round(v, 4) for p, v in s_ph.items()},
+                  "critical_path_ms_median": round(s_crit[len(s_crit) // 2], 4)}
+        for _ in range(2):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
 
     # timed region: K steps, the dominant kernel bracketed by HIP events
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     cgs.profile_start(dom, args.steps * 64 + 64)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for j in range(args.steps):
-        step(args.warmup + j, evs[j])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    ms_per_step, ph, crit = timed(i, args.steps)
     cgs.profile_stop()
     dom_ms, dom_n = cgs.profile_result(dom)
-    ms_per_step = 1e3 * elapsed / args.steps
-    ph = {p: sum(evs[j][q].elapsed_time(evs[j][q + 1]) for j in range(args.steps)) / args.steps
-          for q, p in enumerate(phases)}
 
     flops, byts = site_work(dom, w.k, w.K)
     dom_s = dom_ms / 1e3 / dom_n
@@ -453,6 +495,11 @@ def main():
                             "ffn_kernels_ms": round(k_ffn_ms, 4),
                             "note": "18 masked layers incl. residual/RMSNorm glue; MALL-warm"},
         "rebuild_ms_per_entry": round(ph["rebuild"], 4),
+        "critical_path_ms": {"median": round(crit[len(crit) // 2], 4),
+                             "p95": round(crit[min(len(crit) - 1, int(math.ceil(0.95 * len(crit))) - 1)], 4),
+                             "what": "context prefill + anchor + 3 masked steps + mask build of one call"},
+        "rebuild_stream": args.rebuild_stream,
+        "serial_reference": serial,
         "kernel_sites": sites,
     }
     if not args.no_cpu_baseline:

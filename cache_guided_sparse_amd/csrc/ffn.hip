@@ -47,7 +47,8 @@ using CfgS = GemmCfg<64, 2, 2, 4, 2, 4>;    //  64 x 128, 4 waves,  80 KB LDS
 using CfgM = GemmCfg<128, 4, 2, 4, 2, 4>;   // 128 x 128, 8 waves,  96 KB
 using CfgL = GemmCfg<256, 4, 2, 4, 2, 5>;   // 256 x 128, 8 waves, 144 KB
 using CfgX = GemmCfg<192, 2, 4, 4, 2, 3>;   // 192 x 256, 8 waves, 144 KB
-enum TileId { kTileS = 0, kTileM = 1, kTileL = 2, kTileX = 3 };
+using CfgG = GemmCfg<128, 4, 2, 8, 2, 4>;   // 128 x 256, 8 waves, 160 KB (32 x 128 wave tiles)
+enum TileId { kTileS = 0, kTileM = 1, kTileL = 2, kTileX = 3, kTileG = 4 };
 
 template <typename Cfg, typename T, bool GLU, bool GATHER>
 void launch_cfg(const GemmArgs<T>& g, const char* site, hipStream_t s) {
@@ -62,6 +63,9 @@ void launch_tile(int tile, const GemmArgs<T>& g, const char* site, hipStream_t s
     case kTileS: launch_cfg<CfgS, T, GLU, GATHER>(g, site, s); break;
     case kTileM: launch_cfg<CfgM, T, GLU, GATHER>(g, site, s); break;
     case kTileL: launch_cfg<CfgL, T, GLU, GATHER>(g, site, s); break;
+    case kTileG:
+      if constexpr (sizeof(T) == 2) launch_cfg<CfgG, T, GLU, GATHER>(g, site, s);
+      break;
     default:
       if constexpr (sizeof(T) == 2) launch_cfg<CfgX, T, GLU, GATHER>(g, site, s);
       break;
@@ -183,6 +187,7 @@ void pick_tile(int tile, int* bm, int* bn) {
     case kTileS: *bm = CfgS::kBM; *bn = CfgS::kBN; break;
     case kTileM: *bm = CfgM::kBM; *bn = CfgM::kBN; break;
     case kTileL: *bm = CfgL::kBM; *bn = CfgL::kBN; break;
+    case kTileG: *bm = CfgG::kBM; *bn = CfgG::kBN; break;
     default: *bm = CfgX::kBM; *bn = CfgX::kBN; break;
   }
 }
@@ -193,11 +198,11 @@ FfnPlan plan_ffn(int M, int d, int ff, int dtype) {
   const bool wide = dtype == CGS_BF16 && d % CfgX::kBN == 0 && ff % (CfgX::kBN / 2) == 0;
   if (M <= 64) p.tile = kTileS;
   else if (M <= 128) p.tile = kTileM;
-  else if (M <= 256 || !wide) p.tile = kTileL;
-  else p.tile = kTileX;
+  else if (M <= 256) p.tile = wide ? kTileG : kTileL;
+  else p.tile = wide ? kTileX : kTileL;
   // Down projection: 129..256 rows use two 128-row tiles, which keeps ~256
   // workgroups with half the K splits (half the fp32 partial traffic).
-  p.dtile = (p.tile == kTileL && M <= 256) ? kTileM : p.tile;
+  p.dtile = (M > 128 && M <= 256) ? kTileM : p.tile;
   pick_tile(p.tile, &p.bm, &p.bn);
   pick_tile(p.dtile, &p.dbm, &p.dbn);
   p.m_tiles = std::max(1, (M + p.bm - 1) / p.bm);
