@@ -11,7 +11,9 @@ hot path once, with all inputs resident in HBM:
   * Action Cache denoise (§4.1, Eq. 4): action expert of 18 layers, d 1024,
     ff 4096, 50 action tokens, 4 denoising steps in one group: step 0 is the
     dense anchor, steps 1-3 update it with the group mask (coverage 0.844 of
-    the contribution score);
+    the contribution score), reading the mask's weight rows from compact
+    buffers that a side stream fills while the context prefill runs (§4.1,
+    §5);
   * group mask construction (§5) for the 18 expert layers from the reference
     run's activations (offline on the pages, timed here);
   * one dense rebuild of a reference entry (§4.2): the 17-layer prefill of the
@@ -171,7 +173,11 @@ class World:
         self.mw2 = torch.empty_like(self.mask_words)
         self.mi2 = torch.empty_like(self.mask_idx)
         self.mc2 = torch.empty_like(self.mask_cnt)
-        self.g_ctx, self.g_anchor, self.g_masked, self.g_mask = [], None, None, None
+        # compact weights of the group's masks (§4.1 / §5): the rows each masked
+        # step reads, gathered once per call
+        self.compact_weights = True
+        self.cexp = [cgs.act_gather_rows(self.exp[l], self.masks[l]) for l in range(L_EXP)]
+        self.g_ctx, self.g_anchor, self.g_masked, self.g_mask, self.g_gather = [], None, None, None, None
         log(f"setup {time.time() - t0:.1f}s; masked neurons per layer {min(self.K)}..{max(self.K)} "
             f"of {FFE} (mean {sum(self.K) / len(self.K) / FFE:.3f})")
 
@@ -223,9 +229,21 @@ class World:
         cgs = self.cgs
         for t in range(1, STEPS):
             for l in range(L_EXP):
-                cgs.act_ffn_masked(self.exp[l], self.xa, self.masks[l], y_anchor=self.y_anc[l],
-                                   h_anchor=self.h_anc[l], y_out=self.ya,
-                                   glue=(self.ra, self.dtemb[t] if l == L_EXP - 1 else None, self.xa))
+                glue = (self.ra, self.dtemb[t] if l == L_EXP - 1 else None, self.xa)
+                if self.compact_weights:
+                    cgs.act_ffn_masked_compact(self.cexp[l], self.xa, self.masks[l], y_anchor=self.y_anc[l],
+                                               h_anchor=self.h_anc[l], y_out=self.ya, glue=glue)
+                else:
+                    cgs.act_ffn_masked(self.exp[l], self.xa, self.masks[l], y_anchor=self.y_anc[l],
+                                       h_anchor=self.h_anc[l], y_out=self.ya, glue=glue)
+
+    def _gather(self):
+        for l in range(L_EXP):
+            self.cgs.act_gather_rows(self.exp[l], self.masks[l], out=self.cexp[l])
+
+    def gather(self):
+        if self.compact_weights:
+            self.g_gather.replay() if self.g_gather else self._gather()
 
     def _mask_build(self):
         self.build_masks(self.mw2, self.mi2, self.mc2)
@@ -245,9 +263,9 @@ class World:
 
     def capture(self):
         """HIP graphs of the launch-bound phases (fixed buffers): the 17 context
-        layers of each working-set slot, the anchor step, the three masked steps
-        and the mask build.  The rebuild (long kernels) and each call's first
-        RMSNorm stay eager."""
+        layers of each working-set slot, the anchor step, the three masked steps,
+        the mask build and the compact-weight gather.  The rebuild (long kernels)
+        and each call's first RMSNorm stay eager."""
         import torch
         torch.cuda.synchronize()
 
@@ -260,6 +278,7 @@ class World:
         self.g_anchor = cap(self._anchor)
         self.g_masked = cap(self._masked)
         self.g_mask = cap(self._mask_build)
+        self.g_gather = cap(self._gather)
         torch.cuda.synchronize()
 
 
@@ -330,6 +349,8 @@ def main():
                     help="launch every kernel eagerly instead of replaying HIP graphs")
     ap.add_argument("--rebuild-stream", choices=("side", "main"), default="main",
                     help="run the entry rebuild on a side stream (overlapped) or in line")
+    ap.add_argument("--no-compact", action="store_true",
+                    help="masked steps gather the mask's weight rows in place (no compact buffers)")
     ap.add_argument("--serial-steps", type=int, default=8,
                     help="calls timed with everything on one stream, for comparison")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
@@ -347,24 +368,38 @@ def main():
     dev = torch.device("cuda:0")
     w = World(dev)
 
-    phases = ["ctx_prefill", "act_anchor", "act_masked", "mask_build", "rebuild"]
-    # The rebuild of the entry 16 calls ahead runs on a side stream (default
-    # priority): it waits for the call's context prefill to release the slot,
-    # and the prefill that next uses the slot waits for the rebuild.
+    phases = ["ctx_prefill", "act_anchor", "act_masked", "mask_build", "rebuild", "gather"]
+    # The compact weights of the group's masks are gathered on a side stream
+    # while the context prefill runs (the masked steps wait for them; the
+    # gather waits until the previous call's masked steps are done with the
+    # buffers).  The rebuild of the entry 16 calls ahead runs in line after the
+    # call, or on a second side stream (then `serial` steps put it back in
+    # line for comparison): it waits for the call's context prefill to release
+    # the slot, and the prefill that next uses the slot waits for the rebuild.
+    # All streams have the default priority.
+    w.compact_weights = not args.no_compact
     main_s = torch.cuda.current_stream()
+    gather_s = torch.cuda.Stream(device=dev)
     side = torch.cuda.Stream(device=dev) if args.rebuild_stream == "side" else None
     ctx_done = [torch.cuda.Event() for _ in range(SLOTS)]
     rebuilt = [torch.cuda.Event() for _ in range(SLOTS)]
     pending = [False] * SLOTS
+    gathered, masked_done = torch.cuda.Event(), torch.cuda.Event()
 
     def step(i, ev=None, serial=False):
-        """One call.  ev: 7 timing events; 0-4 bracket the main-stream phases,
-        5-6 the rebuild on the stream that runs it."""
+        """One call.  ev: 9 timing events; 0-4 bracket the main-stream phases,
+        5-6 the rebuild and 7-8 the gather on the streams that run them."""
         e = i % SLOTS
         rec = (lambda q: ev[q].record()) if ev is not None else (lambda q: None)
         if pending[e]:
             main_s.wait_event(rebuilt[e])
             pending[e] = False
+        gather_s.wait_event(masked_done)
+        with torch.cuda.stream(gather_s):
+            rec(7)
+            w.gather()
+            rec(8)
+            gathered.record(gather_s)
         rec(0)
         w.ctx_prefill(i)
         rec(1)
@@ -379,7 +414,9 @@ def main():
             pending[e] = True
         w.act_anchor()
         rec(2)
+        main_s.wait_event(gathered)
         w.act_masked()
+        masked_done.record(main_s)
         rec(3)
         w.mask_build()
         rec(4)
@@ -389,14 +426,14 @@ def main():
             rec(6)
 
     def timed(first, n, serial=False):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(n)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for j in range(n):
             step(first + j, evs[j], serial)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / n
-        bounds = [(0, 1), (1, 2), (2, 3), (3, 4), (5, 6)]
+        bounds = [(0, 1), (1, 2), (2, 3), (3, 4), (5, 6), (7, 8)]
         ph = {p: sum(evs[j][a].elapsed_time(evs[j][b]) for j in range(n)) / n
               for p, (a, b) in zip(phases, bounds)}
         crit = sorted(evs[j][0].elapsed_time(evs[j][4]) for j in range(n))
@@ -415,8 +452,8 @@ def main():
     sites = {}
     for s in ("ctx.score", "ctx.topk", "ctx.glu", "ctx.down", "ctx.finish", "rebuild.norm",
               "rebuild.glu", "rebuild.down", "rebuild.finish", "act.glu.dense", "act.down.dense",
-              "act.glu.masked", "act.down.masked", "act.finish", "mask.contrib", "mask.select",
-              "glue.rmsnorm"):
+              "act.glu.masked", "act.down.masked", "act.finish", "act.gather", "mask.contrib",
+              "mask.select", "glue.rmsnorm"):
         t, n = cgs.profile_result(s)
         if n:
             sites[s] = {"launches_per_step": n / n_prof, "mean_us": round(1e3 * t / n, 2),
@@ -479,9 +516,11 @@ def main():
         "config": {"workload": ("policy-call slice: 17-layer Context Cache prefill (768 tokens, d 2048, "
                                 "ff 16384, rho_p 0.3) + 4-step Action Cache denoise (18 layers, d 1024, "
                                 "ff 4096, 50 tokens, coverage 0.844, anchor step 0) + group mask build "
-                                "+ one 17-layer dense entry rebuild; 16-entry working set"),
+                                "+ one 17-layer dense entry rebuild; 16-entry working set; the masks' "
+                                "weight rows gathered into compact buffers on a side stream"),
                    "tokens": P, "rho_p": RHO_P, "k": w.k, "coverage": COVERAGE,
-                   "hip_graphs": not args.no_graphs,
+                   "hip_graphs": not args.no_graphs, "compact_weights": not args.no_compact,
+                   "rebuild_stream": args.rebuild_stream,
                    "masked_neurons_mean": round(sum(Km) / len(Km), 1)},
         "roofline": roofline,
         "breakdown_ms": {p: round(v, 4) for p, v in ph.items()},

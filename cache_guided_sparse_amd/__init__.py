@@ -81,6 +81,8 @@ _SIGS = {
     "act_build_mask": (_i, [_vp, _i, _i, _vp, _i, _i, _d, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cgs_act_ffn_masked_workspace": (_sz, [_i, _i, _i, _i]),
     "act_ffn_masked": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "act_ffn_masked_compact": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "act_gather_rows": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp]),
     "cgs_ref_rebuild_dense_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "ref_rebuild_dense": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
     "cgs_residual_rmsnorm": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _vp, _i, _vp]),
@@ -251,6 +253,39 @@ def act_ffn_masked(w: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=None, y_f
     _check(lib().act_ffn_masked(ctypes.byref(c), _ptr(x), S, _ptr(idx), K, _ptr(y_anchor),
                                 _ptr(h_anchor), _ptr(y_out), _ptr(y_f32_out), _ptr(h_out),
                                 _glue(glue), _ptr(ws), ws.numel(), _stream(stream)), "act_ffn_masked")
+    return y_out
+
+
+def act_gather_rows(w: FFN, idx, out: FFN = None, stream=None) -> FFN:
+    """Compact FFN of the mask idx: rows idx of w_gate, w_up and the
+    neuron-major w_down, each [K][d] (into ``out`` when given)."""
+    K = int(idx.numel())
+    if out is None:
+        shape = (K, w.d)
+        out = FFN(torch.empty(shape, dtype=w.w_gate.dtype, device=w.w_gate.device),
+                  torch.empty(shape, dtype=w.w_gate.dtype, device=w.w_gate.device),
+                  torch.empty(shape, dtype=w.w_gate.dtype, device=w.w_gate.device), "fd")
+    c = w.cstruct()
+    _check(lib().act_gather_rows(ctypes.byref(c), _ptr(idx), K, _ptr(out.w_gate), _ptr(out.w_up),
+                                 _ptr(out.w_down), _stream(stream)), "act_gather_rows")
+    return out
+
+
+def act_ffn_masked_compact(wc: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=None, y_f32_out=None,
+                           h_out=None, glue=None, ws=None, stream=None, K=None):
+    """Eq. 4 on the compact FFN of a mask (act_gather_rows); idx (original
+    neuron ids) addresses h_anchor / h_out rows only and may be None without them."""
+    S, d = x.shape
+    K = wc.ff if K is None else int(K)
+    if y_out is None:
+        y_out = torch.empty_like(x)
+    c = wc.cstruct()
+    nbytes = lib().cgs_act_ffn_masked_workspace(S, K, d, max(K, 1))
+    ws = workspace(nbytes, x.device, "act") if ws is None else ws
+    _check(lib().act_ffn_masked_compact(ctypes.byref(c), _ptr(x), S, _ptr(idx), K, _ptr(y_anchor),
+                                        _ptr(h_anchor), _ptr(y_out), _ptr(y_f32_out), _ptr(h_out),
+                                        _glue(glue), _ptr(ws), ws.numel(), _stream(stream)),
+           "act_ffn_masked_compact")
     return y_out
 
 

@@ -39,7 +39,9 @@ constexpr int kCols = 64;      // output columns per down workgroup
 constexpr int kTokDown = 64;   // tokens per down workgroup (4 waves x 16)
 constexpr int kMaxSteps = 8;   // K steps per down workgroup (LDS: 8 x 32 rows)
 
-template <typename T, int MTW>
+// COMPACT: the weights hold the mask's rows only (row i is mask position i);
+// idx then only addresses h_anchor / h_out rows and may be NULL without them.
+template <typename T, int MTW, bool COMPACT>
 __global__ __launch_bounds__(kThreads) void act_glu_kernel(
     const T* __restrict__ x, int S, int d, const int32_t* __restrict__ idx, int K, int K_pad,
     const T* __restrict__ wg, const T* __restrict__ wu, const float* __restrict__ h_anchor,
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void act_glu_kernel(
 
   const int i_lane = i0 + r;
   const bool nvalid = i_lane < K;
-  const size_t wrow = nvalid ? static_cast<size_t>(idx[i_lane]) * d : 0;
+  const size_t wrow = nvalid ? static_cast<size_t>(COMPACT ? i_lane : idx[i_lane]) * d : 0;
 
   // Epilogue elements of this thread: e = tid + 256 j -> (token e / 16, mask
   // position e % 16).  Their neuron rows and anchor activations are fetched
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void act_glu_kernel(
     const int e = tid + kThreads * j;
     const int i = i0 + e % kNB, sg = s0 + e / kNB;
     ev[j] = i < K && sg < S;
-    hn[j] = ev[j] ? static_cast<size_t>(idx[i]) * S + sg : 0;
+    hn[j] = (ev[j] && idx) ? static_cast<size_t>(idx[i]) * S + sg : 0;
     ha[j] = (ev[j] && h_anchor) ? h_anchor[hn[j]] : 0.f;
   }
   const T* xrow[MTW];
@@ -160,7 +162,7 @@ __device__ __forceinline__ void gather_b_frag<float>(const char* tile, int pitch
   f.hi = u32x4_t{w[4], w[5], w[6], w[7]};
 }
 
-template <typename T>
+template <typename T, bool COMPACT>
 __global__ __launch_bounds__(kThreads) void act_down_kernel(
     const T* __restrict__ D, int S, int K_pad, const int32_t* __restrict__ idx, int K,
     const T* __restrict__ wd, int d, int steps_per_split, float* __restrict__ part) {
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void act_down_kernel(
   for (int t = 0; t < QMAX; ++t) {
     const int q = wave + 4 * t;
     const int i = min(st_begin * kStep + q * RPD + lrow, K - 1);
-    src[t] = (q < nq) ? idx[i] : 0;
+    src[t] = (q < nq) ? (COMPACT ? i : idx[i]) : 0;
   }
 #pragma unroll
   for (int t = 0; t < QMAX; ++t) {
@@ -260,6 +262,24 @@ __global__ __launch_bounds__(kThreads) void act_finish_kernel(
   if (glue.r && glue.x_next) glue_norm(glue, ro, d, ss, red);
 }
 
+// Rows idx[0..K-1] of three [ff][d] matrices into compact [K][d] buffers:
+// one wavefront per row, 16 bytes per lane per access.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(const T* __restrict__ a, const T* __restrict__ b,
+                                                               const T* __restrict__ c,
+                                                               const int32_t* __restrict__ idx, int K, int d,
+                                                               T* __restrict__ ao, T* __restrict__ bo,
+                                                               T* __restrict__ co) {
+  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= 3 * K) return;
+  const int m = row / K, i = row - m * K;
+  const T* src = (m == 0 ? a : m == 1 ? b : c) + static_cast<size_t>(idx[i]) * d;
+  T* dst = (m == 0 ? ao : m == 1 ? bo : co) + static_cast<size_t>(i) * d;
+  constexpr int V = 16 / static_cast<int>(sizeof(T));
+  for (int e = (threadIdx.x & 63) * V; e < d; e += 64 * V)
+    *reinterpret_cast<u32x4_t*>(dst + e) = *reinterpret_cast<const u32x4_t*>(src + e);
+}
+
 struct ActPlan {
   int K_pad, S_pad, tt, splits, steps_per_split;
   size_t d_elems, part_elems;
@@ -283,7 +303,7 @@ ActPlan plan_act(int S, int K, int d) {
 
 bool act_shape_ok(int d, int ff) { return d > 0 && ff > 0 && d % 128 == 0; }
 
-template <typename T>
+template <typename T, bool COMPACT>
 int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const float* ya,
           const float* ha, T* y_out, float* y_f32, float* h_out, const cgs_glue* gl, void* ws,
           hipStream_t s) {
@@ -293,18 +313,20 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
   float* part = cv.take<float>(std::max<size_t>(p.part_elems, 1));
   if (K > 0) {
     {
-      ProfScope ps(K == w.ff ? "act.glu.dense" : "act.glu.masked", s);
+      ProfScope ps(K == w.ff && !COMPACT ? "act.glu.dense" : "act.glu.masked", s);
       const dim3 grid((p.K_pad + kNB - 1) / kNB, (p.S_pad + p.tt - 1) / p.tt);
       if (p.tt == 16)
-        hipLaunchKernelGGL((act_glu_kernel<T, 1>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K, p.K_pad,
-                           static_cast<const T*>(w.w_gate), static_cast<const T*>(w.w_up), ha, h_out, D);
+        hipLaunchKernelGGL((act_glu_kernel<T, 1, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
+                           p.K_pad, static_cast<const T*>(w.w_gate), static_cast<const T*>(w.w_up), ha,
+                           h_out, D);
       else
-        hipLaunchKernelGGL((act_glu_kernel<T, 2>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K, p.K_pad,
-                           static_cast<const T*>(w.w_gate), static_cast<const T*>(w.w_up), ha, h_out, D);
+        hipLaunchKernelGGL((act_glu_kernel<T, 2, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
+                           p.K_pad, static_cast<const T*>(w.w_gate), static_cast<const T*>(w.w_up), ha,
+                           h_out, D);
     }
     if (!launch_ok()) return CGS_ERR_LAUNCH;
-    ProfScope ps(K == w.ff ? "act.down.dense" : "act.down.masked", s);
-    hipLaunchKernelGGL((act_down_kernel<T>), dim3(w.d / kCols, p.splits, p.S_pad / kTokDown), dim3(kThreads),
+    ProfScope ps(K == w.ff && !COMPACT ? "act.down.dense" : "act.down.masked", s);
+    hipLaunchKernelGGL((act_down_kernel<T, COMPACT>), dim3(w.d / kCols, p.splits, p.S_pad / kTokDown), dim3(kThreads),
                        0, s, D, S, p.K_pad, idx, K, static_cast<const T*>(w.w_down), w.d,
                        p.steps_per_split, part);
     if (!launch_ok()) return CGS_ERR_LAUNCH;
@@ -342,8 +364,53 @@ extern "C" int act_ffn_masked(const cgs_ffn* w, const void* x, int S, const int3
   if (!ws || ws_bytes < cgs_act_ffn_masked_workspace(S, K, w->d, w->ff)) return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w->dtype == CGS_BF16)
-    return act_t<uint16_t>(*w, static_cast<const uint16_t*>(x), S, idx, K, y_anchor, h_anchor,
-                           static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s);
-  return act_t<float>(*w, static_cast<const float*>(x), S, idx, K, y_anchor, h_anchor,
-                      static_cast<float*>(y_out), y_f32_out, h_out, glue, ws, s);
+    return act_t<uint16_t, false>(*w, static_cast<const uint16_t*>(x), S, idx, K, y_anchor, h_anchor,
+                                  static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s);
+  return act_t<float, false>(*w, static_cast<const float*>(x), S, idx, K, y_anchor, h_anchor,
+                             static_cast<float*>(y_out), y_f32_out, h_out, glue, ws, s);
+}
+
+extern "C" int act_ffn_masked_compact(const cgs_ffn* wc, const void* x, int S, const int32_t* idx, int K,
+                                      const float* y_anchor, const float* h_anchor, void* y_out,
+                                      float* y_f32_out, float* h_out, const cgs_glue* glue, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  if (!wc || (K > 0 && (!wc->w_gate || !wc->w_up || !wc->w_down)) || !valid_dtype(wc->dtype) ||
+      wc->down_layout != CGS_DOWN_FD || !x || !y_out || !glue_ok(glue) ||
+      (K > 0 && !idx && (h_anchor || h_out)))
+    return CGS_ERR_ARG;
+  if (!act_shape_ok(wc->d, std::max(wc->ff, 1))) return CGS_ERR_UNSUPPORTED;
+  if (S < 0 || K < 0 || K != wc->ff) return CGS_ERR_SHAPE;
+  if (S == 0) return CGS_OK;
+  if (!ws || ws_bytes < cgs_act_ffn_masked_workspace(S, K, wc->d, std::max(K, 1))) return CGS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (wc->dtype == CGS_BF16)
+    return act_t<uint16_t, true>(*wc, static_cast<const uint16_t*>(x), S, idx, K, y_anchor, h_anchor,
+                                 static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s);
+  return act_t<float, true>(*wc, static_cast<const float*>(x), S, idx, K, y_anchor, h_anchor,
+                            static_cast<float*>(y_out), y_f32_out, h_out, glue, ws, s);
+}
+
+extern "C" int act_gather_rows(const cgs_ffn* w, const int32_t* idx, int K, void* wg_out, void* wu_out,
+                               void* wd_out, void* stream) {
+  if (!w || !w->w_gate || !w->w_up || !w->w_down || !valid_dtype(w->dtype) ||
+      w->down_layout != CGS_DOWN_FD)
+    return CGS_ERR_ARG;
+  if (!act_shape_ok(w->d, w->ff)) return CGS_ERR_UNSUPPORTED;
+  if (K < 0 || K > w->ff) return CGS_ERR_SHAPE;
+  if (K == 0) return CGS_OK;
+  if (!idx || !wg_out || !wu_out || !wd_out) return CGS_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ProfScope ps("act.gather", s);
+  const dim3 grid((3 * K + kThreads / 64 - 1) / (kThreads / 64));
+  if (w->dtype == CGS_BF16)
+    hipLaunchKernelGGL((gather_rows_kernel<uint16_t>), grid, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(w->w_gate), static_cast<const uint16_t*>(w->w_up),
+                       static_cast<const uint16_t*>(w->w_down), idx, K, w->d, static_cast<uint16_t*>(wg_out),
+                       static_cast<uint16_t*>(wu_out), static_cast<uint16_t*>(wd_out));
+  else
+    hipLaunchKernelGGL((gather_rows_kernel<float>), grid, dim3(kThreads), 0, s,
+                       static_cast<const float*>(w->w_gate), static_cast<const float*>(w->w_up),
+                       static_cast<const float*>(w->w_down), idx, K, w->d, static_cast<float*>(wg_out),
+                       static_cast<float*>(wu_out), static_cast<float*>(wd_out));
+  return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
 }

@@ -201,6 +201,33 @@ int act_ffn_masked(const cgs_ffn* w, const void* x, int S, const int32_t* idx, i
                    const float* y_anchor, const float* h_anchor, void* y_out, float* y_f32_out,
                    float* h_out, const cgs_glue* glue, void* ws, size_t ws_bytes, void* stream);
 
+/* §4.1 and §5: the selected neuron weights of a group prepared once, into
+ * compact buffers that every masked step of the group reuses (the pages
+ * gather them on a side stream while the prefill runs).  Copies rows
+ * idx[0..K-1] of w_gate, w_up and the neuron-major w_down into [K][d]
+ * buffers.
+ *   w      : FFN with down_layout CGS_DOWN_FD.
+ *   idx    : [K] int32 in [0, ff) (device).
+ *   wg_out, wu_out, wd_out : [K][d] dtype each (device, caller-owned, not
+ *            overlapping the weights).
+ * (wg_out, wu_out, wd_out) with ff = K and CGS_DOWN_FD is the compact FFN of
+ * act_ffn_masked_compact.  K = 0 is a no-op.  No workspace. */
+int act_gather_rows(const cgs_ffn* w, const int32_t* idx, int K, void* wg_out, void* wu_out,
+                    void* wd_out, void* stream);
+
+/* §4.1, Eq. 4 on compact weights: as act_ffn_masked for the full FFN and the
+ * mask idx, but wc holds only the mask's rows (wc->ff == K; row i is neuron
+ * idx[i], as act_gather_rows writes them), so no weight address depends on
+ * the index list.  idx [K] (original neuron ids) addresses only the rows of
+ * h_anchor and h_out, which stay [ff][S] over the original neurons; it may be
+ * NULL when both are NULL.  With K = 0 the weights may be NULL.  Results are
+ * identical to act_ffn_masked's.
+ * Workspace: cgs_act_ffn_masked_workspace(S, K, d, K). */
+int act_ffn_masked_compact(const cgs_ffn* wc, const void* x, int S, const int32_t* idx, int K,
+                           const float* y_anchor, const float* h_anchor, void* y_out,
+                           float* y_f32_out, float* h_out, const cgs_glue* glue, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* ---- Reference rebuild ------------------------------------------------- */
 
 /* Workspace bytes for ref_rebuild_dense. */

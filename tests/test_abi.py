@@ -105,6 +105,16 @@ def test_host_validation_without_launch():
     assert L.ctx_select_from_keys(buf, 70000, 1, buf, None) == 2
     assert L.ctx_select_from_keys(None, 8, 1, buf, None) == 1
     assert L.ctx_select_from_keys(None, 8, 0, None, None) == 0
+    # act_gather_rows: wrong layout, K > ff, null index; K = 0 is a no-op
+    assert L.act_gather_rows(ctypes.byref(w), buf, 4, buf, buf, buf, None) == 1
+    assert L.act_gather_rows(ctypes.byref(wf), buf, 2000, buf, buf, buf, None) == 2
+    assert L.act_gather_rows(ctypes.byref(wf), None, 4, buf, buf, buf, None) == 1
+    assert L.act_gather_rows(ctypes.byref(wf), None, 0, None, None, None, None) == 0
+    # act_ffn_masked_compact: K must equal the compact row count; anchors need idx
+    wc = _ffn(layout=1, ff=64)
+    assert L.act_ffn_masked_compact(ctypes.byref(wc), buf, 4, buf, 10, None, None, buf, None, None, None, buf, 1 << 30, None) == 2
+    assert L.act_ffn_masked_compact(ctypes.byref(wc), buf, 4, None, 64, None, buf, buf, None, None, None, buf, 1 << 30, None) == 1
+    assert L.act_ffn_masked_compact(ctypes.byref(wc), buf, 4, None, 64, None, None, buf, None, None, None, buf, 4, None) == 3
     # act_build_mask: bad mode, K, coverage, S*T too large
     assert L.act_build_mask(buf, 2, 8, ctypes.byref(wf), 9, 4, 0.0, buf, buf, buf, buf, 1 << 30, None) == 1
     assert L.act_build_mask(buf, 2, 8, ctypes.byref(wf), 0, 5000, 0.0, buf, buf, buf, buf, 1 << 30, None) == 2
