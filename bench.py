@@ -458,7 +458,14 @@ def main():
         if n:
             sites[s] = {"launches_per_step": n / n_prof, "mean_us": round(1e3 * t / n, 2),
                         "ms_per_step": round(t / n_prof, 4)}
-    dom = max((s for s in sites if site_work(s, w.k, w.K)), key=lambda s: sites[s]["ms_per_step"])
+    # The dominant kernel is timed per launch in the timed region, which needs
+    # its launches to be eager: with HIP graphs only the rebuild's are.
+    eager = (lambda s: True) if args.no_graphs else (lambda s: s.startswith("rebuild."))
+    dom_all = max((s for s in sites if site_work(s, w.k, w.K)), key=lambda s: sites[s]["ms_per_step"])
+    dom = max((s for s in sites if site_work(s, w.k, w.K) and eager(s)), key=lambda s: sites[s]["ms_per_step"])
+    if dom != dom_all:
+        log(f"note: {dom_all} takes more time per step than {dom} but runs inside a HIP graph; "
+            f"the roofline is reported for {dom}")
     if not args.no_graphs:
         w.capture()
     i = n_prof + 1
@@ -485,6 +492,8 @@ def main():
     dom_ms, dom_n = cgs.profile_result(dom)
 
     flops, byts = site_work(dom, w.k, w.K)
+    if dom_n == 0:
+        sys.exit(f"no timed launches of {dom}")
     dom_s = dom_ms / 1e3 / dom_n
     mfma = flops / byts > RIDGE
     achieved = (flops / dom_s / 1e12) if mfma else (byts / dom_s / 1e9)
@@ -492,7 +501,8 @@ def main():
     traffic, traffic_src = stored_traffic(dom)
     roofline = {"bound": "mfma" if mfma else "hbm", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s" if mfma else "GB/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic, "kernel": dom, "mean_us": round(dom_s * 1e6, 2),
+                "traffic": traffic, "kernel": dom, "largest_site_in_warmup": dom_all,
+                "mean_us": round(dom_s * 1e6, 2),
                 "launches": dom_n, "flops_per_launch": flops, "bytes_per_launch": byts,
                 "traffic_source": traffic_src,
                 "traffic_over_algorithmic": round(traffic / byts, 3) if traffic else None}
