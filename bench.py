@@ -16,9 +16,11 @@ hot path once, with all inputs resident in HBM:
     §5);
   * group mask construction (§5) for the 18 expert layers from the reference
     run's activations (offline on the pages, timed here);
-  * one dense rebuild of a reference entry (§4.2): the 17-layer prefill of the
-    entry 16 calls ahead, into the slot the current call just used (a
-    16-entry sliding working set).
+  * one dense rebuild of a reference entry (§4.2): a 16-slot sliding working
+    set over an 800-entry repository of compact entries in pinned host
+    memory advances one position per call (the native window planner,
+    Eq. 5 budget); the entering entry is copied to the device and expanded
+    by the 17-layer prefill into the slot the leaving entry released.
 Prints one JSON line.  Synthetic seeded data of the pages' shapes; the
 weights are random (no trained model is involved).
 """
@@ -43,7 +45,8 @@ RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
 # workload
 P, D, FF, L_VLM, RHO_P = 768, 2048, 16384, 17, 0.3
 S, DE, FFE, L_EXP, STEPS, COVERAGE = 50, 1024, 4096, 18, 4, 0.844
-SLOTS, RING = 16, 64
+STORE, SLOTS, LOOKAHEAD = 800, 16, 15   # repository entries, device slots, window lookahead
+T_AVL_MS = 500.0                           # a 15-action chunk at 30 Hz (the paper's example)
 
 
 def log(*a):
@@ -118,18 +121,44 @@ class World:
         # VLM FFN layers (Context Cache path, W_down [d][ff])
         self.vlm = [cgs.FFN(randn(FF, D, std=0.02).to(bf), randn(FF, D, std=0.02).to(bf),
                             randn(D, FF, std=0.02).to(bf), "df") for _ in range(L_VLM)]
-        # compact entries (reference residual inputs) and current-call inputs
-        self.compact = randn(RING, P, D).to(bf)
-        sig = torch.full((RING, P, 1), 0.1752, device=dev)
-        for i in range(RING):
-            perm = torch.randperm(P, device=dev, generator=g)[: math.ceil(RHO_P * P - 1e-9)]
-            sig[i, perm] = 1.3333
-        self.current = (self.compact.float() + randn(RING, P, D) * sig).contiguous()
-        # expanded working set: SLOTS entries of (xbar, ybar) per layer
+        # reference repository: STORE compact entries (the residual stream that
+        # enters layer 0) in pinned host memory, one reference episode of STORE
+        # positions; the current call at position q sees that entry's input
+        # with 231 tokens strongly perturbed (cos ~0.6) and the rest mildly
+        self.store = torch.empty((STORE, P, D), dtype=bf, pin_memory=True)
+        self.current = torch.empty((STORE, P, D), dtype=torch.float32, device=dev)
+        for c0 in range(0, STORE, 64):
+            n = min(64, STORE - c0)
+            comp = randn(n, P, D)
+            sig = torch.full((n, P, 1), 0.1752, device=dev)
+            for j in range(n):
+                perm = torch.randperm(P, device=dev, generator=g)[: math.ceil(RHO_P * P - 1e-9)]
+                sig[j, perm] = 1.3333
+            self.current[c0:c0 + n] = comp + randn(n, P, D) * sig
+            self.store[c0:c0 + n].copy_(comp.to(bf))
+        self.staging = torch.empty((P, D), dtype=bf, device=dev)
+        # expanded working set: SLOTS entries of (xbar, ybar) per layer, managed
+        # as a sliding window (position q .. q + LOOKAHEAD of the episode)
         self.xbar = torch.empty(SLOTS, L_VLM, P, D, dtype=bf, device=dev)
         self.ybar = torch.empty_like(self.xbar)
-        for e in range(SLOTS):
-            cgs.ref_rebuild_dense(self.vlm, self.compact[e], self.xbar[e], self.ybar[e])
+        self.window = cgs.Window(SLOTS)
+        # initial-position preload, timed to estimate T_rec and T_trans of Eq. 5
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        entered, _, _ = self.window.advance([0], [0], [STORE], LOOKAHEAD)
+        for _, q, slot in entered:
+            self.rebuild_entry(q, slot)
+        torch.cuda.synchronize()
+        self.t_rec_ms = 1e3 * (time.perf_counter() - t1) / len(entered)
+        t1 = time.perf_counter()
+        for _ in range(8):
+            self.staging.copy_(self.store[0], non_blocking=True)
+        torch.cuda.synchronize()
+        self.t_trans_ms = 1e3 * (time.perf_counter() - t1) / 8
+        free, _ = torch.cuda.mem_get_info(dev)
+        self.m_entry = 2 * L_VLM * P * D * 2
+        self.budget = (float(free), float(self.m_entry), T_AVL_MS, self.t_trans_ms, self.t_rec_ms)
+        self.entered = []
         # action expert (Action Cache path, neuron-major W_down with log-normal row scale)
         self.exp = []
         for _ in range(L_EXP):
@@ -209,9 +238,24 @@ class World:
             glue = (self.r, None, self.x, self.xbar[e, l + 1], self.skey) if l + 1 < L_VLM else (self.r, None, None)
             cgs.ctx_ffn_recompute(self.vlm[l], self.x, self.ybar[e, l], self.idx, y_out=self.y, glue=glue)
 
-    def ctx_prefill(self, i):
-        e = i % SLOTS
-        self.cgs.residual_rmsnorm(self.r, r_in=self.current[i % RING], x_out=self.x)
+    @staticmethod
+    def position(i):
+        """Matched position of call i: the window advances one entry per call."""
+        return i % (STORE - LOOKAHEAD)
+
+    def advance(self, i):
+        """Slide the window to call i's position; returns (slot of the call's
+        entry, entries to rebuild [(episode, position, slot)])."""
+        q = self.position(i)
+        entered, _, _ = self.window.advance([0], [q], [STORE], LOOKAHEAD, self.budget)
+        self.entered.append(len(entered))
+        slot = self.window.slot(0, q)
+        if slot < 0:
+            raise RuntimeError(f"entry {q} is not resident")
+        return slot, entered
+
+    def ctx_prefill(self, i, e):
+        self.cgs.residual_rmsnorm(self.r, r_in=self.current[self.position(i)], x_out=self.x)
         if self.g_ctx:
             self.g_ctx[e].replay()
         else:
@@ -257,9 +301,15 @@ class World:
     def mask_build(self):
         self.g_mask.replay() if self.g_mask else self._mask_build()
 
-    def rebuild(self, i):
-        e = i % SLOTS
-        self.cgs.ref_rebuild_dense(self.vlm, self.compact[(i + SLOTS) % RING], self.xbar[e], self.ybar[e])
+    def rebuild_entry(self, q, slot):
+        """Transfer compact entry q to the device and expand it into `slot`
+        (on the current stream)."""
+        self.staging.copy_(self.store[q], non_blocking=True)
+        self.cgs.ref_rebuild_dense(self.vlm, self.staging, self.xbar[slot], self.ybar[slot])
+
+    def rebuild(self, entered):
+        for _, q, slot in entered:
+            self.rebuild_entry(q, slot)
 
     def capture(self):
         """HIP graphs of the launch-bound phases (fixed buffers): the 17 context
@@ -389,7 +439,7 @@ def main():
     def step(i, ev=None, serial=False):
         """One call.  ev: 9 timing events; 0-4 bracket the main-stream phases,
         5-6 the rebuild and 7-8 the gather on the streams that run them."""
-        e = i % SLOTS
+        e, entered = w.advance(i)
         rec = (lambda q: ev[q].record()) if ev is not None else (lambda q: None)
         if pending[e]:
             main_s.wait_event(rebuilt[e])
@@ -401,17 +451,21 @@ def main():
             rec(8)
             gathered.record(gather_s)
         rec(0)
-        w.ctx_prefill(i)
+        w.ctx_prefill(i, e)
         rec(1)
+        ctx_done[e].record(main_s)
         if side is not None and not serial:
-            ctx_done[e].record(main_s)
+            # a slot taken by an entering entry was last read by an earlier
+            # call's prefill; the next prefill that reads it waits for this
             with torch.cuda.stream(side):
-                side.wait_event(ctx_done[e])
+                for _, _, s_ in entered:
+                    side.wait_event(ctx_done[s_])
                 rec(5)
-                w.rebuild(i)
+                w.rebuild(entered)
                 rec(6)
-                rebuilt[e].record(side)
-            pending[e] = True
+                for _, _, s_ in entered:
+                    rebuilt[s_].record(side)
+                    pending[s_] = True
         w.act_anchor()
         rec(2)
         main_s.wait_event(gathered)
@@ -422,7 +476,7 @@ def main():
         rec(4)
         if side is None or serial:
             rec(5)
-            w.rebuild(i)
+            w.rebuild(entered)
             rec(6)
 
     def timed(first, n, serial=False):
@@ -526,8 +580,10 @@ def main():
         "config": {"workload": ("policy-call slice: 17-layer Context Cache prefill (768 tokens, d 2048, "
                                 "ff 16384, rho_p 0.3) + 4-step Action Cache denoise (18 layers, d 1024, "
                                 "ff 4096, 50 tokens, coverage 0.844, anchor step 0) + group mask build "
-                                "+ one 17-layer dense entry rebuild; 16-entry working set; the masks' "
-                                "weight rows gathered into compact buffers on a side stream"),
+                                "+ one 17-layer dense entry rebuild (host-to-device transfer of the compact "
+                                "entry included) for a 16-slot sliding window over an 800-entry pinned host "
+                                "repository; the masks' weight rows gathered into compact buffers on a side "
+                                "stream"),
                    "tokens": P, "rho_p": RHO_P, "k": w.k, "coverage": COVERAGE,
                    "hip_graphs": not args.no_graphs, "compact_weights": not args.no_compact,
                    "rebuild_stream": args.rebuild_stream,
@@ -543,7 +599,13 @@ def main():
                             "hbm_frac": round(masked_bytes / masked_step_ms / 1e6 / PEAK_HBM_GBPS, 4),
                             "ffn_kernels_ms": round(k_ffn_ms, 4),
                             "note": "18 masked layers incl. residual/RMSNorm glue; MALL-warm"},
-        "rebuild_ms_per_entry": round(ph["rebuild"], 4),
+        "rebuild_ms_per_entry": round(ph["rebuild"] / max(1e-9, sum(w.entered[-args.steps:]) / args.steps), 4),
+        "working_set": {"repository_entries": STORE, "repository_bytes": STORE * P * D * 2,
+                        "slots": SLOTS, "window": {"episodes": 1, "lookahead": LOOKAHEAD},
+                        "entered_per_call": round(sum(w.entered[-args.steps:]) / args.steps, 3),
+                        "eq5": {"m_free": w.budget[0], "m_entry": w.budget[1], "t_avl_ms": T_AVL_MS,
+                                "t_trans_ms": round(w.t_trans_ms, 4), "t_rec_ms": round(w.t_rec_ms, 4),
+                                "n_prep_bound": cgs.prep_budget(10 ** 6, *w.budget)}},
         "critical_path_ms": {"median": round(crit[len(crit) // 2], 4),
                              "p95": round(crit[min(len(crit) - 1, int(math.ceil(0.95 * len(crit))) - 1)], 4),
                              "what": "context prefill + anchor + 3 masked steps + mask build of one call"},

@@ -86,6 +86,12 @@ _SIGS = {
     "cgs_ref_rebuild_dense_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "ref_rebuild_dense": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
     "cgs_residual_rmsnorm": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _vp, _i, _vp]),
+    "cgs_prep_budget": (_i, [_i, _d, _d, _d, _d, _d]),
+    "cgs_window_create": (_vp, [_i]),
+    "cgs_window_destroy": (None, [_vp]),
+    "cgs_window_slot": (_i, [_vp, _i, _i]),
+    "cgs_window_resident": (_i, [_vp]),
+    "cgs_window_advance": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "cgs_profile_start": (_i, [ctypes.c_char_p, _i]),
     "cgs_profile_stop": (_i, []),
     "cgs_profile_result": (_i, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -287,6 +293,58 @@ def act_ffn_masked_compact(wc: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=
                                         _glue(glue), _ptr(ws), ws.numel(), _stream(stream)),
            "act_ffn_masked_compact")
     return y_out
+
+
+class _Budget(ctypes.Structure):
+    _fields_ = [("m_free", ctypes.c_double), ("m_entry", ctypes.c_double), ("t_avl", ctypes.c_double),
+                ("t_trans", ctypes.c_double), ("t_rec", ctypes.c_double)]
+
+
+def prep_budget(n_cand: int, m_free: float, m_entry: float, t_avl: float, t_trans: float, t_rec: float) -> int:
+    """Eq. 5: the number of new entries to reconstruct."""
+    n = lib().cgs_prep_budget(int(n_cand), float(m_free), float(m_entry), float(t_avl), float(t_trans),
+                              float(t_rec))
+    if n < 0:
+        raise CgsError("prep_budget: invalid arguments")
+    return n
+
+
+class Window:
+    """Sliding GPU working set of `slots` expanded entries (host bookkeeping
+    in libcgs; the caller rebuilds the entries an advance admits)."""
+
+    def __init__(self, slots: int):
+        self.slots = int(slots)
+        self._h = lib().cgs_window_create(self.slots)
+        if not self._h:
+            raise CgsError("cgs_window_create: invalid slot count")
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            _lib.cgs_window_destroy(h)
+
+    def slot(self, episode: int, position: int) -> int:
+        return lib().cgs_window_slot(self._h, int(episode), int(position))
+
+    def resident(self) -> int:
+        return lib().cgs_window_resident(self._h)
+
+    def advance(self, episodes, positions, lengths, L: int, budget=None):
+        """One advance; budget = (m_free, m_entry, t_avl, t_trans, t_rec) or None.
+        Returns (entered [(episode, position, slot)], left slots, n_candidates)."""
+        T = len(episodes)
+        arr = lambda v: (ctypes.c_int32 * max(T, 1))(*[int(x) for x in v])
+        ep, pos, ln = arr(episodes), arr(positions), arr(lengths)
+        out = lambda: (ctypes.c_int32 * self.slots)()
+        e_ep, e_pos, e_slot, l_slot = out(), out(), out(), out()
+        ne, nl, nc = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        b = ctypes.byref(_Budget(*[float(x) for x in budget])) if budget is not None else None
+        _check(lib().cgs_window_advance(self._h, T, ep, pos, ln, int(L), b, e_ep, e_pos, e_slot,
+                                        ctypes.byref(ne), l_slot, ctypes.byref(nl), ctypes.byref(nc)),
+               "cgs_window_advance")
+        entered = [(e_ep[i], e_pos[i], e_slot[i]) for i in range(ne.value)]
+        return entered, [l_slot[i] for i in range(nl.value)], nc.value
 
 
 def ref_rebuild_dense(layers, r0, x_ref_out=None, y_ref_out=None, ws=None, stream=None):

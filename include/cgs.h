@@ -280,6 +280,60 @@ int cgs_profile_stop(void);
  * cover the kept ones). */
 int cgs_profile_result(const char* site, double* total_ms, int* launches);
 
+/* ------------------------------------------------------------------------
+ * Sliding GPU working set (§4.2 "Sliding Window Prefetching", Figure 12) and
+ * reconstruction budget (§4.2 Eq. 5, Table 2).  Host logic only: these calls
+ * touch no device memory and launch nothing; the caller rebuilds the entries
+ * an advance admits (ref_rebuild_dense into the named slot).
+ * ------------------------------------------------------------------------ */
+
+/* Eq. 5: N_prep = min(N_cand, floor(M_free / M_entry), floor((T_avl - T_trans) / T_rec)),
+ * clamped at 0.  Memory in bytes, times in one unit (e.g. ms); T_avl may be
+ * +inf.  Returns -1 for n_cand < 0, M_entry <= 0, T_rec <= 0, M_free < 0 or a
+ * NaN time. */
+int cgs_prep_budget(int n_cand, double m_free, double m_entry, double t_avl, double t_trans,
+                    double t_rec);
+
+/* Table 2's parameters for one advance of the window. */
+typedef struct {
+  double m_free;   /* free device memory for new entries, bytes */
+  double m_entry;  /* expanded footprint of one entry, bytes */
+  double t_avl;    /* time available for reconstruction before the next call */
+  double t_trans;  /* input-transfer time of the batch (same unit) */
+  double t_rec;    /* average reconstruction time of one entry (same unit), > 0 */
+} cgs_budget;
+
+/* The working set: `slots` device slots (1 .. 2^20), initially empty. */
+typedef struct cgs_window cgs_window;
+cgs_window* cgs_window_create(int slots);
+void cgs_window_destroy(cgs_window* w);
+
+/* Slot holding (episode, position), or -1 if that entry is not resident. */
+int cgs_window_slot(const cgs_window* w, int episode, int position);
+
+/* Number of resident entries (-1 for a NULL window). */
+int cgs_window_resident(const cgs_window* w);
+
+/* One advance.  The window is, for each of the T candidate episodes in rank
+ * order (episode[r], distinct, >= 0), the positions position[r] .. position[r]
+ * + L that are below length[r].  Resident entries outside the window are
+ * released: their slots, ascending, go to leave_slot[0 .. *n_leave).  The
+ * window's entries that are not resident are the candidates (count in
+ * *n_cand, may be NULL), ordered nearest position first (offset from
+ * position[r]), then by episode rank; the first N_prep of them take the
+ * lowest free slots and are listed in enter_ep/enter_pos/enter_slot[0 ..
+ * *n_enter), where N_prep = min(candidates, free slots, Eq. 5 of `budget`
+ * when budget is non-NULL).  Candidates beyond N_prep stay candidates at the
+ * next advance.  The initial-position preload is an advance with the task's
+ * reference episodes at position 0 and L = 0.  All output arrays are host
+ * memory of at least `slots` elements.  Invalid arguments (a NULL pointer, a
+ * negative T, L, episode, position or length, an episode listed twice, a bad
+ * budget) return an error before the working set changes. */
+int cgs_window_advance(cgs_window* w, int T, const int32_t* episode, const int32_t* position,
+                       const int32_t* length, int L, const cgs_budget* budget, int32_t* enter_ep,
+                       int32_t* enter_pos, int32_t* enter_slot, int32_t* n_enter, int32_t* leave_slot,
+                       int32_t* n_leave, int32_t* n_cand);
+
 #ifdef __cplusplus
 }
 #endif
