@@ -193,7 +193,7 @@ class World:
         self._denoise_dense(a_ref, self.h_ref)
         self.mask_words = torch.empty(L_EXP, (FFE + 63) // 64, dtype=torch.int64, device=dev)
         self.mask_idx = torch.empty(L_EXP, FFE, dtype=torch.int32, device=dev)
-        self.mask_cnt = torch.empty(L_EXP, 1, dtype=torch.int32, device=dev)
+        self.mask_cnt = torch.empty(L_EXP, dtype=torch.int32, device=dev)
         self.build_masks(self.mask_words, self.mask_idx, self.mask_cnt)
         torch.cuda.synchronize()
         self.K = [int(c) for c in self.mask_cnt.view(-1).tolist()]
@@ -220,9 +220,9 @@ class World:
                                      x_out=self.xa)
 
     def build_masks(self, words, idx, cnt):
-        for l in range(L_EXP):
-            self.cgs.act_build_mask(self.h_ref[l], self.exp[l], "coverage", coverage=COVERAGE,
-                                    mask_out=words[l], idx_out=idx[l], count_out=cnt[l])
+        # the 18 layers' masks are independent: one batched build
+        self.cgs.act_build_masks(self.h_ref, self.exp, "coverage", coverage=COVERAGE,
+                                 mask_out=words, idx_out=idx, count_out=cnt)
 
     # --- one policy call -------------------------------------------------------
     # Between layers the residual add, the RMSNorm of the next layer's input and

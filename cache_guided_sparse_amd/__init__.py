@@ -79,6 +79,8 @@ _SIGS = {
     "ctx_ffn_recompute": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "cgs_act_build_mask_workspace": (_sz, [_i, _i, _i, _i]),
     "act_build_mask": (_i, [_vp, _i, _i, _vp, _i, _i, _d, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "cgs_act_build_masks_workspace": (_sz, [_i, _i, _i, _i, _i]),
+    "act_build_masks": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _d, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cgs_act_ffn_masked_workspace": (_sz, [_i, _i, _i, _i]),
     "act_ffn_masked": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "act_ffn_masked_compact": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -242,6 +244,31 @@ def act_build_mask(h_ref, w: FFN, mode: str = "topk", K: int = 0, coverage: floa
     _check(lib().act_build_mask(_ptr(h_ref), T, S, ctypes.byref(c), _MODE[mode], int(K),
                                 float(coverage), _ptr(mask_out), _ptr(idx_out), _ptr(count_out),
                                 _ptr(ws), ws.numel(), _stream(stream)), "act_build_mask")
+    return mask_out, idx_out, count_out
+
+
+def act_build_masks(h_ref, layers, mode: str = "topk", K: int = 0, coverage: float = 0.0,
+                    mask_out=None, idx_out=None, count_out=None, ws=None, stream=None):
+    """Group masks of several layers at once: h_ref [layers][T][ff][S] float32,
+    layers = list of FFN (layout 'fd'); returns (mask words [layers][words],
+    idx [layers][ff], count [layers])."""
+    Lr, T, ff, S = h_ref.shape
+    if len(layers) != Lr:
+        raise CgsError("act_build_masks: one FFN per layer of h_ref")
+    dev = h_ref.device
+    words = (ff + 63) // 64
+    if mask_out is None:
+        mask_out = torch.empty((Lr, words), dtype=torch.int64, device=dev)
+    if idx_out is None:
+        idx_out = torch.empty((Lr, ff), dtype=torch.int32, device=dev)
+    if count_out is None:
+        count_out = torch.empty(Lr, dtype=torch.int32, device=dev)
+    arr = (_Ffn * Lr)(*[w.cstruct() for w in layers])
+    nbytes = lib().cgs_act_build_masks_workspace(Lr, T, S, ff, layers[0].d)
+    ws = workspace(nbytes, dev, "mask") if ws is None else ws
+    _check(lib().act_build_masks(_ptr(h_ref), Lr, T, S, arr, _MODE[mode], int(K), float(coverage),
+                                 _ptr(mask_out), _ptr(idx_out), _ptr(count_out), _ptr(ws), ws.numel(),
+                                 _stream(stream)), "act_build_masks")
     return mask_out, idx_out, count_out
 
 

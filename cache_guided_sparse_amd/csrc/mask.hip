@@ -50,15 +50,28 @@ template <> struct W8<float> {
 
 constexpr int kContribT = 8;  // reference steps whose activations are loaded up front
 
+// The W_down of every layer of a batched build (one kernel argument).
+constexpr int kMaxMaskLayers = 64;
+struct LayerPtrs {
+  const void* p[kMaxMaskLayers];
+};
+
+// blockIdx.y = layer: its h_ref block [T][ff][S], W_down and key slices.
 template <typename T>
 __global__ __launch_bounds__(256) void contrib_kernel(const float* __restrict__ h, int T_steps,
-                                                      int S, const T* __restrict__ wd, int d, int ff,
+                                                      int S, LayerPtrs wdp, int d, int ff,
                                                       uint64_t* __restrict__ ckey,
                                                       uint64_t* __restrict__ skey,
                                                       double* __restrict__ sval, bool vec) {
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (n >= ff) return;
+  const int layer = blockIdx.y;
+  const T* wd = static_cast<const T*>(wdp.p[layer]);
+  h += static_cast<size_t>(layer) * T_steps * ff * S;
+  ckey += static_cast<size_t>(layer) * T_steps * ff;
+  skey += static_cast<size_t>(layer) * ff;
+  sval += static_cast<size_t>(layer) * ff;
   const T* wr = wd + static_cast<size_t>(n) * d;
   // The activations of up to kContribT steps (S <= 64: one per lane) are
   // fetched before the weight row, so both loads are in flight together.
@@ -147,11 +160,23 @@ __device__ __forceinline__ long long block_sum_ll(long long v, MaskShared& sm) {
   return r;
 }
 
+// One workgroup per layer (blockIdx.x): its key slices, scratch and outputs.
 __global__ __launch_bounds__(kSelThreads) void mask_select_kernel(
     const uint64_t* __restrict__ ckey, const uint64_t* __restrict__ skey,
     const double* __restrict__ sval, int T_steps, int ff, int mode, int K, double coverage,
     int q_bits, uint32_t* __restrict__ uni, uint32_t* __restrict__ flag,
     uint64_t* __restrict__ mask_out, int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out) {
+  {
+    const size_t layer = blockIdx.x;
+    ckey += layer * T_steps * ff;
+    skey += layer * ff;
+    sval += layer * ff;
+    uni += layer * ff;
+    flag += layer * ff;
+    mask_out += layer * ((ff + 63) / 64);
+    idx_out += layer * ff;
+    count_out += layer;
+  }
   __shared__ MaskShared sm;
   __shared__ uint32_t bm[kSelThreads * kChunkR / 32];  // mask bits of the cached path
   const int tid = threadIdx.x;
@@ -270,14 +295,15 @@ struct MaskWs {
   size_t bytes;
 };
 
-MaskWs carve_mask(void* ws, int T, int ff) {
+MaskWs carve_mask(void* ws, int layers, int T, int ff) {
   Carve cv(ws);
   MaskWs m{};
-  m.ckey = cv.take<uint64_t>(static_cast<size_t>(T) * ff);
-  m.skey = cv.take<uint64_t>(ff);
-  m.sval = cv.take<double>(ff);
-  m.uni = cv.take<uint32_t>(ff);
-  m.flag = cv.take<uint32_t>(ff);
+  const size_t lf = static_cast<size_t>(layers) * ff;
+  m.ckey = cv.take<uint64_t>(lf * T);
+  m.skey = cv.take<uint64_t>(lf);
+  m.sval = cv.take<double>(lf);
+  m.uni = cv.take<uint32_t>(lf);
+  m.flag = cv.take<uint32_t>(lf);
   m.bytes = cv.bytes();
   return m;
 }
@@ -293,45 +319,63 @@ int bit_length(unsigned v) {
 
 using namespace cgs;
 
-extern "C" size_t cgs_act_build_mask_workspace(int T, int S, int ff, int d) {
+extern "C" size_t cgs_act_build_masks_workspace(int layers, int T, int S, int ff, int d) {
   (void)S; (void)d;
-  if (T <= 0 || ff <= 0) return 0;
-  return carve_mask(nullptr, T, ff).bytes;
+  if (layers <= 0 || layers > kMaxMaskLayers || T <= 0 || ff <= 0) return 0;
+  return carve_mask(nullptr, layers, T, ff).bytes;
 }
 
-extern "C" int act_build_mask(const float* h_ref, int T, int S, const cgs_ffn* w, int mode, int K,
-                              double coverage, uint64_t* mask_out, int32_t* idx_out,
-                              int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
-  if (!h_ref || !w || !w->w_down || !valid_dtype(w->dtype) || w->down_layout != CGS_DOWN_FD ||
-      !mask_out || !idx_out || !count_out)
-    return CGS_ERR_ARG;
+extern "C" size_t cgs_act_build_mask_workspace(int T, int S, int ff, int d) {
+  return cgs_act_build_masks_workspace(1, T, S, ff, d);
+}
+
+extern "C" int act_build_masks(const float* h_ref, int layers, int T, int S, const cgs_ffn* w, int mode,
+                               int K, double coverage, uint64_t* mask_out, int32_t* idx_out,
+                               int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!h_ref || !w || !mask_out || !idx_out || !count_out) return CGS_ERR_ARG;
+  if (layers <= 0 || layers > kMaxMaskLayers) return CGS_ERR_SHAPE;
+  for (int l = 0; l < layers; ++l)
+    if (!w[l].w_down || !valid_dtype(w[l].dtype) || w[l].down_layout != CGS_DOWN_FD) return CGS_ERR_ARG;
   if (mode != CGS_MASK_TOPK && mode != CGS_MASK_COVERAGE) return CGS_ERR_ARG;
-  const int ff = w->ff, d = w->d;
+  const int ff = w[0].ff, d = w[0].d, dt = w[0].dtype;
+  for (int l = 1; l < layers; ++l)
+    if (w[l].ff != ff || w[l].d != d || w[l].dtype != dt) return CGS_ERR_SHAPE;
   if (T <= 0 || S <= 0 || ff <= 0 || d <= 0 || d > 4096 || ff > 65536 ||
       static_cast<long long>(S) * T > (1 << 14))
     return CGS_ERR_SHAPE;
   if (mode == CGS_MASK_TOPK && (K < 0 || K > ff)) return CGS_ERR_SHAPE;
   if (mode == CGS_MASK_COVERAGE && !(coverage >= 0.0 && coverage <= 1.0)) return CGS_ERR_SHAPE;
-  if (!ws || ws_bytes < cgs_act_build_mask_workspace(T, S, ff, d)) return CGS_ERR_WORKSPACE;
+  if (!ws || ws_bytes < cgs_act_build_masks_workspace(layers, T, S, ff, d)) return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const MaskWs m = carve_mask(ws, T, ff);
-  const dim3 grid((ff + 3) / 4), block(256);
+  const MaskWs m = carve_mask(ws, layers, T, ff);
+  LayerPtrs wdp{};
+  // 16-byte weight loads when every row of every layer starts 16-byte aligned
+  bool vec = d % 8 == 0 && (static_cast<size_t>(d) * elem_bytes(dt)) % 16 == 0;
+  for (int l = 0; l < layers; ++l) {
+    wdp.p[l] = w[l].w_down;
+    vec = vec && reinterpret_cast<uintptr_t>(w[l].w_down) % 16 == 0;
+  }
+  const dim3 grid((ff + 3) / 4, layers), block(256);
   {
   ProfScope ps("mask.contrib", s);
-  // 16-byte weight loads when every row starts 16-byte aligned
-  const bool vec = d % 8 == 0 && reinterpret_cast<uintptr_t>(w->w_down) % 16 == 0 &&
-                   (static_cast<size_t>(d) * elem_bytes(w->dtype)) % 16 == 0;
-  if (w->dtype == CGS_BF16)
-    hipLaunchKernelGGL((contrib_kernel<uint16_t>), grid, block, 0, s, h_ref, T, S,
-                       static_cast<const uint16_t*>(w->w_down), d, ff, m.ckey, m.skey, m.sval, vec);
+  if (dt == CGS_BF16)
+    hipLaunchKernelGGL((contrib_kernel<uint16_t>), grid, block, 0, s, h_ref, T, S, wdp, d, ff, m.ckey,
+                       m.skey, m.sval, vec);
   else
-    hipLaunchKernelGGL((contrib_kernel<float>), grid, block, 0, s, h_ref, T, S,
-                       static_cast<const float*>(w->w_down), d, ff, m.ckey, m.skey, m.sval, vec);
+    hipLaunchKernelGGL((contrib_kernel<float>), grid, block, 0, s, h_ref, T, S, wdp, d, ff, m.ckey,
+                       m.skey, m.sval, vec);
   }
   if (!launch_ok()) return CGS_ERR_LAUNCH;
   const int q_bits = 61 - bit_length(static_cast<unsigned>(ff - 1));
   ProfScope ps("mask.select", s);
-  hipLaunchKernelGGL(mask_select_kernel, dim3(1), dim3(kSelThreads), 0, s, m.ckey, m.skey, m.sval,
+  hipLaunchKernelGGL(mask_select_kernel, dim3(layers), dim3(kSelThreads), 0, s, m.ckey, m.skey, m.sval,
                      T, ff, mode, K, coverage, q_bits, m.uni, m.flag, mask_out, idx_out, count_out);
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
+}
+
+extern "C" int act_build_mask(const float* h_ref, int T, int S, const cgs_ffn* w, int mode, int K,
+                              double coverage, uint64_t* mask_out, int32_t* idx_out,
+                              int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
+  return act_build_masks(h_ref, 1, T, S, w, mode, K, coverage, mask_out, idx_out, count_out, ws, ws_bytes,
+                         stream);
 }

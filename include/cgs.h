@@ -179,6 +179,19 @@ int act_build_mask(const float* h_ref, int T, int S, const cgs_ffn* w, int mode,
                    double coverage, uint64_t* mask_out, int32_t* idx_out, int32_t* count_out,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes for act_build_masks over `layers` layers (1 .. 64). */
+size_t cgs_act_build_masks_workspace(int layers, int T, int S, int ff, int d);
+
+/* act_build_mask for `layers` layers of one group in one pair of launches
+ * (the layers are independent: §5 builds each layer's mask from its own
+ * contributions).  h_ref: [layers][T][ff][S] float; w: host array of
+ * `layers` FFNs with equal d, ff and dtype, CGS_DOWN_FD; mask_out:
+ * [layers][ceil(ff/64)]; idx_out: [layers][ff]; count_out: [layers] (device).
+ * Every layer's outputs are exactly act_build_mask's for that layer. */
+int act_build_masks(const float* h_ref, int layers, int T, int S, const cgs_ffn* w, int mode, int K,
+                    double coverage, uint64_t* mask_out, int32_t* idx_out, int32_t* count_out,
+                    void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for act_ffn_masked with S tokens and K masked neurons. */
 size_t cgs_act_ffn_masked_workspace(int S, int K, int d, int ff);
 

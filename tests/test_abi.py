@@ -110,6 +110,13 @@ def test_host_validation_without_launch():
     assert L.act_gather_rows(ctypes.byref(wf), buf, 2000, buf, buf, buf, None) == 2
     assert L.act_gather_rows(ctypes.byref(wf), None, 4, buf, buf, buf, None) == 1
     assert L.act_gather_rows(ctypes.byref(wf), None, 0, None, None, None, None) == 0
+    # act_build_masks: layer count, mismatched layers
+    arr2 = (cgs._Ffn * 2)(_ffn(layout=1), _ffn(layout=1, ff=2048))
+    assert L.act_build_masks(buf, 0, 2, 8, ctypes.byref(wf), 0, 4, 0.0, buf, buf, buf, buf, 1 << 30, None) == 2
+    assert L.act_build_masks(buf, 65, 2, 8, ctypes.byref(wf), 0, 4, 0.0, buf, buf, buf, buf, 1 << 30, None) == 2
+    assert L.act_build_masks(buf, 2, 2, 8, arr2, 0, 4, 0.0, buf, buf, buf, buf, 1 << 30, None) == 2
+    assert L.cgs_act_build_masks_workspace(18, 4, 50, 4096, 1024) >= 18 * 4096 * (4 * 8 + 8 + 8 + 4 + 4)
+    assert L.cgs_act_build_masks_workspace(0, 4, 50, 4096, 1024) == 0
     # act_ffn_masked_compact: K must equal the compact row count; anchors need idx
     wc = _ffn(layout=1, ff=64)
     assert L.act_ffn_masked_compact(ctypes.byref(wc), buf, 4, buf, 10, None, None, buf, None, None, None, buf, 1 << 30, None) == 2

@@ -91,3 +91,25 @@ def test_fp32_weights():
     w, h = _setup(24, 2, 1024, 16, 256, dtype="f32")
     _check(h, w, "topk", K=256)
     _check(h, w, "coverage", cov=0.844)
+
+
+@pytest.mark.parametrize("mode,ff,d,S,T", [("coverage", 4096, 1024, 50, 4), ("topk", 4096, 1024, 50, 4),
+                                           ("coverage", 5000, 256, 10, 2), ("topk", 200, 128, 70, 3)])
+def test_batched_layers_equal_single_layer_builds(mode, ff, d, S, T):
+    """act_build_masks over several layers (one launch pair) gives every layer
+    exactly what act_build_mask gives it, and the oracle's mask."""
+    say("batched masks", mode, ff, d, S, T)
+    layers = 5
+    ws = [ffn_weights(50 + l, l, d, ff, down_layout="fd", down_lognormal_sigma=1.5) for l in range(layers)]
+    hs = [synthetic_h_ref(50 + l, l, T, ff, S, neuron_sigma=0.5) for l in range(layers)]
+    K, cov = (max(1, ff // 3), 0.0) if mode == "topk" else (0, 0.844)
+    W = [ffn_dev(w) for w in ws]
+    H = to_dev(np.ascontiguousarray(np.stack(hs), dtype=np.float32), "f32")
+    m, idx, cnt = cgs.act_build_masks(H, W, mode, K=K, coverage=cov)
+    torch.cuda.synchronize()
+    m, idx, cnt = m.cpu().numpy().view(np.uint64), idx.cpu().numpy(), cnt.cpu().numpy()
+    for l in range(layers):
+        gm, gi, gc = _gpu_mask(hs[l], ws[l], mode, K, cov)
+        assert cnt[l] == gc and np.array_equal(idx[l], gi) and np.array_equal(m[l], gm), f"layer {l}"
+        oi, om = O.act_build_mask(hs[l], ws[l], mode, K=K, coverage=cov)
+        assert np.array_equal(gi[:gc], oi) and np.array_equal(gm, om), f"layer {l} vs oracle"
