@@ -3,6 +3,10 @@
 
 One step is one policy-call slice of rMuscle (Zhou et al.), every row of the
 hot path once, with all inputs resident in HBM:
+  * reference retrieval (§4.2, §5): cosine similarity of the call's flattened
+    768 x 1152 ViT features against the 16 prepared entries, top 4, rerank by
+    the joint-history distance, fallback below cosine 0.8; the chosen slot
+    drives the prefill (its index is read back to the host);
   * Context Cache prefill (§4.1, Eq. 2/3): 17 VLM FFN layers, 768 visual tokens
     (3 views x 256 patches), d 2048, ff 16384, bf16; per layer the input drift
     score picks ceil(0.3 x 768) = 231 tokens, their FFN rows are recomputed and
@@ -47,6 +51,8 @@ P, D, FF, L_VLM, RHO_P = 768, 2048, 16384, 17, 0.3
 S, DE, FFE, L_EXP, STEPS, COVERAGE = 50, 1024, 4096, 18, 4, 0.844
 STORE, SLOTS, LOOKAHEAD = 800, 16, 15   # repository entries, device slots, window lookahead
 T_AVL_MS = 500.0                           # a 15-action chunk at 30 Hz (the paper's example)
+FEAT = 768 * 1152                          # ViT layer-15 features of three views, flattened
+HIST_L, JOINTS, TOP_T = 4, 14, 4           # state history, joints (two arms), visual top-T
 
 
 def log(*a):
@@ -137,6 +143,25 @@ class World:
             self.current[c0:c0 + n] = comp + randn(n, P, D) * sig
             self.store[c0:c0 + n].copy_(comp.to(bf))
         self.staging = torch.empty((P, D), dtype=bf, device=dev)
+        # retrieval data of every repository position: ViT features that drift
+        # slowly along the episode (consecutive positions cos ~0.98) and the
+        # robot-state history [HIST_L][JOINTS] of a smooth joint trajectory;
+        # the current call's features / history are its position's plus noise
+        self.feat_store = torch.empty((STORE, FEAT), dtype=bf, pin_memory=True)
+        self.qfeat = torch.empty((STORE, FEAT), dtype=bf, device=dev)
+        f = randn(FEAT)
+        for q in range(STORE):
+            f = 0.98 * f + math.sqrt(1 - 0.98 ** 2) * randn(FEAT)
+            self.feat_store[q].copy_(f.to(bf))
+            self.qfeat[q] = (f + 0.1 * randn(FEAT)).to(bf)
+        traj = torch.cumsum(0.05 * randn(STORE + HIST_L, JOINTS), dim=0)
+        hist = torch.stack([traj[q:q + HIST_L] for q in range(STORE)])
+        self.hist_store = hist.cpu().pin_memory()
+        self.qhist = (hist + 0.005 * randn(STORE, HIST_L, JOINTS)).contiguous()
+        self.slot_feat = torch.empty((SLOTS, FEAT), dtype=bf, device=dev)
+        self.slot_hist = torch.empty((SLOTS, HIST_L, JOINTS), dtype=torch.float32, device=dev)
+        self.choice = torch.empty(1, dtype=torch.int32, device=dev)
+        self.matches, self.fallbacks, self.calls = 0, 0, 0
         # expanded working set: SLOTS entries of (xbar, ybar) per layer, managed
         # as a sliding window (position q .. q + LOOKAHEAD of the episode)
         self.xbar = torch.empty(SLOTS, L_VLM, P, D, dtype=bf, device=dev)
@@ -254,6 +279,22 @@ class World:
             raise RuntimeError(f"entry {q} is not resident")
         return slot, entered
 
+    def retrieve(self, i):
+        """Visual top-T over the prepared slots, joint-history rerank and the
+        fallback test for call i; returns the chosen slot (host sync), or the
+        window's slot for the matched position when retrieval falls back."""
+        q = self.position(i)
+        self.cgs.ret_select(self.qfeat[q], self.slot_feat, TOP_T, self.qhist[q], self.slot_hist, arm=-1,
+                            min_cos=0.8, choice_out=self.choice)
+        c = int(self.choice.item())
+        want = self.window.slot(0, q)
+        self.calls += 1
+        self.matches += c == want
+        if c < 0:
+            self.fallbacks += 1
+            c = want
+        return c
+
     def ctx_prefill(self, i, e):
         self.cgs.residual_rmsnorm(self.r, r_in=self.current[self.position(i)], x_out=self.x)
         if self.g_ctx:
@@ -302,8 +343,10 @@ class World:
         self.g_mask.replay() if self.g_mask else self._mask_build()
 
     def rebuild_entry(self, q, slot):
-        """Transfer compact entry q to the device and expand it into `slot`
-        (on the current stream)."""
+        """Transfer compact entry q (and its retrieval features and history) to
+        the device and expand it into `slot` (on the current stream)."""
+        self.slot_feat[slot].copy_(self.feat_store[q], non_blocking=True)
+        self.slot_hist[slot].copy_(self.hist_store[q], non_blocking=True)
         self.staging.copy_(self.store[q], non_blocking=True)
         self.cgs.ref_rebuild_dense(self.vlm, self.staging, self.xbar[slot], self.ybar[slot])
 
@@ -418,7 +461,7 @@ def main():
     dev = torch.device("cuda:0")
     w = World(dev)
 
-    phases = ["ctx_prefill", "act_anchor", "act_masked", "mask_build", "rebuild", "gather"]
+    phases = ["ctx_prefill", "act_anchor", "act_masked", "mask_build", "rebuild", "gather", "retrieval"]
     # The compact weights of the group's masks are gathered on a side stream
     # while the context prefill runs (the masked steps wait for them; the
     # gather waits until the previous call's masked steps are done with the
@@ -437,19 +480,23 @@ def main():
     gathered, masked_done = torch.cuda.Event(), torch.cuda.Event()
 
     def step(i, ev=None, serial=False):
-        """One call.  ev: 9 timing events; 0-4 bracket the main-stream phases,
-        5-6 the rebuild and 7-8 the gather on the streams that run them."""
-        e, entered = w.advance(i)
+        """One call.  ev: 11 timing events; 9-10 the retrieval, 0-4 the other
+        main-stream phases, 5-6 the rebuild and 7-8 the gather on the streams
+        that run them."""
+        _, entered = w.advance(i)
         rec = (lambda q: ev[q].record()) if ev is not None else (lambda q: None)
-        if pending[e]:
-            main_s.wait_event(rebuilt[e])
-            pending[e] = False
         gather_s.wait_event(masked_done)
         with torch.cuda.stream(gather_s):
             rec(7)
             w.gather()
             rec(8)
             gathered.record(gather_s)
+        rec(9)
+        e = w.retrieve(i)   # the slot the retrieval picks drives the prefill
+        rec(10)
+        if pending[e]:
+            main_s.wait_event(rebuilt[e])
+            pending[e] = False
         rec(0)
         w.ctx_prefill(i, e)
         rec(1)
@@ -480,17 +527,17 @@ def main():
             rec(6)
 
     def timed(first, n, serial=False):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(n)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(11)] for _ in range(n)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for j in range(n):
             step(first + j, evs[j], serial)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / n
-        bounds = [(0, 1), (1, 2), (2, 3), (3, 4), (5, 6), (7, 8)]
+        bounds = [(0, 1), (1, 2), (2, 3), (3, 4), (5, 6), (7, 8), (9, 10)]
         ph = {p: sum(evs[j][a].elapsed_time(evs[j][b]) for j in range(n)) / n
               for p, (a, b) in zip(phases, bounds)}
-        crit = sorted(evs[j][0].elapsed_time(evs[j][4]) for j in range(n))
+        crit = sorted(evs[j][9].elapsed_time(evs[j][4]) for j in range(n))
         return 1e3 * wall, ph, crit
 
     # warmup; after one step that loads every kernel, the first half also times
@@ -507,7 +554,7 @@ def main():
     for s in ("ctx.score", "ctx.topk", "ctx.glu", "ctx.down", "ctx.finish", "rebuild.norm",
               "rebuild.glu", "rebuild.down", "rebuild.finish", "act.glu.dense", "act.down.dense",
               "act.glu.masked", "act.down.masked", "act.finish", "act.gather", "mask.contrib",
-              "mask.select", "glue.rmsnorm"):
+              "mask.select", "ret.dot", "ret.select", "glue.rmsnorm"):
         t, n = cgs.profile_result(s)
         if n:
             sites[s] = {"launches_per_step": n / n_prof, "mean_us": round(1e3 * t / n, 2),
@@ -577,7 +624,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": ("policy-call slice: 17-layer Context Cache prefill (768 tokens, d 2048, "
+        "config": {"workload": ("policy-call slice: retrieval over the 16 prepared entries (cosine of "
+                                "768x1152 ViT features, top-4, joint-history rerank, fallback) + "
+                                "17-layer Context Cache prefill (768 tokens, d 2048, "
                                 "ff 16384, rho_p 0.3) + 4-step Action Cache denoise (18 layers, d 1024, "
                                 "ff 4096, 50 tokens, coverage 0.844, anchor step 0) + group mask build "
                                 "+ one 17-layer dense entry rebuild (host-to-device transfer of the compact "
@@ -608,7 +657,11 @@ def main():
                                 "n_prep_bound": cgs.prep_budget(10 ** 6, *w.budget)}},
         "critical_path_ms": {"median": round(crit[len(crit) // 2], 4),
                              "p95": round(crit[min(len(crit) - 1, int(math.ceil(0.95 * len(crit))) - 1)], 4),
-                             "what": "context prefill + anchor + 3 masked steps + mask build of one call"},
+                             "what": "retrieval + context prefill + anchor + 3 masked steps + mask build "
+                                     "of one call (retrieval includes its host read-back)"},
+        "retrieval": {"ms": round(ph["retrieval"], 4), "top_t": TOP_T, "features": FEAT,
+                      "history": [HIST_L, JOINTS], "calls": w.calls,
+                      "chose_matched_entry": round(w.matches / max(1, w.calls), 4), "fallbacks": w.fallbacks},
         "rebuild_stream": args.rebuild_stream,
         "serial_reference": serial,
         "kernel_sites": sites,

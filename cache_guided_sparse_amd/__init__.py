@@ -88,6 +88,9 @@ _SIGS = {
     "cgs_ref_rebuild_dense_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "ref_rebuild_dense": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
     "cgs_residual_rmsnorm": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _vp, _i, _vp]),
+    "cgs_ret_select_workspace": (_sz, [_i, ctypes.c_longlong]),
+    "ret_select": (_i, [_vp, _vp, _i, ctypes.c_longlong, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                        _sz, _vp]),
     "cgs_prep_budget": (_i, [_i, _d, _d, _d, _d, _d]),
     "cgs_window_create": (_vp, [_i]),
     "cgs_window_destroy": (None, [_vp]),
@@ -320,6 +323,37 @@ def act_ffn_masked_compact(wc: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=
                                         _glue(glue), _ptr(ws), ws.numel(), _stream(stream)),
            "act_ffn_masked_compact")
     return y_out
+
+
+class _Rerank(ctypes.Structure):
+    _fields_ = [("hist_len", ctypes.c_int32), ("joints", ctypes.c_int32), ("arm", ctypes.c_int32),
+                ("min_cos", ctypes.c_double)]
+
+
+def ret_select(query, refs, T: int, q_hist, r_hist, arm: int = -1, min_cos: float = 0.8,
+               cos_out=None, top_out=None, dist_out=None, choice_out=None, ws=None, stream=None):
+    """Visual top-T of the prepared entries, joint-history rerank, fallback.
+    query [F], refs [N][F] (bf16 or float32), q_hist [L][J], r_hist [N][L][J]
+    float32.  Returns (cos [N] f64, top [T] i32, dist [T] f64, choice [1] i32)."""
+    N = refs.shape[0]
+    F = int(query.numel())
+    L, J = q_hist.shape
+    dev = query.device
+    if cos_out is None:
+        cos_out = torch.empty(N, dtype=torch.float64, device=dev)
+    if top_out is None:
+        top_out = torch.empty(T, dtype=torch.int32, device=dev)
+    if dist_out is None:
+        dist_out = torch.empty(T, dtype=torch.float64, device=dev)
+    if choice_out is None:
+        choice_out = torch.empty(1, dtype=torch.int32, device=dev)
+    nbytes = lib().cgs_ret_select_workspace(N, F)
+    ws = workspace(nbytes, dev, "retrieval") if ws is None else ws
+    rr = _Rerank(L, J, int(arm), float(min_cos))
+    _check(lib().ret_select(_ptr(query), _ptr(refs), N, F, _dtype_code(query), int(T), _ptr(q_hist),
+                            _ptr(r_hist), ctypes.byref(rr), _ptr(cos_out), _ptr(top_out), _ptr(dist_out),
+                            _ptr(choice_out), _ptr(ws), ws.numel(), _stream(stream)), "ret_select")
+    return cos_out, top_out, dist_out, choice_out
 
 
 class _Budget(ctypes.Structure):

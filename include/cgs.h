@@ -294,6 +294,36 @@ int cgs_profile_stop(void);
 int cgs_profile_result(const char* site, double* total_ms, int* launches);
 
 /* ------------------------------------------------------------------------
+ * Reference retrieval over the prepared entries (§4.2 "Retrieving a Relevant
+ * Reference"; §5 "Joint-History Retrieval" and "Fallback policy").
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int hist_len;    /* L: aligned robot-state history steps */
+  int joints;      /* J: joints per step, two arms of J/2 (even) */
+  int arm;         /* -1: dual-arm task (larger of the two arm distances); 0 or 1: that arm */
+  double min_cos;  /* below this best visual cosine, no reference is used (the paper: 0.8) */
+} cgs_rerank;
+
+/* Workspace bytes for ret_select over N entries of F features (0 if invalid). */
+size_t cgs_ret_select_workspace(int N, long long F);
+
+/* query: [F] features (dtype, device); refs: [N][F] the prepared entries'
+ * features (1 <= N <= 256, F % 8 == 0, both 16-byte aligned).
+ * Visual match: cos_n = Sqr / sqrt(Sqq Srr) from the exact fixed-point sums
+ * of the token score's cosine kind (every feature product rounded half-even
+ * to an int64 at 2^-24; float64 key, 0 if a norm is 0), written to
+ * cos_out[N].  top_out[T] (1 <= T <= N): the T best entries by (cos desc,
+ * index asc).  Rerank: dist_out[r] = RMS over the L steps and the arm's J/2
+ * joints of q_hist - r_hist[top_out[r]] (float histories [L][J] and
+ * [N][L][J], device), the larger arm for arm = -1.  choice_out[0]: the
+ * candidate of smallest distance (ties to the better visual rank), or -1 if
+ * cos of the best match < min_cos (fallback to dense execution). */
+int ret_select(const void* query, const void* refs, int N, long long F, int dtype, int T,
+               const float* q_hist, const float* r_hist, const cgs_rerank* rr, double* cos_out,
+               int32_t* top_out, double* dist_out, int32_t* choice_out, void* ws, size_t ws_bytes,
+               void* stream);
+
+/* ------------------------------------------------------------------------
  * Sliding GPU working set (§4.2 "Sliding Window Prefetching", Figure 12) and
  * reconstruction budget (§4.2 Eq. 5, Table 2).  Host logic only: these calls
  * touch no device memory and launch nothing; the caller rebuilds the entries
