@@ -247,8 +247,11 @@ __global__ __launch_bounds__(kThreads) void act_finish_kernel(
   const size_t ro = static_cast<size_t>(s) * d;
   const size_t n = static_cast<size_t>(S) * d;
   float ss = 0.f;
-  for (int c = threadIdx.x * 8; c < d; c += kThreads * 8) {
-    float v[8];
+  float keep[kGlueKeep][8];
+  int j = 0;
+  for (int c = threadIdx.x * 8; c < d; c += kThreads * 8, ++j) {
+    float v[8], rr[8], b[8];
+    if (glue.r) glue_prefetch(glue, ro, c, rr, b);
     if (y_anchor) Row8<float>::load(y_anchor + ro + c, v);
     else {
 #pragma unroll
@@ -257,9 +260,15 @@ __global__ __launch_bounds__(kThreads) void act_finish_kernel(
     add_splits(part + ro + c, n, splits, v);
     if (y_f32) Row8<float>::store(y_f32 + ro + c, v);
     Row8<T>::store(y_out + ro + c, v);
-    if (glue.r) ss += glue_add(glue, ro, c, v);
+    if (glue.r) {
+      ss += glue_add(glue, ro, c, v, rr, b);
+      if (j < kGlueKeep) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) keep[j][e] = rr[e];
+      }
+    }
   }
-  if (glue.r && glue.x_next) glue_norm(glue, ro, d, ss, red);
+  if (glue.r && glue.x_next) glue_norm(glue, ro, d, ss, red, keep);
 }
 
 // Rows idx[0..K-1] of three [ff][d] matrices into compact [K][d] buffers:

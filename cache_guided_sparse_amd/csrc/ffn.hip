@@ -113,8 +113,11 @@ __global__ __launch_bounds__(kRowThreads) void row_finish_kernel(
   const size_t ro = static_cast<size_t>(p) * d;
   const size_t io = static_cast<size_t>(i) * d;
   float ss = 0.f;
-  for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8) {
-    float v[8];
+  float keep[kGlueKeep][8];
+  int j = 0;
+  for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8, ++j) {
+    float v[8], rr[8], b[8];
+    if (glue.r) glue_prefetch(glue, ro, c, rr, b);
     if (!sel) {
       Row8<T>::copy(y_ref + ro + c, y_out + ro + c);
       if (!glue.r) continue;
@@ -124,9 +127,15 @@ __global__ __launch_bounds__(kRowThreads) void row_finish_kernel(
       add_splits(part + split_stride + io + c, split_stride, splits - 1, v);
       Row8<T>::store(y_out + ro + c, v);
     }
-    if (glue.r) ss += glue_add(glue, ro, c, v);
+    if (glue.r) {
+      ss += glue_add(glue, ro, c, v, rr, b);
+      if (j < kGlueKeep) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) keep[j][e] = rr[e];
+      }
+    }
   }
-  if (glue.r && glue.x_next) glue_norm_t<T, kRowThreads>(glue, ro, d, ss, red);
+  if (glue.r && glue.x_next) glue_norm_t<T, kRowThreads>(glue, ro, d, ss, red, keep);
 }
 
 // r[m] = (r_src ? decode(r_src[m]) : r[m]) + (y ? decode(y[m]) : 0) + (bias ? bias : 0);

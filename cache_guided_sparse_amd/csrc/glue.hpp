@@ -123,14 +123,25 @@ inline GlueArgs<T> make_glue(const cgs_glue* g, int d) {
   return a;
 }
 
-// r[ro + c .. +8] += round(v) (+ bias[c .. +8]); returns the sum of squares of
-// the updated r values.
+// Runs of 8 elements a thread keeps in registers between the residual update
+// and the normalisation (rows of up to kGlueKeep x 8 x threads elements need
+// no second read of r).
+constexpr int kGlueKeep = 4;
+
+// Loads of r[ro + c .. +8] and bias[c .. +8], issued early so that they are
+// in flight with the loads of the row's output.
 template <typename T>
-__device__ __forceinline__ float glue_add(const GlueArgs<T>& g, size_t ro, int c, float* v) {
-  Row8<T>::round(v);
-  float rr[8], b[8];
+__device__ __forceinline__ void glue_prefetch(const GlueArgs<T>& g, size_t ro, int c, float* rr, float* b) {
   Row8<float>::load(g.r + ro + c, rr);
   if (g.bias) Row8<float>::load(g.bias + c, b);
+}
+
+// rr += round(v) (+ b), stored back to r[ro + c .. +8]; returns the sum of
+// squares of the updated values (left in rr).
+template <typename T>
+__device__ __forceinline__ float glue_add(const GlueArgs<T>& g, size_t ro, int c, float* v, float* rr,
+                                          const float* b) {
+  Row8<T>::round(v);
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -160,15 +171,24 @@ __device__ __forceinline__ long long block_sum_i64(long long v, long long* red) 
 // this thread updated with glue_add; `ss` is its partial sum of squares.  With
 // a score reference, also the Eq. 2 key of the stored (rounded) x_next row
 // against it, exactly as the standalone score kernel computes it.
+// keep[j]: the updated r values of this thread's run j (j < kGlueKeep), as
+// glue_add left them; later runs are read back from r.
 template <typename T, int NT>
-__device__ __forceinline__ void glue_norm_t(const GlueArgs<T>& g, size_t ro, int d, float ss, float* red) {
+__device__ __forceinline__ void glue_norm_t(const GlueArgs<T>& g, size_t ro, int d, float ss, float* red,
+                                            const float (*keep)[8]) {
   const float tot = block_sum<NT>(ss, red);
   const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + 1e-6f);
   ScoreSums sc;
   const bool cosine = g.score_kind == CGS_SCORE_COSINE;
-  for (int c = threadIdx.x * 8; c < d; c += NT * 8) {
+  int j = 0;
+  for (int c = threadIdx.x * 8; c < d; c += NT * 8, ++j) {
     float rr[8];
-    Row8<float>::load(g.r + ro + c, rr);
+    if (j < kGlueKeep) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rr[e] = keep[j][e];
+    } else {
+      Row8<float>::load(g.r + ro + c, rr);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) rr[e] *= inv;
     Row8<T>::store(g.x_next + ro + c, rr);
@@ -198,8 +218,9 @@ __device__ __forceinline__ void glue_norm_t(const GlueArgs<T>& g, size_t ro, int
 }
 
 template <typename T>
-__device__ __forceinline__ void glue_norm(const GlueArgs<T>& g, size_t ro, int d, float ss, float* red) {
-  glue_norm_t<T, 256>(g, ro, d, ss, red);
+__device__ __forceinline__ void glue_norm(const GlueArgs<T>& g, size_t ro, int d, float ss, float* red,
+                                          const float (*keep)[8]) {
+  glue_norm_t<T, 256>(g, ro, d, ss, red, keep);
 }
 
 }  // namespace cgs
