@@ -378,9 +378,9 @@ class World:
 def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
     """The oracle, timed on the host cores over a bounded sample of the step:
     one context layer (select + recompute of 231 rows), one dense anchor
-    layer, one masked layer, one mask build and one dense rebuild layer, each
-    timed `reps` times (mean), scaled to the step's 17 / 18 / 54 / 18 / 17
-    layer counts."""
+    layer, one masked layer, one mask build, one dense rebuild layer and one
+    retrieval over the 16 prepared entries, each timed `reps` times (mean),
+    scaled to the step's 17 / 18 / 54 / 18 / 17 / 1 counts."""
     import numpy as np
     import oracle as O
     from cgs_inputs import act_tokens, ctx_layer_inputs, ffn_weights, random_bf16, synthetic_h_ref
@@ -400,8 +400,12 @@ def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
     r0 = random_bf16(7, 0, "r0", (P, D))
     k = O.ratio_to_count(RHO_P, P)
     m = np.sort(np.random.default_rng(0).permutation(FFE)[:k_masked_mean]).astype(np.int32)
+    from oracle.cgs_retrieval import ret_select as oracle_ret_select
+    g = np.random.default_rng(7)
+    feats = O.round_to_bf16_bits(g.standard_normal((SLOTS + 1, FEAT)))
+    hists = g.standard_normal((SLOTS, HIST_L, JOINTS))
     tm = {"ctx_layer": 0.0, "anchor_layer": 0.0, "masked_layer": 0.0, "mask_layer": 0.0,
-          "rebuild_layer": 0.0}
+          "rebuild_layer": 0.0, "retrieval": 0.0}
     for _ in range(reps):
         t0 = time.perf_counter()
         idx, _ = O.ctx_select(inp["x"], inp["x_ref"], k)
@@ -419,15 +423,19 @@ def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
         t0 = time.perf_counter()
         O.rebuild_dense([w], r0)
         tm["rebuild_layer"] += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        oracle_ret_select(feats[0], feats[1:], TOP_T, hists[0], hists)
+        tm["retrieval"] += time.perf_counter() - t0
     total = sum(tm.values())
     tm = {k_: v / reps for k_, v in tm.items()}
     per_step = (L_VLM * tm["ctx_layer"] + L_EXP * tm["anchor_layer"]
                 + (STEPS - 1) * L_EXP * tm["masked_layer"] + L_EXP * tm["mask_layer"]
-                + L_VLM * tm["rebuild_layer"])
+                + L_VLM * tm["rebuild_layer"] + tm["retrieval"])
     return {"value": round(per_step * 1e3, 1), "unit": "ms", "cores": cores, "kind": "oracle",
             "sample": (f"one layer of each row, timed {reps} times on the host (mean) and scaled to the step: "
                        "17 x (ctx select + 231-row recompute) + 18 x dense anchor + 54 x masked "
-                       "+ 18 x mask build + 17 x dense rebuild layer; NumPy float64"),
+                       "+ 18 x mask build + 17 x dense rebuild layer + one retrieval over 16 entries; "
+                       "NumPy float64"),
             "sample_seconds": round(total, 2),
             "per_layer_ms": {k_: round(v * 1e3, 2) for k_, v in tm.items()}}
 
