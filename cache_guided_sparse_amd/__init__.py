@@ -85,6 +85,7 @@ _SIGS = {
     "act_ffn_masked": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "act_ffn_masked_compact": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "act_gather_rows": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp]),
+    "act_ffn_joint": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cgs_ref_rebuild_dense_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "ref_rebuild_dense": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
     "cgs_residual_rmsnorm": (_i, [_vp, _vp, _vp, _i, _vp, _i, _i, _vp, _i, _vp]),
@@ -406,6 +407,24 @@ class Window:
                "cgs_window_advance")
         entered = [(e_ep[i], e_pos[i], e_slot[i]) for i in range(ne.value)]
         return entered, [l_slot[i] for i in range(nl.value)], nc.value
+
+
+def act_ffn_joint(wc: FFN, x, tok, idx, y_anchor, h_anchor=None, y_out=None, y_f32_out=None, glue=None,
+                  ws=None, stream=None):
+    """Token + neuron sparsity: Eq. 4 on the rows tok (ascending) of x with the
+    compact weights of the mask idx; every other row keeps y_anchor."""
+    S, d = x.shape
+    k = 0 if tok is None else int(tok.numel())
+    K = wc.ff
+    if y_out is None:
+        y_out = torch.empty_like(x)
+    c = wc.cstruct()
+    nbytes = lib().cgs_act_ffn_masked_workspace(max(k, 1), K, d, max(K, 1))
+    ws = workspace(nbytes, x.device, "act") if ws is None else ws
+    _check(lib().act_ffn_joint(ctypes.byref(c), _ptr(x), S, _ptr(tok), k, _ptr(idx), K, _ptr(y_anchor),
+                               _ptr(h_anchor), _ptr(y_out), _ptr(y_f32_out), _glue(glue), _ptr(ws), ws.numel(),
+                               _stream(stream)), "act_ffn_joint")
+    return y_out
 
 
 def ref_rebuild_dense(layers, r0, x_ref_out=None, y_ref_out=None, ws=None, stream=None):

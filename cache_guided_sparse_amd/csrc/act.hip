@@ -41,11 +41,13 @@ constexpr int kMaxSteps = 8;   // K steps per down workgroup (LDS: 8 x 32 rows)
 
 // COMPACT: the weights hold the mask's rows only (row i is mask position i);
 // idx then only addresses h_anchor / h_out rows and may be NULL without them.
+// tok (NULL = identity): the S computed rows are rows tok[0..S) of x, of
+// S_all rows in all (the row index of h_anchor / h_out columns).
 template <typename T, int MTW, bool COMPACT>
 __global__ __launch_bounds__(kThreads) void act_glu_kernel(
     const T* __restrict__ x, int S, int d, const int32_t* __restrict__ idx, int K, int K_pad,
     const T* __restrict__ wg, const T* __restrict__ wu, const float* __restrict__ h_anchor,
-    float* __restrict__ h_out, T* __restrict__ D) {
+    float* __restrict__ h_out, T* __restrict__ D, const int32_t* __restrict__ tok, int S_all) {
   constexpr int TT = 16 * MTW;  // tokens per workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i0 = blockIdx.x * kNB;
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void act_glu_kernel(
     const int e = tid + kThreads * j;
     const int i = i0 + e % kNB, sg = s0 + e / kNB;
     ev[j] = i < K && sg < S;
-    hn[j] = (ev[j] && idx) ? static_cast<size_t>(idx[i]) * S + sg : 0;
+    hn[j] = (ev[j] && idx) ? static_cast<size_t>(idx[i]) * S_all + (tok ? tok[sg] : sg) : 0;
     ha[j] = (ev[j] && h_anchor) ? h_anchor[hn[j]] : 0.f;
   }
   const T* xrow[MTW];
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void act_glu_kernel(
   for (int mt = 0; mt < MTW; ++mt) {
     const int s = s0 + mt * 16 + r;
     tvalid[mt] = s < S;
-    xrow[mt] = x + static_cast<size_t>(tvalid[mt] ? s : 0) * d;
+    xrow[mt] = x + static_cast<size_t>(tvalid[mt] ? (tok ? tok[s] : s) : 0) * d;
   }
 
   f32x4_t ag[MTW], au[MTW];
@@ -238,14 +240,27 @@ __global__ __launch_bounds__(kThreads) void act_down_kernel(
 
 // One workgroup per token row: y = y_a + sum over splits (split order), then
 // the optional residual/RMSNorm glue on the rounded y.
+// Output row s = blockIdx.x of S_all.  With tok (ascending, S entries), the
+// partials hold only the rows tok[i]: row s takes partial row i if tok[i] = s
+// and none otherwise (y = y_a).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void act_finish_kernel(
     const float* __restrict__ part, int splits, int S, int d, const float* __restrict__ y_anchor,
-    T* __restrict__ y_out, float* __restrict__ y_f32, GlueArgs<T> glue) {
+    T* __restrict__ y_out, float* __restrict__ y_f32, GlueArgs<T> glue, const int32_t* __restrict__ tok) {
   __shared__ float red[kThreads / 64];
   const int s = blockIdx.x;
   const size_t ro = static_cast<size_t>(s) * d;
   const size_t n = static_cast<size_t>(S) * d;
+  size_t po = ro;  // this row's partials
+  if (tok) {
+    int lo = 0, hi = S;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(tok[mid]) < s) lo = mid + 1; else hi = mid;
+    }
+    if (lo < S && tok[lo] == s) po = static_cast<size_t>(lo) * d;
+    else splits = 0;
+  }
   float ss = 0.f;
   float keep[kGlueKeep][8];
   int j = 0;
@@ -257,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void act_finish_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = 0.f;
     }
-    add_splits(part + ro + c, n, splits, v);
+    add_splits(part + po + c, n, splits, v);
     if (y_f32) Row8<float>::store(y_f32 + ro + c, v);
     Row8<T>::store(y_out + ro + c, v);
     if (glue.r) {
@@ -312,26 +327,28 @@ ActPlan plan_act(int S, int K, int d) {
 
 bool act_shape_ok(int d, int ff) { return d > 0 && ff > 0 && d % 128 == 0; }
 
+// S rows computed (rows tok[0..S) of S_all when tok is given, else all).
 template <typename T, bool COMPACT>
 int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const float* ya,
           const float* ha, T* y_out, float* y_f32, float* h_out, const cgs_glue* gl, void* ws,
-          hipStream_t s) {
+          hipStream_t s, const int32_t* tok = nullptr, int S_all = -1) {
+  if (S_all < 0) S_all = S;
   const ActPlan p = plan_act(S, K, w.d);
   Carve cv(ws);
   T* D = cv.take<T>(p.d_elems);
   float* part = cv.take<float>(std::max<size_t>(p.part_elems, 1));
-  if (K > 0) {
+  if (K > 0 && S > 0) {
     {
       ProfScope ps(K == w.ff && !COMPACT ? "act.glu.dense" : "act.glu.masked", s);
       const dim3 grid((p.K_pad + kNB - 1) / kNB, (p.S_pad + p.tt - 1) / p.tt);
       if (p.tt == 16)
         hipLaunchKernelGGL((act_glu_kernel<T, 1, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
                            p.K_pad, static_cast<const T*>(w.w_gate), static_cast<const T*>(w.w_up), ha,
-                           h_out, D);
+                           h_out, D, tok, S_all);
       else
         hipLaunchKernelGGL((act_glu_kernel<T, 2, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
                            p.K_pad, static_cast<const T*>(w.w_gate), static_cast<const T*>(w.w_up), ha,
-                           h_out, D);
+                           h_out, D, tok, S_all);
     }
     if (!launch_ok()) return CGS_ERR_LAUNCH;
     ProfScope ps(K == w.ff && !COMPACT ? "act.down.dense" : "act.down.masked", s);
@@ -341,8 +358,8 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
     if (!launch_ok()) return CGS_ERR_LAUNCH;
   }
   ProfScope ps("act.finish", s);
-  hipLaunchKernelGGL((act_finish_kernel<T>), dim3(S), dim3(kThreads), 0, s, part, K > 0 ? p.splits : 0,
-                     S, w.d, ya, y_out, y_f32, make_glue<T>(gl, w.d));
+  hipLaunchKernelGGL((act_finish_kernel<T>), dim3(S_all), dim3(kThreads), 0, s, part,
+                     (K > 0 && S > 0) ? p.splits : 0, S, w.d, ya, y_out, y_f32, make_glue<T>(gl, w.d), tok);
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
 }
 
@@ -397,6 +414,28 @@ extern "C" int act_ffn_masked_compact(const cgs_ffn* wc, const void* x, int S, c
                                  static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s);
   return act_t<float, true>(*wc, static_cast<const float*>(x), S, idx, K, y_anchor, h_anchor,
                             static_cast<float*>(y_out), y_f32_out, h_out, glue, ws, s);
+}
+
+extern "C" int act_ffn_joint(const cgs_ffn* wc, const void* x, int S, const int32_t* tok, int k,
+                             const int32_t* idx, int K, const float* y_anchor, const float* h_anchor,
+                             void* y_out, float* y_f32_out, const cgs_glue* glue, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!wc || (K > 0 && (!wc->w_gate || !wc->w_up || !wc->w_down)) || !valid_dtype(wc->dtype) ||
+      wc->down_layout != CGS_DOWN_FD || !x || !y_out || !y_anchor || !glue_ok(glue) ||
+      (k > 0 && !tok) || (K > 0 && k > 0 && (!idx || !h_anchor)))
+    return CGS_ERR_ARG;
+  if (!act_shape_ok(wc->d, std::max(wc->ff, 1))) return CGS_ERR_UNSUPPORTED;
+  if (S < 0 || k < 0 || k > S || K < 0 || K != wc->ff) return CGS_ERR_SHAPE;
+  if (S == 0) return CGS_OK;
+  if (!ws || ws_bytes < cgs_act_ffn_masked_workspace(std::max(k, 1), K, wc->d, std::max(K, 1)))
+    return CGS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // with k = 0 every row is unselected: no partials (tok is not read)
+  if (wc->dtype == CGS_BF16)
+    return act_t<uint16_t, true>(*wc, static_cast<const uint16_t*>(x), k, idx, K, y_anchor, h_anchor,
+                                 static_cast<uint16_t*>(y_out), y_f32_out, nullptr, glue, ws, s, tok, S);
+  return act_t<float, true>(*wc, static_cast<const float*>(x), k, idx, K, y_anchor, h_anchor,
+                            static_cast<float*>(y_out), y_f32_out, nullptr, glue, ws, s, tok, S);
 }
 
 extern "C" int act_gather_rows(const cgs_ffn* w, const int32_t* idx, int K, void* wg_out, void* wu_out,

@@ -293,6 +293,25 @@ int cgs_profile_stop(void);
  * cover the kept ones). */
 int cgs_profile_result(const char* site, double* total_ms, int* launches);
 
+/* Joint token and neuron sparsity inside the denoising loop (§6.1: for a
+ * model whose visual features are concatenated with the denoising actions,
+ * visual-token sparsity and neuron sparsity apply together).  Rows tok[0..k)
+ * (ascending, unique, in [0, S); the caller's selection, e.g. ctx_select of
+ * x against the anchor step's input) get Eq. 4 with the mask:
+ *   y[p] = y_anchor[p] + (h^M(x[p]) - h_anchor^M[:, p]) W_down[M];
+ * every other row keeps the anchor output, y[p] = y_anchor[p] (rounded to
+ * dtype).  Weights are compact (wc->ff == K, row i is neuron idx[i]; see
+ * act_gather_rows); idx [K] addresses the rows of h_anchor [ff][S].
+ *   x: [S][d]; y_anchor: [S][d] float (required); h_anchor: [ff][S] float
+ *   (required when k > 0 and K > 0); y_out: [S][d] dtype; y_f32_out: [S][d]
+ *   float or NULL; glue: NULL or the residual/RMSNorm glue on all S rows.
+ * k = S with tok = 0..S-1 equals act_ffn_masked_compact; k = 0 gives the
+ * anchor output on every row.  Workspace: cgs_act_ffn_masked_workspace(max(k,
+ * 1), K, d, max(K, 1)). */
+int act_ffn_joint(const cgs_ffn* wc, const void* x, int S, const int32_t* tok, int k, const int32_t* idx,
+                  int K, const float* y_anchor, const float* h_anchor, void* y_out, float* y_f32_out,
+                  const cgs_glue* glue, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Reference retrieval over the prepared entries (§4.2 "Retrieving a Relevant
  * Reference"; §5 "Joint-History Retrieval" and "Fallback policy").

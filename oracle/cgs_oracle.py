@@ -43,7 +43,7 @@ __all__ = [
     "score_floor", "ctx_score_keys", "topk_ascending", "ctx_select",
     "gelu_tanh", "ffn_geglu", "ctx_ffn_recompute", "contribution_scores",
     "mask_topk", "coverage_exponent_bits", "mask_coverage", "act_build_mask", "mask_bits",
-    "act_ffn_masked", "rms_norm", "rebuild_dense", "entry_bytes",
+    "act_ffn_masked", "act_ffn_joint", "rms_norm", "rebuild_dense", "entry_bytes",
 ]
 
 
@@ -341,6 +341,21 @@ def act_ffn_masked(w: dict, x, idx, y_anchor=None, h_anchor=None):
         y = np.zeros((S, wd.shape[1])) if y_anchor is None else \
             np.asarray(y_anchor, dtype=np.float32).astype(np.float64).copy()
     return y, h.T.copy()
+
+
+def act_ffn_joint(w: dict, x, tok, idx, y_anchor, h_anchor):
+    """Paper §6.1 (visual-token and neuron sparsity together inside the
+    denoising loop): Eq. 4 on the rows tok of x with the mask idx and the
+    anchor state of those rows; every other row keeps the anchor output.
+    Returns y float64 [S][d]."""
+    tok = np.asarray(tok, dtype=np.int64)
+    ya = np.asarray(y_anchor, dtype=np.float32).astype(np.float64)
+    y = ya.copy()
+    if len(tok):
+        xs = np.asarray(x)[tok]
+        ha = np.asarray(h_anchor, dtype=np.float32)[:, tok]
+        y[tok], _ = act_ffn_masked(w, xs, idx, np.asarray(y_anchor, dtype=np.float32)[tok], ha)
+    return y
 
 
 # --------------------------------------------------------------------------

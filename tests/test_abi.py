@@ -110,6 +110,12 @@ def test_host_validation_without_launch():
     assert L.act_gather_rows(ctypes.byref(wf), buf, 2000, buf, buf, buf, None) == 2
     assert L.act_gather_rows(ctypes.byref(wf), None, 4, buf, buf, buf, None) == 1
     assert L.act_gather_rows(ctypes.byref(wf), None, 0, None, None, None, None) == 0
+    # act_ffn_joint: y_anchor required, k > S, K != compact rows, selected rows need h_anchor
+    wc64 = _ffn(layout=1, ff=64)
+    assert L.act_ffn_joint(ctypes.byref(wc64), buf, 8, buf, 2, buf, 64, None, buf, buf, None, None, buf, 1 << 30, None) == 1
+    assert L.act_ffn_joint(ctypes.byref(wc64), buf, 8, buf, 9, buf, 64, buf, buf, buf, None, None, buf, 1 << 30, None) == 2
+    assert L.act_ffn_joint(ctypes.byref(wc64), buf, 8, buf, 2, buf, 63, buf, buf, buf, None, None, buf, 1 << 30, None) == 2
+    assert L.act_ffn_joint(ctypes.byref(wc64), buf, 8, buf, 2, buf, 64, buf, None, buf, None, None, buf, 1 << 30, None) == 1
     # act_build_masks: layer count, mismatched layers
     arr2 = (cgs._Ffn * 2)(_ffn(layout=1), _ffn(layout=1, ff=2048))
     assert L.act_build_masks(buf, 0, 2, 8, ctypes.byref(wf), 0, 4, 0.0, buf, buf, buf, buf, 1 << 30, None) == 2

@@ -95,3 +95,60 @@ def test_compact_empty_mask():
     y = cgs.act_ffn_masked_compact(wc, x, None, y_anchor=to_dev(ya, "f32"))
     torch.cuda.synchronize()
     assert np.array_equal(bits(y), O.round_to_bf16_bits(ya.astype(np.float64)))
+
+
+def _joint_case(seed, S, d, ff, k, K):
+    w = ffn_weights(seed, 0, d, ff, down_layout="fd", down_lognormal_sigma=1.5)
+    t = act_tokens(seed, 0, S, d, noise_sigma=0.33)
+    ya, ha = O.act_ffn_masked(w, t["x_pert"], np.arange(ff))
+    tok = np.sort(rng(seed, 1, "perm").permutation(S)[:k]).astype(np.int32)
+    idx = _idx(ff, K, seed)
+    return w, t["x"], ya.astype(np.float32), ha.astype(np.float32), tok, idx
+
+
+@pytest.mark.parametrize("S,d,ff,k,K", [(306, 1024, 4096, 127, 1229), (50, 1024, 4096, 50, 1229),
+                                        (70, 128, 200, 33, 80), (40, 256, 1024, 1, 1024)])
+def test_joint_token_and_neuron_sparsity(S, d, ff, k, K):
+    """Eq. 4 on the selected rows, the anchor output elsewhere (oracle parity);
+    all rows selected = act_ffn_masked_compact bit for bit."""
+    say("joint", S, d, ff, k, K)
+    w, x, ya, ha, tok, idx = _joint_case(44, S, d, ff, k, K)
+    W = ffn_dev(w)
+    idx_d = torch.from_numpy(idx).to(dev())
+    wc = cgs.act_gather_rows(W, idx_d)
+    yf = torch.empty(S, d, dtype=torch.float32, device=dev())
+    y = cgs.act_ffn_joint(wc, to_dev(x), torch.from_numpy(tok).to(dev()), idx_d, to_dev(ya, "f32"),
+                          to_dev(ha, "f32"), y_f32_out=yf)
+    torch.cuda.synchronize()
+    y_o = O.act_ffn_joint(w, x, tok, idx, ya, ha)
+    assert_close(values(yf), y_o, "y_f32")
+    assert_close(values(y), y_o, "y", out="bf16")
+    rest = np.setdiff1d(np.arange(S), tok)
+    assert np.array_equal(values(yf)[rest], ya[rest]), "unselected rows must keep the anchor output"
+    if k == S:
+        y2 = cgs.act_ffn_masked_compact(wc, to_dev(x), idx_d, y_anchor=to_dev(ya, "f32"), h_anchor=to_dev(ha, "f32"))
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2)
+
+
+def test_joint_no_rows_and_glue():
+    say("joint empty + glue")
+    S, d, ff = 60, 1024, 4096
+    w, x, ya, ha, _, idx = _joint_case(45, S, d, ff, 0, 1000)
+    W = ffn_dev(w)
+    idx_d = torch.from_numpy(idx).to(dev())
+    wc = cgs.act_gather_rows(W, idx_d)
+    y = cgs.act_ffn_joint(wc, to_dev(x), None, idx_d, to_dev(ya, "f32"), to_dev(ha, "f32"))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(y), O.round_to_bf16_bits(ya.astype(np.float64)))
+    # glue over every row, selected or not
+    tok = np.arange(0, S, 4, dtype=np.int32)
+    r0 = rng(45, 2, "misc").standard_normal((S, d)).astype(np.float32)
+    r = to_dev(r0, "f32")
+    xn = torch.empty(S, d, dtype=torch.bfloat16, device=dev())
+    y = cgs.act_ffn_joint(wc, to_dev(x), torch.from_numpy(tok).to(dev()), idx_d, to_dev(ya, "f32"),
+                          to_dev(ha, "f32"), glue=(r, None, xn))
+    torch.cuda.synchronize()
+    r_exp = r0.astype(np.float64) + values(y)
+    assert_close(values(r), r_exp, "residual")
+    assert_close(values(xn), O.rms_norm(r_exp), "x_next", out="bf16")
