@@ -375,6 +375,69 @@ class World:
         torch.cuda.synchronize()
 
 
+def joint_denoise(w, reps: int = 10) -> dict:
+    """Visual-token and neuron sparsity together inside the denoising loop
+    (§6.1): 256 visual rows + 50 action rows through the 18 expert layers;
+    the anchor step runs dense and keeps every layer's input, output and
+    activations; each masked step selects, per layer, the 30% of visual rows
+    whose input drifted most from the anchor step's (Eq. 2) and runs Eq. 4 on
+    them and on every action row with the group mask (compact weights); the
+    other visual rows keep the anchor output.  Timed with HIP graphs against
+    the same masked steps on all 306 rows."""
+    import torch
+    cgs = w.cgs
+    dev = w.dev
+    V, A = 256, S
+    R = V + A
+    kv = cgs.ratio_to_count(RHO_P, V)
+    g = torch.Generator(device=dev)
+    g.manual_seed(99)
+    bf = torch.bfloat16
+    a0 = torch.randn(R, DE, device=dev, generator=g)
+    xs = torch.empty(L_EXP + 1, R, DE, dtype=bf, device=dev)    # anchor-step layer inputs
+    ya = torch.empty(L_EXP, R, DE, dtype=torch.float32, device=dev)
+    ha = torch.empty(L_EXP, FFE, R, dtype=torch.float32, device=dev)
+    r = torch.empty(R, DE, dtype=torch.float32, device=dev)
+    x = torch.empty(R, DE, dtype=bf, device=dev)
+    y = torch.empty(R, DE, dtype=bf, device=dev)
+    cgs.residual_rmsnorm(r, r_in=a0, x_out=xs[0])
+    for l in range(L_EXP):
+        cgs.act_ffn_masked(w.exp[l], xs[l], w.full, y_out=y, y_f32_out=ya[l], h_out=ha[l],
+                           glue=(r, None, xs[l + 1]))
+    a1 = (a0 + 0.05 * torch.randn(R, DE, device=dev, generator=g)).contiguous()
+    tok = torch.cat([torch.zeros(kv, dtype=torch.int32, device=dev),
+                     torch.arange(V, R, dtype=torch.int32, device=dev)])
+    full_rows = torch.arange(R, dtype=torch.int32, device=dev)
+
+    def masked_step(joint):
+        cgs.residual_rmsnorm(r, r_in=a1, x_out=x)
+        for l in range(L_EXP):
+            if joint:
+                cgs.ctx_select(x[:V], xs[l][:V], kv, idx_out=tok[:kv])
+                cgs.act_ffn_joint(w.cexp[l], x, tok, w.masks[l], ya[l], ha[l], y_out=y, glue=(r, None, x))
+            else:
+                cgs.act_ffn_joint(w.cexp[l], x, full_rows, w.masks[l], ya[l], ha[l], y_out=y, glue=(r, None, x))
+
+    out = {"rows": R, "visual_rows": V, "action_rows": A, "visual_selected": kv}
+    for name, joint in (("joint_ms", True), ("all_rows_ms", False)):
+        masked_step(joint)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            masked_step(joint)
+        gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / reps, 4)
+    out["note"] = "one masked denoise step of 18 layers; joint includes the per-layer token selection"
+    return out
+
+
 def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
     """The oracle, timed on the host cores over a bounded sample of the step:
     one context layer (select + recompute of 231 rows), one dense anchor
@@ -674,6 +737,7 @@ def main():
         "serial_reference": serial,
         "kernel_sites": sites,
     }
+    out["joint_denoise"] = joint_denoise(w)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(int(round(sum(Km) / len(Km))))
