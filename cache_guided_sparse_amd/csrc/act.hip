@@ -38,6 +38,7 @@ constexpr int kStep = 32;      // mask positions per down K step
 constexpr int kCols = 64;      // output columns per down workgroup
 constexpr int kTokDown = 64;   // tokens per down workgroup (4 waves x 16)
 constexpr int kMaxSteps = 8;   // K steps per down workgroup (LDS: 8 x 32 rows)
+constexpr int kDownSplits = 8; // preferred K splits of the down projection
 
 // COMPACT: the weights hold the mask's rows only (row i is mask position i);
 // idx then only addresses h_anchor / h_out rows and may be NULL without them.
@@ -315,8 +316,10 @@ ActPlan plan_act(int S, int K, int d) {
   p.tt = S <= 16 ? 16 : 32;  // tokens per GLU workgroup
   p.S_pad = (S + kTokDown - 1) / kTokDown * kTokDown;
   const int steps = p.K_pad / kStep;
-  const int base = (d / kCols) * (p.S_pad / kTokDown);
-  int splits = std::max(1, std::min(std::max(steps, 1), (256 + base - 1) / std::max(base, 1)));
+  // up to kDownSplits K splits (fewer partials for the finish kernel; measured
+  // best for the 18-layer expert's ~1250-row masks), more only when a split
+  // would exceed the kMaxSteps rows of W_down that fit in LDS
+  int splits = std::max(1, std::min(std::max(steps, 1), kDownSplits));
   splits = std::max(splits, (steps + kMaxSteps - 1) / kMaxSteps);
   p.steps_per_split = std::max(1, (steps + splits - 1) / splits);
   p.splits = steps > 0 ? (steps + p.steps_per_split - 1) / p.steps_per_split : 0;
