@@ -7,7 +7,7 @@
 // 18-layer expert moves ~7.5 MB), so every kernel puts all of its weight
 // loads in flight before it computes:
 //
-//   act_glu_kernel    a workgroup owns 16 mask positions and TT tokens; its
+//   act_glu_kernel    a workgroup owns 16 (32 for large masks) mask positions and TT tokens; its
 //       four waves split d into quarters.  Each wave issues all of its
 //       gathered gate/up fragments and its x fragments of a chunk at once,
 //       then runs the MFMAs; the quarters are summed in LDS in a fixed order.
@@ -32,45 +32,52 @@ namespace cgs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kNB = 16;        // mask positions per GLU workgroup
 constexpr int kChunk = 8;      // 32-wide K steps per load batch of a GLU wave
 constexpr int kStep = 32;      // mask positions per down K step
 constexpr int kCols = 64;      // output columns per down workgroup
 constexpr int kTokDown = 64;   // tokens per down workgroup (4 waves x 16)
 constexpr int kMaxSteps = 8;   // K steps per down workgroup (LDS: 8 x 32 rows)
 constexpr int kDownSplits = 8; // preferred K splits of the down projection
+constexpr int kWideGluK = 2048;  // masks of at least this many positions use 32-position GLU workgroups
 
 // COMPACT: the weights hold the mask's rows only (row i is mask position i);
 // idx then only addresses h_anchor / h_out rows and may be NULL without them.
 // tok (NULL = identity): the S computed rows are rows tok[0..S) of x, of
 // S_all rows in all (the row index of h_anchor / h_out columns).
-template <typename T, int MTW, bool COMPACT>
+// NTW: 16-wide tiles of mask positions per workgroup (NB = 16 NTW positions).
+template <typename T, int MTW, int NTW, bool COMPACT>
 __global__ __launch_bounds__(kThreads) void act_glu_kernel(
     const T* __restrict__ x, int S, int d, const int32_t* __restrict__ idx, int K, int K_pad,
     const T* __restrict__ wg, const T* __restrict__ wu, const float* __restrict__ h_anchor,
     float* __restrict__ h_out, T* __restrict__ D, const int32_t* __restrict__ tok, int S_all) {
   constexpr int TT = 16 * MTW;  // tokens per workgroup
+  constexpr int NB = 16 * NTW;  // mask positions per workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i0 = blockIdx.x * kNB;
+  const int i0 = blockIdx.x * NB;
   const int s0 = blockIdx.y * TT;
   const int r = lane & 15, grp = lane >> 4;
   const int dq = d / 4;
 
-  const int i_lane = i0 + r;
-  const bool nvalid = i_lane < K;
-  const size_t wrow = nvalid ? static_cast<size_t>(COMPACT ? i_lane : idx[i_lane]) * d : 0;
+  bool nvalid[NTW];
+  size_t wrow[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int i_lane = i0 + nt * 16 + r;
+    nvalid[nt] = i_lane < K;
+    wrow[nt] = nvalid[nt] ? static_cast<size_t>(COMPACT ? i_lane : idx[i_lane]) * d : 0;
+  }
 
-  // Epilogue elements of this thread: e = tid + 256 j -> (token e / 16, mask
-  // position e % 16).  Their neuron rows and anchor activations are fetched
+  // Epilogue elements of this thread: e = tid + 256 j -> (token e / NB, mask
+  // position e % NB).  Their neuron rows and anchor activations are fetched
   // now, so that the wait for them overlaps the weight loads below.
-  constexpr int EPT = TT * kNB / kThreads;
+  constexpr int EPT = TT * NB / kThreads;
   size_t hn[EPT];
   bool ev[EPT];
   float ha[EPT];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int e = tid + kThreads * j;
-    const int i = i0 + e % kNB, sg = s0 + e / kNB;
+    const int i = i0 + e % NB, sg = s0 + e / NB;
     ev[j] = i < K && sg < S;
     hn[j] = (ev[j] && idx) ? static_cast<size_t>(idx[i]) * S_all + (tok ? tok[sg] : sg) : 0;
     ha[j] = (ev[j] && h_anchor) ? h_anchor[hn[j]] : 0.f;
@@ -84,45 +91,55 @@ __global__ __launch_bounds__(kThreads) void act_glu_kernel(
     xrow[mt] = x + static_cast<size_t>(tvalid[mt] ? (tok ? tok[s] : s) : 0) * d;
   }
 
-  f32x4_t ag[MTW], au[MTW];
+  f32x4_t ag[MTW][NTW], au[MTW][NTW];
 #pragma unroll
-  for (int mt = 0; mt < MTW; ++mt) ag[mt] = au[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) ag[mt][nt] = au[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  constexpr int CH = kChunk / NTW;  // 32-wide K steps per load batch (same registers in flight)
   const int kb = wave * dq, ke = kb + dq;
-  for (int k0 = kb; k0 < ke; k0 += kChunk * 32) {
-    Frag<T> bg[kChunk], bu[kChunk], a[kChunk][MTW];
+  for (int k0 = kb; k0 < ke; k0 += CH * 32) {
+    Frag<T> bg[CH][NTW], bu[CH][NTW], a[CH][MTW];
 #pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
+    for (int c = 0; c < CH; ++c) {
       const int kk = k0 + c * 32 + grp * 8;
       const bool kv = k0 + c * 32 < ke;
-      if (nvalid && kv) { bg[c].load(wg + wrow + kk); bu[c].load(wu + wrow + kk); }
-      else { bg[c].zero(); bu[c].zero(); }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        if (nvalid[nt] && kv) { bg[c][nt].load(wg + wrow[nt] + kk); bu[c][nt].load(wu + wrow[nt] + kk); }
+        else { bg[c][nt].zero(); bu[c][nt].zero(); }
+      }
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt) {
         if (tvalid[mt] && kv) a[c][mt].load(xrow[mt] + kk); else a[c][mt].zero();
       }
     }
 #pragma unroll
-    for (int c = 0; c < kChunk; ++c)
+    for (int c = 0; c < CH; ++c)
 #pragma unroll
-      for (int mt = 0; mt < MTW; ++mt) {
-        ag[mt] = mma(a[c][mt], bg[c], ag[mt]);
-        au[mt] = mma(a[c][mt], bu[c], au[mt]);
-      }
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          ag[mt][nt] = mma(a[c][mt], bg[c][nt], ag[mt][nt]);
+          au[mt][nt] = mma(a[c][mt], bu[c][nt], au[mt][nt]);
+        }
   }
-  // Lane holds rows (tokens) mt*16 + 4*grp + v of column (mask position) r.
-  __shared__ float part[4][2][TT][kNB];
+  // Lane holds rows (tokens) mt*16 + 4*grp + v of column (mask position) nt*16 + r.
+  __shared__ float part[4][2][TT][NB];
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      part[wave][0][mt * 16 + 4 * grp + v][r] = ag[mt][v];
-      part[wave][1][mt * 16 + 4 * grp + v][r] = au[mt][v];
-    }
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        part[wave][0][mt * 16 + 4 * grp + v][nt * 16 + r] = ag[mt][nt][v];
+        part[wave][1][mt * 16 + 4 * grp + v][nt * 16 + r] = au[mt][nt][v];
+      }
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const int e = tid + kThreads * j;
-    const int s = e / kNB, c = e % kNB;
+    const int s = e / NB, c = e % NB;
     const float gsum = part[0][0][s][c] + part[1][0][s][c] + part[2][0][s][c] + part[3][0][s][c];
     const float usum = part[0][1][s][c] + part[1][1][s][c] + part[2][1][s][c] + part[3][1][s][c];
     const int i = i0 + c, sg = s0 + s;
@@ -343,15 +360,24 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
   if (K > 0 && S > 0) {
     {
       ProfScope ps(K == w.ff && !COMPACT ? "act.glu.dense" : "act.glu.masked", s);
-      const dim3 grid((p.K_pad + kNB - 1) / kNB, (p.S_pad + p.tt - 1) / p.tt);
-      if (p.tt == 16)
-        hipLaunchKernelGGL((act_glu_kernel<T, 1, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
-                           p.K_pad, static_cast<const T*>(w.w_gate), static_cast<const T*>(w.w_up), ha,
-                           h_out, D, tok, S_all);
+      const T* wgp = static_cast<const T*>(w.w_gate);
+      const T* wup = static_cast<const T*>(w.w_up);
+      // two 16-wide position tiles per workgroup for large masks (x is then
+      // read once per 32 positions), one otherwise (more workgroups)
+      const int ntw = K >= kWideGluK ? 2 : 1;
+      const dim3 grid((p.K_pad + 16 * ntw - 1) / (16 * ntw), (p.S_pad + p.tt - 1) / p.tt);
+      if (p.tt == 16 && ntw == 1)
+        hipLaunchKernelGGL((act_glu_kernel<T, 1, 1, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
+                           p.K_pad, wgp, wup, ha, h_out, D, tok, S_all);
+      else if (p.tt == 16)
+        hipLaunchKernelGGL((act_glu_kernel<T, 1, 2, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
+                           p.K_pad, wgp, wup, ha, h_out, D, tok, S_all);
+      else if (ntw == 1)
+        hipLaunchKernelGGL((act_glu_kernel<T, 2, 1, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
+                           p.K_pad, wgp, wup, ha, h_out, D, tok, S_all);
       else
-        hipLaunchKernelGGL((act_glu_kernel<T, 2, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
-                           p.K_pad, static_cast<const T*>(w.w_gate), static_cast<const T*>(w.w_up), ha,
-                           h_out, D, tok, S_all);
+        hipLaunchKernelGGL((act_glu_kernel<T, 2, 2, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
+                           p.K_pad, wgp, wup, ha, h_out, D, tok, S_all);
     }
     if (!launch_ok()) return CGS_ERR_LAUNCH;
     ProfScope ps(K == w.ff && !COMPACT ? "act.down.dense" : "act.down.masked", s);
