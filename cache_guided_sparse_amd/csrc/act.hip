@@ -39,14 +39,16 @@ constexpr int kTokDown = 64;   // tokens per down workgroup (4 waves x 16)
 constexpr int kMaxSteps = 8;   // K steps per down workgroup (LDS: 8 x 32 rows)
 constexpr int kDownSplits = 8; // preferred K splits of the down projection
 constexpr int kWideGluK = 2048;  // masks of at least this many positions use 32-position GLU workgroups
+constexpr int kGluWaves = 8;     // waves (d slices) of a gate/up workgroup when d allows (else 4)
 
 // COMPACT: the weights hold the mask's rows only (row i is mask position i);
 // idx then only addresses h_anchor / h_out rows and may be NULL without them.
 // tok (NULL = identity): the S computed rows are rows tok[0..S) of x, of
 // S_all rows in all (the row index of h_anchor / h_out columns).
 // NTW: 16-wide tiles of mask positions per workgroup (NB = 16 NTW positions).
-template <typename T, int MTW, int NTW, bool COMPACT>
-__global__ __launch_bounds__(kThreads) void act_glu_kernel(
+// NW waves split d into NW slices.
+template <typename T, int MTW, int NTW, bool COMPACT, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void act_glu_kernel(
     const T* __restrict__ x, int S, int d, const int32_t* __restrict__ idx, int K, int K_pad,
     const T* __restrict__ wg, const T* __restrict__ wu, const float* __restrict__ h_anchor,
     float* __restrict__ h_out, T* __restrict__ D, const int32_t* __restrict__ tok, int S_all) {
@@ -56,7 +58,8 @@ __global__ __launch_bounds__(kThreads) void act_glu_kernel(
   const int i0 = blockIdx.x * NB;
   const int s0 = blockIdx.y * TT;
   const int r = lane & 15, grp = lane >> 4;
-  const int dq = d / 4;
+  constexpr int NTH = 64 * NW;
+  const int dq = d / NW;
 
   bool nvalid[NTW];
   size_t wrow[NTW];
@@ -67,18 +70,19 @@ __global__ __launch_bounds__(kThreads) void act_glu_kernel(
     wrow[nt] = nvalid[nt] ? static_cast<size_t>(COMPACT ? i_lane : idx[i_lane]) * d : 0;
   }
 
-  // Epilogue elements of this thread: e = tid + 256 j -> (token e / NB, mask
+  // Epilogue elements of this thread: e = tid + NTH j -> (token e / NB, mask
   // position e % NB).  Their neuron rows and anchor activations are fetched
   // now, so that the wait for them overlaps the weight loads below.
-  constexpr int EPT = TT * NB / kThreads;
+  constexpr int NE = TT * NB;                 // epilogue elements of the workgroup
+  constexpr int EPT = (NE + NTH - 1) / NTH;
   size_t hn[EPT];
   bool ev[EPT];
   float ha[EPT];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
-    const int e = tid + kThreads * j;
+    const int e = tid + NTH * j;
     const int i = i0 + e % NB, sg = s0 + e / NB;
-    ev[j] = i < K && sg < S;
+    ev[j] = e < NE && i < K && sg < S;
     hn[j] = (ev[j] && idx) ? static_cast<size_t>(idx[i]) * S_all + (tok ? tok[sg] : sg) : 0;
     ha[j] = (ev[j] && h_anchor) ? h_anchor[hn[j]] : 0.f;
   }
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void act_glu_kernel(
         }
   }
   // Lane holds rows (tokens) mt*16 + 4*grp + v of column (mask position) nt*16 + r.
-  __shared__ float part[4][2][TT][NB];
+  __shared__ float part[NW][2][TT][NB];
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
@@ -138,10 +142,15 @@ __global__ __launch_bounds__(kThreads) void act_glu_kernel(
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
-    const int e = tid + kThreads * j;
+    const int e = tid + NTH * j;
+    if (NE % NTH != 0 && e >= NE) break;
     const int s = e / NB, c = e % NB;
-    const float gsum = part[0][0][s][c] + part[1][0][s][c] + part[2][0][s][c] + part[3][0][s][c];
-    const float usum = part[0][1][s][c] + part[1][1][s][c] + part[2][1][s][c] + part[3][1][s][c];
+    float gsum = part[0][0][s][c], usum = part[0][1][s][c];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) {
+      gsum += part[q][0][s][c];
+      usum += part[q][1][s][c];
+    }
     const int i = i0 + c, sg = s0 + s;
     float delta = 0.f;
     if (ev[j]) {
@@ -366,18 +375,23 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
       // read once per 32 positions), one otherwise (more workgroups)
       const int ntw = K >= kWideGluK ? 2 : 1;
       const dim3 grid((p.K_pad + 16 * ntw - 1) / (16 * ntw), (p.S_pad + p.tt - 1) / p.tt);
-      if (p.tt == 16 && ntw == 1)
-        hipLaunchKernelGGL((act_glu_kernel<T, 1, 1, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
-                           p.K_pad, wgp, wup, ha, h_out, D, tok, S_all);
-      else if (p.tt == 16)
-        hipLaunchKernelGGL((act_glu_kernel<T, 1, 2, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
-                           p.K_pad, wgp, wup, ha, h_out, D, tok, S_all);
-      else if (ntw == 1)
-        hipLaunchKernelGGL((act_glu_kernel<T, 2, 1, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
-                           p.K_pad, wgp, wup, ha, h_out, D, tok, S_all);
-      else
-        hipLaunchKernelGGL((act_glu_kernel<T, 2, 2, COMPACT>), grid, dim3(kThreads), 0, s, x, S, w.d, idx, K,
-                           p.K_pad, wgp, wup, ha, h_out, D, tok, S_all);
+      // NW waves split d (8 when d allows: more loads in flight per workgroup)
+      const bool w8 = w.d % (kGluWaves * 32) == 0;
+      const dim3 blk(w8 ? 64 * kGluWaves : kThreads);
+#define CGS_GLU(MTW_, NTW_)                                                                              \
+  do {                                                                                                   \
+    if (w8)                                                                                              \
+      hipLaunchKernelGGL((act_glu_kernel<T, MTW_, NTW_, COMPACT, kGluWaves>), grid, blk, 0, s, x, S, w.d, idx, K, \
+                         p.K_pad, wgp, wup, ha, h_out, D, tok, S_all);                                   \
+    else                                                                                                 \
+      hipLaunchKernelGGL((act_glu_kernel<T, MTW_, NTW_, COMPACT, 4>), grid, blk, 0, s, x, S, w.d, idx, K, \
+                         p.K_pad, wgp, wup, ha, h_out, D, tok, S_all);                                   \
+  } while (0)
+      if (p.tt == 16 && ntw == 1) CGS_GLU(1, 1);
+      else if (p.tt == 16) CGS_GLU(1, 2);
+      else if (ntw == 1) CGS_GLU(2, 1);
+      else CGS_GLU(2, 2);
+#undef CGS_GLU
     }
     if (!launch_ok()) return CGS_ERR_LAUNCH;
     ProfScope ps(K == w.ff && !COMPACT ? "act.down.dense" : "act.down.masked", s);
