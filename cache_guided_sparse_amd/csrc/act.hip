@@ -34,7 +34,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunk = 8;      // 32-wide K steps per load batch of a GLU wave
 constexpr int kStep = 32;      // mask positions per down K step
-constexpr int kCols = 64;      // output columns per down workgroup
+constexpr int kCols = 32;      // output columns per down workgroup
 constexpr int kTokDown = 64;   // tokens per down workgroup (4 waves x 16)
 constexpr int kMaxSteps = 8;   // K steps per down workgroup (LDS: 8 x 32 rows)
 constexpr int kDownSplits = 8; // preferred K splits of the down projection
@@ -195,7 +195,7 @@ template <typename T, bool COMPACT>
 __global__ __launch_bounds__(kThreads) void act_down_kernel(
     const T* __restrict__ D, int S, int K_pad, const int32_t* __restrict__ idx, int K,
     const T* __restrict__ wd, int d, int steps_per_split, float* __restrict__ part) {
-  constexpr int RB = kCols * static_cast<int>(sizeof(T));  // bytes of a row segment (128 / 256)
+  constexpr int RB = kCols * static_cast<int>(sizeof(T));  // bytes of a row segment
   constexpr int RPD = 1024 / RB;                           // rows per 1 KB DMA transfer
   constexpr int DPS = kStep / RPD;                         // transfers per K step
   __shared__ __attribute__((aligned(1024))) char tile[kMaxSteps * kStep * RB];
@@ -241,15 +241,16 @@ __global__ __launch_bounds__(kThreads) void act_down_kernel(
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-  f32x4_t acc[4];
+  constexpr int NTD = kCols / 16;  // 16-column MFMA tiles per wave
+  f32x4_t acc[NTD];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NTD; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int st = 0; st < kMaxSteps; ++st) {
     if (st >= nst) break;
     const char* tl = tile + st * kStep * RB;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < NTD; ++nt) {
       Frag<T> b;
       gather_b_frag<T>(tl, RB, nt * 16 + r, grp, b);
       acc[nt] = mma(a[st], b, acc[nt]);
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void act_down_kernel(
   }
   const size_t so = static_cast<size_t>(split) * S * d;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int nt = 0; nt < NTD; ++nt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int s = s0 + wave * 16 + 4 * grp + v;
