@@ -513,6 +513,8 @@ def main():
                     help="launch every kernel eagerly instead of replaying HIP graphs")
     ap.add_argument("--rebuild-stream", choices=("side", "main"), default="main",
                     help="run the entry rebuild on a side stream (overlapped) or in line")
+    ap.add_argument("--no-joint", action="store_true",
+                    help="skip the separate joint token + neuron sparsity measurement")
     ap.add_argument("--no-compact", action="store_true",
                     help="masked steps gather the mask's weight rows in place (no compact buffers)")
     ap.add_argument("--serial-steps", type=int, default=8,
@@ -737,7 +739,8 @@ def main():
         "serial_reference": serial,
         "kernel_sites": sites,
     }
-    out["joint_denoise"] = joint_denoise(w)
+    if not args.no_joint:
+        out["joint_denoise"] = joint_denoise(w)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(int(round(sum(Km) / len(Km))))

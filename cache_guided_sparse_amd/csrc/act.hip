@@ -40,6 +40,7 @@ constexpr int kMaxSteps = 8;   // K steps per down workgroup (LDS: 8 x 32 rows)
 constexpr int kDownSplits = 8; // preferred K splits of the down projection
 constexpr int kWideGluK = 2048;  // masks of at least this many positions use 32-position GLU workgroups
 constexpr int kGluWaves = 8;     // waves (d slices) of a gate/up workgroup when d allows (else 4)
+constexpr bool kXcdMap = true;   // XCD-aware workgroup numbering (xcd_tile)
 
 // COMPACT: the weights hold the mask's rows only (row i is mask position i);
 // idx then only addresses h_anchor / h_out rows and may be NULL without them.
@@ -47,6 +48,18 @@ constexpr int kGluWaves = 8;     // waves (d slices) of a gate/up workgroup when
 // S_all rows in all (the row index of h_anchor / h_out columns).
 // NTW: 16-wide tiles of mask positions per workgroup (NB = 16 NTW positions).
 // NW waves split d into NW slices.
+// Workgroups are dealt round-robin over the 8 XCDs.  With kXcdMap, the
+// linear workgroup id is renumbered so that each XCD runs a contiguous range
+// of logical (x fastest) tiles: tiles that share operand rows then share that
+// XCD's L2.  Returns the logical (x, y) of this workgroup.
+// lx: the logical x extent (lx * ly = gridDim.x * gridDim.y).
+__device__ __forceinline__ int2 xcd_tile(int lx) {
+  const int b = blockIdx.x + gridDim.x * blockIdx.y;
+  const int n = gridDim.x * gridDim.y;
+  const int l = (kXcdMap && n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b;
+  return make_int2(l % lx, l / lx);
+}
+
 template <typename T, int MTW, int NTW, bool COMPACT, int NW = 4>
 __global__ __launch_bounds__(64 * NW) void act_glu_kernel(
     const T* __restrict__ x, int S, int d, const int32_t* __restrict__ idx, int K, int K_pad,
@@ -55,8 +68,11 @@ __global__ __launch_bounds__(64 * NW) void act_glu_kernel(
   constexpr int TT = 16 * MTW;  // tokens per workgroup
   constexpr int NB = 16 * NTW;  // mask positions per workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i0 = blockIdx.x * NB;
-  const int s0 = blockIdx.y * TT;
+  // logical tile: token block fastest, so both token blocks of a neuron
+  // block (the same weight rows) run on one XCD
+  const int2 tl = xcd_tile(gridDim.y);
+  const int i0 = tl.y * NB;
+  const int s0 = tl.x * TT;
   const int r = lane & 15, grp = lane >> 4;
   constexpr int NTH = 64 * NW;
   const int dq = d / NW;
@@ -202,8 +218,12 @@ __global__ __launch_bounds__(kThreads) void act_down_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, grp = lane >> 4;
-  const int j0 = blockIdx.x * kCols;
-  const int split = blockIdx.y;
+  // logical tile: column block fastest, so the column blocks of one split
+  // (the same delta rows, neighbouring 64-byte halves of W_down lines) run on
+  // one XCD
+  const int2 tl = xcd_tile(gridDim.x);
+  const int j0 = tl.x * kCols;
+  const int split = tl.y;
   const int s0 = blockIdx.z * kTokDown;
   const int st_begin = split * steps_per_split;
   const int nst = min(K_pad / kStep, st_begin + steps_per_split) - st_begin;
