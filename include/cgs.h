@@ -48,7 +48,7 @@ typedef enum {
   CGS_ERR_ARG = 1,          /* null pointer or invalid enum value */
   CGS_ERR_SHAPE = 2,        /* size or count out of range */
   CGS_ERR_WORKSPACE = 3,    /* ws too small or null while needed */
-  CGS_ERR_UNSUPPORTED = 4,  /* dtype / layout / size this build does not handle */
+  CGS_ERR_UNSUPPORTED = 4,  /* dtype / layout / size the library does not handle */
   CGS_ERR_LAUNCH = 5        /* a kernel launch failed */
 } cgs_status;
 
