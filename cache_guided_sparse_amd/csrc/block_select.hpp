@@ -245,14 +245,22 @@ __device__ __forceinline__ void chunk_load(SelChunk<R>& c, int n, KeyFn key_of) 
   for (int j = 0; j < R; ++j) c.key[j] = (j < c.cnt) ? key_of(c.lo + j) : 0ull;
 }
 
+constexpr int kResolveMax = 64;  // bucket size resolved by one wave instead of more passes
+
 struct alignas(16) SelShared2 {
   uint32_t hist[2][256];
   unsigned long long hsum[2][256];
   uint32_t scan[kSelThreads / kWave];
   uint64_t digit[2];
   long long above[2];
+  uint32_t inbin[2];   // candidates in the chosen bucket
   int need;
   long long tie_z;
+  uint32_t nres;                     // resolve list length
+  uint64_t rkey[kResolveMax];        // resolve list: keys and indices of the bucket
+  int32_t ridx[kResolveMax];
+  uint64_t rT;
+  int rneed;
 };
 
 // One radix pass over the candidates (key & pmask) == prefix: the digit at
@@ -281,6 +289,7 @@ __device__ __forceinline__ void chunk_pass(const SelChunk<R>& c, uint64_t prefix
       if (above < remaining && remaining <= above + h) {
         sm.digit[b] = static_cast<uint64_t>(4 * lane + j);
         sm.above[b] = above;
+        sm.inbin[b] = static_cast<uint32_t>(h);
       }
       above += h;
     }
@@ -328,6 +337,7 @@ __device__ int chunk_topk(const SelChunk<R>& c, int n, int k, EmitFn emit, SelSh
     return n;
   }
   for (int q = threadIdx.x; q < 256; q += blockDim.x) sm.hist[0][q] = 0;
+  if (threadIdx.x == 0) sm.nres = 0;
   __syncthreads();
   uint64_t prefix = 0, pmask = 0;
   long long remaining = k;
@@ -337,6 +347,40 @@ __device__ int chunk_topk(const SelChunk<R>& c, int n, int k, EmitFn emit, SelSh
     prefix |= sm.digit[b] << shift;
     pmask |= 0xffull << shift;
     remaining -= sm.above[b];
+    if (shift > 0 && sm.inbin[b] <= static_cast<uint32_t>(kResolveMax)) {
+      // Few candidates left in the bucket: list them, and one wave ranks them
+      // by (key desc, index asc); the rank-`remaining` one gives T, and `need`
+      // counts the chosen elements equal to T.
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        if (j < c.cnt && (c.key[j] & pmask) == prefix) {
+          const uint32_t slot = atomicAdd(&sm.nres, 1u);
+          sm.rkey[slot] = c.key[j];
+          sm.ridx[slot] = c.lo + j;
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x < kWave) {
+        const int m = static_cast<int>(sm.nres);
+        const int t = threadIdx.x;
+        if (t < m) {
+          const uint64_t kt = sm.rkey[t];
+          const int it = sm.ridx[t];
+          int rank = 0, gt = 0;
+          for (int u = 0; u < m; ++u) {
+            const uint64_t ku = sm.rkey[u];
+            rank += (ku > kt) || (ku == kt && sm.ridx[u] < it);
+            gt += ku > kt;
+          }
+          if (rank == remaining - 1) {
+            sm.rT = kt;
+            sm.rneed = static_cast<int>(remaining) - gt;
+          }
+        }
+      }
+      __syncthreads();
+      return chunk_emit(c, sm.rT, sm.rneed, emit, sm);
+    }
   }
   return chunk_emit(c, prefix, static_cast<int>(remaining), emit, sm);
 }
