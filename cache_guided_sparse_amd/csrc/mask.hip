@@ -28,20 +28,20 @@ namespace {
 constexpr double kTwo24 = 16777216.0;      // 2^24
 constexpr double kTwo40 = 1099511627776.0; // 2^40
 
-// Eight consecutive weights of a row as float64 (exact).
+// Eight consecutive weights of a row as float (exact; widened to float64 at use).
 template <typename T> struct W8;
 template <> struct W8<uint16_t> {
-  static __device__ __forceinline__ void load(const uint16_t* p, double* v) {
+  static __device__ __forceinline__ void load(const uint16_t* p, float* v) {
     const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = static_cast<double>(__uint_as_float(u[i] << 16));
-      v[2 * i + 1] = static_cast<double>(__uint_as_float(u[i] & 0xffff0000u));
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
     }
   }
 };
 template <> struct W8<float> {
-  static __device__ __forceinline__ void load(const float* p, double* v) {
+  static __device__ __forceinline__ void load(const float* p, float* v) {
     const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0], b = reinterpret_cast<const f32x4_t*>(p)[1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void contrib_kernel(const float* __restrict__ 
   long long b = 0;
   if (vec) {
     for (int j0 = lane * 8; j0 < d; j0 += 4 * kWave * 8) {
-      double w[4][8];
+      float w[4][8];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (j0 + q * kWave * 8 < d) W8<T>::load(wr + j0 + q * kWave * 8, w[q]);
@@ -91,7 +91,10 @@ __global__ __launch_bounds__(256) void contrib_kernel(const float* __restrict__ 
       for (int q = 0; q < 4; ++q) {
         if (j0 + q * kWave * 8 >= d) continue;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) b += static_cast<long long>(rint((w[q][i] * w[q][i]) * kTwo40));
+        for (int i = 0; i < 8; ++i) {
+          const double wv = static_cast<double>(w[q][i]);
+          b += static_cast<long long>(rint((wv * wv) * kTwo40));
+        }
       }
     }
   } else {
