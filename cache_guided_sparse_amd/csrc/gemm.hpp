@@ -241,27 +241,47 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> g) {
     wait_for(0, min(SA - 2, nk - 1), min(SB - 2, nk - 1));
     if (S_own - 1 < nk) issue(S_own - 1);
   }
+  auto mfmas = [&](const Frag<T> (&a)[MT], const Frag<T> (&b)[NT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mma(a[mt], b[nt], acc[mt][nt]);
+  };
+  // Every K step but the last loads the fragments of the next one before its
+  // MFMAs; the loop covers all tiles but the last, so its loads are
+  // unconditional and the fragment registers alternate without copies.
   Frag<T> ca[MT], cb[NT];
-  if (nk > 0) load(0, 0, ca, cb);
-  for (int kt = 0; kt < nk; ++kt) {
+  if (nk > 0) {
+    load(0, 0, ca, cb);
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        Frag<T> na[MT], nb_[NT];
+        if (ks + 1 < KS) {
+          load(kt, ks + 1, na, nb_);
+        } else {
+          wait_for(kt + 1, min(kt + SA - 1, nk - 1), min(kt + SB - 1, nk - 1));
+          if (kt + S_own < nk) issue(kt + S_own);
+          load(kt + 1, 0, na, nb_);
+        }
+        mfmas(ca, cb);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) ca[mt] = na[mt];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) cb[nt] = nb_[nt];
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       Frag<T> na[MT], nb_[NT];
+      if (ks + 1 < KS) load(nk - 1, ks + 1, na, nb_);
+      mfmas(ca, cb);
       if (ks + 1 < KS) {
-        load(kt, ks + 1, na, nb_);
-      } else if (kt + 1 < nk) {
-        wait_for(kt + 1, min(kt + SA - 1, nk - 1), min(kt + SB - 1, nk - 1));
-        if (kt + S_own < nk) issue(kt + S_own);
-        load(kt + 1, 0, na, nb_);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) ca[mt] = na[mt];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) cb[nt] = nb_[nt];
       }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mma(ca[mt], cb[nt], acc[mt][nt]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) ca[mt] = na[mt];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) cb[nt] = nb_[nt];
     }
   }
 
