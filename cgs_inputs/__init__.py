@@ -19,6 +19,7 @@ from .gen import (  # noqa: F401
     rng,
     f32_to_bf16_bits,
     ffn_weights,
+    ffn_weight_pool,
     ctx_layer_inputs,
     act_tokens,
     synthetic_h_ref,

@@ -65,6 +65,34 @@ def ffn_weights(seed: int, layer: int, d: int, ff: int, dtype: str = "bf16",
     }
 
 
+def ffn_weight_pool(seed: int, layers: int, d: int, ff: int, std: float = 0.02) -> list:
+    """bf16 GeGLU weights of ``layers`` Context Cache layers (w_gate, w_up
+    [ff][d], w_down [d][ff]) cut from one shared pool of N(0, std) values.
+
+    The pool holds 2 ff d values; matrix m of layer l is the ff d consecutive
+    values that start at a seeded offset (one draw per layer and matrix), so
+    every layer gets different weights at the cost of drawing two matrices.
+    Used where a deep full-size chain would otherwise spend minutes drawing
+    independent weights; the arrays are views of the pool (do not write to them).
+    """
+    n = ff * d
+    vals = rng(seed, 0, "w_gate").standard_normal(2 * n, dtype=np.float32)
+    vals *= np.float32(std)
+    pool = np.empty(2 * n, dtype=np.uint16)
+    step = 1 << 22  # encode in chunks: small temporaries
+    for c in range(0, 2 * n, step):
+        pool[c: c + step] = f32_to_bf16_bits(vals[c: c + step])
+    del vals
+    out = []
+    for l in range(layers):
+        off = rng(seed, l, "w_down_scale").integers(0, n + 1, size=3)
+        m = [pool[o: o + n] for o in off]
+        out.append({"w_gate": m[0].reshape(ff, d), "w_up": m[1].reshape(ff, d),
+                    "w_down": m[2].reshape(d, ff), "d": d, "ff": ff, "dtype": "bf16",
+                    "down_layout": "df"})
+    return out
+
+
 def ctx_layer_inputs(seed: int, layer: int, P: int, d: int, n_changed: int,
                      sigma_changed: float, sigma_stable: float, dtype: str = "bf16") -> dict:
     """Current FFN input x ~ N(0,1) and reference input x_ref = x + sigma * N(0,1).

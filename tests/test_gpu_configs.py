@@ -1,0 +1,200 @@
+"""Full-size chained parity of the two multi-layer workloads, run the way the
+benchmark runs them.
+
+* Context Cache prefill (rMuscle §4.1, Eq. 2 and Eq. 3; §4.2 for the entry):
+  17 VLM FFN layers of 768 tokens, d 2048, ff 16384.  A compact entry is
+  expanded by the dense rebuild into (xbar_l, ybar_l); the current input is the
+  entry with 231 tokens moved to cosine ~0.6 and the rest to ~0.985; each layer
+  selects ceil(rho_p P) tokens (layer 0 by ctx_select, later layers from the
+  keys the previous layer's finish kernel formed), recomputes them and carries
+  the residual stream to the next layer.  rho_p in {0.1, 0.3, 0.5, 1.0}.
+* Action Cache denoise (§3.4 Eq. 1, §4.1 Eq. 4, §5): 18 expert layers of 50
+  action tokens, d 1024, ff 4096.  A dense reference denoise from a perturbed
+  start (cosine ~0.95) yields h_ref; group masks keep the top neurons until
+  84.4% of the summed contribution is covered; the 4-step denoise runs step 0
+  dense (the anchor) and steps 1-3 masked on compact weight copies.
+
+Teacher forcing: every layer is checked on the GPU's own inputs of that layer
+(its x, the rebuilt xbar/ybar, the reference run's h, the anchor's y_a/h_a), so
+index sets and masks must match the oracle bit for bit and outputs must be
+within 1e-2 x RMS of it; drift between two independent chains is not gated.
+The 17 VLM layers' weights are cut from one seeded pool at seeded offsets
+(cgs_inputs.ffn_weight_pool) so the host does not spend minutes drawing them.
+"""
+import numpy as np
+import pytest
+import torch
+
+import cache_guided_sparse_amd as cgs
+import oracle as O
+from cgs_inputs import act_tokens, ctx_layer_inputs, ffn_weight_pool, ffn_weights, timestep_embedding
+from gpu_helpers import assert_close, bits, dev, ffn_dev, say, to_dev, values
+
+pytestmark = pytest.mark.gpu
+
+L_VLM, P, D, FF = 17, 768, 2048, 16384
+N_CHANGED = 231
+L_EXP, S, DE, FFE, STEPS = 18, 50, 1024, 4096, 4
+COVERAGE = 0.844
+
+
+@pytest.fixture(scope="module")
+def vlm():
+    say("configs: drawing 17 VLM layers")
+    layers = ffn_weight_pool(40, L_VLM, D, FF)
+    W = [ffn_dev(w) for w in layers]
+    inp = ctx_layer_inputs(40, 0, P, D, N_CHANGED, 1.3333, 0.1752)
+    entry, current = inp["x"], inp["x_ref"]
+    say("configs: dense rebuild of the entry")
+    xbar, ybar = cgs.ref_rebuild_dense(W, to_dev(entry))
+    torch.cuda.synchronize()
+    return {"layers": layers, "W": W, "entry": entry, "current": current, "changed": inp["changed"],
+            "xbar": xbar, "ybar": ybar, "xbar_h": bits(xbar), "ybar_h": bits(ybar)}
+
+
+def test_rebuilt_entry_first_layer(vlm):
+    """The entry the prefill runs against: xbar_0 = RMSNorm(entry), ybar_0 =
+    F_0(xbar_0) on a sample of tokens (later layers: test_gpu_rebuild)."""
+    xb0 = vlm["xbar_h"][0]
+    assert_close(O.decode(xb0, "bf16"), O.rms_norm(O.decode(vlm["entry"], "bf16")), "xbar_0", out="bf16")
+    rows = np.linspace(0, P - 1, 8).astype(int)
+    y_o = O.ffn_geglu(O.decode(xb0[rows], "bf16"), vlm["layers"][0])
+    assert_close(O.decode(vlm["ybar_h"][0][rows], "bf16"), y_o, "ybar_0 rows", out="bf16")
+
+
+@pytest.mark.parametrize("rho", [0.1, 0.3, 0.5, 1.0])
+def test_prefill_chain_17_layers(vlm, rho):
+    say("configs: 17-layer prefill", rho)
+    W, xbar, ybar = vlm["W"], vlm["xbar"], vlm["ybar"]
+    k = cgs.ratio_to_count(rho, P)
+    assert k == O.ratio_to_count(rho, P)
+    r = to_dev(O.decode(vlm["current"], "bf16").astype(np.float32), "f32")
+    xs = torch.empty(L_VLM, P, D, dtype=torch.bfloat16, device=dev())
+    ys = torch.empty(L_VLM, P, D, dtype=torch.bfloat16, device=dev())
+    idx = torch.empty(L_VLM, k, dtype=torch.int32, device=dev())
+    skey = torch.empty(P, dtype=torch.float64, device=dev())
+    cgs.residual_rmsnorm(r, r_in=r.clone(), x_out=xs[0])
+    r_snap = []
+    for l in range(L_VLM):
+        if l == 0:
+            cgs.ctx_select(xs[0], xbar[0], k, idx_out=idx[0])
+        else:
+            cgs.ctx_select_from_keys(skey, k, idx_out=idx[l])
+        r_snap.append(r.clone())
+        glue = (r, None, xs[l + 1], xbar[l + 1], skey) if l + 1 < L_VLM else (r, None, None)
+        cgs.ctx_ffn_recompute(W[l], xs[l], ybar[l], idx[l], y_out=ys[l], glue=glue)
+    r_snap.append(r.clone())
+    torch.cuda.synchronize()
+
+    x_h, y_h, idx_h = bits(xs), bits(ys), idx.cpu().numpy()
+    r_h = [values(t) for t in r_snap]
+    assert_close(O.decode(x_h[0], "bf16"), O.rms_norm(O.decode(vlm["current"], "bf16")), "x_0", out="bf16")
+    for l in range(L_VLM):
+        idx_o, _ = O.ctx_select(x_h[l], vlm["xbar_h"][l], k)
+        assert np.array_equal(idx_h[l], idx_o), f"layer {l}: selected tokens differ from the oracle"
+        rec = np.zeros(P, dtype=bool)
+        rec[idx_o] = True
+        assert np.array_equal(y_h[l][~rec], vlm["ybar_h"][l][~rec]), f"layer {l}: copied rows"
+        r_exp = r_h[l] + O.decode(y_h[l], "bf16")
+        assert_close(r_h[l + 1], r_exp, f"layer {l}: residual")
+        if l + 1 < L_VLM:
+            assert_close(O.decode(x_h[l + 1], "bf16"), O.rms_norm(r_h[l + 1]), f"layer {l + 1}: input",
+                         out="bf16")
+    if k == N_CHANGED:
+        assert np.array_equal(idx_h[0], vlm["changed"]), "layer 0 must select the planted tokens"
+    for l in (0, L_VLM // 2, L_VLM - 1):
+        sample = idx_h[l][np.linspace(0, k - 1, 6).astype(int)]
+        y_o = O.ffn_geglu(O.decode(x_h[l][sample], "bf16"), vlm["layers"][l])
+        assert_close(O.decode(y_h[l][sample], "bf16"), y_o, f"layer {l}: recomputed rows", out="bf16")
+
+
+@pytest.fixture(scope="module")
+def expert():
+    say("configs: drawing 18 expert layers")
+    layers = [ffn_weights(41, l, DE, FFE, down_layout="fd", down_lognormal_sigma=1.5) for l in range(L_EXP)]
+    t = act_tokens(41, 0, S, DE, noise_sigma=0.33)
+    temb = [timestep_embedding(1.0 - s / STEPS, DE) for s in range(STEPS + 1)]
+    return {"layers": layers, "W": [ffn_dev(w) for w in layers], "a0": O.decode(t["x"], "bf16"),
+            "a_ref": O.decode(t["x_pert"], "bf16"), "temb0": temb[0],
+            "dtemb": [temb[s + 1] - temb[s] for s in range(STEPS)]}
+
+
+def _f32(a):
+    return to_dev(np.ascontiguousarray(a, dtype=np.float32), "f32")
+
+
+def test_denoise_chain_18_layers_4_steps(expert):
+    say("configs: reference run, masks, 4-step denoise")
+    W, layers = expert["W"], expert["layers"]
+    temb0, dtemb = _f32(expert["temb0"]), [_f32(v) for v in expert["dtemb"]]
+    full = torch.arange(FFE, dtype=torch.int32, device=dev())
+    ra = torch.empty(S, DE, dtype=torch.float32, device=dev())
+    xa = torch.empty(S, DE, dtype=torch.bfloat16, device=dev())
+    ya = torch.empty_like(xa)
+
+    # dense reference denoise -> h_ref [layer][step][ff][S]
+    h_ref = torch.empty(L_EXP, STEPS, FFE, S, dtype=torch.float32, device=dev())
+    x_ref_in = []
+    cgs.residual_rmsnorm(ra, r_in=_f32(expert["a_ref"]), bias=temb0, x_out=xa)
+    for t in range(STEPS):
+        for l in range(L_EXP):
+            x_ref_in.append(xa.clone())
+            cgs.act_ffn_masked(W[l], xa, full, y_out=ya, h_out=h_ref[l, t])
+            cgs.residual_rmsnorm(ra, y=ya, bias=dtemb[t] if l == L_EXP - 1 else None, x_out=xa)
+    words, midx, cnt = cgs.act_build_masks(h_ref, W, "coverage", coverage=COVERAGE)
+    torch.cuda.synchronize()
+    h_ref_h = h_ref.cpu().numpy()
+    # the reference run's activations at two points, against the oracle's dense FFN
+    for t, l in ((0, 0), (STEPS - 1, L_EXP - 1)):
+        _, h_o = O.act_ffn_masked(layers[l], bits(x_ref_in[t * L_EXP + l]), np.arange(FFE))
+        assert_close(h_ref_h[l, t], h_o, f"h_ref step {t} layer {l}")
+    K = [int(c) for c in cnt.cpu().numpy()]
+    say("configs: neuron ratios", [round(k / FFE, 3) for k in K])
+    words_h, midx_h = words.cpu().numpy().view(np.uint64), midx.cpu().numpy()
+    masks = []
+    for l in range(L_EXP):
+        idx_o, words_o = O.act_build_mask(h_ref_h[l], layers[l], "coverage", coverage=COVERAGE)
+        assert np.array_equal(midx_h[l][: K[l]], idx_o), f"layer {l}: mask indices"
+        assert np.array_equal(words_h[l], words_o), f"layer {l}: mask words"
+        assert 0.15 <= K[l] / FFE <= 0.45, f"layer {l}: neuron ratio {K[l] / FFE:.3f}"
+        masks.append(midx[l, : K[l]].contiguous())
+    cexp = [cgs.act_gather_rows(W[l], masks[l]) for l in range(L_EXP)]
+
+    # the denoise: step 0 dense (anchor), steps 1..3 Eq. 4 on compact weights
+    y_anc = torch.empty(L_EXP, S, DE, dtype=torch.float32, device=dev())
+    h_anc = torch.empty(L_EXP, FFE, S, dtype=torch.float32, device=dev())
+    xin, yout, rin = [], [], []
+    cgs.residual_rmsnorm(ra, r_in=_f32(expert["a0"]), bias=temb0, x_out=xa)
+    for t in range(STEPS):
+        for l in range(L_EXP):
+            bias = dtemb[t] if l == L_EXP - 1 else None
+            xin.append(xa.clone())
+            rin.append(ra.clone())
+            if t == 0:
+                cgs.act_ffn_masked(W[l], xa, full, y_out=ya, y_f32_out=y_anc[l], h_out=h_anc[l],
+                                   glue=(ra, bias, xa))
+            else:
+                cgs.act_ffn_masked_compact(cexp[l], xa, masks[l], y_anchor=y_anc[l], h_anchor=h_anc[l],
+                                           y_out=ya, glue=(ra, bias, xa))
+            yout.append(ya.clone())
+    rin.append(ra.clone())
+    xin.append(xa.clone())
+    torch.cuda.synchronize()
+
+    y_anc_h, h_anc_h = y_anc.cpu().numpy(), h_anc.cpu().numpy()
+    for t in range(STEPS):
+        for l in range(L_EXP):
+            i = t * L_EXP + l
+            x_h, y_h = bits(xin[i]), values(yout[i])
+            if t == 0:
+                y_o, h_o = O.act_ffn_masked(layers[l], x_h, np.arange(FFE))
+                assert_close(y_anc_h[l], y_o, f"anchor layer {l}: y_a")
+                assert_close(h_anc_h[l], h_o, f"anchor layer {l}: h_a")
+            else:
+                y_o, _ = O.act_ffn_masked(layers[l], x_h, midx_h[l][: K[l]], y_anc_h[l], h_anc_h[l])
+            assert_close(y_h, y_o, f"step {t} layer {l}: y", out="bf16")
+            r_exp = values(rin[i]) + y_h
+            if l == L_EXP - 1:
+                r_exp = r_exp + expert["dtemb"][t].astype(np.float64)
+            assert_close(values(rin[i + 1]), r_exp, f"step {t} layer {l}: residual")
+            assert_close(values(xin[i + 1]), O.rms_norm(r_exp), f"step {t} layer {l}: next input", out="bf16")
