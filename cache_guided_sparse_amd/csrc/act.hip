@@ -32,7 +32,7 @@ namespace cgs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 8;      // 32-wide K steps per load batch of a GLU wave
+constexpr int kChunk = 4;      // 32-wide K steps per load batch of a GLU wave (any NTW)
 constexpr int kStep = 32;      // mask positions per down K step
 constexpr int kCols = 32;      // output columns per down workgroup
 constexpr int kTokDown = 64;   // tokens per down workgroup (4 waves x 16)
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(64 * NW) void act_glu_kernel(
   for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) ag[mt][nt] = au[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  constexpr int CH = kChunk / NTW;  // 32-wide K steps per load batch (same registers in flight)
+  constexpr int CH = kChunk;  // 32-wide K steps per load batch
   const int kb = wave * dq, ke = kb + dq;
   for (int k0 = kb; k0 < ke; k0 += CH * 32) {
     Frag<T> bg[CH][NTW], bu[CH][NTW], a[CH][MTW];

@@ -138,6 +138,114 @@ __global__ __launch_bounds__(kRowThreads) void row_finish_kernel(
   if (glue.r && glue.x_next) glue_norm_t<T, kRowThreads>(glue, ro, d, ss, red, keep);
 }
 
+// The same finish for d = 8 kRowThreads (each thread owns one run of 8
+// elements), with the row's latency chain shortened: the index list is
+// loaded first, then every load that does not depend on whether p is
+// selected (residual, bias, the cached output row, the next layer's cached
+// input row) goes out before the search, and only the split partials of a
+// selected row wait for it.  The presence of the optional arguments is a
+// template parameter and every load is unconditional (an absent bias reads
+// the residual row and is not added), so the waits for these loads stay in
+// issue order.  SCORE implies GLUE.
+template <typename T, bool SCATTER, bool GLUE, bool SCORE>
+__global__ __launch_bounds__(kRowThreads) void row_finish1_kernel(
+    const float* __restrict__ part, int splits, size_t split_stride, int d,
+    const int32_t* __restrict__ idx, int k, const T* __restrict__ y_ref, T* __restrict__ y_out,
+    GlueArgs<T> glue) {
+  constexpr int IR = kFinishIdxLds / kRowThreads;            // index-list entries per thread
+  constexpr int RW = 4 * static_cast<int>(sizeof(T)) / 8;    // 16-byte words of 8 elements
+  __shared__ float red[kRowThreads / 64];
+  __shared__ int32_t sidx[kFinishIdxLds];
+  const int p = blockIdx.x, tid = threadIdx.x, c = tid * 8;
+  const size_t ro = static_cast<size_t>(p) * d;
+  const bool staged = SCATTER && k <= kFinishIdxLds;
+  int32_t iv[IR];
+  if constexpr (SCATTER) {
+    // with k = 0 the (unused) loads read the partial buffer, which always exists
+    const int32_t* isrc = k > 0 ? idx : reinterpret_cast<const int32_t*>(part);
+    const int last = k > 0 ? min(k, kFinishIdxLds) - 1 : 0;
+#pragma unroll
+    for (int q = 0; q < IR; ++q) iv[q] = isrc[min(tid + q * kRowThreads, last)];
+  }
+  float rr[1][8], bb[8];
+  u32x4_t yraw[RW], sraw[RW];
+  if constexpr (GLUE) {
+    Row8<float>::load(glue.r + ro + c, rr[0]);
+    Row8<float>::load((glue.bias ? glue.bias : glue.r + ro) + c, bb);
+  }
+  if constexpr (SCATTER) {
+#pragma unroll
+    for (int w = 0; w < RW; ++w) yraw[w] = reinterpret_cast<const u32x4_t*>(y_ref + ro + c)[w];
+  }
+  if constexpr (SCORE) {
+#pragma unroll
+    for (int w = 0; w < RW; ++w) sraw[w] = reinterpret_cast<const u32x4_t*>(glue.score_ref + ro + c)[w];
+  }
+  int i = p;
+  bool sel = true;
+  if constexpr (SCATTER) {
+    int lo = 0, hi = k;
+    if (staged) {
+#pragma unroll
+      for (int q = 0; q < IR; ++q) {
+        const int e = tid + q * kRowThreads;
+        if (e < k) sidx[e] = iv[q];
+      }
+      __syncthreads();
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sidx[mid] < p) lo = mid + 1; else hi = mid;
+      }
+      sel = (lo < k) && (sidx[lo] == p);
+    } else {
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (__builtin_amdgcn_readfirstlane(idx[mid]) < p) lo = mid + 1; else hi = mid;
+      }
+      sel = (lo < k) && (idx[lo] == p);
+    }
+    i = lo;
+  }
+  float v[8];
+  if (!sel) {
+    // the cached row, bit for bit
+#pragma unroll
+    for (int w = 0; w < RW; ++w) reinterpret_cast<u32x4_t*>(y_out + ro + c)[w] = yraw[w];
+    if constexpr (!GLUE) return;
+    raw_to_f32<T>(yraw, v);
+  } else {
+    const size_t io = static_cast<size_t>(i) * d;
+    Row8<float>::load(part + io + c, v);
+    add_splits(part + split_stride + io + c, split_stride, splits - 1, v);
+    Row8<T>::store(y_out + ro + c, v);
+  }
+  if constexpr (GLUE) {
+    const float ss = glue_add(glue, ro, c, v, rr[0], bb);
+    if (glue.x_next) {
+      float sr[1][8];
+      if constexpr (SCORE) raw_to_f32<T>(sraw, sr[0]);
+      glue_norm_t<T, kRowThreads>(glue, ro, d, ss, red, rr, SCORE ? sr : nullptr);
+    }
+  }
+}
+
+template <typename T>
+void launch_finish1(dim3 grid, hipStream_t s, const float* part, int splits, size_t split_stride, int d,
+                    bool scatter, const int32_t* idx, int k, const T* y_ref, T* y_out, const GlueArgs<T>& g) {
+  if (!scatter)
+    hipLaunchKernelGGL((row_finish1_kernel<T, false, true, false>), grid, dim3(kRowThreads), 0, s, part,
+                       splits, split_stride, d, idx, k, y_ref, y_out, g);
+  else if (!g.r)
+    hipLaunchKernelGGL((row_finish1_kernel<T, true, false, false>), grid, dim3(kRowThreads), 0, s, part,
+                       splits, split_stride, d, idx, k, y_ref, y_out, g);
+  else if (!g.score_key)
+    hipLaunchKernelGGL((row_finish1_kernel<T, true, true, false>), grid, dim3(kRowThreads), 0, s, part,
+                       splits, split_stride, d, idx, k, y_ref, y_out, g);
+  else
+    hipLaunchKernelGGL((row_finish1_kernel<T, true, true, true>), grid, dim3(kRowThreads), 0, s, part,
+                       splits, split_stride, d, idx, k, y_ref, y_out, g);
+}
+
 // r[m] = (r_src ? decode(r_src[m]) : r[m]) + (y ? decode(y[m]) : 0) + (bias ? bias : 0);
 // x_out[m] = RMSNorm(r[m]).  One workgroup per row.
 template <typename TS, typename TY, typename TO>
@@ -271,8 +379,12 @@ int ctx_recompute_t(const cgs_ffn& w, const T* x, const T* y_ref, const int32_t*
   }
   {
     ProfScope ps("ctx.finish", s);
-    hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kRowThreads), 0, s, part, p.splits,
-                       static_cast<size_t>(k) * w.d, w.d, true, idx, k, y_ref, y_out, make_glue<T>(gl, w.d));
+    if (w.d == 8 * kRowThreads)
+      launch_finish1<T>(dim3(P), s, part, p.splits, static_cast<size_t>(k) * w.d, w.d, true, idx, k, y_ref,
+                        y_out, make_glue<T>(gl, w.d));
+    else
+      hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kRowThreads), 0, s, part, p.splits,
+                         static_cast<size_t>(k) * w.d, w.d, true, idx, k, y_ref, y_out, make_glue<T>(gl, w.d));
   }
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
 }
@@ -296,11 +408,15 @@ int rebuild_t(const cgs_ffn* layers, int L, const T* r0, int P, T* xo, T* yo, vo
     launch_ffn_core<T>(layers[l], xo + l * lay, nullptr, P, p, H, part, "rebuild.glu",
                        "rebuild.down", s);
     ProfScope ps("rebuild.finish", s);
-    hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kRowThreads), 0, s, part, p.splits, lay,
-                       w0.d, false, static_cast<const int32_t*>(nullptr), P, static_cast<const T*>(nullptr),
-                       yo + l * lay,
-                       GlueArgs<T>{r, nullptr, (l + 1 < L) ? xo + (l + 1) * lay : static_cast<T*>(nullptr),
-                                  nullptr, nullptr, 0, 0});
+    const GlueArgs<T> ga{r, nullptr, (l + 1 < L) ? xo + (l + 1) * lay : static_cast<T*>(nullptr),
+                         nullptr, nullptr, 0, 0};
+    if (w0.d == 8 * kRowThreads)
+      launch_finish1<T>(dim3(P), s, part, p.splits, lay, w0.d, false, static_cast<const int32_t*>(nullptr), P,
+                        static_cast<const T*>(nullptr), yo + l * lay, ga);
+    else
+      hipLaunchKernelGGL((row_finish_kernel<T>), dim3(P), dim3(kRowThreads), 0, s, part, p.splits, lay,
+                         w0.d, false, static_cast<const int32_t*>(nullptr), P, static_cast<const T*>(nullptr),
+                         yo + l * lay, ga);
     if (!launch_ok()) return CGS_ERR_LAUNCH;
   }
   return CGS_OK;

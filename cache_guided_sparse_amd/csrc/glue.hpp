@@ -56,6 +56,22 @@ template <> struct Row8<float> {
   }
 };
 
+// Eight elements held as raw 16-byte words (one word of bf16, two of fp32)
+// decoded to fp32.
+template <typename T>
+__device__ __forceinline__ void raw_to_f32(const u32x4_t* w, float* v) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(w[0][e] << 16);
+      v[2 * e + 1] = __uint_as_float(w[0][e] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(w[e / 4][e % 4]);
+  }
+}
+
 // Sum over the threads of a workgroup of NT threads (NT/64 wave partials in
 // `red`, summed in wave order).  Contains barriers: call from every thread.
 template <int NT>
@@ -172,10 +188,11 @@ __device__ __forceinline__ long long block_sum_i64(long long v, long long* red) 
 // a score reference, also the Eq. 2 key of the stored (rounded) x_next row
 // against it, exactly as the standalone score kernel computes it.
 // keep[j]: the updated r values of this thread's run j (j < kGlueKeep), as
-// glue_add left them; later runs are read back from r.
+// glue_add left them; later runs are read back from r.  sref (or NULL): the
+// score reference runs j < kGlueKeep, already loaded by the caller.
 template <typename T, int NT>
 __device__ __forceinline__ void glue_norm_t(const GlueArgs<T>& g, size_t ro, int d, float ss, float* red,
-                                            const float (*keep)[8]) {
+                                            const float (*keep)[8], const float (*sref)[8] = nullptr) {
   const float tot = block_sum<NT>(ss, red);
   const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + 1e-6f);
   ScoreSums sc;
@@ -195,7 +212,12 @@ __device__ __forceinline__ void glue_norm_t(const GlueArgs<T>& g, size_t ro, int
     if (g.score_key) {
       float xr[8];
       Row8<T>::round(rr);
-      Row8<T>::load(g.score_ref + ro + c, xr);
+      if (sref && j < kGlueKeep) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xr[e] = sref[j][e];
+      } else {
+        Row8<T>::load(g.score_ref + ro + c, xr);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (cosine) sc.add<true>(static_cast<double>(rr[e]), static_cast<double>(xr[e]));

@@ -40,11 +40,14 @@ def test_tiny_fp32(rho):
     _check_full(w, inp["x"], y_ref, idx)
 
 
-@pytest.mark.parametrize("k", [0, 1, 37, 64, 65, 129, 200, 300])
-def test_ragged_bf16(k):
-    """k spans the 64/128/256-row tiles, several M tiles and a ragged tail."""
-    say("ctx ragged", k)
-    P, d, ff = 300, 256, 512
+@pytest.mark.parametrize("d,k", [(256, 0), (256, 1), (256, 37), (256, 64), (256, 65), (256, 129), (256, 200),
+                                 (256, 300), (2048, 0), (2048, 1), (2048, 231), (2048, 300)])
+def test_ragged_bf16(d, k):
+    """k spans the 64/128/256-row tiles, several M tiles and a ragged tail;
+    d = 2048 (one 8-element run per finish thread) takes the finish kernel
+    that loads its rows before the index search."""
+    say("ctx ragged", d, k)
+    P, ff = 300, 512
     w = ffn_weights(1, 0, d, ff)
     x = random_bf16(1, 0, "x", (P, d))
     y_ref = random_bf16(1, 0, "y_ref", (P, d))
@@ -99,36 +102,42 @@ def test_deterministic_repeats():
     assert np.array_equal(a, b)
 
 
-def test_fused_glue():
+@pytest.mark.parametrize("d,with_bias", [(256, False), (2048, False), (2048, True)])
+def test_fused_glue(d, with_bias):
     """Residual/RMSNorm glue in the finish kernel on all P rows (recomputed and
     copied), checked on the GPU's own y against the oracle's RMSNorm."""
-    say("ctx glue")
-    P, d, ff = 300, 256, 512
+    say("ctx glue", d, with_bias)
+    P, ff = 300, 512
     inp = ctx_layer_inputs(21, 0, P, d, 90, 1.3333, 0.1752)
     w = ffn_weights(21, 0, d, ff)
     y_ref = random_bf16(21, 0, "y_ref", (P, d))
     idx, _ = O.ctx_select(inp["x"], inp["x_ref"], 90)
     r0 = rng(21, 1, "misc").standard_normal((P, d)).astype(np.float32)
+    bias = rng(21, 2, "misc").standard_normal(d).astype(np.float32) if with_bias else None
     r = to_dev(r0, "f32")
     xn = torch.empty(P, d, dtype=torch.bfloat16, device=dev())
     y = cgs.ctx_ffn_recompute(ffn_dev(w), to_dev(inp["x"]), to_dev(y_ref),
-                              torch.from_numpy(idx).to(dev()), glue=(r, None, xn))
+                              torch.from_numpy(idx).to(dev()),
+                              glue=(r, None if bias is None else to_dev(bias, "f32"), xn))
     torch.cuda.synchronize()
     y_o, rec = O.ctx_ffn_recompute(w, inp["x"], y_ref, idx)
     assert_close(values(y)[rec], y_o[rec], "recomputed rows", out="bf16")
     assert np.array_equal(bits(y)[~rec], y_ref[~rec])
     r_exp = r0.astype(np.float64) + values(y)
+    if bias is not None:
+        r_exp = r_exp + bias.astype(np.float64)
     assert_close(values(r), r_exp, "residual")
     assert_close(values(xn), O.rms_norm(r_exp), "x_next", out="bf16")
 
 
+@pytest.mark.parametrize("d", [256, 2048])
 @pytest.mark.parametrize("kind", ["rel_rms", "cosine"])
-def test_fused_next_score(kind):
+def test_fused_next_score(kind, d):
     """The finish kernel's Eq. 2 keys of x_next against the next layer's cached
     input are bit-identical to ctx_select's keys of the same pair and to the
     oracle's; selecting from them gives the oracle's index set."""
-    say("ctx fused score", kind)
-    P, d, ff, k = 300, 256, 512, 90
+    say("ctx fused score", kind, d)
+    P, ff, k = 300, 512, 90
     inp = ctx_layer_inputs(22, 0, P, d, k, 1.3333, 0.1752)
     nxt = ctx_layer_inputs(22, 1, P, d, k, 1.3333, 0.1752)
     w = ffn_weights(22, 0, d, ff)
