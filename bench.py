@@ -438,6 +438,131 @@ def joint_denoise(w, reps: int = 10) -> dict:
     return out
 
 
+def masked_layer_bytes(K: int) -> int:
+    """Algorithmic bytes of one masked expert layer (Eq. 4 on compact weights,
+    glue included): the K rows of W_gate, W_up and W_down, x, y_a (fp32), the
+    K anchor activation rows (fp32), y, the index list."""
+    return K * DE * 2 * 3 + S * DE * 2 + S * DE * 4 + K * S * 4 + S * DE * 2 + K * 4
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2]
+
+
+def ctx_sweep(w, reps: int = 8) -> dict:
+    """The 17-layer Context Cache prefill at recompute ratios 0.1 / 0.3 / 0.5 /
+    1.0 (HIP graph per ratio, working-set slot 0, inputs resident), each call
+    timed with HIP events; roofline = max(FLOP / bf16 peak, bytes / HBM peak)."""
+    import torch
+    cgs = w.cgs
+    out = {}
+    for rho in (0.1, 0.3, 0.5, 1.0):
+        k = cgs.ratio_to_count(rho, P)
+        idx = torch.empty(k, dtype=torch.int32, device=w.dev)
+
+        def layers(idx=idx, k=k):
+            for l in range(L_VLM):
+                if l == 0:
+                    cgs.ctx_select(w.x, w.xbar[0, l], k, idx_out=idx)
+                else:
+                    cgs.ctx_select_from_keys(w.skey, k, idx_out=idx)
+                glue = (w.r, None, w.x, w.xbar[0, l + 1], w.skey) if l + 1 < L_VLM else (w.r, None, None)
+                cgs.ctx_ffn_recompute(w.vlm[l], w.x, w.ybar[0, l], idx, y_out=w.y, glue=glue)
+
+        def start():
+            cgs.residual_rmsnorm(w.r, r_in=w.current[0], x_out=w.x)
+
+        start()
+        layers()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layers()
+        ts = []
+        for _ in range(reps + 1):
+            start()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = _median(ts[1:])
+        flops = L_VLM * (2.0 * k * D * 2 * FF + 2.0 * k * FF * D)
+        byts = L_VLM * (3 * FF * D * 2 + 2 * k * D * 2 + k * FF * 4 + 2 * P * D * 2)
+        roof = 1e3 * max(flops / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBPS * 1e9))
+        out[f"rho_{rho}"] = {"k": k, "ms": round(ms, 4), "per_layer_us": round(1e3 * ms / L_VLM, 2),
+                             "tflops": round(flops / ms / 1e9, 1),
+                             "GBps": round(byts / ms / 1e6, 1), "roofline_ms": round(roof, 4),
+                             "bound": "mfma" if flops / byts > RIDGE else "hbm",
+                             "frac_of_roofline": round(roof / ms, 4),
+                             "mfma_frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    out["note"] = ("17 layers per call incl. selection, fused glue and next-layer keys; bytes = weights + "
+                   "gathered rows + h round trip + cached output copy")
+    return out
+
+
+def act_sweep(w, reps: int = 10) -> dict:
+    """One masked denoise step (18 expert layers on compact weights, glue
+    included) MALL-warm (back-to-back replays) and cold (a 512 MB write before
+    each replay evicts the MALL), with the coverage masks of the run and with
+    top-K masks at neuron ratios 0.2 / 0.3 / 0.4 built from the same reference
+    activations (§5's rule)."""
+    import torch
+    cgs = w.cgs
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=w.dev)
+    out = {}
+    cases = [("coverage_0.844", w.masks, w.cexp)]
+    for rho in (0.2, 0.3, 0.4):
+        K = cgs.ratio_to_count(rho, FFE)
+        _, mi, mc = cgs.act_build_masks(w.h_ref, w.exp, "topk", K=K)
+        torch.cuda.synchronize()
+        cnt = [int(c) for c in mc.tolist()]
+        masks = [mi[l, : cnt[l]].contiguous() for l in range(L_EXP)]
+        cases.append((f"topk_{rho}", masks, [cgs.act_gather_rows(w.exp[l], masks[l]) for l in range(L_EXP)]))
+    for name, masks, cexp in cases:
+        def step(masks=masks, cexp=cexp):
+            for l in range(L_EXP):
+                cgs.act_ffn_masked_compact(cexp[l], w.xa, masks[l], y_anchor=w.y_anc[l], h_anchor=w.h_anc[l],
+                                           y_out=w.ya, glue=(w.ra, w.dtemb[1] if l == L_EXP - 1 else None, w.xa))
+
+        def start():
+            cgs.residual_rmsnorm(w.ra, r_in=w.a0, bias=w.temb0, x_out=w.xa)
+
+        start()
+        step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        res = {}
+        for mode in ("warm", "cold"):
+            ts = []
+            for _ in range(reps + 1):
+                start()
+                if mode == "cold":
+                    flush.fill_(1)
+                else:
+                    g.replay()
+                    start()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            res[mode] = _median(ts[1:])
+        Ks = [int(m.numel()) for m in masks]
+        byts = sum(masked_layer_bytes(K) for K in Ks)
+        out[name] = {"neurons_mean": round(sum(Ks) / len(Ks), 1), "bytes": byts,
+                     **{f"{m}_ms": round(res[m], 4) for m in res},
+                     **{f"{m}_GBps": round(byts / res[m] / 1e6, 1) for m in res},
+                     **{f"{m}_hbm_frac": round(byts / res[m] / 1e6 / PEAK_HBM_GBPS, 4) for m in res}}
+    out["note"] = "one masked step (18 layers); cold = MALL evicted by a 512 MB write before the step"
+    return out
+
+
 def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
     """The oracle, timed on the host cores over a bounded sample of the step:
     one context layer (select + recompute of 231 rows), one dense anchor
@@ -515,6 +640,8 @@ def main():
                     help="run the entry rebuild on a side stream (overlapped) or in line")
     ap.add_argument("--no-joint", action="store_true",
                     help="skip the separate joint token + neuron sparsity measurement")
+    ap.add_argument("--no-sweeps", action="store_true",
+                    help="skip the recompute-ratio and neuron-ratio sweeps (reported beside the step)")
     ap.add_argument("--no-compact", action="store_true",
                     help="masked steps gather the mask's weight rows in place (no compact buffers)")
     ap.add_argument("--serial-steps", type=int, default=8,
@@ -683,8 +810,7 @@ def main():
 
     # Action Cache masked step: algorithmic bytes over its measured time (FFN + glue)
     Km = w.K
-    masked_bytes = sum(K * DE * 2 * 3 + S * DE * 2 + S * DE * 4 + K * S * 4 + S * DE * 2 + K * 4
-                       for K in Km)
+    masked_bytes = sum(masked_layer_bytes(K) for K in Km)
     masked_step_ms = ph["act_masked"] / (STEPS - 1)
     k_ffn_ms = (sites.get("act.glu.masked", {}).get("ms_per_step", 0)
                 + sites.get("act.down.masked", {}).get("ms_per_step", 0)
@@ -720,7 +846,9 @@ def main():
                             "GBps": round(masked_bytes / masked_step_ms / 1e6, 1),
                             "hbm_frac": round(masked_bytes / masked_step_ms / 1e6 / PEAK_HBM_GBPS, 4),
                             "ffn_kernels_ms": round(k_ffn_ms, 4),
-                            "note": "18 masked layers incl. residual/RMSNorm glue; MALL-warm"},
+                            "note": "18 masked layers incl. residual/RMSNorm glue, inside the call: the first "
+                                    "masked step finds its compact weights evicted by the prefill's weight "
+                                    "stream, the next two MALL-warm (act_sweep has cold and warm apart)"},
         "rebuild_ms_per_entry": round(ph["rebuild"] / max(1e-9, sum(w.entered[-args.steps:]) / args.steps), 4),
         "working_set": {"repository_entries": STORE, "repository_bytes": STORE * P * D * 2,
                         "slots": SLOTS, "window": {"episodes": 1, "lookahead": LOOKAHEAD},
@@ -741,6 +869,10 @@ def main():
     }
     if not args.no_joint:
         out["joint_denoise"] = joint_denoise(w)
+    if not args.no_sweeps:
+        log("ratio sweeps ...")
+        out["ctx_sweep"] = ctx_sweep(w)
+        out["act_sweep"] = act_sweep(w)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(int(round(sum(Km) / len(Km))))
