@@ -1,0 +1,124 @@
+"""Consecutive policy calls through the sliding working set (rMuscle §4.2:
+sliding window prefetching, asynchronous online reconstruction, retrieving a
+relevant reference; §5: joint-history retrieval and fallback; §4.1: the
+Context Cache prefill against the retrieved entry), as the benchmark runs
+them, checked against the oracle on every call.
+
+A repository of compact entries (residual-stream inputs of 768 x 2048, bf16)
+stands for one reference episode; the 16-slot working set covers the matched
+position and the next 15.  Each call advances the window by one position
+(native planner against the plain model), rebuilds the entering entries into
+the slots they were given (17-layer dense prefill), retrieves among the
+prepared slots (visual cosine of the 768 x 1152 features, top 4, joint-history
+rerank, fallback below 0.8) and runs the 17-layer selective prefill at
+rho_p = 0.3 against the chosen slot.  Per call: admissions equal the model's,
+the retrieval's cosines and choice equal the oracle's bit for bit, the chosen
+slot holds the matched position's entry, every layer's selection equals the
+oracle's on the GPU's own inputs (teacher forcing), copied rows are the
+cached bits, and at layer 0 the planted tokens are the selection.  The
+repository holds 24 positions here (the benchmark's 800 only lengthen the
+episode); the 17 layers' weights come from the seeded pool.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import cache_guided_sparse_amd as cgs
+import oracle as O
+from cgs_inputs import ctx_layer_inputs, ffn_weight_pool, rng
+from gpu_helpers import assert_close, bits, dev, ffn_dev, say, to_dev
+from oracle.cgs_retrieval import ret_select as oracle_select
+from oracle.cgs_window import WindowModel
+
+pytestmark = pytest.mark.gpu
+
+L_VLM, P, D, FF = 17, 768, 2048, 16384
+STORE, SLOTS, LOOKAHEAD, CALLS = 24, 16, 15, 4
+FEAT, HIST_L, JOINTS, TOP_T = 768 * 1152, 4, 14, 4
+RHO_P, N_CHANGED = 0.3, 231
+
+
+def _retrieval_data(seed):
+    """Features drifting along the episode (consecutive positions at cosine
+    ~0.98), a smooth joint trajectory; each call's query is its position's
+    features and history plus noise."""
+    g = rng(seed, 0, "misc")
+    feats = np.empty((STORE, FEAT), dtype=np.uint16)
+    queries = np.empty((STORE, FEAT), dtype=np.uint16)
+    f = g.standard_normal(FEAT)
+    for q in range(STORE):
+        f = 0.98 * f + math.sqrt(1 - 0.98 ** 2) * g.standard_normal(FEAT)
+        feats[q] = O.round_to_bf16_bits(f)
+        queries[q] = O.round_to_bf16_bits(f + 0.1 * g.standard_normal(FEAT))
+    traj = np.cumsum(0.05 * g.standard_normal((STORE + HIST_L, JOINTS)), axis=0)
+    hist = np.stack([traj[q:q + HIST_L] for q in range(STORE)]).astype(np.float32)
+    qhist = (hist + 0.005 * g.standard_normal(hist.shape)).astype(np.float32)
+    return feats, queries, hist, qhist
+
+
+def test_consecutive_calls_through_the_working_set():
+    say("policy calls: setup")
+    layers = ffn_weight_pool(44, L_VLM, D, FF)
+    W = [ffn_dev(w) for w in layers]
+    entries = [ctx_layer_inputs(45, q, P, D, N_CHANGED, 1.3333, 0.1752) for q in range(STORE)]
+    feats, queries, hist, qhist = _retrieval_data(46)
+    xbar = torch.empty(SLOTS, L_VLM, P, D, dtype=torch.bfloat16, device=dev())
+    ybar = torch.empty_like(xbar)
+    slot_feat = torch.empty(SLOTS, FEAT, dtype=torch.bfloat16, device=dev())
+    slot_hist = torch.empty(SLOTS, HIST_L, JOINTS, dtype=torch.float32, device=dev())
+    slot_pos = [-1] * SLOTS
+    window, model = cgs.Window(SLOTS), WindowModel(SLOTS)
+    k = cgs.ratio_to_count(RHO_P, P)
+    r = torch.empty(P, D, dtype=torch.float32, device=dev())
+    xs = torch.empty(L_VLM, P, D, dtype=torch.bfloat16, device=dev())
+    ys = torch.empty_like(xs)
+    idx = torch.empty(L_VLM, k, dtype=torch.int32, device=dev())
+    skey = torch.empty(P, dtype=torch.float64, device=dev())
+
+    for q in range(CALLS):
+        say("policy call", q)
+        entered, left, ncand = window.advance([0], [q], [STORE], LOOKAHEAD)
+        assert (entered, left, ncand) == model.advance([0], [q], [STORE], LOOKAHEAD), "window admissions"
+        assert len(entered) == (SLOTS if q == 0 else 1)
+        for _, pos, slot in entered:
+            slot_feat[slot] = to_dev(feats[pos])
+            slot_hist[slot] = to_dev(hist[pos], "f32")
+            cgs.ref_rebuild_dense(W, to_dev(entries[pos]["x"]), x_ref_out=xbar[slot], y_ref_out=ybar[slot])
+            slot_pos[slot] = pos
+        cos, top, dist, choice = cgs.ret_select(to_dev(queries[q]), slot_feat, TOP_T, to_dev(qhist[q], "f32"),
+                                                slot_hist, arm=-1, min_cos=0.8)
+        torch.cuda.synchronize()
+        c = int(choice.item())
+        want = oracle_select(queries[q], bits(slot_feat), TOP_T, qhist[q], slot_hist.cpu().numpy(), arm=-1,
+                             min_cos=0.8)
+        assert np.array_equal(cos.cpu().numpy(), want[0]) and c == want[3], "retrieval differs from the oracle"
+        assert c == window.slot(0, q) and slot_pos[c] == q, "the matched position's entry must be chosen"
+
+        # 17-layer selective prefill against the chosen slot, as the benchmark chains it
+        cur = entries[q]["x_ref"]
+        cgs.residual_rmsnorm(r, r_in=to_dev(O.decode(cur, "bf16").astype(np.float32), "f32"), x_out=xs[0])
+        for l in range(L_VLM):
+            if l == 0:
+                cgs.ctx_select(xs[0], xbar[c, 0], k, idx_out=idx[0])
+            else:
+                cgs.ctx_select_from_keys(skey, k, idx_out=idx[l])
+            glue = (r, None, xs[l + 1], xbar[c, l + 1], skey) if l + 1 < L_VLM else (r, None, None)
+            cgs.ctx_ffn_recompute(W[l], xs[l], ybar[c, l], idx[l], y_out=ys[l], glue=glue)
+        torch.cuda.synchronize()
+        x_h, y_h, idx_h = bits(xs), bits(ys), idx.cpu().numpy()
+        xb_h, yb_h = bits(xbar[c]), bits(ybar[c])
+        assert_close(O.decode(xb_h[0], "bf16"), O.rms_norm(O.decode(entries[q]["x"], "bf16")),
+                     "rebuilt xbar_0 of the chosen slot", out="bf16")
+        for l in range(L_VLM):
+            idx_o, _ = O.ctx_select(x_h[l], xb_h[l], k)
+            assert np.array_equal(idx_h[l], idx_o), f"call {q} layer {l}: selection"
+            rec = np.zeros(P, dtype=bool)
+            rec[idx_o] = True
+            assert np.array_equal(y_h[l][~rec], yb_h[l][~rec]), f"call {q} layer {l}: copied rows"
+        assert np.array_equal(idx_h[0], entries[q]["changed"]), "layer 0 must select the planted tokens"
+        if q in (0, CALLS - 1):
+            sample = idx_h[0][np.linspace(0, k - 1, 6).astype(int)]
+            y_o = O.ffn_geglu(O.decode(x_h[0][sample], "bf16"), layers[0])
+            assert_close(O.decode(y_h[0][sample], "bf16"), y_o, f"call {q}: recomputed rows", out="bf16")
