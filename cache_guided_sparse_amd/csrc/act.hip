@@ -7,8 +7,8 @@
 // 18-layer expert moves ~7.5 MB), so every kernel puts all of its weight
 // loads in flight before it computes:
 //
-//   act_glu_kernel    a workgroup owns 16 (32 for large masks) mask positions and TT tokens; its
-//       four waves split d into quarters.  Each wave issues all of its
+//   act_glu_kernel    a workgroup owns 16 (32 for large masks) mask positions and TT tokens (64
+//       for dense-size masks of at most 64 tokens); its waves split d into slices.  Each wave issues all of its
 //       gathered gate/up fragments and its x fragments of a chunk at once,
 //       then runs the MFMAs; the quarters are summed in LDS in a fixed order.
 //       Epilogue: h (optionally stored to the neuron-major h_out rows) and the
@@ -392,10 +392,15 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
       ProfScope ps(K == w.ff && !COMPACT ? "act.glu.dense" : "act.glu.masked", s);
       const T* wgp = static_cast<const T*>(w.w_gate);
       const T* wup = static_cast<const T*>(w.w_up);
-      // two 16-wide position tiles per workgroup for large masks (x is then
-      // read once per 32 positions), one otherwise (more workgroups)
-      const int ntw = K >= kWideGluK ? 2 : 1;
-      const dim3 grid((p.K_pad + 16 * ntw - 1) / (16 * ntw), (p.S_pad + p.tt - 1) / p.tt);
+      // Masks of dense size with at most 64 tokens: one 64-token workgroup per
+      // 16 positions, so every weight row is read once and the grid keeps
+      // K/16 workgroups.  Otherwise two 16-wide position tiles per workgroup
+      // for large masks (x is then read once per 32 positions) and one for
+      // small ones (more workgroups).
+      const bool dense64 = sizeof(T) == 2 && K >= kWideGluK && p.S_pad <= 64;
+      const int tt = dense64 ? 64 : p.tt;
+      const int ntw = (K >= kWideGluK && !dense64) ? 2 : 1;
+      const dim3 grid((p.K_pad + 16 * ntw - 1) / (16 * ntw), (p.S_pad + tt - 1) / tt);
       // NW waves split d (8 when d allows: more loads in flight per workgroup)
       const bool w8 = w.d % (kGluWaves * 32) == 0;
       const dim3 blk(w8 ? 64 * kGluWaves : kThreads);
@@ -408,8 +413,10 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
       hipLaunchKernelGGL((act_glu_kernel<T, MTW_, NTW_, COMPACT, 4>), grid, blk, 0, s, x, S, w.d, idx, K, \
                          p.K_pad, wgp, wup, ha, h_out, D, tok, S_all);                                   \
   } while (0)
-      if (p.tt == 16 && ntw == 1) CGS_GLU(1, 1);
-      else if (p.tt == 16) CGS_GLU(1, 2);
+      if (tt == 64) {
+        if constexpr (sizeof(T) == 2) CGS_GLU(4, 1);
+      } else if (tt == 16 && ntw == 1) CGS_GLU(1, 1);
+      else if (tt == 16) CGS_GLU(1, 2);
       else if (ntw == 1) CGS_GLU(2, 1);
       else CGS_GLU(2, 2);
 #undef CGS_GLU

@@ -34,6 +34,7 @@ def test_gather_rows_bit_exact(dtype, d, ff, K):
 
 
 @pytest.mark.parametrize("dtype,S,d,ff,rho", [("bf16", 50, 1024, 4096, 0.3), ("bf16", 16, 256, 1024, 1.0),
+                                              ("bf16", 50, 1024, 4096, 0.6),
                                               ("f32", 16, 256, 1024, 0.25), ("bf16", 70, 128, 200, 0.4),
                                               ("bf16", 50, 1024, 4096, 0.01)])
 def test_compact_equals_in_place_gather(dtype, S, d, ff, rho):
