@@ -21,9 +21,10 @@
 // rebuild), all with 8 waves except the smallest:
 //   M <= 64   64 x 128, 4 waves
 //   M <= 128  128 x 128
-//   M <= 256  256 x 128 (the 231-row Context Cache layer: one M tile, ff/64 =
-//             256 workgroups stream every weight row once, 4 weight tiles
-//             in flight per workgroup)
+//   M <= 256  128 x 256 gate/up tiles with 32 x 128 wave tiles (bf16 with
+//             d % 256 == 0; the 231-row Context Cache layer: 2 x 128 tiles,
+//             one round of 256 workgroups), 256 x 128 otherwise; the down
+//             projection keeps 128 x 128 tiles (2 x 16 tiles x 8 K splits)
 //   M > 256   192 x 256 (bf16 with d % 256 == 0: the 768-row rebuild is
 //             4 x 128 gate/up tiles and 4 x 8 x 8 down tiles, two and one
 //             rounds of 256 workgroups); else 256 x 128.
