@@ -636,8 +636,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graphs", action="store_true",
                     help="launch every kernel eagerly instead of replaying HIP graphs")
-    ap.add_argument("--rebuild-stream", choices=("side", "main"), default="main",
-                    help="run the entry rebuild on a side stream (overlapped) or in line")
+    ap.add_argument("--rebuild-stream", choices=("side", "overlap", "main"), default="main",
+                    help="run the entry rebuild in line (main), on a side stream as soon as its slot is free "
+                         "(side), or on a side stream after the call's context prefill with the next call's "
+                         "prefill waiting for it (overlap: the rebuild shares the GPU with the action path only)")
     ap.add_argument("--no-joint", action="store_true",
                     help="skip the separate joint token + neuron sparsity measurement")
     ap.add_argument("--no-sweeps", action="store_true",
@@ -669,11 +671,16 @@ def main():
     # call, or on a second side stream (then `serial` steps put it back in
     # line for comparison): it waits for the call's context prefill to release
     # the slot, and the prefill that next uses the slot waits for the rebuild.
+    # In the overlap schedule the rebuild starts after the call's prefill and
+    # the next call's prefill waits for it, so it shares the GPU with the
+    # latency-bound action path only.
     # All streams have the default priority.
     w.compact_weights = not args.no_compact
     main_s = torch.cuda.current_stream()
     gather_s = torch.cuda.Stream(device=dev)
-    side = torch.cuda.Stream(device=dev) if args.rebuild_stream == "side" else None
+    side = torch.cuda.Stream(device=dev) if args.rebuild_stream in ("side", "overlap") else None
+    overlap = args.rebuild_stream == "overlap"
+    rebuild_done = torch.cuda.Event()
     ctx_done = [torch.cuda.Event() for _ in range(SLOTS)]
     rebuilt = [torch.cuda.Event() for _ in range(SLOTS)]
     pending = [False] * SLOTS
@@ -697,6 +704,8 @@ def main():
         if pending[e]:
             main_s.wait_event(rebuilt[e])
             pending[e] = False
+        if overlap and not serial:
+            main_s.wait_event(rebuild_done)   # the previous call's rebuild ends before this prefill
         rec(0)
         w.ctx_prefill(i, e)
         rec(1)
@@ -707,12 +716,16 @@ def main():
             with torch.cuda.stream(side):
                 for _, _, s_ in entered:
                     side.wait_event(ctx_done[s_])
+                if overlap:
+                    side.wait_event(ctx_done[e])   # start once this call's prefill is done
                 rec(5)
                 w.rebuild(entered)
                 rec(6)
                 for _, _, s_ in entered:
                     rebuilt[s_].record(side)
                     pending[s_] = True
+                if overlap:
+                    rebuild_done.record(side)
         w.act_anchor()
         rec(2)
         main_s.wait_event(gathered)
