@@ -25,6 +25,7 @@ CGS_BF16, CGS_F32 = 0, 1
 CGS_SCORE_REL_RMS, CGS_SCORE_COSINE = 0, 1
 CGS_MASK_TOPK, CGS_MASK_COVERAGE = 0, 1
 CGS_DOWN_DF, CGS_DOWN_FD = 0, 1
+CGS_ERR_DATA = 6
 
 _KIND = {"rel_rms": CGS_SCORE_REL_RMS, "cosine": CGS_SCORE_COSINE}
 _MODE = {"topk": CGS_MASK_TOPK, "coverage": CGS_MASK_COVERAGE}
@@ -32,7 +33,12 @@ _LAYOUT = {"df": CGS_DOWN_DF, "fd": CGS_DOWN_FD}
 
 
 class CgsError(RuntimeError):
-    pass
+    """A libcgs call failed; ``status`` is its cgs_status code (0 when the
+    binding itself refused the call)."""
+
+    def __init__(self, msg: str, status: int = 0):
+        super().__init__(msg)
+        self.status = status
 
 
 class _Glue(ctypes.Structure):
@@ -72,6 +78,7 @@ _SIGS = {
     "cgs_ratio_to_count": (_i, [_d, _i]),
     "cgs_status_str": (ctypes.c_char_p, [_i]),
     "cgs_version": (_i, []),
+    "cgs_set_validate": (_i, [_i]),
     "cgs_ctx_select_workspace": (_sz, [_i, _i]),
     "ctx_select": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "ctx_select_from_keys": (_i, [_vp, _i, _i, _vp, _vp]),
@@ -123,7 +130,7 @@ def lib():
 
 def _check(status: int, what: str):
     if status != 0:
-        raise CgsError(f"{what}: {lib().cgs_status_str(status).decode()} (status {status})")
+        raise CgsError(f"{what}: {lib().cgs_status_str(status).decode()} (status {status})", status)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -184,6 +191,13 @@ class FFN:
                 raise CgsError("FFN weights must share one dtype")
         return _Ffn(self.d, self.ff, dt, _LAYOUT[self.layout], _ptr(self.w_gate),
                     _ptr(self.w_up), _ptr(self.w_down))
+
+
+def set_validate(on: bool) -> bool:
+    """Checked mode (debugging): calls first verify their documented device-data
+    preconditions and raise CgsError (status CGS_ERR_DATA) on a violation;
+    synchronises streams, so never while capturing.  Returns the previous setting."""
+    return bool(lib().cgs_set_validate(1 if on else 0))
 
 
 def ratio_to_count(rho: float, n: int) -> int:

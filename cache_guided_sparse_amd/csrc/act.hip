@@ -27,6 +27,7 @@
 #include "gemm.hpp"
 #include "glue.hpp"
 #include "profile.hpp"
+#include "validate.hpp"
 
 namespace cgs {
 namespace {
@@ -460,6 +461,7 @@ extern "C" int act_ffn_masked(const cgs_ffn* w, const void* x, int S, const int3
   if (S == 0) return CGS_OK;
   if (!ws || ws_bytes < cgs_act_ffn_masked_workspace(S, K, w->d, w->ff)) return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (const int st = validate_index(idx, K, w->ff, s)) return st;
   if (w->dtype == CGS_BF16)
     return act_t<uint16_t, false>(*w, static_cast<const uint16_t*>(x), S, idx, K, y_anchor, h_anchor,
                                   static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s);
@@ -480,6 +482,7 @@ extern "C" int act_ffn_masked_compact(const cgs_ffn* wc, const void* x, int S, c
   if (S == 0) return CGS_OK;
   if (!ws || ws_bytes < cgs_act_ffn_masked_workspace(S, K, wc->d, std::max(K, 1))) return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (const int st = validate_index(idx, K, INT32_MAX, s)) return st;
   if (wc->dtype == CGS_BF16)
     return act_t<uint16_t, true>(*wc, static_cast<const uint16_t*>(x), S, idx, K, y_anchor, h_anchor,
                                  static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s);
@@ -501,6 +504,9 @@ extern "C" int act_ffn_joint(const cgs_ffn* wc, const void* x, int S, const int3
   if (!ws || ws_bytes < cgs_act_ffn_masked_workspace(std::max(k, 1), K, wc->d, std::max(K, 1)))
     return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (const int st = validate_index(tok, k, S, s)) return st;
+  if (K > 0 && k > 0)
+    if (const int st = validate_index(idx, K, INT32_MAX, s)) return st;
   // with k = 0 every row is unselected: no partials (tok is not read)
   if (wc->dtype == CGS_BF16)
     return act_t<uint16_t, true>(*wc, static_cast<const uint16_t*>(x), k, idx, K, y_anchor, h_anchor,
@@ -519,6 +525,7 @@ extern "C" int act_gather_rows(const cgs_ffn* w, const int32_t* idx, int K, void
   if (K == 0) return CGS_OK;
   if (!idx || !wg_out || !wu_out || !wd_out) return CGS_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (const int st = validate_index(idx, K, w->ff, s)) return st;
   ProfScope ps("act.gather", s);
   const dim3 grid((3 * K + kThreads / 64 - 1) / (kThreads / 64));
   if (w->dtype == CGS_BF16)

@@ -19,6 +19,7 @@ extern "C" const char* cgs_status_str(int status) {
     case CGS_ERR_WORKSPACE: return "workspace too small";
     case CGS_ERR_UNSUPPORTED: return "unsupported dtype, layout or size";
     case CGS_ERR_LAUNCH: return "kernel launch failed";
+    case CGS_ERR_DATA: return "device data break a documented precondition";
     default: return "unknown status";
   }
 }

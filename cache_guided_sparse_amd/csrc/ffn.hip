@@ -34,6 +34,7 @@
 #include "gemm.hpp"
 #include "glue.hpp"
 #include "profile.hpp"
+#include "validate.hpp"
 
 namespace cgs {
 namespace {
@@ -450,6 +451,7 @@ extern "C" int ctx_ffn_recompute(const cgs_ffn* w, const void* x, const void* y_
   if (!ws || ws_bytes < cgs_ctx_ffn_recompute_workspace(k, P, w->d, w->ff, w->dtype))
     return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (const int st = validate_index(idx, k, P, s)) return st;
   if (w->dtype == CGS_BF16)
     return ctx_recompute_t<uint16_t>(*w, static_cast<const uint16_t*>(x),
                                      static_cast<const uint16_t*>(y_ref), idx, k, P,

@@ -21,6 +21,7 @@
 #include "block_select.hpp"
 #include "common.hpp"
 #include "profile.hpp"
+#include "validate.hpp"
 
 namespace cgs {
 namespace {
@@ -350,6 +351,13 @@ extern "C" int act_build_masks(const float* h_ref, int layers, int T, int S, con
   if (mode == CGS_MASK_COVERAGE && !(coverage >= 0.0 && coverage <= 1.0)) return CGS_ERR_SHAPE;
   if (!ws || ws_bytes < cgs_act_build_masks_workspace(layers, T, S, ff, d)) return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_on()) {
+    // fixed-point ranges of the contribution scores: |h| < 2^24, |w| < 2^5
+    int st = validate_abs(h_ref, static_cast<size_t>(layers) * T * ff * S, CGS_F32, 16777215.0f, s);
+    for (int l = 0; l < layers && st == CGS_OK; ++l)
+      st = validate_abs(w[l].w_down, static_cast<size_t>(ff) * d, dt, 31.999998f, s);
+    if (st != CGS_OK) return st;
+  }
   const MaskWs m = carve_mask(ws, layers, T, ff);
   LayerPtrs wdp{};
   // 16-byte weight loads when every row of every layer starts 16-byte aligned

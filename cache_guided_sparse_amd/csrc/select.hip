@@ -16,6 +16,7 @@
 #include "common.hpp"
 #include "profile.hpp"
 #include "score.hpp"
+#include "validate.hpp"
 
 namespace cgs {
 namespace {
@@ -130,6 +131,7 @@ extern "C" int ctx_select_from_keys(const double* keys, int P, int k, int32_t* i
   if (P == 0 || k == 0) return CGS_OK;
   if (!keys || !idx_out) return CGS_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (const int st = validate_finite_f64(keys, P, s)) return st;
   ProfScope ps("ctx.topk", s);
   hipLaunchKernelGGL(topk_values_kernel, dim3(1), dim3(kSelThreads), 0, s, keys, P, k, idx_out);
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
@@ -151,6 +153,11 @@ extern "C" int ctx_select(const void* x, const void* x_ref, int P, int d, int dt
   if (!x || !x_ref || (k > 0 && !idx_out)) return CGS_ERR_ARG;
   if (!ws || ws_bytes < cgs_ctx_select_workspace(P, d)) return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_on()) {  // fixed-point range of the score sums: |x|, |x_ref| <= 2^12
+    int st = validate_abs(x, static_cast<size_t>(P) * d, dtype, 4096.0f, s);
+    if (st == CGS_OK) st = validate_abs(x_ref, static_cast<size_t>(P) * d, dtype, 4096.0f, s);
+    if (st != CGS_OK) return st;
+  }
   uint64_t* okeys = static_cast<uint64_t*>(ws);
   // d * eps^2 in the 2^-24 fixed point, rounded up, at least 1 (eps = 1e-6)
   const long long floor_e = score_floor(d);

@@ -49,7 +49,8 @@ typedef enum {
   CGS_ERR_SHAPE = 2,        /* size or count out of range */
   CGS_ERR_WORKSPACE = 3,    /* ws too small or null while needed */
   CGS_ERR_UNSUPPORTED = 4,  /* dtype / layout / size the library does not handle */
-  CGS_ERR_LAUNCH = 5        /* a kernel launch failed */
+  CGS_ERR_LAUNCH = 5,       /* a kernel launch failed */
+  CGS_ERR_DATA = 6          /* device data break a documented precondition (checked mode only) */
 } cgs_status;
 
 typedef enum { CGS_BF16 = 0, CGS_F32 = 1 } cgs_dtype;
@@ -103,6 +104,17 @@ int cgs_ratio_to_count(double rho, int n);
 
 /* Static string for a cgs_status value. */
 const char* cgs_status_str(int status);
+
+/* Checked mode, for debugging callers (initially on iff the environment
+ * variable CGS_VALIDATE is set and not "0"): entry points that take index
+ * lists or values with a documented range first check them on the device
+ * (idx ascending, unique and in range; |x| <= 2^12 for the token score;
+ * |h| < 2^24 and |w| < 2^5 for contribution scores; finite keys), wait for
+ * the check on their stream and return CGS_ERR_DATA before launching
+ * anything else.  The mode synchronises streams and allocates one int per
+ * device on first use, so it must not be on while a stream is captured.
+ * Returns the previous setting. */
+int cgs_set_validate(int on);
 
 /* ABI version (major*100 + minor). */
 int cgs_version(void);
