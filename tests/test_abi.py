@@ -144,3 +144,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(cgs, "_lib", None)
     with pytest.raises(cgs.CgsError):
         cgs.lib()
+
+
+def test_checked_mode_switch_and_environment_default():
+    """cgs_set_validate returns the previous setting; the initial setting comes
+    from CGS_VALIDATE (read in a fresh process, no GPU call is made)."""
+    import os
+    import subprocess
+    import sys
+    L = cgs.lib()
+    prev = L.cgs_set_validate(1)
+    try:
+        assert L.cgs_set_validate(0) == 1
+        assert L.cgs_set_validate(0) == 0
+    finally:
+        L.cgs_set_validate(prev)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = "import cache_guided_sparse_amd as c; print(c.lib().cgs_set_validate(0))"
+    for env, want in (("1", "1"), ("0", "0"), (None, "0")):
+        e = dict(os.environ)
+        e.pop("CGS_VALIDATE", None)
+        if env is not None:
+            e["CGS_VALIDATE"] = env
+        out = subprocess.run([sys.executable, "-c", code], cwd=root, env=e, capture_output=True, text=True,
+                             timeout=300)
+        assert out.returncode == 0, out.stderr
+        assert out.stdout.strip().splitlines()[-1] == want
+    assert L.cgs_status_str(6) == b"device data break a documented precondition"
