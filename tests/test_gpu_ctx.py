@@ -55,6 +55,26 @@ def test_ragged_bf16(d, k):
     _check_full(w, x, y_ref, idx)
 
 
+@pytest.mark.parametrize("d", [256, 2048])
+def test_index_list_longer_than_the_staged_search(d):
+    """k > 4096 selected rows: the finish kernels search the index list in
+    global memory instead of LDS.  Copied rows bit for bit, a sample of
+    recomputed rows against the oracle."""
+    say("ctx long index list", d)
+    P, ff, k = 5000, 512, 4500
+    w = ffn_weights(4, 0, d, ff)
+    x = random_bf16(4, 0, "x", (P, d))
+    y_ref = random_bf16(4, 0, "y_ref", (P, d))
+    idx = np.sort(rng(4, k, "perm").permutation(P)[:k]).astype(np.int32)
+    y = bits(_recompute(w, x, y_ref, idx))
+    rec = np.zeros(P, dtype=bool)
+    rec[idx] = True
+    assert np.array_equal(y[~rec], y_ref[~rec])
+    sample = idx[np.linspace(0, k - 1, 24).astype(int)]
+    y_o = O.ffn_geglu(O.decode(x[sample], "bf16"), w)
+    assert_close(O.decode(y[sample], "bf16"), y_o, "sampled recomputed rows", out="bf16")
+
+
 def test_dense_equals_rebuild_layer():
     """k = P is the dense FFN: equal to one rebuild layer's output at the same input."""
     say("ctx dense vs rebuild")
