@@ -10,6 +10,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "common.hpp"
@@ -21,7 +22,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 int* g_flag[kMaxDevices] = {};
 std::mutex g_flag_mu;
-int g_validate = -1;  // -1: not read from the environment yet
+std::atomic<int> g_validate{-1};  // -1: not read from the environment yet
 
 // Sets *bad when idx[0..n) is not strictly ascending or leaves [0, limit).
 __global__ __launch_bounds__(256) void check_index_kernel(const int32_t* __restrict__ idx, int n, int limit,
@@ -81,11 +82,16 @@ int grid_for(size_t n) { return static_cast<int>(std::min<size_t>((n + 255) / 25
 }  // namespace
 
 bool validate_on() {
-  if (g_validate < 0) {
+  int v = g_validate.load(std::memory_order_relaxed);
+  if (v < 0) {
     const char* e = getenv("CGS_VALIDATE");
-    g_validate = (e && e[0] && e[0] != '0') ? 1 : 0;
+    int expect = -1;
+    // the first reader publishes the environment's setting unless a call of
+    // cgs_set_validate got there first
+    g_validate.compare_exchange_strong(expect, (e && e[0] && e[0] != '0') ? 1 : 0);
+    v = g_validate.load(std::memory_order_relaxed);
   }
-  return g_validate == 1;
+  return v == 1;
 }
 
 int validate_index(const int32_t* idx, int n, int limit, hipStream_t s) {
@@ -117,7 +123,6 @@ int validate_finite_f64(const double* a, int n, hipStream_t s) {
 }  // namespace cgs
 
 extern "C" int cgs_set_validate(int on) {
-  const int prev = cgs::validate_on() ? 1 : 0;
-  cgs::g_validate = on ? 1 : 0;
-  return prev;
+  cgs::validate_on();  // settle the environment default first
+  return cgs::g_validate.exchange(on ? 1 : 0) == 1 ? 1 : 0;
 }
