@@ -379,10 +379,11 @@ ActPlan plan_act(int S, int K, int d) {
 bool act_shape_ok(int d, int ff) { return d > 0 && ff > 0 && d % 128 == 0; }
 
 // S rows computed (rows tok[0..S) of S_all when tok is given, else all).
+// dense: the mask takes every neuron (profiling site names only).
 template <typename T, bool COMPACT>
 int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const float* ya,
           const float* ha, T* y_out, float* y_f32, float* h_out, const cgs_glue* gl, void* ws,
-          hipStream_t s, const int32_t* tok = nullptr, int S_all = -1) {
+          hipStream_t s, bool dense, const int32_t* tok = nullptr, int S_all = -1) {
   if (S_all < 0) S_all = S;
   const ActPlan p = plan_act(S, K, w.d);
   Carve cv(ws);
@@ -390,7 +391,7 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
   float* part = cv.take<float>(std::max<size_t>(p.part_elems, 1));
   if (K > 0 && S > 0) {
     {
-      ProfScope ps(K == w.ff && !COMPACT ? "act.glu.dense" : "act.glu.masked", s);
+      ProfScope ps(dense ? "act.glu.dense" : "act.glu.masked", s);
       const T* wgp = static_cast<const T*>(w.w_gate);
       const T* wup = static_cast<const T*>(w.w_up);
       // Masks of dense size with at most 64 tokens: one 64-token workgroup per
@@ -423,7 +424,7 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
 #undef CGS_GLU
     }
     if (!launch_ok()) return CGS_ERR_LAUNCH;
-    ProfScope ps(K == w.ff && !COMPACT ? "act.down.dense" : "act.down.masked", s);
+    ProfScope ps(dense ? "act.down.dense" : "act.down.masked", s);
     hipLaunchKernelGGL((act_down_kernel<T, COMPACT>), dim3(w.d / kCols, p.splits, p.S_pad / kTokDown), dim3(kThreads),
                        0, s, D, S, p.K_pad, idx, K, static_cast<const T*>(w.w_down), w.d,
                        p.steps_per_split, part);
@@ -462,11 +463,22 @@ extern "C" int act_ffn_masked(const cgs_ffn* w, const void* x, int S, const int3
   if (!ws || ws_bytes < cgs_act_ffn_masked_workspace(S, K, w->d, w->ff)) return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (const int st = validate_index(idx, K, w->ff, s)) return st;
+  // An ascending, duplicate-free list of ff neurons is 0 .. ff-1: the full
+  // weights are then the compact weights of the mask, and no kernel waits
+  // for an index before it can address a weight row (the list still
+  // addresses the h_anchor / h_out rows, off that chain).
+  if (K == w->ff) {
+    if (w->dtype == CGS_BF16)
+      return act_t<uint16_t, true>(*w, static_cast<const uint16_t*>(x), S, idx, K, y_anchor, h_anchor,
+                                   static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s, true);
+    return act_t<float, true>(*w, static_cast<const float*>(x), S, idx, K, y_anchor, h_anchor,
+                              static_cast<float*>(y_out), y_f32_out, h_out, glue, ws, s, true);
+  }
   if (w->dtype == CGS_BF16)
     return act_t<uint16_t, false>(*w, static_cast<const uint16_t*>(x), S, idx, K, y_anchor, h_anchor,
-                                  static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s);
+                                  static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s, false);
   return act_t<float, false>(*w, static_cast<const float*>(x), S, idx, K, y_anchor, h_anchor,
-                             static_cast<float*>(y_out), y_f32_out, h_out, glue, ws, s);
+                             static_cast<float*>(y_out), y_f32_out, h_out, glue, ws, s, false);
 }
 
 extern "C" int act_ffn_masked_compact(const cgs_ffn* wc, const void* x, int S, const int32_t* idx, int K,
@@ -485,9 +497,9 @@ extern "C" int act_ffn_masked_compact(const cgs_ffn* wc, const void* x, int S, c
   if (const int st = validate_index(idx, K, INT32_MAX, s)) return st;
   if (wc->dtype == CGS_BF16)
     return act_t<uint16_t, true>(*wc, static_cast<const uint16_t*>(x), S, idx, K, y_anchor, h_anchor,
-                                 static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s);
+                                 static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s, false);
   return act_t<float, true>(*wc, static_cast<const float*>(x), S, idx, K, y_anchor, h_anchor,
-                            static_cast<float*>(y_out), y_f32_out, h_out, glue, ws, s);
+                            static_cast<float*>(y_out), y_f32_out, h_out, glue, ws, s, false);
 }
 
 extern "C" int act_ffn_joint(const cgs_ffn* wc, const void* x, int S, const int32_t* tok, int k,
@@ -510,9 +522,9 @@ extern "C" int act_ffn_joint(const cgs_ffn* wc, const void* x, int S, const int3
   // with k = 0 every row is unselected: no partials (tok is not read)
   if (wc->dtype == CGS_BF16)
     return act_t<uint16_t, true>(*wc, static_cast<const uint16_t*>(x), k, idx, K, y_anchor, h_anchor,
-                                 static_cast<uint16_t*>(y_out), y_f32_out, nullptr, glue, ws, s, tok, S);
+                                 static_cast<uint16_t*>(y_out), y_f32_out, nullptr, glue, ws, s, false, tok, S);
   return act_t<float, true>(*wc, static_cast<const float*>(x), k, idx, K, y_anchor, h_anchor,
-                            static_cast<float*>(y_out), y_f32_out, nullptr, glue, ws, s, tok, S);
+                            static_cast<float*>(y_out), y_f32_out, nullptr, glue, ws, s, false, tok, S);
 }
 
 extern "C" int act_gather_rows(const cgs_ffn* w, const int32_t* idx, int K, void* wg_out, void* wu_out,
