@@ -40,7 +40,7 @@ def _setup(seed, S, d, ff, dtype="bf16", sigma=1.0):
 @pytest.mark.parametrize("dtype,S,d,ff", [("f32", 16, 256, 1024), ("bf16", 16, 256, 1024),
                                           ("bf16", 50, 1024, 4096), ("bf16", 70, 128, 200),
                                           ("bf16", 16, 256, 2048), ("bf16", 64, 128, 4096),
-                                          ("f32", 50, 256, 2048)])
+                                          ("f32", 50, 256, 2048), ("bf16", 100, 256, 2048)])
 def test_dense_anchor(dtype, S, d, ff):
     """Full mask, no anchors: the dense FFN, its fp32 output and every h row."""
     say("act dense anchor", dtype, S, d, ff)
@@ -55,7 +55,8 @@ def test_dense_anchor(dtype, S, d, ff):
 @pytest.mark.parametrize("dtype,S,d,ff,rho", [("f32", 16, 256, 1024, 0.25), ("f32", 16, 256, 1024, 1.0),
                                               ("bf16", 16, 256, 1024, 0.25), ("bf16", 50, 1024, 4096, 0.3),
                                               ("bf16", 50, 1024, 4096, 0.01), ("bf16", 70, 128, 200, 0.4),
-                                              ("bf16", 50, 1024, 4096, 0.6)])
+                                              ("bf16", 50, 1024, 4096, 0.6), ("bf16", 50, 1024, 4096, 1.0),
+                                              ("bf16", 100, 256, 2048, 1.0)])
 def test_masked_with_anchor(dtype, S, d, ff, rho):
     say("act masked", dtype, S, d, ff, rho)
     w, x, xa = _setup(11, S, d, ff, dtype)
