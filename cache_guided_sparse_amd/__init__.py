@@ -155,14 +155,27 @@ def _stream(stream):
 
 
 _ws_cache: dict = {}
+_ws_retired: list = []
 
 
-def workspace(nbytes: int, device, tag: str = "default") -> torch.Tensor:
-    """A cached device workspace of at least nbytes for (device, tag)."""
-    key = (str(device), tag)
+def workspace(nbytes: int, device, tag: str = "default", stream=None) -> torch.Tensor:
+    """A cached workspace of at least nbytes for (device, stream, tag).
+
+    Calls on one stream run in order and may share a buffer; calls on other
+    streams get their own, so concurrent streams never share scratch memory.
+    A buffer outgrown by a larger request is kept allocated for the life of
+    the process: a captured HIP graph, or a kernel still queued, may address
+    it.  Growth is geometric, so few buffers are ever retired."""
+    dev = torch.device(device)
+    skey = _stream(stream) if dev.type == "cuda" else 0
+    key = (str(dev), skey, tag)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        size = max(int(nbytes), 256)
+        if buf is not None:
+            _ws_retired.append(buf)
+            size = max(size, 2 * buf.numel())
+        buf = torch.empty(size, dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf
     return buf
 
@@ -211,7 +224,7 @@ def ctx_select(x, x_ref, k: int, kind: str = "rel_rms", idx_out=None, key_out=No
     if idx_out is None:
         idx_out = torch.empty(k, dtype=torch.int32, device=x.device)
     nbytes = lib().cgs_ctx_select_workspace(P, d)
-    ws = workspace(nbytes, x.device, "select") if ws is None else ws
+    ws = workspace(nbytes, x.device, "select", stream) if ws is None else ws
     _check(lib().ctx_select(_ptr(x), _ptr(x_ref), P, d, _dtype_code(x), int(k), _KIND[kind],
                             _ptr(idx_out), _ptr(key_out), _ptr(ws), ws.numel(), _stream(stream)),
            "ctx_select")
@@ -237,7 +250,7 @@ def ctx_ffn_recompute(w: FFN, x, y_ref, idx, y_out=None, glue=None, ws=None, str
         y_out = torch.empty_like(y_ref)
     c = w.cstruct()
     nbytes = lib().cgs_ctx_ffn_recompute_workspace(k, P, d, w.ff, c.dtype)
-    ws = workspace(nbytes, x.device, "ctx") if ws is None else ws
+    ws = workspace(nbytes, x.device, "ctx", stream) if ws is None else ws
     _check(lib().ctx_ffn_recompute(ctypes.byref(c), _ptr(x), _ptr(y_ref), _ptr(idx), k, P,
                                    _ptr(y_out), _glue(glue), _ptr(ws), ws.numel(), _stream(stream)),
            "ctx_ffn_recompute")
@@ -258,7 +271,7 @@ def act_build_mask(h_ref, w: FFN, mode: str = "topk", K: int = 0, coverage: floa
         count_out = torch.empty(1, dtype=torch.int32, device=dev)
     c = w.cstruct()
     nbytes = lib().cgs_act_build_mask_workspace(T, S, ff, w.d)
-    ws = workspace(nbytes, dev, "mask") if ws is None else ws
+    ws = workspace(nbytes, dev, "mask", stream) if ws is None else ws
     _check(lib().act_build_mask(_ptr(h_ref), T, S, ctypes.byref(c), _MODE[mode], int(K),
                                 float(coverage), _ptr(mask_out), _ptr(idx_out), _ptr(count_out),
                                 _ptr(ws), ws.numel(), _stream(stream)), "act_build_mask")
@@ -283,7 +296,7 @@ def act_build_masks(h_ref, layers, mode: str = "topk", K: int = 0, coverage: flo
         count_out = torch.empty(Lr, dtype=torch.int32, device=dev)
     arr = (_Ffn * Lr)(*[w.cstruct() for w in layers])
     nbytes = lib().cgs_act_build_masks_workspace(Lr, T, S, ff, layers[0].d)
-    ws = workspace(nbytes, dev, "mask") if ws is None else ws
+    ws = workspace(nbytes, dev, "mask", stream) if ws is None else ws
     _check(lib().act_build_masks(_ptr(h_ref), Lr, T, S, arr, _MODE[mode], int(K), float(coverage),
                                  _ptr(mask_out), _ptr(idx_out), _ptr(count_out), _ptr(ws), ws.numel(),
                                  _stream(stream)), "act_build_masks")
@@ -300,7 +313,7 @@ def act_ffn_masked(w: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=None, y_f
         y_out = torch.empty_like(x)
     c = w.cstruct()
     nbytes = lib().cgs_act_ffn_masked_workspace(S, K, d, w.ff)
-    ws = workspace(nbytes, x.device, "act") if ws is None else ws
+    ws = workspace(nbytes, x.device, "act", stream) if ws is None else ws
     _check(lib().act_ffn_masked(ctypes.byref(c), _ptr(x), S, _ptr(idx), K, _ptr(y_anchor),
                                 _ptr(h_anchor), _ptr(y_out), _ptr(y_f32_out), _ptr(h_out),
                                 _glue(glue), _ptr(ws), ws.numel(), _stream(stream)), "act_ffn_masked")
@@ -332,7 +345,7 @@ def act_ffn_masked_compact(wc: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=
         y_out = torch.empty_like(x)
     c = wc.cstruct()
     nbytes = lib().cgs_act_ffn_masked_workspace(S, K, d, max(K, 1))
-    ws = workspace(nbytes, x.device, "act") if ws is None else ws
+    ws = workspace(nbytes, x.device, "act", stream) if ws is None else ws
     _check(lib().act_ffn_masked_compact(ctypes.byref(c), _ptr(x), S, _ptr(idx), K, _ptr(y_anchor),
                                         _ptr(h_anchor), _ptr(y_out), _ptr(y_f32_out), _ptr(h_out),
                                         _glue(glue), _ptr(ws), ws.numel(), _stream(stream)),
@@ -363,7 +376,7 @@ def ret_select(query, refs, T: int, q_hist, r_hist, arm: int = -1, min_cos: floa
     if choice_out is None:
         choice_out = torch.empty(1, dtype=torch.int32, device=dev)
     nbytes = lib().cgs_ret_select_workspace(N, F)
-    ws = workspace(nbytes, dev, "retrieval") if ws is None else ws
+    ws = workspace(nbytes, dev, "retrieval", stream) if ws is None else ws
     rr = _Rerank(L, J, int(arm), float(min_cos))
     _check(lib().ret_select(_ptr(query), _ptr(refs), N, F, _dtype_code(query), int(T), _ptr(q_hist),
                             _ptr(r_hist), ctypes.byref(rr), _ptr(cos_out), _ptr(top_out), _ptr(dist_out),
@@ -434,7 +447,7 @@ def act_ffn_joint(wc: FFN, x, tok, idx, y_anchor, h_anchor=None, y_out=None, y_f
         y_out = torch.empty_like(x)
     c = wc.cstruct()
     nbytes = lib().cgs_act_ffn_masked_workspace(max(k, 1), K, d, max(K, 1))
-    ws = workspace(nbytes, x.device, "act") if ws is None else ws
+    ws = workspace(nbytes, x.device, "act", stream) if ws is None else ws
     _check(lib().act_ffn_joint(ctypes.byref(c), _ptr(x), S, _ptr(tok), k, _ptr(idx), K, _ptr(y_anchor),
                                _ptr(h_anchor), _ptr(y_out), _ptr(y_f32_out), _glue(glue), _ptr(ws), ws.numel(),
                                _stream(stream)), "act_ffn_joint")
@@ -452,7 +465,7 @@ def ref_rebuild_dense(layers, r0, x_ref_out=None, y_ref_out=None, ws=None, strea
     arr = (_Ffn * L)(*[w.cstruct() for w in layers])
     c0 = arr[0]
     nbytes = lib().cgs_ref_rebuild_dense_workspace(L, P, d, c0.ff, c0.dtype)
-    ws = workspace(nbytes, r0.device, "rebuild") if ws is None else ws
+    ws = workspace(nbytes, r0.device, "rebuild", stream) if ws is None else ws
     _check(lib().ref_rebuild_dense(arr, L, _ptr(r0), P, _ptr(x_ref_out), _ptr(y_ref_out),
                                    _ptr(ws), ws.numel(), _stream(stream)), "ref_rebuild_dense")
     return x_ref_out, y_ref_out

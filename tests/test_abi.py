@@ -171,3 +171,19 @@ def test_checked_mode_switch_and_environment_default():
         assert out.returncode == 0, out.stderr
         assert out.stdout.strip().splitlines()[-1] == want
     assert L.cgs_status_str(6) == b"device data break a documented precondition"
+
+
+def test_workspace_cache_reuses_grows_and_retires():
+    """The binding's workspace cache (host logic, on CPU tensors): one buffer
+    per (device, stream, op family); a larger request retires the old buffer
+    (kept alive) and at least doubles the size."""
+    cgs._ws_cache.clear()
+    cgs._ws_retired.clear()
+    a = cgs.workspace(1000, "cpu", "t")
+    assert a.numel() >= 1000 and cgs.workspace(500, "cpu", "t") is a
+    b = cgs.workspace(1500, "cpu", "t")
+    assert b is not a and b.numel() >= 2 * a.numel()
+    assert any(r is a for r in cgs._ws_retired)
+    assert cgs.workspace(10, "cpu", "other") is not b
+    cgs._ws_cache.clear()
+    cgs._ws_retired.clear()

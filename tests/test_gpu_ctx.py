@@ -190,3 +190,38 @@ def test_select_from_keys(P, k):
     idx = cgs.ctx_select_from_keys(torch.from_numpy(keys).to(dev()), k)
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), O.topk_ascending(keys, k))
+
+
+def test_concurrent_streams_keep_their_own_scratch():
+    """The same entry point on two streams at once (split-K partials in each
+    stream's own workspace): each result equals the same call run alone, bit
+    for bit."""
+    say("ctx two streams")
+    P, d, ff, k = 300, 256, 1024, 90
+    w = ffn_weights(5, 0, d, ff)
+    W = ffn_dev(w)
+    ins = []
+    for j in range(2):
+        x = to_dev(random_bf16(5, j, "x", (P, d)))
+        y_ref = to_dev(random_bf16(5, j, "y_ref", (P, d)))
+        idx = torch.from_numpy(np.sort(rng(5, j, "perm").permutation(P)[:k]).astype(np.int32)).to(dev())
+        ins.append((x, y_ref, idx))
+    alone = [cgs.ctx_ffn_recompute(W, *a) for a in ins]
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(3):
+        for st in streams:
+            st.wait_stream(main)
+        ys = []
+        for st, a in zip(streams, ins):
+            with torch.cuda.stream(st):
+                ys.append(cgs.ctx_ffn_recompute(W, *a))
+        for st in streams:
+            main.wait_stream(st)
+        outs.append(ys)
+    torch.cuda.synchronize()
+    for ys in outs:
+        for y, y0 in zip(ys, alone):
+            assert torch.equal(y, y0)
