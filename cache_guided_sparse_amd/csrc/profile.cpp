@@ -31,6 +31,9 @@ bool matches(const char* site) {
 
 void prof_begin(const char* site, hipStream_t s) {
   if (!matches(site)) return;
+  // a launch being captured into a graph is not timed (no event enters the graph)
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
   if (g_prof.used + 2 > g_prof.ev.size()) { g_prof.overflow = true; return; }
   hipEventRecord(g_prof.ev[g_prof.used], s);
   g_prof.site[g_prof.used / 2] = site;

@@ -1,9 +1,10 @@
 // Optional per-kernel timing with HIP events (used by benchmarks).
 //
 // While a profile is active, every launch whose site name contains the filter
-// string is bracketed by two events recorded on its own stream; the result
-// query waits for them and sums the elapsed times.  Inactive: one branch per
-// launch.  Not thread-safe: start, launch and query from one host thread.
+// string is bracketed by two events recorded on its own stream (unless the
+// stream is being captured); the result query waits for them and sums the
+// elapsed times.  Inactive: one branch per launch.  Not thread-safe: start,
+// launch and query from one host thread.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -289,11 +289,13 @@ int cgs_residual_rmsnorm(float* r, const float* r_in, const void* y, int y_dtype
  * ("" = all).  Site names: "ctx.score", "ctx.topk", "ctx.glu", "ctx.down",
  * "ctx.finish", "rebuild.norm", "rebuild.glu", "rebuild.down",
  * "rebuild.finish", "act.glu.dense", "act.glu.masked", "act.down.dense",
- * "act.down.masked", "act.finish", "mask.contrib", "mask.select",
- * "glue.rmsnorm".  Each matching launch is bracketed by two HIP events
- * recorded on its stream; at most max_launches are kept, later ones are
- * counted as overflow.  Process-wide host state: start, launch and query
- * from one thread, and not while a stream is being captured. */
+ * "act.down.masked", "act.finish", "act.gather", "mask.contrib",
+ * "mask.select", "ret.dot", "ret.select", "glue.rmsnorm".  Each matching
+ * launch is bracketed by two HIP events recorded on its stream; at most
+ * max_launches are kept, later ones are counted as overflow.  Launches on a
+ * stream that is being captured are not timed (a graph replay cannot be
+ * bracketed per launch).  Process-wide host state: start, launch and query
+ * from one thread. */
 int cgs_profile_start(const char* site_filter, int max_launches);
 
 /* Stop recording (the recorded launches stay queryable). */
