@@ -16,8 +16,8 @@ hot path once, with all inputs resident in HBM:
     ff 4096, 50 action tokens, 4 denoising steps in one group: step 0 is the
     dense anchor, steps 1-3 update it with the group mask (coverage 0.844 of
     the contribution score), reading the mask's weight rows from compact
-    buffers that a side stream fills while the context prefill runs (§4.1,
-    §5);
+    buffers that a side stream fills beside the anchor step (§4.1, §5; the
+    pages overlap the gathering with the prefill, which is an option here);
   * group mask construction (§5) for the 18 expert layers from the reference
     run's activations (offline on the pages, timed here);
   * one dense rebuild of a reference entry (§4.2): a 16-slot sliding working
@@ -644,6 +644,10 @@ def main():
                     help="skip the separate joint token + neuron sparsity measurement")
     ap.add_argument("--no-sweeps", action="store_true",
                     help="skip the recompute-ratio and neuron-ratio sweeps (reported beside the step)")
+    ap.add_argument("--gather-during", choices=("prefill", "anchor"), default="anchor",
+                    help="run the compact-weight gather beside the anchor step, after the context prefill "
+                         "(default: the rows are then still in the MALL when the masked steps read them), "
+                         "or beside the prefill, as the pages overlap it")
     ap.add_argument("--no-compact", action="store_true",
                     help="masked steps gather the mask's weight rows in place (no compact buffers)")
     ap.add_argument("--serial-steps", type=int, default=8,
@@ -665,9 +669,9 @@ def main():
 
     phases = ["ctx_prefill", "act_anchor", "act_masked", "mask_build", "rebuild", "gather", "retrieval"]
     # The compact weights of the group's masks are gathered on a side stream
-    # while the context prefill runs (the masked steps wait for them; the
-    # gather waits until the previous call's masked steps are done with the
-    # buffers).  The rebuild of the entry 16 calls ahead runs in line after the
+    # beside the anchor step, after the context prefill (or beside the
+    # prefill); the masked steps wait for them, and the gather waits until the
+    # previous call's masked steps are done with the buffers.  The rebuild of the entry 16 calls ahead runs in line after the
     # call, or on a second side stream (then `serial` steps put it back in
     # line for comparison): it waits for the call's context prefill to release
     # the slot, and the prefill that next uses the slot waits for the rebuild.
@@ -685,6 +689,7 @@ def main():
     rebuilt = [torch.cuda.Event() for _ in range(SLOTS)]
     pending = [False] * SLOTS
     gathered, masked_done = torch.cuda.Event(), torch.cuda.Event()
+    gather_after_prefill = args.gather_during == "anchor"
 
     def step(i, ev=None, serial=False):
         """One call.  ev: 11 timing events; 9-10 the retrieval, 0-4 the other
@@ -692,12 +697,18 @@ def main():
         that run them."""
         _, entered = w.advance(i)
         rec = (lambda q: ev[q].record()) if ev is not None else (lambda q: None)
-        gather_s.wait_event(masked_done)
-        with torch.cuda.stream(gather_s):
-            rec(7)
-            w.gather()
-            rec(8)
-            gathered.record(gather_s)
+
+        def launch_gather(after=None):
+            gather_s.wait_event(masked_done)
+            if after is not None:
+                gather_s.wait_event(after)
+            with torch.cuda.stream(gather_s):
+                rec(7)
+                w.gather()
+                rec(8)
+                gathered.record(gather_s)
+        if not gather_after_prefill:
+            launch_gather()
         rec(9)
         e = w.retrieve(i)   # the slot the retrieval picks drives the prefill
         rec(10)
@@ -710,6 +721,8 @@ def main():
         w.ctx_prefill(i, e)
         rec(1)
         ctx_done[e].record(main_s)
+        if gather_after_prefill:
+            launch_gather(ctx_done[e])
         if side is not None and not serial:
             # a slot taken by an entering entry was last read by an earlier
             # call's prefill; the next prefill that reads it waits for this
@@ -844,10 +857,10 @@ def main():
                                 "+ one 17-layer dense entry rebuild (host-to-device transfer of the compact "
                                 "entry included) for a 16-slot sliding window over an 800-entry pinned host "
                                 "repository; the masks' weight rows gathered into compact buffers on a side "
-                                "stream"),
+                                "stream beside the " + args.gather_during + " step"),
                    "tokens": P, "rho_p": RHO_P, "k": w.k, "coverage": COVERAGE,
                    "hip_graphs": not args.no_graphs, "compact_weights": not args.no_compact,
-                   "rebuild_stream": args.rebuild_stream,
+                   "rebuild_stream": args.rebuild_stream, "gather_during": args.gather_during,
                    "masked_neurons_mean": round(sum(Km) / len(Km), 1)},
         "roofline": roofline,
         "breakdown_ms": {p: round(v, 4) for p, v in ph.items()},
@@ -859,9 +872,13 @@ def main():
                             "GBps": round(masked_bytes / masked_step_ms / 1e6, 1),
                             "hbm_frac": round(masked_bytes / masked_step_ms / 1e6 / PEAK_HBM_GBPS, 4),
                             "ffn_kernels_ms": round(k_ffn_ms, 4),
-                            "note": "18 masked layers incl. residual/RMSNorm glue, inside the call: the first "
-                                    "masked step finds its compact weights evicted by the prefill's weight "
-                                    "stream, the next two MALL-warm (act_sweep has cold and warm apart)"},
+                            "note": "18 masked layers incl. residual/RMSNorm glue, inside the call: "
+                                    + ("the compact weights were gathered beside the anchor step, so the "
+                                       "masked steps find them in the MALL"
+                                       if args.gather_during == "anchor" else
+                                       "the first masked step finds its compact weights evicted by the "
+                                       "prefill's weight stream, the next two MALL-warm")
+                                    + " (act_sweep has cold and warm apart)"},
         "rebuild_ms_per_entry": round(ph["rebuild"] / max(1e-9, sum(w.entered[-args.steps:]) / args.steps), 4),
         "working_set": {"repository_entries": STORE, "repository_bytes": STORE * P * D * 2,
                         "slots": SLOTS, "window": {"episodes": 1, "lookahead": LOOKAHEAD},
