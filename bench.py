@@ -216,6 +216,8 @@ class World:
         self.h_ref = torch.empty(L_EXP, STEPS, FFE, S, dtype=torch.float32, device=dev)
         a_ref = (self.a0 + 0.33 * randn(S, DE)).contiguous()
         self._denoise_dense(a_ref, self.h_ref)
+        # Eq. 1's down-projection norms are a property of the weights: computed once
+        self.exp_norms = self.cgs.act_down_norms(self.exp)
         self.mask_words = torch.empty(L_EXP, (FFE + 63) // 64, dtype=torch.int64, device=dev)
         self.mask_idx = torch.empty(L_EXP, FFE, dtype=torch.int32, device=dev)
         self.mask_cnt = torch.empty(L_EXP, dtype=torch.int32, device=dev)
@@ -245,9 +247,10 @@ class World:
                                      x_out=self.xa)
 
     def build_masks(self, words, idx, cnt):
-        # the 18 layers' masks are independent: one batched build
-        self.cgs.act_build_masks(self.h_ref, self.exp, "coverage", coverage=COVERAGE,
-                                 mask_out=words, idx_out=idx, count_out=cnt)
+        # the 18 layers' masks are independent: one batched build, from the
+        # stored weight norms (only the reference activations are read)
+        self.cgs.act_build_masks(self.h_ref, None, "coverage", coverage=COVERAGE,
+                                 mask_out=words, idx_out=idx, count_out=cnt, norms=self.exp_norms)
 
     # --- one policy call -------------------------------------------------------
     # Between layers the residual add, the RMSNorm of the next layer's input and
@@ -516,7 +519,7 @@ def act_sweep(w, reps: int = 10) -> dict:
     cases = [("coverage_0.844", w.masks, w.cexp)]
     for rho in (0.2, 0.3, 0.4):
         K = cgs.ratio_to_count(rho, FFE)
-        _, mi, mc = cgs.act_build_masks(w.h_ref, w.exp, "topk", K=K)
+        _, mi, mc = cgs.act_build_masks(w.h_ref, None, "topk", K=K, norms=w.exp_norms)
         torch.cuda.synchronize()
         cnt = [int(c) for c in mc.tolist()]
         masks = [mi[l, : cnt[l]].contiguous() for l in range(L_EXP)]

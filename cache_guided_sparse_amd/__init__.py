@@ -88,6 +88,8 @@ _SIGS = {
     "act_build_mask": (_i, [_vp, _i, _i, _vp, _i, _i, _d, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cgs_act_build_masks_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "act_build_masks": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _d, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "act_down_norms": (_i, [_vp, _i, _vp, _vp]),
+    "act_build_masks_normed": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _i, _d, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cgs_act_ffn_masked_workspace": (_sz, [_i, _i, _i, _i]),
     "act_ffn_masked": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "act_ffn_masked_compact": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -278,14 +280,29 @@ def act_build_mask(h_ref, w: FFN, mode: str = "topk", K: int = 0, coverage: floa
     return mask_out, idx_out, count_out
 
 
+def act_down_norms(layers, out=None, stream=None):
+    """Eq. 1's down-projection norms of each layer's W_down (layout 'fd'),
+    float64 [layers][ff]; a property of the weights, computed once."""
+    Lr = len(layers)
+    ff = layers[0].ff
+    if out is None:
+        out = torch.empty((Lr, ff), dtype=torch.float64, device=layers[0].w_down.device)
+    arr = (_Ffn * Lr)(*[w.cstruct() for w in layers])
+    _check(lib().act_down_norms(arr, Lr, _ptr(out), _stream(stream)), "act_down_norms")
+    return out
+
+
 def act_build_masks(h_ref, layers, mode: str = "topk", K: int = 0, coverage: float = 0.0,
-                    mask_out=None, idx_out=None, count_out=None, ws=None, stream=None):
+                    mask_out=None, idx_out=None, count_out=None, ws=None, stream=None, norms=None):
     """Group masks of several layers at once: h_ref [layers][T][ff][S] float32,
     layers = list of FFN (layout 'fd'); returns (mask words [layers][words],
-    idx [layers][ff], count [layers])."""
+    idx [layers][ff], count [layers]).  With ``norms`` (act_down_norms of the
+    same weights) the weights are not read and ``layers`` may be None."""
     Lr, T, ff, S = h_ref.shape
-    if len(layers) != Lr:
+    if norms is None and (layers is None or len(layers) != Lr):
         raise CgsError("act_build_masks: one FFN per layer of h_ref")
+    if norms is not None and tuple(norms.shape) != (Lr, ff):
+        raise CgsError("act_build_masks: norms must be [layers][ff]")
     dev = h_ref.device
     words = (ff + 63) // 64
     if mask_out is None:
@@ -294,9 +311,16 @@ def act_build_masks(h_ref, layers, mode: str = "topk", K: int = 0, coverage: flo
         idx_out = torch.empty((Lr, ff), dtype=torch.int32, device=dev)
     if count_out is None:
         count_out = torch.empty(Lr, dtype=torch.int32, device=dev)
-    arr = (_Ffn * Lr)(*[w.cstruct() for w in layers])
-    nbytes = lib().cgs_act_build_masks_workspace(Lr, T, S, ff, layers[0].d)
+    nbytes = lib().cgs_act_build_masks_workspace(Lr, T, S, ff, 1)
     ws = workspace(nbytes, dev, "mask", stream) if ws is None else ws
+    if norms is not None:
+        if norms.dtype != torch.float64:
+            raise CgsError("act_build_masks: norms must be float64")
+        _check(lib().act_build_masks_normed(_ptr(h_ref), Lr, T, S, _ptr(norms), ff, _MODE[mode], int(K),
+                                            float(coverage), _ptr(mask_out), _ptr(idx_out), _ptr(count_out),
+                                            _ptr(ws), ws.numel(), _stream(stream)), "act_build_masks_normed")
+        return mask_out, idx_out, count_out
+    arr = (_Ffn * Lr)(*[w.cstruct() for w in layers])
     _check(lib().act_build_masks(_ptr(h_ref), Lr, T, S, arr, _MODE[mode], int(K), float(coverage),
                                  _ptr(mask_out), _ptr(idx_out), _ptr(count_out), _ptr(ws), ws.numel(),
                                  _stream(stream)), "act_build_masks")

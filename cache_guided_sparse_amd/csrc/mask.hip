@@ -57,30 +57,9 @@ struct LayerPtrs {
   const void* p[kMaxMaskLayers];
 };
 
-// blockIdx.y = layer: its h_ref block [T][ff][S], W_down and key slices.
+// The wave's share of B[n] = sum_j rint(2^40 w_nj^2) for the row wr (lane-strided).
 template <typename T>
-__global__ __launch_bounds__(256) void contrib_kernel(const float* __restrict__ h, int T_steps,
-                                                      int S, LayerPtrs wdp, int d, int ff,
-                                                      uint64_t* __restrict__ ckey,
-                                                      uint64_t* __restrict__ skey,
-                                                      double* __restrict__ sval, bool vec) {
-  const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= ff) return;
-  const int layer = blockIdx.y;
-  const T* wd = static_cast<const T*>(wdp.p[layer]);
-  h += static_cast<size_t>(layer) * T_steps * ff * S;
-  ckey += static_cast<size_t>(layer) * T_steps * ff;
-  skey += static_cast<size_t>(layer) * ff;
-  sval += static_cast<size_t>(layer) * ff;
-  const T* wr = wd + static_cast<size_t>(n) * d;
-  // The activations of up to kContribT steps (S <= 64: one per lane) are
-  // fetched before the weight row, so both loads are in flight together.
-  const bool fast_h = T_steps <= kContribT && S <= kWave;
-  float hv[kContribT];
-#pragma unroll
-  for (int t = 0; t < kContribT; ++t)
-    hv[t] = (fast_h && t < T_steps && lane < S) ? h[(static_cast<size_t>(t) * ff + n) * S + lane] : 0.f;
+__device__ __forceinline__ long long row_b(const T* __restrict__ wr, int d, int lane, bool vec) {
   long long b = 0;
   if (vec) {
     for (int j0 = lane * 8; j0 < d; j0 += 4 * kWave * 8) {
@@ -104,8 +83,53 @@ __global__ __launch_bounds__(256) void contrib_kernel(const float* __restrict__ 
       b += static_cast<long long>(rint((w * w) * kTwo40));
     }
   }
-  b = wave_sum_i64(b);
-  const double nrm = __dsqrt_rn(static_cast<double>(b));
+  return b;
+}
+
+// nrm[n] = sqrt(fl64(B[n])) (correctly rounded) of every neuron of every
+// layer; one wavefront per neuron, blockIdx.y = layer.
+template <typename T>
+__global__ __launch_bounds__(256) void down_norm_kernel(LayerPtrs wdp, int d, int ff,
+                                                        double* __restrict__ nrm_out, bool vec) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= ff) return;
+  const T* wr = static_cast<const T*>(wdp.p[blockIdx.y]) + static_cast<size_t>(n) * d;
+  const long long b = wave_sum_i64(row_b<T>(wr, d, lane, vec));
+  if (lane == 0) nrm_out[static_cast<size_t>(blockIdx.y) * ff + n] = __dsqrt_rn(static_cast<double>(b));
+}
+
+// blockIdx.y = layer: its h_ref block [T][ff][S], W_down and key slices.
+// pre (NULL: computed from W_down): nrm[layer][n] from down_norm_kernel.
+template <typename T>
+__global__ __launch_bounds__(256) void contrib_kernel(const float* __restrict__ h, int T_steps,
+                                                      int S, LayerPtrs wdp, const double* __restrict__ pre,
+                                                      int d, int ff, uint64_t* __restrict__ ckey,
+                                                      uint64_t* __restrict__ skey,
+                                                      double* __restrict__ sval, bool vec) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= ff) return;
+  const int layer = blockIdx.y;
+  h += static_cast<size_t>(layer) * T_steps * ff * S;
+  ckey += static_cast<size_t>(layer) * T_steps * ff;
+  skey += static_cast<size_t>(layer) * ff;
+  sval += static_cast<size_t>(layer) * ff;
+  // The activations of up to kContribT steps (S <= 64: one per lane) are
+  // fetched before the weight row (or the stored norm), so both loads are in
+  // flight together.
+  const bool fast_h = T_steps <= kContribT && S <= kWave;
+  float hv[kContribT];
+#pragma unroll
+  for (int t = 0; t < kContribT; ++t)
+    hv[t] = (fast_h && t < T_steps && lane < S) ? h[(static_cast<size_t>(t) * ff + n) * S + lane] : 0.f;
+  double nrm;
+  if (pre) {
+    nrm = pre[static_cast<size_t>(layer) * ff + n];
+  } else {
+    const T* wr = static_cast<const T*>(wdp.p[layer]) + static_cast<size_t>(n) * d;
+    nrm = __dsqrt_rn(static_cast<double>(wave_sum_i64(row_b<T>(wr, d, lane, vec))));
+  }
   long long atot = 0;
   for (int t = 0; t < T_steps; ++t) {
     long long a = 0;
@@ -333,48 +357,59 @@ extern "C" size_t cgs_act_build_mask_workspace(int T, int S, int ff, int d) {
   return cgs_act_build_masks_workspace(1, T, S, ff, d);
 }
 
-extern "C" int act_build_masks(const float* h_ref, int layers, int T, int S, const cgs_ffn* w, int mode,
-                               int K, double coverage, uint64_t* mask_out, int32_t* idx_out,
-                               int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
-  if (!h_ref || !w || !mask_out || !idx_out || !count_out) return CGS_ERR_ARG;
+namespace {
+
+// Shape checks shared by the weight-based and the norm-based builds.
+int mask_shape_status(int layers, int T, int S, int ff, int mode, int K, double coverage) {
   if (layers <= 0 || layers > kMaxMaskLayers) return CGS_ERR_SHAPE;
-  for (int l = 0; l < layers; ++l)
-    if (!w[l].w_down || !valid_dtype(w[l].dtype) || w[l].down_layout != CGS_DOWN_FD) return CGS_ERR_ARG;
   if (mode != CGS_MASK_TOPK && mode != CGS_MASK_COVERAGE) return CGS_ERR_ARG;
-  const int ff = w[0].ff, d = w[0].d, dt = w[0].dtype;
-  for (int l = 1; l < layers; ++l)
-    if (w[l].ff != ff || w[l].d != d || w[l].dtype != dt) return CGS_ERR_SHAPE;
-  if (T <= 0 || S <= 0 || ff <= 0 || d <= 0 || d > 4096 || ff > 65536 ||
-      static_cast<long long>(S) * T > (1 << 14))
+  if (T <= 0 || S <= 0 || ff <= 0 || ff > 65536 || static_cast<long long>(S) * T > (1 << 14))
     return CGS_ERR_SHAPE;
   if (mode == CGS_MASK_TOPK && (K < 0 || K > ff)) return CGS_ERR_SHAPE;
   if (mode == CGS_MASK_COVERAGE && !(coverage >= 0.0 && coverage <= 1.0)) return CGS_ERR_SHAPE;
-  if (!ws || ws_bytes < cgs_act_build_masks_workspace(layers, T, S, ff, d)) return CGS_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (validate_on()) {
-    // fixed-point ranges of the contribution scores: |h| < 2^24, |w| < 2^5
-    int st = validate_abs(h_ref, static_cast<size_t>(layers) * T * ff * S, CGS_F32, 16777215.0f, s);
-    for (int l = 0; l < layers && st == CGS_OK; ++l)
-      st = validate_abs(w[l].w_down, static_cast<size_t>(ff) * d, dt, 31.999998f, s);
-    if (st != CGS_OK) return st;
-  }
-  const MaskWs m = carve_mask(ws, layers, T, ff);
-  LayerPtrs wdp{};
-  // 16-byte weight loads when every row of every layer starts 16-byte aligned
-  bool vec = d % 8 == 0 && (static_cast<size_t>(d) * elem_bytes(dt)) % 16 == 0;
+  return CGS_OK;
+}
+
+// W_down of every layer (FD layout, one shape and dtype); sets *vec when
+// 16-byte row loads are possible.
+int down_layers(const cgs_ffn* w, int layers, LayerPtrs* wdp, bool* vec) {
+  for (int l = 0; l < layers; ++l)
+    if (!w[l].w_down || !valid_dtype(w[l].dtype) || w[l].down_layout != CGS_DOWN_FD) return CGS_ERR_ARG;
+  const int ff = w[0].ff, d = w[0].d, dt = w[0].dtype;
+  for (int l = 1; l < layers; ++l)
+    if (w[l].ff != ff || w[l].d != d || w[l].dtype != dt) return CGS_ERR_SHAPE;
+  if (d <= 0 || d > 4096 || ff <= 0 || ff > 65536) return CGS_ERR_SHAPE;
+  *vec = d % 8 == 0 && (static_cast<size_t>(d) * elem_bytes(dt)) % 16 == 0;
   for (int l = 0; l < layers; ++l) {
-    wdp.p[l] = w[l].w_down;
-    vec = vec && reinterpret_cast<uintptr_t>(w[l].w_down) % 16 == 0;
+    wdp->p[l] = w[l].w_down;
+    *vec = *vec && reinterpret_cast<uintptr_t>(w[l].w_down) % 16 == 0;
   }
+  return CGS_OK;
+}
+
+int validate_down(const cgs_ffn* w, int layers, hipStream_t s) {
+  // fixed-point range of the weight norms: |w| < 2^5
+  int st = CGS_OK;
+  for (int l = 0; l < layers && st == CGS_OK; ++l)
+    st = validate_abs(w[l].w_down, static_cast<size_t>(w[l].ff) * w[l].d, w[l].dtype, 31.999998f, s);
+  return st;
+}
+
+// Contribution keys (from W_down, or from stored norms when pre is given),
+// then the per-layer selection.
+int build_masks(const float* h_ref, int layers, int T, int S, const LayerPtrs& wdp, const double* pre, int d,
+                int ff, int dt, bool vec, int mode, int K, double coverage, uint64_t* mask_out, int32_t* idx_out,
+                int32_t* count_out, void* ws, hipStream_t s) {
+  const MaskWs m = carve_mask(ws, layers, T, ff);
   const dim3 grid((ff + 3) / 4, layers), block(256);
   {
-  ProfScope ps("mask.contrib", s);
-  if (dt == CGS_BF16)
-    hipLaunchKernelGGL((contrib_kernel<uint16_t>), grid, block, 0, s, h_ref, T, S, wdp, d, ff, m.ckey,
-                       m.skey, m.sval, vec);
-  else
-    hipLaunchKernelGGL((contrib_kernel<float>), grid, block, 0, s, h_ref, T, S, wdp, d, ff, m.ckey,
-                       m.skey, m.sval, vec);
+    ProfScope ps("mask.contrib", s);
+    if (dt == CGS_F32)
+      hipLaunchKernelGGL((contrib_kernel<float>), grid, block, 0, s, h_ref, T, S, wdp, pre, d, ff, m.ckey,
+                         m.skey, m.sval, vec);
+    else
+      hipLaunchKernelGGL((contrib_kernel<uint16_t>), grid, block, 0, s, h_ref, T, S, wdp, pre, d, ff, m.ckey,
+                         m.skey, m.sval, vec);
   }
   if (!launch_ok()) return CGS_ERR_LAUNCH;
   const int q_bits = 61 - bit_length(static_cast<unsigned>(ff - 1));
@@ -382,6 +417,65 @@ extern "C" int act_build_masks(const float* h_ref, int layers, int T, int S, con
   hipLaunchKernelGGL(mask_select_kernel, dim3(layers), dim3(kSelThreads), 0, s, m.ckey, m.skey, m.sval,
                      T, ff, mode, K, coverage, q_bits, m.uni, m.flag, mask_out, idx_out, count_out);
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int act_build_masks(const float* h_ref, int layers, int T, int S, const cgs_ffn* w, int mode,
+                               int K, double coverage, uint64_t* mask_out, int32_t* idx_out,
+                               int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!h_ref || !w || !mask_out || !idx_out || !count_out) return CGS_ERR_ARG;
+  if (layers <= 0 || layers > kMaxMaskLayers) return CGS_ERR_SHAPE;
+  LayerPtrs wdp{};
+  bool vec = false;
+  if (const int st = down_layers(w, layers, &wdp, &vec)) return st;
+  const int ff = w[0].ff, d = w[0].d;
+  if (const int st = mask_shape_status(layers, T, S, ff, mode, K, coverage)) return st;
+  if (!ws || ws_bytes < cgs_act_build_masks_workspace(layers, T, S, ff, d)) return CGS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_on()) {
+    // fixed-point range of the activation sums: |h| < 2^24
+    int st = validate_abs(h_ref, static_cast<size_t>(layers) * T * ff * S, CGS_F32, 16777215.0f, s);
+    if (st == CGS_OK) st = validate_down(w, layers, s);
+    if (st != CGS_OK) return st;
+  }
+  return build_masks(h_ref, layers, T, S, wdp, nullptr, d, ff, w[0].dtype, vec, mode, K, coverage, mask_out,
+                     idx_out, count_out, ws, s);
+}
+
+extern "C" int act_down_norms(const cgs_ffn* w, int layers, double* nrm_out, void* stream) {
+  if (!w || !nrm_out) return CGS_ERR_ARG;
+  if (layers <= 0 || layers > kMaxMaskLayers) return CGS_ERR_SHAPE;
+  LayerPtrs wdp{};
+  bool vec = false;
+  if (const int st = down_layers(w, layers, &wdp, &vec)) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_on())
+    if (const int st = validate_down(w, layers, s)) return st;
+  const int ff = w[0].ff, d = w[0].d;
+  const dim3 grid((ff + 3) / 4, layers), block(256);
+  ProfScope ps("mask.norms", s);
+  if (w[0].dtype == CGS_F32)
+    hipLaunchKernelGGL((down_norm_kernel<float>), grid, block, 0, s, wdp, d, ff, nrm_out, vec);
+  else
+    hipLaunchKernelGGL((down_norm_kernel<uint16_t>), grid, block, 0, s, wdp, d, ff, nrm_out, vec);
+  return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
+}
+
+extern "C" int act_build_masks_normed(const float* h_ref, int layers, int T, int S, const double* nrm, int ff,
+                                      int mode, int K, double coverage, uint64_t* mask_out, int32_t* idx_out,
+                                      int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!h_ref || !nrm || !mask_out || !idx_out || !count_out) return CGS_ERR_ARG;
+  if (const int st = mask_shape_status(layers, T, S, ff, mode, K, coverage)) return st;
+  if (!ws || ws_bytes < cgs_act_build_masks_workspace(layers, T, S, ff, 1)) return CGS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_on()) {
+    int st = validate_abs(h_ref, static_cast<size_t>(layers) * T * ff * S, CGS_F32, 16777215.0f, s);
+    if (st == CGS_OK) st = validate_finite_f64(nrm, layers * ff, s, true);
+    if (st != CGS_OK) return st;
+  }
+  return build_masks(h_ref, layers, T, S, LayerPtrs{}, nrm, 0, ff, CGS_BF16, false, mode, K, coverage,
+                     mask_out, idx_out, count_out, ws, s);
 }
 
 extern "C" int act_build_mask(const float* h_ref, int T, int S, const cgs_ffn* w, int mode, int K,

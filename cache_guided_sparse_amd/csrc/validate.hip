@@ -46,9 +46,10 @@ __global__ __launch_bounds__(256) void check_abs_kernel(const T* __restrict__ a,
 
 __global__ void zero_flag_kernel(int* flag) { *flag = 0; }
 
-__global__ void check_finite_f64_kernel(const double* __restrict__ a, int n, int* __restrict__ bad) {
+// Sets *bad when an element of a[0..n) is not finite (or, with nonneg, negative).
+__global__ void check_finite_f64_kernel(const double* __restrict__ a, int n, int nonneg, int* __restrict__ bad) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-    if (!isfinite(a[i])) atomicOr(bad, 1);
+    if (!isfinite(a[i]) || (nonneg && a[i] < 0.0)) atomicOr(bad, 1);
 }
 
 // The calling thread's device flag (allocated once per device).
@@ -113,10 +114,10 @@ int validate_abs(const void* a, size_t n, int dtype, float bound, hipStream_t s)
   });
 }
 
-int validate_finite_f64(const double* a, int n, hipStream_t s) {
+int validate_finite_f64(const double* a, int n, hipStream_t s, bool nonneg) {
   if (!validate_on() || n <= 0 || !a) return CGS_OK;
   return run_check(s, [&](int* flag) {
-    hipLaunchKernelGGL(check_finite_f64_kernel, dim3(grid_for(n)), dim3(256), 0, s, a, n, flag);
+    hipLaunchKernelGGL(check_finite_f64_kernel, dim3(grid_for(n)), dim3(256), 0, s, a, n, nonneg ? 1 : 0, flag);
   });
 }
 

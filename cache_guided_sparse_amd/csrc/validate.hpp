@@ -13,7 +13,7 @@ bool validate_on();
 int validate_index(const int32_t* idx, int n, int limit, hipStream_t s);
 // a[0..n) finite with |a| <= bound (dtype CGS_BF16 or CGS_F32).
 int validate_abs(const void* a, size_t n, int dtype, float bound, hipStream_t s);
-// a[0..n) finite.
-int validate_finite_f64(const double* a, int n, hipStream_t s);
+// a[0..n) finite (and, with nonneg, not negative).
+int validate_finite_f64(const double* a, int n, hipStream_t s, bool nonneg = false);
 
 }  // namespace cgs

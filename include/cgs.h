@@ -204,6 +204,25 @@ int act_build_masks(const float* h_ref, int layers, int T, int S, const cgs_ffn*
                     double coverage, uint64_t* mask_out, int32_t* idx_out, int32_t* count_out,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* The down-projection norms of Eq. 1 (§3.4), a property of the weights:
+ * nrm_out[l][n] = sqrt(fl64(B[n])) of layer l, correctly rounded, with
+ * B[n] = sum_j rint(2^40 fl64(w_nj^2)) (the exact fixed-point sum that
+ * act_build_mask forms).  w: host array of `layers` (1 .. 64) FFNs with
+ * equal d (<= 4096), ff (<= 65536) and dtype, CGS_DOWN_FD; only w_down is
+ * read.  nrm_out: [layers][ff] double (device).  Precondition |w| < 2^5
+ * (checked only in checked mode). */
+int act_down_norms(const cgs_ffn* w, int layers, double* nrm_out, void* stream);
+
+/* act_build_masks with the weight norms given (nrm: [layers][ff] as
+ * act_down_norms writes them, finite and non-negative), so that only h_ref
+ * is read: the group's masks, indices and counts are bit for bit those of
+ * act_build_masks over the weights the norms came from.  The workspace is
+ * cgs_act_build_masks_workspace(layers, T, S, ff, d) for any d.  Errors as
+ * act_build_masks. */
+int act_build_masks_normed(const float* h_ref, int layers, int T, int S, const double* nrm, int ff,
+                           int mode, int K, double coverage, uint64_t* mask_out, int32_t* idx_out,
+                           int32_t* count_out, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for act_ffn_masked with S tokens and K masked neurons. */
 size_t cgs_act_ffn_masked_workspace(int S, int K, int d, int ff);
 
@@ -290,7 +309,7 @@ int cgs_residual_rmsnorm(float* r, const float* r_in, const void* y, int y_dtype
  * "ctx.finish", "rebuild.norm", "rebuild.glu", "rebuild.down",
  * "rebuild.finish", "act.glu.dense", "act.glu.masked", "act.down.dense",
  * "act.down.masked", "act.finish", "act.gather", "mask.contrib",
- * "mask.select", "ret.dot", "ret.select", "glue.rmsnorm".  Each matching
+ * "mask.select", "mask.norms", "ret.dot", "ret.select", "glue.rmsnorm".  Each matching
  * launch is bracketed by two HIP events recorded on its stream; at most
  * max_launches are kept, later ones are counted as overflow.  Launches on a
  * stream that is being captured are not timed (a graph replay cannot be

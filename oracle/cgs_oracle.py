@@ -42,7 +42,7 @@ __all__ = [
     "EPS", "decode", "round_to_bf16_bits", "round_act", "ratio_to_count",
     "score_floor", "ctx_score_keys", "topk_ascending", "ctx_select",
     "gelu_tanh", "ffn_geglu", "ctx_ffn_recompute", "contribution_scores",
-    "mask_topk", "coverage_exponent_bits", "mask_coverage", "act_build_mask", "mask_bits",
+    "down_weight_norms", "mask_topk", "coverage_exponent_bits", "mask_coverage", "act_build_mask", "mask_bits",
     "act_ffn_masked", "act_ffn_joint", "rms_norm", "rebuild_dense", "entry_bytes",
 ]
 
@@ -215,6 +215,15 @@ def ctx_ffn_recompute(w: dict, x, y_ref, idx):
 # --------------------------------------------------------------------------
 # Action Cache: contribution score (Eq. 1) and group masks (§5)
 # --------------------------------------------------------------------------
+def down_weight_norms(w: dict) -> np.ndarray:
+    """Paper §3.4, Eq. 1: the factor ||W_n||_2 of every neuron n, in fixed point:
+      B[n] = sum_j rint(2^40 fl64(w_nj^2)) (int64),  nrm[n] = sqrt(fl64(B[n]))
+    (correctly rounded; the common factor 2^20 is immaterial).  Returns nrm [ff] fp64."""
+    _, _, wd = _weights64(w)
+    B = _fixed_sum(wd * wd, F_W)
+    return np.sqrt(B.astype(np.float64))
+
+
 def contribution_scores(h_ref, w: dict):
     """Paper §3.4, Eq. 1: c_{t,n} = (sum_r |h_{t,r,n}|) * ||W_n||_2, in fixed point.
 
@@ -229,10 +238,8 @@ def contribution_scores(h_ref, w: dict):
     h = np.asarray(h_ref, dtype=np.float32).astype(np.float64)
     if h.ndim != 3:
         raise ValueError("h_ref must be [T][ff][S]")
-    _, _, wd = _weights64(w)
     A = _fixed_sum(np.abs(h), F_ACT)                     # [T][ff]
-    B = _fixed_sum(wd * wd, F_W)                         # [ff]
-    nrm = np.sqrt(B.astype(np.float64))
+    nrm = down_weight_norms(w)                           # [ff]
     c = A.astype(np.float64) * nrm[None, :]
     s = A.sum(axis=0).astype(np.float64) * nrm
     return c, s

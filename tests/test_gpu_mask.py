@@ -113,3 +113,38 @@ def test_batched_layers_equal_single_layer_builds(mode, ff, d, S, T):
         assert cnt[l] == gc and np.array_equal(idx[l], gi) and np.array_equal(m[l], gm), f"layer {l}"
         oi, om = O.act_build_mask(hs[l], ws[l], mode, K=K, coverage=cov)
         assert np.array_equal(gi[:gc], oi) and np.array_equal(gm, om), f"layer {l} vs oracle"
+
+
+@pytest.mark.parametrize("dtype,ff,d", [("bf16", 4096, 1024), ("bf16", 77, 100), ("f32", 300, 256)])
+def test_down_norms_match_oracle(dtype, ff, d):
+    """act_down_norms: Eq. 1's weight norms of every layer, bit for bit."""
+    say("mask norms", dtype, ff, d)
+    ws = [ffn_weights(120 + l, 0, d, ff, dtype=dtype, down_layout="fd", down_lognormal_sigma=1.5)
+          for l in range(3)]
+    nrm = cgs.act_down_norms([ffn_dev(w) for w in ws])
+    torch.cuda.synchronize()
+    got = nrm.cpu().numpy()
+    for l, w in enumerate(ws):
+        assert np.array_equal(got[l].view(np.uint64), O.down_weight_norms(w).view(np.uint64)), f"layer {l}"
+
+
+@pytest.mark.parametrize("mode,K,cov", [("topk", 1229, 0.0), ("coverage", 0, 0.844), ("coverage", 0, 1.0)])
+def test_masks_from_stored_norms_equal_masks_from_weights(mode, K, cov):
+    """act_build_masks_normed reads only h_ref: its masks, indices and counts
+    equal the weight-based build's (and so the oracle's) bit for bit."""
+    say("mask normed", mode, K, cov)
+    L, T, ff, S, d = 4, 4, 4096, 50, 1024
+    ws = [ffn_weights(130 + l, 0, d, ff, down_layout="fd", down_lognormal_sigma=1.5) for l in range(L)]
+    Ws = [ffn_dev(w) for w in ws]
+    h = np.stack([synthetic_h_ref(130 + l, 0, T, ff, S, neuron_sigma=0.5) for l in range(L)])
+    hd = to_dev(np.ascontiguousarray(h, dtype=np.float32), "f32")
+    a = cgs.act_build_masks(hd, Ws, mode, K=K, coverage=cov)
+    b = cgs.act_build_masks(hd, None, mode, K=K, coverage=cov, norms=cgs.act_down_norms(Ws))
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    for l in range(L):
+        oi, om = O.act_build_mask(h[l], ws[l], mode, K=K, coverage=cov)
+        c = int(b[2][l].item())
+        assert c == len(oi) and np.array_equal(b[1][l, :c].cpu().numpy(), oi)
+        assert np.array_equal(b[0][l].cpu().numpy().view(np.uint64), om)

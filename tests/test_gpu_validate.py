@@ -114,3 +114,18 @@ def test_mask_value_ranges(checked):
     Wb = cgs.FFN(W.w_gate, W.w_up, wd, "fd")
     _data_error(lambda: cgs.act_build_mask(h, Wb, "coverage", coverage=0.5))
     torch.cuda.synchronize()
+
+
+def test_stored_norms_must_be_finite_and_non_negative(checked):
+    say("validate norms")
+    T, ff, S, d = 2, 256, 8, 128
+    W = ffn_dev(ffn_weights(74, 0, d, ff, down_layout="fd"))
+    h = to_dev(synthetic_h_ref(74, 0, T, ff, S), "f32")[None]
+    nrm = cgs.act_down_norms([W])
+    cgs.act_build_masks(h, None, "topk", K=32, norms=nrm)
+    bad = nrm.clone()
+    bad[0, 9] = -1.0
+    _data_error(lambda: cgs.act_build_masks(h, None, "topk", K=32, norms=bad))
+    bad[0, 9] = float("inf")
+    _data_error(lambda: cgs.act_build_masks(h, None, "topk", K=32, norms=bad))
+    torch.cuda.synchronize()

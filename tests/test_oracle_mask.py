@@ -148,3 +148,32 @@ def test_mask_bits_layout():
     assert words.tolist() == [1 | (1 << 63), 1, 4]
     with pytest.raises(ValueError):
         O.mask_coverage(np.ones(3), 1.5)
+
+
+def test_down_weight_norms_against_the_plain_norm_and_closed_forms():
+    """||W_n||_2 of Eq. 1 scaled by the fixed point's 2^20: the plain
+    Euclidean norm (torch) to rounding; a row of d copies of 2^-5 gives
+    B = d 2^30 exactly, so nrm = 2^15 sqrt(d) (= 2^20 at d = 1024); a zero row
+    gives 0; and a pure-Python brute force of the fixed-point sum on a few
+    rows is matched exactly."""
+    w, _ = _setup(d=64)
+    nrm = O.down_weight_norms(w)
+    wd = torch.from_numpy(O.decode(w["w_down"], "bf16"))
+    np.testing.assert_allclose(nrm / 2.0 ** 20, torch.linalg.vector_norm(wd, dim=1).numpy(), rtol=1e-6)
+    from cgs_inputs import f32_to_bf16_bits
+    d = 1024
+    rows = np.zeros((3, d), dtype=np.float32)
+    rows[0] = 2.0 ** -5
+    rows[2, ::7] = -0.75
+    wc = {"d": d, "ff": 3, "dtype": "bf16", "down_layout": "fd",
+          "w_gate": f32_to_bf16_bits(np.zeros((3, d), np.float32)),
+          "w_up": f32_to_bf16_bits(np.zeros((3, d), np.float32)),
+          "w_down": f32_to_bf16_bits(rows)}
+    got = O.down_weight_norms(wc)
+    assert got[0] == 2.0 ** 20 and got[1] == 0.0
+    b2 = sum(round(float(v) * float(v) * 2.0 ** 40) for v in rows[2])
+    assert got[2] == float(np.sqrt(np.float64(b2)))
+    # the contribution scores use exactly these norms
+    h = synthetic_h_ref(3, 0, 2, 3, 4)
+    c, _ = O.contribution_scores(h, wc)
+    assert c[0, 1] == 0.0
