@@ -128,12 +128,15 @@ def test_down_norms_match_oracle(dtype, ff, d):
         assert np.array_equal(got[l].view(np.uint64), O.down_weight_norms(w).view(np.uint64)), f"layer {l}"
 
 
-@pytest.mark.parametrize("mode,K,cov", [("topk", 1229, 0.0), ("coverage", 0, 0.844), ("coverage", 0, 1.0)])
-def test_masks_from_stored_norms_equal_masks_from_weights(mode, K, cov):
+@pytest.mark.parametrize("mode,K,cov,L,T,ff,S,d", [
+    ("topk", 1229, 0.0, 4, 4, 4096, 50, 1024), ("coverage", 0, 0.844, 4, 4, 4096, 50, 1024),
+    ("coverage", 0, 1.0, 4, 4, 4096, 50, 1024), ("topk", 20, 0.0, 3, 3, 77, 7, 100),
+    ("coverage", 0, 0.5, 2, 2, 130, 100, 128), ("topk", 9, 0.0, 2, 9, 40, 5, 64)])
+def test_masks_from_stored_norms_equal_masks_from_weights(mode, K, cov, L, T, ff, S, d):
     """act_build_masks_normed reads only h_ref: its masks, indices and counts
-    equal the weight-based build's (and so the oracle's) bit for bit."""
-    say("mask normed", mode, K, cov)
-    L, T, ff, S, d = 4, 4, 4096, 50, 1024
+    equal the weight-based build's (and so the oracle's) bit for bit (ragged
+    neuron counts; more than 64 tokens or 8 steps take the general kernel)."""
+    say("mask normed", mode, K, cov, L, T, ff, S, d)
     ws = [ffn_weights(130 + l, 0, d, ff, down_layout="fd", down_lognormal_sigma=1.5) for l in range(L)]
     Ws = [ffn_dev(w) for w in ws]
     h = np.stack([synthetic_h_ref(130 + l, 0, T, ff, S, neuron_sigma=0.5) for l in range(L)])
