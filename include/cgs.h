@@ -238,7 +238,9 @@ size_t cgs_act_ffn_masked_workspace(int S, int K, int d, int ff);
  *                are not written.
  *   glue       : NULL or the residual/RMSNorm glue applied to y (rows [S][d]).
  * With idx = 0..ff-1 and NULL anchors this is the dense anchor step; its
- * y_f32_out / h_out are the anchor state of later steps.  Only rows idx of
+ * y_f32_out / h_out are the anchor state of later steps.  A list of K = ff
+ * entries can only be 0..ff-1 under the precondition above, so such a call
+ * reads the weight rows in order without consulting idx.  Only rows idx of
  * w_gate, w_up and w_down are read.  The delta h - h_anchor is rounded to
  * dtype before the down projection.  K = 0 gives y = y_anchor (or 0). */
 int act_ffn_masked(const cgs_ffn* w, const void* x, int S, const int32_t* idx, int K,
