@@ -89,3 +89,20 @@ def test_mask_max_activations_per_neuron():
         c = int(cnt.item())
         assert c == len(oi) and np.array_equal(idx.cpu().numpy()[:c], oi)
         assert np.array_equal(m.cpu().numpy().view(np.uint64), om)
+
+
+@pytest.mark.parametrize("T,ff,S,d", [(2, 65536, 8, 128), (16, 128, 1024, 128)])
+def test_masks_from_stored_norms_at_the_limits(T, ff, S, d):
+    """act_build_masks_normed at ff = 65536 and at S*T = 2^14 (the general
+    kernel path): bit for bit the weight-based build."""
+    say("limits: normed masks", T, ff, S, d)
+    w = ffn_weights(85, 0, d, ff, down_layout="fd", down_lognormal_sigma=1.0)
+    W = ffn_dev(w)
+    h = to_dev(synthetic_h_ref(85, 0, T, ff, S, neuron_sigma=0.5), "f32")[None]
+    nrm = cgs.act_down_norms([W])
+    for mode, K, cov in (("topk", ff // 3, 0.0), ("coverage", 0, 0.844)):
+        a = cgs.act_build_masks(h, [W], mode, K=K, coverage=cov)
+        b = cgs.act_build_masks(h, None, mode, K=K, coverage=cov, norms=nrm)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), mode
