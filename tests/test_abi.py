@@ -187,3 +187,30 @@ def test_workspace_cache_reuses_grows_and_retires():
     assert cgs.workspace(10, "cpu", "other") is not b
     cgs._ws_cache.clear()
     cgs._ws_retired.clear()
+
+
+def test_norm_entry_points_validate_before_launch():
+    """act_down_norms and act_build_masks_normed return their status before
+    any launch: null pointers, layer counts, layouts, shapes, mode, workspace."""
+    L = cgs.lib()
+    buf = ctypes.c_void_p(0x1000)
+    wf = (cgs._Ffn * 2)(_ffn(layout=1), _ffn(layout=1))
+    wd = (cgs._Ffn * 1)(_ffn(layout=0))
+    assert L.act_down_norms(None, 1, buf, None) == 1
+    assert L.act_down_norms(wf, 2, None, None) == 1
+    assert L.act_down_norms(wf, 0, buf, None) == 2
+    assert L.act_down_norms(wf, 65, buf, None) == 2
+    assert L.act_down_norms(wd, 1, buf, None) == 1            # W_down must be neuron-major
+    wmix = (cgs._Ffn * 2)(_ffn(layout=1), _ffn(layout=1, d=128))
+    assert L.act_down_norms(wmix, 2, buf, None) == 2          # layers of different shapes
+    ws = L.cgs_act_build_masks_workspace(2, 4, 50, 1024, 1)
+    args = (2, 4, 50, buf, 1024, 0, 10, 0.0, buf, buf, buf, buf, ws, None)
+    assert L.act_build_masks_normed(None, *args) == 1
+    assert L.act_build_masks_normed(buf, 2, 4, 50, None, 1024, 0, 10, 0.0, buf, buf, buf, buf, ws, None) == 1
+    assert L.act_build_masks_normed(buf, 0, 4, 50, buf, 1024, 0, 10, 0.0, buf, buf, buf, buf, ws, None) == 2
+    assert L.act_build_masks_normed(buf, 2, 4, 50, buf, 0, 0, 10, 0.0, buf, buf, buf, buf, ws, None) == 2
+    assert L.act_build_masks_normed(buf, 2, 4, 50, buf, 1024, 7, 10, 0.0, buf, buf, buf, buf, ws, None) == 1
+    assert L.act_build_masks_normed(buf, 2, 4, 50, buf, 1024, 0, 2000, 0.0, buf, buf, buf, buf, ws, None) == 2
+    assert L.act_build_masks_normed(buf, 2, 4, 50, buf, 1024, 1, 0, 1.5, buf, buf, buf, buf, ws, None) == 2
+    assert L.act_build_masks_normed(buf, 2, 400, 50, buf, 1024, 0, 10, 0.0, buf, buf, buf, buf, ws, None) == 2
+    assert L.act_build_masks_normed(buf, 2, 4, 50, buf, 1024, 0, 10, 0.0, buf, buf, buf, buf, 8, None) == 3
