@@ -143,6 +143,43 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise CgsError(f"unsupported dtype {t.dtype}")
 
 
+def _expect(t, name: str, dtype=None, shape=None, required: bool = True):
+    """Refuse a tensor whose dtype or shape is not what the C call will read
+    or write (the kernels size every access from the FFN struct and the counts
+    passed, so a mismatch would address memory outside the tensor)."""
+    if t is None:
+        if required:
+            raise CgsError(f"{name} is required")
+        return
+    if not isinstance(t, torch.Tensor):
+        raise CgsError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise CgsError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(v) for v in shape):
+        raise CgsError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _expect_index(t, name: str, n=None, required: bool = True):
+    """An index list: 1-D int32 (of n entries when n is given)."""
+    _expect(t, name, torch.int32, None if n is None else (n,), required)
+    if t is not None and t.dim() != 1:
+        raise CgsError(f"{name} must be 1-D")
+
+
+def _expect_glue(glue, rows: int, d: int, dt):
+    """Shapes of the residual/RMSNorm glue tensors for `rows` rows of width d."""
+    if glue is None:
+        return
+    r, bias, x_next = glue[:3]
+    _expect(r, "glue residual r", torch.float32, (rows, d))
+    _expect(bias, "glue bias", torch.float32, (d,), required=False)
+    _expect(x_next, "glue x_next", dt, (rows, d), required=False)
+    if len(glue) > 3:
+        _expect(glue[3], "glue score_ref", dt, (rows, d), required=False)
+    if len(glue) > 4:
+        _expect(glue[4], "glue score_key", torch.float64, (rows,), required=False)
+
+
 def _ptr(t):
     if t is None:
         return None
@@ -199,8 +236,17 @@ class FFN:
     def ff(self) -> int:
         return self.w_gate.shape[0]
 
+    @property
+    def dtype(self):
+        return self.w_gate.dtype
+
     def cstruct(self) -> _Ffn:
         dt = _dtype_code(self.w_gate)
+        if self.w_gate.dim() != 2 or tuple(self.w_up.shape) != tuple(self.w_gate.shape):
+            raise CgsError("FFN w_gate and w_up must both be [ff][d]")
+        want = (self.ff, self.d) if self.layout == "fd" else (self.d, self.ff)
+        if tuple(self.w_down.shape) != want:
+            raise CgsError(f"FFN w_down must be {want} for layout {self.layout!r}")
         for t in (self.w_up, self.w_down):
             if _dtype_code(t) != dt:
                 raise CgsError("FFN weights must share one dtype")
@@ -222,9 +268,16 @@ def ratio_to_count(rho: float, n: int) -> int:
 def ctx_select(x, x_ref, k: int, kind: str = "rel_rms", idx_out=None, key_out=None,
                ws=None, stream=None):
     """Top-k token indices (ascending int32) by the Eq. 2 drift score."""
+    _expect(x, "x")
+    if x.dim() != 2:
+        raise CgsError("x must be [P][d]")
     P, d = x.shape
+    _dtype_code(x)
+    _expect(x_ref, "x_ref", x.dtype, (P, d))
     if idx_out is None:
         idx_out = torch.empty(k, dtype=torch.int32, device=x.device)
+    _expect_index(idx_out, "idx_out", int(k))
+    _expect(key_out, "key_out", torch.float64, (P,), required=False)
     nbytes = lib().cgs_ctx_select_workspace(P, d)
     ws = workspace(nbytes, x.device, "select", stream) if ws is None else ws
     _check(lib().ctx_select(_ptr(x), _ptr(x_ref), P, d, _dtype_code(x), int(k), _KIND[kind],
@@ -235,9 +288,11 @@ def ctx_select(x, x_ref, k: int, kind: str = "rel_rms", idx_out=None, key_out=No
 
 def ctx_select_from_keys(keys, k: int, idx_out=None, stream=None):
     """The k highest of precomputed Eq. 2 keys (float64 [P]), indices ascending."""
+    _expect(keys, "keys", torch.float64)
     P = int(keys.numel())
     if idx_out is None:
         idx_out = torch.empty(int(k), dtype=torch.int32, device=keys.device)
+    _expect_index(idx_out, "idx_out", int(k))
     _check(lib().ctx_select_from_keys(_ptr(keys), P, int(k), _ptr(idx_out), _stream(stream)),
            "ctx_select_from_keys")
     return idx_out
@@ -246,11 +301,18 @@ def ctx_select_from_keys(keys, k: int, idx_out=None, stream=None):
 def ctx_ffn_recompute(w: FFN, x, y_ref, idx, y_out=None, glue=None, ws=None, stream=None):
     """Eq. 3: F(x) on the rows idx, the reference outputs elsewhere.  ``glue`` =
     (r, bias, x_next) applies r += y (+ bias), x_next = RMSNorm(r) per row."""
+    c = w.cstruct()
+    _expect(x, "x", w.dtype)
+    if x.dim() != 2 or x.shape[1] != w.d:
+        raise CgsError(f"x must be [P][{w.d}]")
     P, d = x.shape
+    _expect(y_ref, "y_ref", w.dtype, (P, d))
+    _expect_index(idx, "idx")
     k = int(idx.numel())
     if y_out is None:
         y_out = torch.empty_like(y_ref)
-    c = w.cstruct()
+    _expect(y_out, "y_out", w.dtype, (P, d))
+    _expect_glue(glue, P, d, w.dtype)
     nbytes = lib().cgs_ctx_ffn_recompute_workspace(k, P, d, w.ff, c.dtype)
     ws = workspace(nbytes, x.device, "ctx", stream) if ws is None else ws
     _check(lib().ctx_ffn_recompute(ctypes.byref(c), _ptr(x), _ptr(y_ref), _ptr(idx), k, P,
@@ -263,6 +325,10 @@ def act_build_mask(h_ref, w: FFN, mode: str = "topk", K: int = 0, coverage: floa
                    mask_out=None, idx_out=None, count_out=None, ws=None, stream=None):
     """Group mask from the reference steps' activations h_ref [T][ff][S] (fp32).
     Returns (mask words uint64 as int64 tensor, idx int32 [ff], count int32 [1])."""
+    c = w.cstruct()
+    _expect(h_ref, "h_ref", torch.float32)
+    if h_ref.dim() != 3 or h_ref.shape[1] != w.ff:
+        raise CgsError(f"h_ref must be [T][{w.ff}][S]")
     T, ff, S = h_ref.shape
     dev = h_ref.device
     if mask_out is None:
@@ -271,7 +337,9 @@ def act_build_mask(h_ref, w: FFN, mode: str = "topk", K: int = 0, coverage: floa
         idx_out = torch.empty(ff, dtype=torch.int32, device=dev)
     if count_out is None:
         count_out = torch.empty(1, dtype=torch.int32, device=dev)
-    c = w.cstruct()
+    _expect(mask_out, "mask_out", torch.int64, ((ff + 63) // 64,))
+    _expect_index(idx_out, "idx_out", ff)
+    _expect(count_out, "count_out", torch.int32, (1,))
     nbytes = lib().cgs_act_build_mask_workspace(T, S, ff, w.d)
     ws = workspace(nbytes, dev, "mask", stream) if ws is None else ws
     _check(lib().act_build_mask(_ptr(h_ref), T, S, ctypes.byref(c), _MODE[mode], int(K),
@@ -285,9 +353,10 @@ def act_down_norms(layers, out=None, stream=None):
     float64 [layers][ff]; a property of the weights, computed once."""
     Lr = len(layers)
     ff = layers[0].ff
+    arr = (_Ffn * Lr)(*[w.cstruct() for w in layers])
     if out is None:
         out = torch.empty((Lr, ff), dtype=torch.float64, device=layers[0].w_down.device)
-    arr = (_Ffn * Lr)(*[w.cstruct() for w in layers])
+    _expect(out, "out", torch.float64, (Lr, ff))
     _check(lib().act_down_norms(arr, Lr, _ptr(out), _stream(stream)), "act_down_norms")
     return out
 
@@ -298,7 +367,12 @@ def act_build_masks(h_ref, layers, mode: str = "topk", K: int = 0, coverage: flo
     layers = list of FFN (layout 'fd'); returns (mask words [layers][words],
     idx [layers][ff], count [layers]).  With ``norms`` (act_down_norms of the
     same weights) the weights are not read and ``layers`` may be None."""
+    _expect(h_ref, "h_ref", torch.float32)
+    if h_ref.dim() != 4:
+        raise CgsError("h_ref must be [layers][T][ff][S]")
     Lr, T, ff, S = h_ref.shape
+    if norms is None and layers is not None and any(w.ff != ff for w in layers):
+        raise CgsError("act_build_masks: h_ref's ff differs from the layers'")
     if norms is None and (layers is None or len(layers) != Lr):
         raise CgsError("act_build_masks: one FFN per layer of h_ref")
     if norms is not None and tuple(norms.shape) != (Lr, ff):
@@ -311,6 +385,9 @@ def act_build_masks(h_ref, layers, mode: str = "topk", K: int = 0, coverage: flo
         idx_out = torch.empty((Lr, ff), dtype=torch.int32, device=dev)
     if count_out is None:
         count_out = torch.empty(Lr, dtype=torch.int32, device=dev)
+    _expect(mask_out, "mask_out", torch.int64, (Lr, words))
+    _expect(idx_out, "idx_out", torch.int32, (Lr, ff))
+    _expect(count_out, "count_out", torch.int32, (Lr,))
     nbytes = lib().cgs_act_build_masks_workspace(Lr, T, S, ff, 1)
     ws = workspace(nbytes, dev, "mask", stream) if ws is None else ws
     if norms is not None:
@@ -327,15 +404,38 @@ def act_build_masks(h_ref, layers, mode: str = "topk", K: int = 0, coverage: flo
     return mask_out, idx_out, count_out
 
 
+def _check_act_io(w: FFN, x, y_anchor, h_anchor, y_f32_out, h_out, glue, ff_rows=None):
+    """Activation tensors of an Action Cache call: x [S][d] in the weights'
+    dtype, the fp32 anchors y_anchor [S][d] and h_anchor [ff][S], y_f32_out
+    [S][d], h_out [ff][S].  ff_rows: the neuron rows of the [ff][S] tensors
+    (default w.ff; -1 when w is a compact FFN and they span the full FFN's
+    neurons, which the call does not know)."""
+    _expect(x, "x", w.dtype)
+    if x.dim() != 2 or x.shape[1] != w.d:
+        raise CgsError(f"x must be [S][{w.d}]")
+    S = x.shape[0]
+    nf = w.ff if ff_rows is None else ff_rows
+    _expect(y_anchor, "y_anchor", torch.float32, (S, w.d), required=False)
+    _expect(y_f32_out, "y_f32_out", torch.float32, (S, w.d), required=False)
+    for t, name in ((h_anchor, "h_anchor"), (h_out, "h_out")):
+        _expect(t, name, torch.float32, None, required=False)
+        if t is not None and (t.dim() != 2 or t.shape[1] != S or (nf >= 0 and t.shape[0] != nf)):
+            raise CgsError(f"{name} must be [{'ff' if nf < 0 else nf}][{S}] float32")
+    _expect_glue(glue, S, w.d, w.dtype)
+
+
 def act_ffn_masked(w: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=None, y_f32_out=None,
                    h_out=None, glue=None, ws=None, stream=None):
     """Eq. 4 masked update of a dense anchor (dense anchor step when idx covers
     every neuron and no anchors are given).  ``glue`` = (r, bias, x_next)."""
+    c = w.cstruct()
+    _check_act_io(w, x, y_anchor, h_anchor, y_f32_out, h_out, glue)
     S, d = x.shape
+    _expect_index(idx, "idx")
     K = int(idx.numel())
     if y_out is None:
         y_out = torch.empty_like(x)
-    c = w.cstruct()
+    _expect(y_out, "y_out", w.dtype, (S, d))
     nbytes = lib().cgs_act_ffn_masked_workspace(S, K, d, w.ff)
     ws = workspace(nbytes, x.device, "act", stream) if ws is None else ws
     _check(lib().act_ffn_masked(ctypes.byref(c), _ptr(x), S, _ptr(idx), K, _ptr(y_anchor),
@@ -347,13 +447,16 @@ def act_ffn_masked(w: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=None, y_f
 def act_gather_rows(w: FFN, idx, out: FFN = None, stream=None) -> FFN:
     """Compact FFN of the mask idx: rows idx of w_gate, w_up and the
     neuron-major w_down, each [K][d] (into ``out`` when given)."""
+    c = w.cstruct()
+    _expect_index(idx, "idx")
     K = int(idx.numel())
     if out is None:
         shape = (K, w.d)
         out = FFN(torch.empty(shape, dtype=w.w_gate.dtype, device=w.w_gate.device),
                   torch.empty(shape, dtype=w.w_gate.dtype, device=w.w_gate.device),
                   torch.empty(shape, dtype=w.w_gate.dtype, device=w.w_gate.device), "fd")
-    c = w.cstruct()
+    for t, name in ((out.w_gate, "out.w_gate"), (out.w_up, "out.w_up"), (out.w_down, "out.w_down")):
+        _expect(t, name, w.dtype, (K, w.d))
     _check(lib().act_gather_rows(ctypes.byref(c), _ptr(idx), K, _ptr(out.w_gate), _ptr(out.w_up),
                                  _ptr(out.w_down), _stream(stream)), "act_gather_rows")
     return out
@@ -363,11 +466,14 @@ def act_ffn_masked_compact(wc: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=
                            h_out=None, glue=None, ws=None, stream=None, K=None):
     """Eq. 4 on the compact FFN of a mask (act_gather_rows); idx (original
     neuron ids) addresses h_anchor / h_out rows only and may be None without them."""
-    S, d = x.shape
+    c = wc.cstruct()
     K = wc.ff if K is None else int(K)
+    _check_act_io(wc, x, y_anchor, h_anchor, y_f32_out, h_out, glue, ff_rows=-1)
+    _expect_index(idx, "idx", K, required=False)
+    S, d = x.shape
     if y_out is None:
         y_out = torch.empty_like(x)
-    c = wc.cstruct()
+    _expect(y_out, "y_out", wc.dtype, (S, d))
     nbytes = lib().cgs_act_ffn_masked_workspace(S, K, d, max(K, 1))
     ws = workspace(nbytes, x.device, "act", stream) if ws is None else ws
     _check(lib().act_ffn_masked_compact(ctypes.byref(c), _ptr(x), S, _ptr(idx), K, _ptr(y_anchor),
@@ -387,9 +493,18 @@ def ret_select(query, refs, T: int, q_hist, r_hist, arm: int = -1, min_cos: floa
     """Visual top-T of the prepared entries, joint-history rerank, fallback.
     query [F], refs [N][F] (bf16 or float32), q_hist [L][J], r_hist [N][L][J]
     float32.  Returns (cos [N] f64, top [T] i32, dist [T] f64, choice [1] i32)."""
-    N = refs.shape[0]
+    _expect(query, "query")
+    _dtype_code(query)
     F = int(query.numel())
+    _expect(refs, "refs", query.dtype)
+    if refs.dim() != 2 or refs.shape[1] != F:
+        raise CgsError(f"refs must be [N][{F}]")
+    N = refs.shape[0]
+    _expect(q_hist, "q_hist", torch.float32)
+    if q_hist.dim() != 2:
+        raise CgsError("q_hist must be [L][J]")
     L, J = q_hist.shape
+    _expect(r_hist, "r_hist", torch.float32, (N, L, J))
     dev = query.device
     if cos_out is None:
         cos_out = torch.empty(N, dtype=torch.float64, device=dev)
@@ -399,6 +514,10 @@ def ret_select(query, refs, T: int, q_hist, r_hist, arm: int = -1, min_cos: floa
         dist_out = torch.empty(T, dtype=torch.float64, device=dev)
     if choice_out is None:
         choice_out = torch.empty(1, dtype=torch.int32, device=dev)
+    _expect(cos_out, "cos_out", torch.float64, (N,))
+    _expect(top_out, "top_out", torch.int32, (T,))
+    _expect(dist_out, "dist_out", torch.float64, (T,))
+    _expect(choice_out, "choice_out", torch.int32, (1,))
     nbytes = lib().cgs_ret_select_workspace(N, F)
     ws = workspace(nbytes, dev, "retrieval", stream) if ws is None else ws
     rr = _Rerank(L, J, int(arm), float(min_cos))
@@ -464,12 +583,16 @@ def act_ffn_joint(wc: FFN, x, tok, idx, y_anchor, h_anchor=None, y_out=None, y_f
                   ws=None, stream=None):
     """Token + neuron sparsity: Eq. 4 on the rows tok (ascending) of x with the
     compact weights of the mask idx; every other row keeps y_anchor."""
+    c = wc.cstruct()
+    _check_act_io(wc, x, y_anchor, h_anchor, y_f32_out, None, glue, ff_rows=-1)
     S, d = x.shape
+    _expect_index(tok, "tok", required=False)
+    _expect_index(idx, "idx", wc.ff, required=False)
     k = 0 if tok is None else int(tok.numel())
     K = wc.ff
     if y_out is None:
         y_out = torch.empty_like(x)
-    c = wc.cstruct()
+    _expect(y_out, "y_out", wc.dtype, (S, d))
     nbytes = lib().cgs_act_ffn_masked_workspace(max(k, 1), K, d, max(K, 1))
     ws = workspace(nbytes, x.device, "act", stream) if ws is None else ws
     _check(lib().act_ffn_joint(ctypes.byref(c), _ptr(x), S, _ptr(tok), k, _ptr(idx), K, _ptr(y_anchor),
@@ -481,12 +604,17 @@ def act_ffn_joint(wc: FFN, x, tok, idx, y_anchor, h_anchor=None, y_out=None, y_f
 def ref_rebuild_dense(layers, r0, x_ref_out=None, y_ref_out=None, ws=None, stream=None):
     """Dense rebuild of an entry: returns (x_ref [L][P][d], y_ref [L][P][d])."""
     L = len(layers)
+    arr = (_Ffn * L)(*[w.cstruct() for w in layers])
+    _expect(r0, "r0", layers[0].dtype)
+    if r0.dim() != 2 or r0.shape[1] != layers[0].d:
+        raise CgsError(f"r0 must be [P][{layers[0].d}]")
     P, d = r0.shape
     if x_ref_out is None:
         x_ref_out = torch.empty((L, P, d), dtype=r0.dtype, device=r0.device)
     if y_ref_out is None:
         y_ref_out = torch.empty((L, P, d), dtype=r0.dtype, device=r0.device)
-    arr = (_Ffn * L)(*[w.cstruct() for w in layers])
+    _expect(x_ref_out, "x_ref_out", r0.dtype, (L, P, d))
+    _expect(y_ref_out, "y_ref_out", r0.dtype, (L, P, d))
     c0 = arr[0]
     nbytes = lib().cgs_ref_rebuild_dense_workspace(L, P, d, c0.ff, c0.dtype)
     ws = workspace(nbytes, r0.device, "rebuild", stream) if ws is None else ws
@@ -497,7 +625,14 @@ def ref_rebuild_dense(layers, r0, x_ref_out=None, y_ref_out=None, ws=None, strea
 
 def residual_rmsnorm(r, y=None, bias=None, x_out=None, r_in=None, stream=None):
     """r = (r_in or r) + y + bias (fp32); x_out = RMSNorm(r) (eps 1e-6, no scale)."""
+    _expect(r, "r", torch.float32)
+    if r.dim() != 2:
+        raise CgsError("r must be [M][d]")
     M, d = r.shape
+    _expect(r_in, "r_in", torch.float32, (M, d), required=False)
+    _expect(bias, "bias", torch.float32, (d,), required=False)
+    for t, name in ((y, "y"), (x_out, "x_out")):
+        _expect(t, name, None, (M, d), required=False)
     ydt = _dtype_code(y) if y is not None else CGS_BF16
     odt = _dtype_code(x_out) if x_out is not None else CGS_BF16
     _check(lib().cgs_residual_rmsnorm(_ptr(r), _ptr(r_in), _ptr(y), ydt, _ptr(bias), M, d,

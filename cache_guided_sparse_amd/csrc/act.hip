@@ -376,7 +376,10 @@ ActPlan plan_act(int S, int K, int d) {
   return p;
 }
 
-bool act_shape_ok(int d, int ff) { return d > 0 && ff > 0 && d % 128 == 0; }
+// The down projection reads W_down rows by LDS DMA (32-bit byte offsets):
+// the [ff][d] matrix it addresses spans < 2^32 bytes (4-byte elements, the
+// wider type).
+bool act_shape_ok(int d, int ff) { return d > 0 && ff > 0 && d % 128 == 0 && dma_span_ok(ff, d, 4); }
 
 // S rows computed (rows tok[0..S) of S_all when tok is given, else all).
 // dense: the mask takes every neuron (profiling site names only).

@@ -204,4 +204,13 @@ struct Carve {
 inline int elem_bytes(int dtype) { return dtype == CGS_BF16 ? 2 : 4; }
 inline bool valid_dtype(int dtype) { return dtype == CGS_BF16 || dtype == CGS_F32; }
 
+// LDS-DMA transfers (global_load_lds) address their source with a 32-bit
+// per-lane byte offset from a 64-bit base, so an operand that the GEMM cores
+// or the action down projection read that way must span fewer than 2^32
+// bytes: rows * cols elements of esize bytes.
+constexpr long long kDmaSpan = 1ll << 32;
+inline bool dma_span_ok(long long rows, long long cols, int esize) {
+  return rows >= 0 && cols >= 0 && rows * cols * esize < kDmaSpan;
+}
+
 }  // namespace cgs

@@ -429,9 +429,16 @@ int rebuild_t(const cgs_ffn* layers, int L, const T* r0, int P, T* xo, T* yo, vo
 
 using namespace cgs;
 
+// Every LDS-DMA operand of the gate/up and down GEMMs spans < 2^32 bytes:
+// the activations [P][d], the weights [ff][d] / [d][ff], the hidden rows [M][ff].
+bool ffn_span_ok(long long P, long long M, int d, int ff, int dtype) {
+  const int es = elem_bytes(dtype);
+  return dma_span_ok(P, d, es) && dma_span_ok(ff, d, es) && dma_span_ok(M, ff, es);
+}
+
 extern "C" size_t cgs_ctx_ffn_recompute_workspace(int k, int P, int d, int ff, int dtype) {
-  (void)P;
-  if (!valid_dtype(dtype) || !ffn_shape_ok(d, ff, dtype) || k < 0) return 0;
+  if (!valid_dtype(dtype) || !ffn_shape_ok(d, ff, dtype) || k < 0 || P < k || !ffn_span_ok(P, k, d, ff, dtype))
+    return 0;
   const FfnPlan p = plan_ffn(std::max(k, 1), d, ff, dtype);
   Carve cv(nullptr);
   cv.take<char>(p.h_elems * elem_bytes(dtype));
@@ -446,6 +453,7 @@ extern "C" int ctx_ffn_recompute(const cgs_ffn* w, const void* x, const void* y_
     return CGS_ERR_ARG;
   if (!ffn_shape_ok(w->d, w->ff, w->dtype)) return CGS_ERR_UNSUPPORTED;
   if (P < 0 || k < 0 || k > P) return CGS_ERR_SHAPE;
+  if (!ffn_span_ok(P, k, w->d, w->ff, w->dtype)) return CGS_ERR_UNSUPPORTED;
   if (P == 0) return CGS_OK;
   if (y_out == y_ref || y_out == x) return CGS_ERR_ARG;
   if (!ws || ws_bytes < cgs_ctx_ffn_recompute_workspace(k, P, w->d, w->ff, w->dtype))
@@ -462,7 +470,7 @@ extern "C" int ctx_ffn_recompute(const cgs_ffn* w, const void* x, const void* y_
 
 extern "C" size_t cgs_ref_rebuild_dense_workspace(int L, int P, int d, int ff, int dtype) {
   (void)L;
-  if (!valid_dtype(dtype) || !ffn_shape_ok(d, ff, dtype) || P <= 0) return 0;
+  if (!valid_dtype(dtype) || !ffn_shape_ok(d, ff, dtype) || P <= 0 || !ffn_span_ok(P, P, d, ff, dtype)) return 0;
   const FfnPlan p = plan_ffn(P, d, ff, dtype);
   Carve cv(nullptr);
   cv.take<float>(static_cast<size_t>(P) * d);
@@ -482,7 +490,8 @@ extern "C" int ref_rebuild_dense(const cgs_ffn* layers, int L, const void* r0, i
       return CGS_ERR_SHAPE;
   }
   const cgs_ffn& w0 = layers[0];
-  if (!ffn_shape_ok(w0.d, w0.ff, w0.dtype)) return CGS_ERR_UNSUPPORTED;
+  if (!ffn_shape_ok(w0.d, w0.ff, w0.dtype) || !ffn_span_ok(P, P, w0.d, w0.ff, w0.dtype))
+    return CGS_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < cgs_ref_rebuild_dense_workspace(L, P, w0.d, w0.ff, w0.dtype))
     return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -31,6 +31,9 @@ namespace {
 constexpr int kRetThreads = 256;
 constexpr int kRetChunks = 64;
 constexpr int kRetMaxN = 256;
+// Features per entry, at most: with |feature| <= 2^7 every rounded product is
+// <= 2^38 and a sum of 2^24 of them stays below 2^63.
+constexpr long long kRetMaxF = 1ll << 24;
 
 template <typename T> struct Feat8;
 template <> struct Feat8<uint16_t> {
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(kRetThreads) void ret_select_kernel(
 using namespace cgs;
 
 extern "C" size_t cgs_ret_select_workspace(int N, long long F) {
-  if (N <= 0 || N > kRetMaxN || F <= 0) return 0;
+  if (N <= 0 || N > kRetMaxN || F <= 0 || F > kRetMaxF) return 0;
   return static_cast<size_t>(N + 1) * kRetChunks * 2 * sizeof(long long);
 }
 
@@ -180,7 +183,7 @@ extern "C" int ret_select(const void* query, const void* refs, int N, long long 
   if (!query || !refs || !rr || !q_hist || !r_hist || !cos_out || !top_out || !dist_out || !choice_out ||
       !valid_dtype(dtype))
     return CGS_ERR_ARG;
-  if (N <= 0 || N > kRetMaxN || F <= 0 || F % 8 != 0 || T <= 0 || T > N || rr->hist_len <= 0 ||
+  if (N <= 0 || N > kRetMaxN || F <= 0 || F > kRetMaxF || F % 8 != 0 || T <= 0 || T > N || rr->hist_len <= 0 ||
       rr->joints <= 0 || rr->joints % 2 != 0 || rr->arm < -1 || rr->arm > 1 ||
       static_cast<long long>(rr->hist_len) * rr->joints > (1 << 16))
     return CGS_ERR_SHAPE;

@@ -32,6 +32,13 @@
  *     (CGS_DOWN_DF, the Context Cache path and the rebuild) or neuron-major
  *     [ff][d] (CGS_DOWN_FD, the Action Cache path, so that a neuron's down
  *     weights are one contiguous row).
+ *   - Size limit: the GEMM kernels move operand tiles into LDS with transfers
+ *     that address their source by a 32-bit byte offset, so every matrix they
+ *     read that way must span fewer than 2^32 bytes.  The FFN entry points
+ *     return CGS_ERR_UNSUPPORTED (and the workspace queries 0) when one does
+ *     not: ctx_ffn_recompute and ref_rebuild_dense need P*d, ff*d and
+ *     rows*ff elements (rows = k, resp. P) times the element size below 2^32;
+ *     the Action Cache calls need ff*d*4 < 2^32 (wc->ff*d*4 for compact weights).
  */
 #ifndef CGS_H
 #define CGS_H
@@ -161,7 +168,8 @@ size_t cgs_ctx_ffn_recompute_workspace(int k, int P, int d, int ff, int dtype);
  * Unselected rows are copied bit for bit.  k = 0 is a pure copy; k = P is
  * the dense FFN.  The hidden activation is rounded to dtype before the down
  * projection; products accumulate in fp32.  Row pointers must be 16-byte
- * aligned (d % 128 == 0 does it for aligned bases). */
+ * aligned (d % 128 == 0 does it for aligned bases).  CGS_ERR_UNSUPPORTED if
+ * P*d, ff*d or k*ff elements span 2^32 bytes or more (see the size limit). */
 int ctx_ffn_recompute(const cgs_ffn* w, const void* x, const void* y_ref, const int32_t* idx,
                       int k, int P, void* y_out, const cgs_glue* glue, void* ws, size_t ws_bytes,
                       void* stream);
@@ -285,7 +293,8 @@ size_t cgs_ref_rebuild_dense_workspace(int L, int P, int d, int ff, int dtype);
  *   x_ref_out : [L][P][d] dtype, xbar_l = RMSNorm(r_l) (no learned scale,
  *               eps 1e-6) rounded to dtype.
  *   y_ref_out : [L][P][d] dtype, ybar_l = F_l(xbar_l).
- * r_{l+1} = r_l + ybar_l with r kept in fp32. */
+ * r_{l+1} = r_l + ybar_l with r kept in fp32.  CGS_ERR_UNSUPPORTED if P*d,
+ * ff*d or P*ff elements span 2^32 bytes or more (see the size limit). */
 int ref_rebuild_dense(const cgs_ffn* layers, int L, const void* r0, int P, void* x_ref_out,
                       void* y_ref_out, void* ws, size_t ws_bytes, void* stream);
 
@@ -362,7 +371,9 @@ typedef struct {
 size_t cgs_ret_select_workspace(int N, long long F);
 
 /* query: [F] features (dtype, device); refs: [N][F] the prepared entries'
- * features (1 <= N <= 256, F % 8 == 0, both 16-byte aligned).
+ * features (1 <= N <= 256, 8 <= F <= 2^24, F % 8 == 0, both 16-byte aligned).
+ * Precondition |feature| <= 2^7, so that the integer sums below cannot
+ * overflow (every rounded product is <= 2^38, a sum of 2^24 of them < 2^63).
  * Visual match: cos_n = Sqr / sqrt(Sqq Srr) from the exact fixed-point sums
  * of the token score's cosine kind (every feature product rounded half-even
  * to an int64 at 2^-24; float64 key, 0 if a norm is 0), written to

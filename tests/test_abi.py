@@ -214,3 +214,105 @@ def test_norm_entry_points_validate_before_launch():
     assert L.act_build_masks_normed(buf, 2, 4, 50, buf, 1024, 1, 0, 1.5, buf, buf, buf, buf, ws, None) == 2
     assert L.act_build_masks_normed(buf, 2, 400, 50, buf, 1024, 0, 10, 0.0, buf, buf, buf, buf, ws, None) == 2
     assert L.act_build_masks_normed(buf, 2, 4, 50, buf, 1024, 0, 10, 0.0, buf, buf, buf, buf, 8, None) == 3
+
+
+def test_binding_refuses_mismatched_tensors(monkeypatch):
+    """The binding checks every tensor's dtype and shape against the FFN and
+    the counts before a pointer reaches the library (the kernels size their
+    accesses from those, so a mismatch would read or write outside the
+    tensor).  CPU tensors stand in for device ones: pointers are faked, and
+    every case below is refused before any library call that launches."""
+    import torch
+    monkeypatch.setattr(cgs, "_ptr", lambda t: None if t is None else 0x1000)
+    bf, f32 = torch.bfloat16, torch.float32
+    d, ff, P, S = 256, 1024, 16, 8
+
+    def z(*shape, dt=bf):
+        return torch.zeros(*shape, dtype=dt)
+
+    def refuses(fn, what):
+        with pytest.raises(cgs.CgsError, match=what):
+            fn()
+
+    W = cgs.FFN(z(ff, d), z(ff, d), z(d, ff), "df")
+    x, idx = z(P, d), torch.arange(4, dtype=torch.int32)
+    refuses(lambda: cgs.ctx_ffn_recompute(W, x, z(P, d, dt=f32), idx), "y_ref")
+    refuses(lambda: cgs.ctx_ffn_recompute(W, x.float(), x, idx), "x must be")
+    refuses(lambda: cgs.ctx_ffn_recompute(W, z(P, 128), x, idx), "x must be")
+    refuses(lambda: cgs.ctx_ffn_recompute(W, x, x, idx.long()), "idx")
+    refuses(lambda: cgs.ctx_ffn_recompute(W, x, x, idx.view(2, 2)), "idx")
+    refuses(lambda: cgs.ctx_ffn_recompute(W, x, x, idx, y_out=z(P, d, dt=f32)), "y_out")
+    refuses(lambda: cgs.ctx_ffn_recompute(W, x, x, idx, glue=(z(P, d), None, None)), "glue residual")
+    refuses(lambda: cgs.ctx_ffn_recompute(W, x, x, idx, glue=(z(P, d, dt=f32), None, z(P - 1, d))), "x_next")
+    refuses(lambda: cgs.ctx_ffn_recompute(W, x, x, idx, glue=(z(P, d, dt=f32), None, x, x, z(P, dt=f32))),
+            "score_key")
+    refuses(lambda: cgs.ctx_ffn_recompute(cgs.FFN(W.w_gate, W.w_up, z(ff, d), "df"), x, x, idx), "w_down")
+    refuses(lambda: cgs.ctx_select(x, z(P, d, dt=f32), 4), "x_ref")
+    refuses(lambda: cgs.ctx_select(x, x, 4, idx_out=torch.zeros(4, dtype=torch.int64)), "idx_out")
+    refuses(lambda: cgs.ctx_select(x, x, 4, key_out=z(P, dt=f32)), "key_out")
+    refuses(lambda: cgs.ctx_select_from_keys(z(P, dt=f32), 4), "keys")
+
+    Wa = cgs.FFN(z(ff, d), z(ff, d), z(ff, d), "fd")
+    xa, full = z(S, d), torch.arange(ff, dtype=torch.int32)
+    refuses(lambda: cgs.act_ffn_masked(Wa, xa, full, y_anchor=z(S, d)), "y_anchor")
+    refuses(lambda: cgs.act_ffn_masked(Wa, xa, full, h_anchor=z(S, ff, dt=f32)), "h_anchor")
+    refuses(lambda: cgs.act_ffn_masked(Wa, xa, full, h_out=z(ff, S + 1, dt=f32)), "h_out")
+    refuses(lambda: cgs.act_ffn_masked(Wa, xa, full, y_f32_out=z(S, d)), "y_f32_out")
+    refuses(lambda: cgs.act_ffn_masked(Wa, xa, full.long()), "idx")
+    refuses(lambda: cgs.act_ffn_masked(Wa, xa.float(), full), "x must be")
+    refuses(lambda: cgs.act_ffn_masked(Wa, xa, full, y_out=z(S, d, dt=f32)), "y_out")
+    refuses(lambda: cgs.act_ffn_masked(Wa, xa, full, glue=(z(S + 1, d, dt=f32), None, xa)), "glue residual")
+    Wc = cgs.FFN(z(64, d), z(64, d), z(64, d), "fd")
+    refuses(lambda: cgs.act_ffn_masked_compact(Wc, xa, torch.arange(63, dtype=torch.int32)), "idx")
+    refuses(lambda: cgs.act_ffn_masked_compact(Wc, xa, full[:64], h_anchor=z(ff, S + 2, dt=f32)), "h_anchor")
+    refuses(lambda: cgs.act_ffn_joint(Wc, xa, torch.arange(2, dtype=torch.int64), full[:64], z(S, d, dt=f32)),
+            "tok")
+    refuses(lambda: cgs.act_gather_rows(Wa, full[:64], out=cgs.FFN(z(64, d), z(64, d), z(63, d), "fd")),
+            "w_down")
+    refuses(lambda: cgs.ref_rebuild_dense([W], z(P, d, dt=f32)), "r0")
+    refuses(lambda: cgs.ref_rebuild_dense([W], x, x_ref_out=z(2, P, d)), "x_ref_out")
+    refuses(lambda: cgs.act_build_mask(z(1, ff, S, dt=torch.float64), Wa), "h_ref")
+    refuses(lambda: cgs.act_build_mask(z(1, ff + 64, S, dt=f32), Wa), "h_ref")
+    refuses(lambda: cgs.act_build_mask(z(1, ff, S, dt=f32), Wa, idx_out=torch.zeros(ff, dtype=torch.int64)),
+            "idx_out")
+    refuses(lambda: cgs.act_build_masks(z(2, 1, ff, S, dt=f32), [Wa, Wa], count_out=z(3, dt=torch.int32)),
+            "count_out")
+    refuses(lambda: cgs.act_down_norms([Wa], out=z(1, ff, dt=f32)), "out")
+    refuses(lambda: cgs.residual_rmsnorm(z(P, d, dt=f32), y=z(P, d + 8)), "y")
+    refuses(lambda: cgs.residual_rmsnorm(z(P, d)), "r must be")
+    refuses(lambda: cgs.residual_rmsnorm(z(P, d, dt=f32), bias=z(d + 1, dt=f32)), "bias")
+    q = z(1024)
+    refuses(lambda: cgs.ret_select(q, z(4, 1000), 2, z(4, 14, dt=f32), z(4, 4, 14, dt=f32)), "refs")
+    refuses(lambda: cgs.ret_select(q, z(4, 1024), 2, z(4, 14, dt=f32), z(3, 4, 14, dt=f32)), "r_hist")
+
+
+def test_operands_past_32_bit_offsets_are_unsupported():
+    """The GEMM cores address LDS-DMA sources with 32-bit byte offsets: a
+    matrix spanning 2^32 bytes or more is refused before any launch (status
+    CGS_ERR_UNSUPPORTED, workspace query 0), one case per operand."""
+    L = cgs.lib()
+    buf = ctypes.c_void_p(0x1000)
+    out = ctypes.c_void_p(0x2000)
+    assert L.cgs_ctx_ffn_recompute_workspace(231, 768, 2048, 16384, 0) > 0
+    assert L.cgs_ctx_ffn_recompute_workspace(1, 1 << 20, 2048, 1024, 0) == 0        # x: P*d*2 = 2^32
+    assert L.cgs_ctx_ffn_recompute_workspace(1, 8, 2048, 1 << 20, 0) == 0           # weights: ff*d*2 = 2^32
+    assert L.cgs_ctx_ffn_recompute_workspace(1 << 17, 1 << 17, 128, 1 << 14, 0) == 0  # H: k*ff*2 = 2^32
+    assert L.cgs_ref_rebuild_dense_workspace(1, 1 << 18, 128, 1 << 13, 1) == 0       # H: P*ff*4 = 2^33
+    assert L.ctx_ffn_recompute(ctypes.byref(_ffn(d=2048, ff=1 << 20)), buf, buf, buf, 1, 8, out, None, buf,
+                               1 << 40, None) == 4
+    assert L.ctx_ffn_recompute(ctypes.byref(_ffn(d=2048, ff=1024)), buf, buf, buf, 1, 1 << 20, out, None, buf,
+                               1 << 40, None) == 4
+    arr = (cgs._Ffn * 1)(_ffn(d=2048, ff=1024))
+    assert L.ref_rebuild_dense(arr, 1, buf, 1 << 20, buf, out, buf, 1 << 40, None) == 4
+    wbig = _ffn(d=1024, ff=1 << 20, layout=1)                                       # W_down: ff*d*4 = 2^32
+    assert L.act_ffn_masked(ctypes.byref(wbig), buf, 4, buf, 10, None, None, out, None, None, None, buf,
+                            1 << 40, None) == 4
+    assert L.act_ffn_masked_compact(ctypes.byref(wbig), buf, 4, buf, 1 << 20, None, None, out, None, None,
+                                    None, buf, 1 << 40, None) == 4
+    assert L.cgs_act_ffn_masked_workspace(50, 10, 1024, 1 << 20) == 0
+    # retrieval: at most 2^24 features (their integer sums stay below 2^63)
+    assert L.cgs_ret_select_workspace(16, 1 << 24) > 0
+    assert L.cgs_ret_select_workspace(16, (1 << 24) + 8) == 0
+    rr = cgs._Rerank(4, 14, -1, 0.8)
+    assert L.ret_select(buf, buf, 16, (1 << 24) + 8, 0, 4, buf, buf, ctypes.byref(rr), buf, buf, buf, buf, buf,
+                        1 << 30, None) == 2
