@@ -1,11 +1,19 @@
 """Helpers shared by the GPU parity tests: host <-> device marshalling and the
 tolerance check.
 
-Tolerance: |gpu - oracle| <= 1e-2 x RMS(oracle output) for every element of a
-float32 output.  A bf16 output is the rounding of the computed value to bf16,
-which by itself moves an element by up to half a bf16 ulp (2^-9 relative); so
-for bf16 outputs each element may additionally differ by half an ulp of its
-magnitude: |gpu - oracle| <= 1e-2 x RMS + ulp_bf16(max(|gpu|, |oracle|)) / 2.
+Tolerance (the workload's bound for bf16 outputs): max |gpu - oracle| <=
+1e-2 x RMS(oracle output of that call), applied to every element.
+
+* float32 outputs are checked literally.
+* bf16 outputs are the kernel's fp32 value stored with round-to-nearest-even,
+  and the bound applies to that computed value: the check is that the stored
+  bf16 is the RNE image of some value within the bound, i.e.
+      RNE(oracle - a) <= gpu <= RNE(oracle + a),   a = 1e-2 x RMS.
+  No looser allowance: a perfectly computed output already misses the
+  literal unrounded bound wherever |y| > 2^9 a / 1e-2 (about 2.6 x RMS), since
+  the storage rounding alone moves it by up to 2^-9 |y| (pinned on the CPU in
+  tests/test_tolerance.py).  Where a kernel also writes the fp32 value, tests
+  check that value literally and its bf16 output bit for bit against RNE of it.
 """
 import sys
 
@@ -52,14 +60,18 @@ def ffn_dev(w: dict) -> cgs.FFN:
                    layout=w["down_layout"])
 
 
-def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
-    """Half the spacing of bf16 numbers at |v| (8 significant bits)."""
-    _, e = np.frexp(np.abs(v))                    # |v| = m 2^e, 0.5 <= m < 1
-    return np.ldexp(np.ones_like(v), np.maximum(e, -125) - 9)
+def bf16_bracket(ref: np.ndarray, a) -> tuple:
+    """(RNE(ref - a), RNE(ref + a)) as float64: the bf16 values a result within
+    a of ref may be stored as (RNE is monotone)."""
+    import oracle as O
+    lo = O.decode(O.round_to_bf16_bits(ref - a), "bf16")
+    hi = O.decode(O.round_to_bf16_bits(ref + a), "bf16")
+    return lo, hi
 
 
 def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str, tol: float = TOL, out: str = "f32"):
-    """Max-abs check against the oracle; ``out='bf16'`` for outputs stored in bf16."""
+    """Max-abs check against the oracle (module docstring); ``out='bf16'`` for
+    outputs stored in bf16.  Returns max |gpu - ref| / RMS(ref)."""
     ref = np.asarray(ref, dtype=np.float64)
     gpu = np.asarray(gpu, dtype=np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
@@ -67,32 +79,45 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str, tol: float = TOL, 
         return 0.0
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
     rms = max(float(np.sqrt(np.mean(ref ** 2))), 1e-30)
+    a = tol * rms
     diff = np.abs(gpu - ref)
-    allow = tol * rms
     if out == "bf16":
-        allow = allow + half_ulp_bf16(np.maximum(np.abs(gpu), np.abs(ref)))
-    bad = diff > allow
+        lo, hi = bf16_bracket(ref, a)
+        bad = (gpu < lo) | (gpu > hi)
+    else:
+        bad = diff > a
     assert not bad.any(), (f"{what}: {int(bad.sum())} elements out of tolerance; max abs err "
                            f"{float(diff.max()):.3e}, rms {rms:.3e}")
     return float(diff.max()) / rms
 
 
-def assert_close_chain(gpu: np.ndarray, ref: np.ndarray, what: str, depth: int, out: str = "f32"):
-    """Outputs of a layer chain run independently on both sides.
+def assert_rne_of(bf16_bits: np.ndarray, f32: np.ndarray, what: str):
+    """The bf16 output is exactly RNE of the fp32 output of the same call."""
+    import oracle as O
+    want = O.round_to_bf16_bits(np.asarray(f32, dtype=np.float32).astype(np.float64))
+    assert np.array_equal(np.asarray(bf16_bits), want), f"{what}: bf16 output is not RNE of the fp32 output"
 
-    depth 0 (no earlier layer feeds it): the single-call rule above.  depth >= 1:
-    earlier layers' bf16 rounding decisions may resolve differently on the two
-    sides and shift this layer's input by an ulp here and there, so the check is
-    the RMS-relative error ||gpu - ref||_2 / ||ref||_2 <= 1e-2, with a max-abs cap
-    of 5e-2 x RMS against localised errors."""
-    if depth == 0:
-        return assert_close(gpu, ref, what, out=out)
-    ref = np.asarray(ref, dtype=np.float64)
-    gpu = np.asarray(gpu, dtype=np.float64)
-    assert gpu.shape == ref.shape and np.all(np.isfinite(gpu)), what
-    rms = max(float(np.sqrt(np.mean(ref ** 2))), 1e-30)
-    rel = float(np.sqrt(np.mean((gpu - ref) ** 2))) / rms
-    mx = float(np.max(np.abs(gpu - ref))) / rms
-    assert rel <= TOL, f"{what}: rms-relative error {rel:.3e}"
-    assert mx <= 5 * TOL, f"{what}: max abs error {mx:.3e} x rms"
-    return rel
+
+def check_rebuild_teacher_forced(layers, r0, xo, yo, dtype="bf16", rows=None, full_rows_layers=()):
+    """Teacher-forced check of a dense rebuild, per layer l: xbar_l (every row)
+    against RMSNorm(r_l), r_l rebuilt from r_0 and the GPU's ybar_0..l-1, and
+    ybar_l (rows `rows`; every row for l in full_rows_layers) against F_l of the
+    GPU's own xbar_l.  Returns the largest ybar error / RMS."""
+    import oracle as O
+    xg = bits(xo) if dtype == "bf16" else values(xo)
+    yg = bits(yo) if dtype == "bf16" else values(yo)
+    P = xg.shape[1]
+    rows = np.arange(P) if rows is None else np.asarray(rows)
+    r = O.decode(r0, dtype)
+    worst = 0.0
+    for l in range(len(layers)):
+        sel = np.arange(P) if l in full_rows_layers else rows
+        x_all = xg[l] if dtype == "bf16" else xg[l].astype(np.float32)
+        assert_close(O.decode(x_all, dtype), O.rms_norm(r), f"xbar layer {l}", out=dtype)
+        x_l = x_all[sel]
+        y_l = yg[l][sel] if dtype == "bf16" else yg[l][sel].astype(np.float32)
+        y_o = O.ffn_geglu(O.decode(x_l, dtype), layers[l])
+        worst = max(worst, assert_close(O.decode(y_l, dtype), y_o, f"ybar layer {l}", out=dtype))
+        yl_all = yg[l] if dtype == "bf16" else yg[l].astype(np.float32)
+        r = r + O.decode(yl_all, dtype)
+    return worst

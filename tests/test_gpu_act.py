@@ -8,7 +8,7 @@ import torch
 import cache_guided_sparse_amd as cgs
 import oracle as O
 from cgs_inputs import act_tokens, ffn_weights, rng
-from gpu_helpers import assert_close, bits, dev, ffn_dev, say, to_dev, values
+from gpu_helpers import assert_close, assert_rne_of, bits, dev, ffn_dev, say, to_dev, values
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,14 @@ def _setup(seed, S, d, ff, dtype="bf16", sigma=1.0):
     return w, t["x"], t["x_pert"]
 
 
+def _stored_is_rounding(y, yf, dtype):
+    """The dtype output is the fp32 output rounded once (bf16: RNE; f32: equal)."""
+    if dtype == "bf16":
+        assert_rne_of(bits(y), values(yf), "y")
+    else:
+        assert torch.equal(y, yf)
+
+
 @pytest.mark.parametrize("dtype,S,d,ff", [("f32", 16, 256, 1024), ("bf16", 16, 256, 1024),
                                           ("bf16", 50, 1024, 4096), ("bf16", 70, 128, 200),
                                           ("bf16", 16, 256, 2048), ("bf16", 64, 128, 4096),
@@ -48,7 +56,8 @@ def test_dense_anchor(dtype, S, d, ff):
     y, yf, h = _masked(w, x, np.arange(ff), want_h=True)
     y_o, h_o = O.act_ffn_masked(w, x, np.arange(ff))
     assert_close(values(yf), y_o, "y_f32")
-    assert_close(values(y), y_o, "y", out="bf16")
+    assert_close(values(y), y_o, "y", out=dtype)
+    _stored_is_rounding(y, yf, dtype)
     assert_close(values(h), h_o, "h_out")
 
 
@@ -67,7 +76,8 @@ def test_masked_with_anchor(dtype, S, d, ff, rho):
     y, yf, h = _masked(w, x, idx, ya32, ha32, want_h=True)
     y_o, h_o = O.act_ffn_masked(w, x, idx, ya32, ha32)
     assert_close(values(yf), y_o, "y_f32")
-    assert_close(values(y), y_o, "y", out="bf16")
+    assert_close(values(y), y_o, "y", out=dtype)
+    _stored_is_rounding(y, yf, dtype)
     hv = values(h)
     assert_close(hv[idx], h_o, "h_out rows of the mask")
     untouched = np.ones(ff, dtype=bool)

@@ -28,7 +28,8 @@ import torch
 import cache_guided_sparse_amd as cgs
 import oracle as O
 from cgs_inputs import act_tokens, ctx_layer_inputs, ffn_weight_pool, ffn_weights, timestep_embedding
-from gpu_helpers import assert_close, bits, dev, ffn_dev, say, to_dev, values
+from gpu_helpers import (assert_close, assert_rne_of, bits, check_rebuild_teacher_forced, dev, ffn_dev,
+                         say, to_dev, values)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,14 +53,12 @@ def vlm():
             "xbar": xbar, "ybar": ybar, "xbar_h": bits(xbar), "ybar_h": bits(ybar)}
 
 
-def test_rebuilt_entry_first_layer(vlm):
-    """The entry the prefill runs against: xbar_0 = RMSNorm(entry), ybar_0 =
-    F_0(xbar_0) on a sample of tokens (later layers: test_gpu_rebuild)."""
-    xb0 = vlm["xbar_h"][0]
-    assert_close(O.decode(xb0, "bf16"), O.rms_norm(O.decode(vlm["entry"], "bf16")), "xbar_0", out="bf16")
-    rows = np.linspace(0, P - 1, 8).astype(int)
-    y_o = O.ffn_geglu(O.decode(xb0[rows], "bf16"), vlm["layers"][0])
-    assert_close(O.decode(vlm["ybar_h"][0][rows], "bf16"), y_o, "ybar_0 rows", out="bf16")
+def test_rebuilt_entry_all_layers(vlm):
+    """The entry the prefill runs against, all 17 layers teacher-forced: xbar_l
+    against RMSNorm of the residual rebuilt from the GPU's ybar_<l (every row),
+    ybar_l against F_l of the GPU's xbar_l (24 rows per layer)."""
+    rows = np.linspace(0, P - 1, 24).astype(int)
+    check_rebuild_teacher_forced(vlm["layers"], vlm["entry"], vlm["xbar"], vlm["ybar"], "bf16", rows=rows)
 
 
 @pytest.mark.parametrize("rho", [0.1, 0.3, 0.5, 1.0])
@@ -102,8 +101,9 @@ def test_prefill_chain_17_layers(vlm, rho):
                          out="bf16")
     if k == N_CHANGED:
         assert np.array_equal(idx_h[0], vlm["changed"]), "layer 0 must select the planted tokens"
-    for l in (0, L_VLM // 2, L_VLM - 1):
-        sample = idx_h[l][np.linspace(0, k - 1, 6).astype(int)]
+    # recomputed rows of every layer on the GPU's own input (all rows when k <= 77)
+    for l in range(L_VLM):
+        sample = idx_h[l] if k <= 77 else idx_h[l][np.linspace(0, k - 1, 24).astype(int)]
         y_o = O.ffn_geglu(O.decode(x_h[l][sample], "bf16"), vlm["layers"][l])
         assert_close(O.decode(y_h[l][sample], "bf16"), y_o, f"layer {l}: recomputed rows", out="bf16")
 
@@ -163,7 +163,8 @@ def test_denoise_chain_18_layers_4_steps(expert):
     # the denoise: step 0 dense (anchor), steps 1..3 Eq. 4 on compact weights
     y_anc = torch.empty(L_EXP, S, DE, dtype=torch.float32, device=dev())
     h_anc = torch.empty(L_EXP, FFE, S, dtype=torch.float32, device=dev())
-    xin, yout, rin = [], [], []
+    xin, yout, rin, yf32 = [], [], [], []
+    yf = torch.empty(S, DE, dtype=torch.float32, device=dev())
     cgs.residual_rmsnorm(ra, r_in=_f32(expert["a0"]), bias=temb0, x_out=xa)
     for t in range(STEPS):
         for l in range(L_EXP):
@@ -175,8 +176,9 @@ def test_denoise_chain_18_layers_4_steps(expert):
                                    glue=(ra, bias, xa))
             else:
                 cgs.act_ffn_masked_compact(cexp[l], xa, masks[l], y_anchor=y_anc[l], h_anchor=h_anc[l],
-                                           y_out=ya, glue=(ra, bias, xa))
+                                           y_out=ya, y_f32_out=yf, glue=(ra, bias, xa))
             yout.append(ya.clone())
+            yf32.append(yf.clone() if t > 0 else y_anc[l].clone())
     rin.append(ra.clone())
     xin.append(xa.clone())
     torch.cuda.synchronize()
@@ -193,6 +195,9 @@ def test_denoise_chain_18_layers_4_steps(expert):
             else:
                 y_o, _ = O.act_ffn_masked(layers[l], x_h, midx_h[l][: K[l]], y_anc_h[l], h_anc_h[l])
             assert_close(y_h, y_o, f"step {t} layer {l}: y", out="bf16")
+            yf_h = yf32[i].cpu().numpy()
+            assert_close(yf_h, y_o, f"step {t} layer {l}: y (fp32, before rounding)")
+            assert_rne_of(bits(yout[i]), yf_h, f"step {t} layer {l}")
             r_exp = values(rin[i]) + y_h
             if l == L_EXP - 1:
                 r_exp = r_exp + expert["dtemb"][t].astype(np.float64)

@@ -118,7 +118,8 @@ def test_consecutive_calls_through_the_working_set():
             rec[idx_o] = True
             assert np.array_equal(y_h[l][~rec], yb_h[l][~rec]), f"call {q} layer {l}: copied rows"
         assert np.array_equal(idx_h[0], entries[q]["changed"]), "layer 0 must select the planted tokens"
-        if q in (0, CALLS - 1):
-            sample = idx_h[0][np.linspace(0, k - 1, 6).astype(int)]
-            y_o = O.ffn_geglu(O.decode(x_h[0][sample], "bf16"), layers[0])
-            assert_close(O.decode(y_h[0][sample], "bf16"), y_o, f"call {q}: recomputed rows", out="bf16")
+        for l in range(L_VLM):
+            sample = idx_h[l][np.linspace(0, k - 1, 8).astype(int)]
+            y_o = O.ffn_geglu(O.decode(x_h[l][sample], "bf16"), layers[l])
+            assert_close(O.decode(y_h[l][sample], "bf16"), y_o, f"call {q} layer {l}: recomputed rows",
+                         out="bf16")
