@@ -26,6 +26,7 @@ CGS_SCORE_REL_RMS, CGS_SCORE_COSINE = 0, 1
 CGS_MASK_TOPK, CGS_MASK_COVERAGE = 0, 1
 CGS_DOWN_DF, CGS_DOWN_FD = 0, 1
 CGS_ERR_DATA = 6
+CGS_ERR_TIMEOUT = 7
 
 _KIND = {"rel_rms": CGS_SCORE_REL_RMS, "cosine": CGS_SCORE_COSINE}
 _MODE = {"topk": CGS_MASK_TOPK, "coverage": CGS_MASK_COVERAGE}
@@ -107,6 +108,10 @@ _SIGS = {
     "cgs_window_slot": (_i, [_vp, _i, _i]),
     "cgs_window_resident": (_i, [_vp]),
     "cgs_window_advance": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "act_gather_rows_t": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _vp]),
+    "cgs_act_denoise_step_workspace": (_sz, [_i, _i, _i, _i]),
+    "act_denoise_step": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "cgs_set_step_wait_limit": (ctypes.c_longlong, [ctypes.c_longlong]),
     "cgs_profile_start": (_i, [ctypes.c_char_p, _i]),
     "cgs_profile_stop": (_i, []),
     "cgs_profile_result": (_i, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -657,3 +662,125 @@ def profile_result(site: str | None = None):
     _check(lib().cgs_profile_result(None if site is None else site.encode(), ctypes.byref(t),
                                     ctypes.byref(n)), "cgs_profile_result")
     return t.value, n.value
+
+
+# --------------------------------------------------------------------------
+# One whole masked denoising step in one persistent launch
+# --------------------------------------------------------------------------
+class _StepLayer(ctypes.Structure):
+    _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down_t", ctypes.c_void_p),
+                ("K", ctypes.c_int32), ("ldk", ctypes.c_int32), ("idx", ctypes.c_void_p),
+                ("y_anchor", ctypes.c_void_p), ("h_anchor", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("y_out", ctypes.c_void_p), ("y_f32_out", ctypes.c_void_p), ("h_out", ctypes.c_void_p)]
+
+
+@dataclass
+class CompactT:
+    """Compact weights of a mask for act_denoise_step: w_gate, w_up [K][d] and
+    the down weights transposed, w_down_t [d][ldk] (act_gather_rows_t)."""
+    w_gate: torch.Tensor
+    w_up: torch.Tensor
+    w_down_t: torch.Tensor
+
+    @property
+    def K(self) -> int:
+        return self.w_gate.shape[0]
+
+    @property
+    def d(self) -> int:
+        return self.w_down_t.shape[0]
+
+    @property
+    def ldk(self) -> int:
+        return self.w_down_t.shape[1]
+
+
+def act_gather_rows_t(w: FFN, idx=None, K: int = None, ldk: int = None, out: CompactT = None,
+                      stream=None) -> CompactT:
+    """Rows idx of w_gate / w_up ([K][d]) and the same neurons' down weights
+    transposed ([d][ldk], zero past K).  idx None: the first K neurons (K = ff
+    by default: the full FFN in the step kernel's layout)."""
+    c = w.cstruct()
+    if w.layout != "fd" or w.dtype != torch.bfloat16:
+        raise CgsError("act_gather_rows_t: bf16 weights with neuron-major w_down ('fd')")
+    _expect_index(idx, "idx", required=False)
+    K = (w.ff if idx is None else int(idx.numel())) if K is None else int(K)
+    if idx is not None and int(idx.numel()) != K:
+        raise CgsError("act_gather_rows_t: K differs from the index list")
+    ldk = (K + 31) // 32 * 32 if ldk is None else int(ldk)
+    dev = w.w_gate.device
+    if out is None:
+        out = CompactT(torch.empty((K, w.d), dtype=torch.bfloat16, device=dev),
+                       torch.empty((K, w.d), dtype=torch.bfloat16, device=dev),
+                       torch.empty((w.d, ldk), dtype=torch.bfloat16, device=dev))
+    _expect(out.w_gate, "out.w_gate", torch.bfloat16, (K, w.d))
+    _expect(out.w_up, "out.w_up", torch.bfloat16, (K, w.d))
+    _expect(out.w_down_t, "out.w_down_t", torch.bfloat16, (w.d, ldk))
+    _check(lib().act_gather_rows_t(ctypes.byref(c), _ptr(idx), K, _ptr(out.w_gate), _ptr(out.w_up),
+                                   _ptr(out.w_down_t), ldk, _stream(stream)), "act_gather_rows_t")
+    return out
+
+
+@dataclass
+class StepLayer:
+    """One layer of act_denoise_step: compact weights (CompactT), the mask's
+    neuron ids (idx, or None for the identity), the anchor state, the bias
+    added to r after the layer and optional outputs."""
+    w: CompactT
+    idx: torch.Tensor = None
+    y_anchor: torch.Tensor = None
+    h_anchor: torch.Tensor = None
+    bias: torch.Tensor = None
+    y_out: torch.Tensor = None
+    y_f32_out: torch.Tensor = None
+    h_out: torch.Tensor = None
+
+
+def act_denoise_step_workspace(L: int, S: int, d: int, K_max: int) -> int:
+    return int(lib().cgs_act_denoise_step_workspace(int(L), int(S), int(d), int(K_max)))
+
+
+def act_denoise_step(layers, r, x, ff: int, status=None, ws=None, stream=None):
+    """All len(layers) masked layers of a denoising step in one persistent
+    launch: x [L+1][S][d] bf16 (x[0] the input, x[1..L] written), r [S][d]
+    fp32 residual (updated).  status: optional int32 [1] device tensor (0, or
+    CGS_ERR_TIMEOUT if a wait inside the kernel gave up)."""
+    L = len(layers)
+    _expect(r, "r", torch.float32)
+    if r.dim() != 2:
+        raise CgsError("r must be [S][d]")
+    S, d = r.shape
+    _expect(x, "x", torch.bfloat16, (L + 1, S, d))
+    _expect(status, "status", torch.int32, (1,), required=False)
+    arr = (_StepLayer * max(L, 1))()
+    kmax = 0
+    for i, ly in enumerate(layers):
+        cw = ly.w
+        K = cw.K
+        kmax = max(kmax, K)
+        _expect(cw.w_gate, f"layer {i} w_gate", torch.bfloat16, (K, d))
+        _expect(cw.w_up, f"layer {i} w_up", torch.bfloat16, (K, d))
+        _expect(cw.w_down_t, f"layer {i} w_down_t", torch.bfloat16)
+        if cw.w_down_t.dim() != 2 or cw.w_down_t.shape[0] != d:
+            raise CgsError(f"layer {i} w_down_t must be [{d}][ldk]")
+        _expect_index(ly.idx, f"layer {i} idx", K, required=False)
+        _expect(ly.y_anchor, f"layer {i} y_anchor", torch.float32, (S, d), required=False)
+        _expect(ly.h_anchor, f"layer {i} h_anchor", torch.float32, (ff, S), required=False)
+        _expect(ly.bias, f"layer {i} bias", torch.float32, (d,), required=False)
+        _expect(ly.y_out, f"layer {i} y_out", torch.bfloat16, (S, d), required=False)
+        _expect(ly.y_f32_out, f"layer {i} y_f32_out", torch.float32, (S, d), required=False)
+        _expect(ly.h_out, f"layer {i} h_out", torch.float32, (ff, S), required=False)
+        arr[i] = _StepLayer(_ptr(cw.w_gate), _ptr(cw.w_up), _ptr(cw.w_down_t), K, cw.ldk, _ptr(ly.idx),
+                            _ptr(ly.y_anchor), _ptr(ly.h_anchor), _ptr(ly.bias), _ptr(ly.y_out),
+                            _ptr(ly.y_f32_out), _ptr(ly.h_out))
+    nbytes = lib().cgs_act_denoise_step_workspace(L, S, d, kmax)
+    ws = workspace(nbytes, r.device, "step", stream) if ws is None else ws
+    _check(lib().act_denoise_step(arr, L, S, d, int(ff), _ptr(r), _ptr(x), _ptr(status), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "act_denoise_step")
+    return x
+
+
+def set_step_wait_limit(ticks: int) -> int:
+    """Time limit of act_denoise_step's internal waits (100 MHz device clock
+    ticks) for later launches; returns the previous one."""
+    return int(lib().cgs_set_step_wait_limit(int(ticks)))

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcgs.so")
-SOURCES = ["select.hip", "ffn.hip", "act.hip", "mask.hip", "retrieval.hip", "validate.hip", "api.cpp",
+SOURCES = ["select.hip", "ffn.hip", "act.hip", "mask.hip", "retrieval.hip", "validate.hip", "step.hip", "api.cpp",
            "profile.cpp", "cache.cpp"]
 
 # -ffp-contract=off: the fixed-point score and mask arithmetic relies on every

@@ -20,6 +20,7 @@ extern "C" const char* cgs_status_str(int status) {
     case CGS_ERR_UNSUPPORTED: return "unsupported dtype, layout or size";
     case CGS_ERR_LAUNCH: return "kernel launch failed";
     case CGS_ERR_DATA: return "device data break a documented precondition";
+    case CGS_ERR_TIMEOUT: return "a persistent kernel's bounded wait gave up";
     default: return "unknown status";
   }
 }

@@ -57,7 +57,8 @@ typedef enum {
   CGS_ERR_WORKSPACE = 3,    /* ws too small or null while needed */
   CGS_ERR_UNSUPPORTED = 4,  /* dtype / layout / size the library does not handle */
   CGS_ERR_LAUNCH = 5,       /* a kernel launch failed */
-  CGS_ERR_DATA = 6          /* device data break a documented precondition (checked mode only) */
+  CGS_ERR_DATA = 6,         /* device data break a documented precondition (checked mode only) */
+  CGS_ERR_TIMEOUT = 7       /* written to a status_out word: a persistent kernel's bounded wait gave up */
 } cgs_status;
 
 typedef enum { CGS_BF16 = 0, CGS_F32 = 1 } cgs_dtype;
@@ -281,6 +282,74 @@ int act_ffn_masked_compact(const cgs_ffn* wc, const void* x, int S, const int32_
                            const float* y_anchor, const float* h_anchor, void* y_out,
                            float* y_f32_out, float* h_out, const cgs_glue* glue, void* ws,
                            size_t ws_bytes, void* stream);
+
+/* ---- Action Cache: one whole masked denoising step in one launch -------- */
+
+/* act_gather_rows for the persistent step below: rows idx[0..K) of w_gate and
+ * w_up into [K][d] buffers, and the same neurons' down weights TRANSPOSED into
+ * wdt_out [d][ldk] (wdt_out[j][i] = w_down[idx[i]][j]; columns K .. ldk-1 are
+ * written as 0), so that the step kernel reads each output column's weights
+ * over the mask contiguously.  idx NULL means the identity (idx[i] = i), e.g.
+ * K = ff for a dense anchor step.  bf16 only; w: CGS_DOWN_FD, d % 64 == 0;
+ * ldk >= K rounded up to 32, ldk % 8 == 0.  K = 0 writes only the zero
+ * columns.  Issued as two kernels on `stream`; no workspace. */
+int act_gather_rows_t(const cgs_ffn* w, const int32_t* idx, int K, void* wg_out, void* wu_out,
+                      void* wdt_out, int ldk, void* stream);
+
+/* One layer of act_denoise_step (§4.1, Eq. 4 with the residual/RMSNorm glue).
+ * The mask M has K neurons; its weights are compact (act_gather_rows_t). */
+typedef struct {
+  const void* w_gate;    /* [K][d] bf16: row i is neuron idx[i]'s gate weights */
+  const void* w_up;      /* [K][d] bf16 */
+  const void* w_down_t;  /* [d][ldk] bf16: column i is neuron idx[i]'s down weights */
+  int32_t K;             /* mask size, 0 <= K <= min(ff, 4096) */
+  int32_t ldk;           /* row stride of w_down_t (>= K rounded up to 32, % 8 == 0) */
+  const int32_t* idx;    /* [K] ascending neuron ids (rows of h_anchor / h_out), or NULL
+                            for the identity (then K must be ff if h_anchor or h_out is set) */
+  const float* y_anchor; /* [S][d] fp32 anchor output, or NULL (= 0) */
+  const float* h_anchor; /* [ff][S] fp32 anchor activations (rows idx read), or NULL (= 0) */
+  const float* bias;     /* [d] fp32 added to r after this layer, or NULL */
+  void* y_out;           /* [S][d] bf16 output y of this layer, or NULL */
+  float* y_f32_out;      /* [S][d] fp32 y before rounding, or NULL */
+  float* h_out;          /* [ff][S] fp32: rows idx receive h^M, or NULL */
+} cgs_step_layer;
+
+/* Workspace bytes for act_denoise_step with masks of at most K_max neurons. */
+size_t cgs_act_denoise_step_workspace(int L, int S, int d, int K_max);
+
+/* A whole denoising step of L stacked masked FFN layers in ONE persistent
+ * launch (plus a small initialising kernel), for layer l = 0 .. L-1:
+ *   y_l = y_anchor_l + (h^M(x_l) - h_anchor_l^M) W_down[M]      (§4.1, Eq. 4)
+ *   r  += round_bf16(y_l) (+ bias_l),   x_{l+1} = RMSNorm(r)    (eps 1e-6, no scale)
+ * i.e. the same results as L calls of act_ffn_masked_compact with the glue
+ * (r, bias_l, x_{l+1}), up to the fp32 summation order.  With K = ff, idx NULL
+ * and no anchors a layer is the dense anchor step (y_f32_out / h_out give the
+ * anchor state of the later steps).
+ *   layers : HOST array of L (1 .. 24) layers.
+ *   S      : action tokens, 1 .. 64;  d: 256, 512 or 1024;  ff: neurons of the
+ *            full FFN (bound of idx and of the h rows).
+ *   r      : [S][d] fp32 residual stream, read at the start and written at the end.
+ *   x      : [L+1][S][d] bf16, 16-byte aligned: x[0] is the first layer's input
+ *            (RMSNorm(r) rounded, supplied by the caller); x[1..L] receive the
+ *            following layers' inputs (x[L] the next step's).  x[1..L] are
+ *            also the hand-off buffers between the kernel's workgroups.
+ *   status_out : device int32 or NULL; 0 on success, CGS_ERR_TIMEOUT if a
+ *            wait inside the kernel gave up (then every output is invalid).
+ * The kernel keeps one workgroup per CU resident for the whole step and hands
+ * data between them through device-coherent memory, polled until it is no
+ * longer the all-ones sentinel; every wait is bounded (cgs_set_step_wait_limit).
+ * Preconditions: finite inputs and weights (no value may round to the bf16 /
+ * fp32 all-ones pattern); no other launch of this kernel may run on the device
+ * at the same time (both would need every CU).  CGS_ERR_UNSUPPORTED when the
+ * device has fewer than 8 d / 32 or S CUs.  Errors as act_ffn_masked. */
+int act_denoise_step(const cgs_step_layer* layers, int L, int S, int d, int ff, float* r, void* x,
+                     int32_t* status_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Time limit of act_denoise_step's waits, in ticks of the 100 MHz device
+ * wall clock (default 2e7 = 0.2 s), for the launches that follow; returns the
+ * previous value (a negative argument only queries).  A test aid: a limit of
+ * 0 makes the first wait that is not already satisfied give up. */
+long long cgs_set_step_wait_limit(long long ticks);
 
 /* ---- Reference rebuild ------------------------------------------------- */
 

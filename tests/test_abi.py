@@ -13,8 +13,8 @@ import oracle as O
 def _declared_functions():
     src = open(cgs.HEADER_PATH).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\**([A-Za-z_][A-Za-z0-9_]*)\s*\(",
-                       src, flags=re.M)
+    names = re.findall(r"^\s*(?:const\s+)?(?:long\s+long|[A-Za-z_][A-Za-z0-9_]*)\s*\*?\s+\**"
+                       r"([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, flags=re.M)
     return sorted(set(names))
 
 
