@@ -30,17 +30,17 @@
 // group's urgent ones.
 //
 // Hand-offs: producers write with device-coherent stores (cache policy sc1),
-// consumers read with device-coherent loads and poll the data itself.  Every
-// hand-off buffer is filled with a sentinel (all ones: a NaN that no finite
-// result rounds to) by a small kernel launched first, so a consumer knows a
-// value is final as soon as it differs from the sentinel; no fence or
-// barrier is involved (a device-scope fence writes back a whole XCD L2).
-// The partial sums are double-buffered: a down tile, once it holds layer
-// l's deltas (which depend on every row finish of layer l-1), writes the
-// sentinel back over its own layer l-1 partials before it publishes layer l's.
-// Only producers write the locations a consumer polls: a value a consumer
-// wrote itself stays valid in its XCD's L2 and would hide later writes from
-// other XCDs (no hardware keeps the eight L2s coherent).
+// wait until the stores are acknowledged and then set a ready flag per wave
+// (x rows, gate/up tiles, down tiles); consumers poll only the flags they
+// depend on (one per lane) and then read the data once with device-coherent
+// loads.  No fence or grid barrier is involved (a device-scope fence writes
+// back a whole XCD L2), and no consumer ever writes a location it polls or
+// reads: a line a consumer wrote itself stays valid in its XCD's L2 and
+// would hide later writes from other XCDs (the eight L2s are not kept
+// coherent).  The flags are zeroed by a small kernel launched first.  The
+// partial sums are double-buffered; a down tile overwrites layer l-2's
+// partials only after its wait for layer l's deltas (or, for an empty K
+// split, for layer l-1's inputs) has shown that their readers are done.
 //
 // Every wait is bounded: past a time limit (or once another wave has given
 // up) a wave sets a device-wide abort flag, records CGS_ERR_TIMEOUT and
@@ -66,7 +66,7 @@ constexpr int kStepSplits = 8;      // K splits of the down projection
 constexpr int kStepCols = 32;       // output columns per down tile
 constexpr int kStepMaxSteps = 16;   // 32-position steps per split (<= 512 positions)
 constexpr int kCoh = 16;            // buffer cache policy: sc1 (device-coherent)
-constexpr uint32_t kSent = 0xffffffffu;
+constexpr int kStepMaxTiles = 256;  // gate/up and down tiles per layer, at most
 
 std::atomic<long long> g_wait_ticks{20000000};  // 0.2 s of the 100 MHz wall clock
 
@@ -91,6 +91,9 @@ struct StepArgs {
   float* r;               // [S][d]
   uint16_t* x;            // [L+1][S][d]
   float* pbuf;            // [2][kStepSplits][S][d]
+  int32_t* xflag;         // [L+1][64][4]: input row published, per wave of its row finish
+  int32_t* aflag;         // [L][2][256][4]: gate/up tile (token block, neuron block) done, per wave
+  int32_t* bflag;         // [L][4][256]: down tile done, per wave (token rows 16 w ..)
   uint32_t* abort_flag;   // workspace word
   int32_t* status_out;    // or NULL
   long long wait_ticks;
@@ -104,14 +107,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 __device__ __forceinline__ u32x4_t ld_coh16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   asm volatile("" ::: "memory");
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoh);
-}
-
-__device__ __forceinline__ bool no_sent16(u32x4_t v) {
-  // no bf16 half equals 0xffff
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if ((v[i] & 0xffffu) == 0xffffu || (v[i] >> 16) == 0xffffu) return false;
-  return true;
 }
 
 // Give up a wait once another wave aborted or the time limit passed.
@@ -154,6 +149,64 @@ __device__ __forceinline__ Frag<uint16_t> frag(u32x4_t v) {
   return f;
 }
 
+// Wait until flags[0 .. n) are all non-zero (n <= 256; lane i polls flags
+// i, i + 64, i + 128, i + 192 with device-coherent loads).  The time limit
+// and the abort flag are checked every 16 polls, so pollers do not all read
+// one word.  Returns false, for the whole wave, if the launch gave up.
+__device__ __forceinline__ bool wait_flags(const int32_t* flags, int n, const StepArgs& a) {
+  const int lane = threadIdx.x & 63;
+  const long long t0 = wall_clock64();
+  for (int it = 1;; ++it) {
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = lane + 64 * q;
+      asm volatile("" ::: "memory");
+      if (i < n) ok = ok && __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    }
+    if (!wave_any(!ok)) break;
+    if ((it & 15) == 0 && wave_any(!keep_waiting(a.abort_flag, a.status_out, a.wait_ticks, t0))) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+  return true;
+}
+
+// The four waves of a group wait for the same flags: wave 0 polls them and
+// then writes the group's wait count to an LDS word the other waves watch
+// (-1 if it gave up), so a flag line has one poller per group, not four.
+// Every spin in this kernel ends: a wait on flags by its time limit, a wait
+// on LDS words once the launch is aborted.
+__device__ __forceinline__ bool group_wait_flags(const int32_t* flags, int n, const StepArgs& a, int* gw,
+                                                 int& count) {
+  ++count;
+  const int wave = (threadIdx.x >> 6) & 3;
+  if (wave == 0) {
+    const bool ok = wait_flags(flags, n, a);
+    if ((threadIdx.x & 63) == 0) __hip_atomic_store(gw, ok ? count : -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return ok;
+  }
+  // Wave 0 may have left the launch without releasing this wait: it leaves
+  // a group barrier once the launch is aborted even if its siblings then
+  // pass that barrier and reach this wait.  So also watch the abort flag.
+  for (int it = 1;; ++it) {
+    const int v = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (v < 0) return false;
+    if (v >= count) break;
+    if ((it & 15) == 0 && __hip_atomic_load(a.abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+  return true;
+}
+
+// A wave publishes its stores: wait until they are acknowledged (device-
+// coherent stores are then visible device-wide), then set its flag.
+__device__ __forceinline__ void publish(int32_t* flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if ((threadIdx.x & 63) == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------------------
 // Stage A: gate/up of tile (token block tb, positions nb*16 .. +15).
 // Wave w covers d columns [w d/4, (w+1) d/4): KSA 32-wide K steps.
@@ -161,21 +214,30 @@ __device__ __forceinline__ Frag<uint16_t> frag(u32x4_t v) {
 template <int D>
 __device__ __attribute__((always_inline)) void step_gate_up(const StepArgs& a, int lw, float (*red)[4][2][kStepTok][16], int* ctr) {
   constexpr int KSA = D / 128;
-  constexpr int KH = KSA / 2 > 0 ? KSA / 2 : 1;  // K steps per x polling half
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, grp = lane >> 4;
   const int kq = wave * (D / 4);
   const int S = a.S;
-  int target = 0;
+  int target = 0, nwait = 0;
   int ntile = 0;  // A tiles processed: the LDS reduction buffer alternates per tile
   u32x4_t bg[KSA], bu[KSA];
   int hn[4];
   float ha[4];
 
+  // Gate/up tile of this workgroup: neuron block nb goes to XCD nb % 8 (its
+  // token blocks on one XCD, which shares their weight rows in L2), filling
+  // each XCD's slots from the first; returns false if there is none.
+  const int spx = a.G / 8, xcd = lw / spx, slot = lw % spx;
+  auto tile_of = [&](const StepLayer& Ly, int& nb, int& tb) -> bool {
+    tb = slot % Ly.ntb;
+    nb = (slot / Ly.ntb) * 8 + xcd;
+    return nb < Ly.nblk;
+  };
   auto prefetch = [&](int l) {
     const StepLayer& Ly = a.lay[l];
-    if (lw >= Ly.nblk * Ly.ntb) return;
-    const int nb = lw / Ly.ntb, tb = lw % Ly.ntb, tt = 4 / Ly.ntb;
+    int nb, tb;
+    if (!tile_of(Ly, nb, tb)) return;
+    const int tt = 4 / Ly.ntb;
     const int i = nb * 16 + r;
     const bool v = i < Ly.K;
 #pragma unroll
@@ -197,50 +259,40 @@ __device__ __attribute__((always_inline)) void step_gate_up(const StepArgs& a, i
   prefetch(0);
   for (int l = 0; l < a.L; ++l) {
     const StepLayer& Ly = a.lay[l];
-    if (lw < Ly.nblk * Ly.ntb) {
-      const int nb = lw / Ly.ntb, tb = lw % Ly.ntb, tt = 4 / Ly.ntb;
+    int nb, tb;
+    if (tile_of(Ly, nb, tb)) {
+      const int tt = 4 / Ly.ntb;
       const int t0 = tb * tt * 16;
+      // the block's input rows (layer 0: the caller's input)
+      const int nrows = min(S, t0 + 16 * tt) - t0;
+      if (l > 0 && nrows > 0 &&
+          !group_wait_flags(a.xflag + (static_cast<size_t>(l) * kStepTok + t0) * 4, nrows * 4, a, ctr + 2, nwait))
+        return;
       const auto rx = rsrc(a.x + static_cast<size_t>(l) * S * D, static_cast<uint32_t>(S) * D * 2);
       f32x4_t ag[4], au[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) ag[mt] = au[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      // x rows t0 .. t0 + 16 tt, in two halves of this wave's K steps; each
-      // half is polled until no value is the sentinel (layer 0: the input)
+      // x in two halves of this wave's K steps (registers)
+      constexpr int KH = KSA / 2;
 #pragma unroll
-      for (int h = 0; h < (KSA + KH - 1) / KH; ++h) {
+      for (int h = 0; h < 2; ++h) {
         u32x4_t xf[4][KH];
-        bool gave_up = false;
-        const long long t_start = wall_clock64();
-        while (true) {
-          bool ok = true;
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const int tok = t0 + mt * 16 + r;
-            const bool v = mt < tt && tok < S;
+        for (int mt = 0; mt < 4; ++mt) {
+          const int tok = t0 + mt * 16 + r;
+          const bool v = mt < tt && tok < S;
 #pragma unroll
-            for (int q = 0; q < KH; ++q) {
-              const int ks = h * KH + q;
-              if (v && ks < KSA) {
-                xf[mt][q] = ld_coh16(rx, static_cast<uint32_t>((tok * D + kq + ks * 32 + grp * 8) * 2));
-                if (l > 0) ok = ok && no_sent16(xf[mt][q]);
-              } else {
-                xf[mt][q] = u32x4_t{0u, 0u, 0u, 0u};
-              }
-            }
-          }
-          if (ok) break;
-          if (!keep_waiting(a.abort_flag, a.status_out, a.wait_ticks, t_start)) { gave_up = true; break; }
+          for (int q = 0; q < KH; ++q)
+            xf[mt][q] = v ? ld_coh16(rx, static_cast<uint32_t>((tok * D + kq + (h * KH + q) * 32 + grp * 8) * 2))
+                          : u32x4_t{0u, 0u, 0u, 0u};
         }
-        if (wave_any(gave_up)) return;
 #pragma unroll
         for (int q = 0; q < KH; ++q) {
-          const int ks = h * KH + q;
-          if (ks >= KSA) break;
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) {
             if (mt < tt) {
-              ag[mt] = mma(frag(xf[mt][q]), frag(bg[ks]), ag[mt]);
-              au[mt] = mma(frag(xf[mt][q]), frag(bu[ks]), au[mt]);
+              ag[mt] = mma(frag(xf[mt][q]), frag(bg[h * KH + q]), ag[mt]);
+              au[mt] = mma(frag(xf[mt][q]), frag(bu[h * KH + q]), au[mt]);
             }
           }
         }
@@ -279,6 +331,7 @@ __device__ __attribute__((always_inline)) void step_gate_up(const StepArgs& a, i
                                                 static_cast<uint32_t>((tok * Ly.kpad + pos) * 2), 0, kCoh);
         }
       }
+      publish(a.aflag + ((static_cast<size_t>(l) * 2 + tb) * kStepMaxTiles + nb) * 4 + wave);
     }
     if (l + 1 < a.L) prefetch(l + 1);
   }
@@ -291,20 +344,25 @@ __device__ __attribute__((always_inline)) void step_gate_up(const StepArgs& a, i
 template <int D, int MS>
 __device__ __attribute__((always_inline)) void step_down_finish(const StepArgs& a, int lw, float (*red)[4], int* ctr) {
   constexpr int NCB = D / kStepCols;
+  constexpr int NBT = kStepSplits * NCB;  // down tiles
   constexpr int CPT = D / 256;  // columns per thread in the row finish
   const int tid = threadIdx.x - 256, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, grp = lane >> 4;
   const int S = a.S;
-  const bool have_b = lw < kStepSplits * NCB;
+  const bool have_b = lw < NBT;
   const int ks_ = lw / NCB, cb = lw % NCB;
-  const bool owner = lw < S;
+  // token row finished by this workgroup (-1: none): rows spread over the
+  // XCDs (row s on XCD s % 8), in the slots the gate/up tiles use last
+  const int spx = a.G / 8, xcd = lw / spx, slot = lw % spx;
+  const int row = (slot >= spx - (S + 7) / 8) ? (spx - 1 - slot) * 8 + xcd : -1;
+  const bool owner = row >= 0 && row < S;
   const int c0 = tid * CPT;
-  int target = 0;
+  int target = 0, nwait = 0;
 
   float rr[CPT], ya[CPT], bi[CPT];
   if (owner) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) rr[c] = a.r[static_cast<size_t>(lw) * D + c0 + c];
+    for (int c = 0; c < CPT; ++c) rr[c] = a.r[static_cast<size_t>(row) * D + c0 + c];
   }
   u32x4_t wf[MS][2];
   auto split_steps = [&](const StepLayer& Ly) {
@@ -329,7 +387,7 @@ __device__ __attribute__((always_inline)) void step_down_finish(const StepArgs& 
     if (owner) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        ya[c] = Ly.ya ? Ly.ya[static_cast<size_t>(lw) * D + c0 + c] : 0.f;
+        ya[c] = Ly.ya ? Ly.ya[static_cast<size_t>(row) * D + c0 + c] : 0.f;
         bi[c] = Ly.bias ? Ly.bias[c0 + c] : 0.f;
       }
     }
@@ -342,121 +400,83 @@ __device__ __attribute__((always_inline)) void step_down_finish(const StepArgs& 
     const auto rp = rsrc(a.pbuf + static_cast<size_t>(l & 1) * kStepSplits * S * D, pbytes);
     if (have_b) {
       const int nst = split_steps(Ly), p0 = ks_ * Ly.kc;
-      const auto rd = rsrc(Ly.dbuf, static_cast<uint32_t>(kStepTok) * Ly.kpad * 2);
       const int tok = wave * 16 + r;
       f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-      constexpr int SH = MS / 2;
+      if (nst > 0) {
+        // deltas of this split for this wave's token rows: the gate/up tiles
+        // of the split's neuron blocks and of the token block holding them
+        const int nb0 = p0 / 16, nb1 = (p0 + nst * 32) / 16;
+        // wave 0 polls for the whole group: every token block's tiles
+        bool ok = true;
+        for (int tb = 0; tb < Ly.ntb && ok; ++tb)
+          ok = group_wait_flags(a.aflag + ((static_cast<size_t>(l) * 2 + tb) * kStepMaxTiles + nb0) * 4,
+                                (nb1 - nb0) * 4, a, ctr + 2, nwait);
+        if (!ok) return;
+        const auto rd = rsrc(Ly.dbuf, static_cast<uint32_t>(kStepTok) * Ly.kpad * 2);
+        constexpr int SH = MS / 2;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (h * SH >= nst) break;
-        u32x4_t df[SH];
-        bool gave_up = false;
-        const long long t_start = wall_clock64();
-        while (true) {
-          bool ok = true;
+        for (int h = 0; h < 2; ++h) {
+          if (h * SH >= nst) break;
+          u32x4_t df[SH];
+#pragma unroll
+          for (int q = 0; q < SH; ++q) {
+            const int st = h * SH + q;
+            df[q] = st < nst ? ld_coh16(rd, static_cast<uint32_t>((tok * Ly.kpad + p0 + st * 32 + grp * 8) * 2))
+                             : u32x4_t{0u, 0u, 0u, 0u};
+          }
 #pragma unroll
           for (int q = 0; q < SH; ++q) {
             const int st = h * SH + q;
             if (st < nst) {
-              df[q] = ld_coh16(rd, static_cast<uint32_t>((tok * Ly.kpad + p0 + st * 32 + grp * 8) * 2));
-              ok = ok && no_sent16(df[q]);
-            } else {
-              df[q] = u32x4_t{0u, 0u, 0u, 0u};
+              acc[0] = mma(frag(df[q]), frag(wf[st][0]), acc[0]);
+              acc[1] = mma(frag(df[q]), frag(wf[st][1]), acc[1]);
             }
           }
-          if (ok) break;
-          if (!keep_waiting(a.abort_flag, a.status_out, a.wait_ticks, t_start)) { gave_up = true; break; }
         }
-        if (wave_any(gave_up)) return;
-#pragma unroll
-        for (int q = 0; q < SH; ++q) {
-          const int st = h * SH + q;
-          if (st < nst) {
-            acc[0] = mma(frag(df[q]), frag(wf[st][0]), acc[0]);
-            acc[1] = mma(frag(df[q]), frag(wf[st][1]), acc[1]);
-          }
-        }
-      }
-      // This tile's layer l-1 partials (the other buffer) back to the
-      // sentinel, for layer l+1.  The rows this wave resets (16 w .. 16 w +
-      // 15) have been read by their row finish of layer l-1 once x_l of those
-      // rows is published (the finish writes x_l after its reads); the wave
-      // polls that first (the deltas of a non-empty split already imply it).
-      // The reset is made by the tile that writes those locations again
-      // (same workgroup, same XCD), never by the row finish that polls them:
-      // a line a consumer wrote itself would stay valid in its XCD's L2 and
-      // hide the next values written from other XCDs.
-      if (l >= 1) {
-        {
-          const int xrow = wave * 16 + r;
-          const auto rx = rsrc(a.x + static_cast<size_t>(l) * S * D, static_cast<uint32_t>(S) * D * 2);
-          bool gave_up = false;
-          const long long t_start = wall_clock64();
-          while (xrow < S) {
-            const u32x4_t v = ld_coh16(rx, static_cast<uint32_t>((xrow * D + grp * 8) * 2));
-            if (no_sent16(v)) break;
-            if (!keep_waiting(a.abort_flag, a.status_out, a.wait_ticks, t_start)) { gave_up = true; break; }
-          }
-          if (wave_any(gave_up)) return;
-        }
-        const auto rq = rsrc(a.pbuf + static_cast<size_t>((l - 1) & 1) * kStepSplits * S * D, pbytes);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int row = wave * 16 + 4 * grp + v;
-            const int col = cb * kStepCols + nt * 16 + r;
-            if (row < S)
-              __builtin_amdgcn_raw_buffer_store_b32(kSent, rq, static_cast<uint32_t>(((ks_ * S + row) * D + col) * 4),
-                                                    0, kCoh);
-          }
-        }
-        // the reset lands before this layer's partials can be observed
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else if (l >= 2) {
+        // An empty split waits for nothing of this layer, but its zero
+        // partials overwrite the buffer of layer l-2: first wait until those
+        // rows' finishes of layer l-2 are done (implied by the published
+        // inputs of layer l-1 for this wave's rows).
+        if (!group_wait_flags(a.xflag + static_cast<size_t>(l - 1) * kStepTok * 4, S * 4, a, ctr + 2, nwait))
+          return;
       }
       // fp32 partials [split][token][column]; rows past S are not stored
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int row = wave * 16 + 4 * grp + v;
+          const int prow = wave * 16 + 4 * grp + v;
           const int col = cb * kStepCols + nt * 16 + r;
-          if (row < S)
+          if (prow < S)
             __builtin_amdgcn_raw_buffer_store_b32(
                 __float_as_uint(acc[nt][v]), rp,
-                static_cast<uint32_t>(((ks_ * S + row) * D + col) * 4), 0, kCoh);
+                static_cast<uint32_t>(((ks_ * S + prow) * D + col) * 4), 0, kCoh);
         }
       }
+      publish(a.bflag + (static_cast<size_t>(l) * 4 + wave) * kStepMaxTiles + lw);
     }
     if (owner) {
-      // partials of every split for row lw, polled until final
+      // partials of every split for this row: the wave row / 16 of every down tile
+      if (!group_wait_flags(a.bflag + (static_cast<size_t>(l) * 4 + row / 16) * kStepMaxTiles, NBT, a, ctr + 2,
+                            nwait))
+        return;
       float pv[kStepSplits][CPT];
-      bool gave_up = false;
-      const long long t_start = wall_clock64();
-      while (true) {
-        bool ok = true;
 #pragma unroll
-        for (int k = 0; k < kStepSplits; ++k) {
-          const uint32_t off = static_cast<uint32_t>(((k * S + lw) * D + c0) * 4);
-          asm volatile("" ::: "memory");
-          if constexpr (CPT == 4) {
-            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCoh);
+      for (int k = 0; k < kStepSplits; ++k) {
+        const uint32_t off = static_cast<uint32_t>(((k * S + row) * D + c0) * 4);
+        if constexpr (CPT == 4) {
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCoh);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) { pv[k][c] = __uint_as_float(v[c]); ok = ok && v[c] != kSent; }
-          } else if constexpr (CPT == 2) {
-            const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rp, off, 0, kCoh));
+          for (int c = 0; c < 4; ++c) pv[k][c] = __uint_as_float(v[c]);
+        } else if constexpr (CPT == 2) {
+          const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rp, off, 0, kCoh));
 #pragma unroll
-            for (int c = 0; c < 2; ++c) { pv[k][c] = __uint_as_float(v[c]); ok = ok && v[c] != kSent; }
-          } else {
-            const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, kCoh);
-            pv[k][0] = __uint_as_float(v);
-            ok = ok && v != kSent;
-          }
+          for (int c = 0; c < 2; ++c) pv[k][c] = __uint_as_float(v[c]);
+        } else {
+          pv[k][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, kCoh));
         }
-        if (ok) break;
-        if (!keep_waiting(a.abort_flag, a.status_out, a.wait_ticks, t_start)) { gave_up = true; break; }
       }
-      if (wave_any(gave_up)) return;
       float ss = 0.f;
       float y[CPT];
 #pragma unroll
@@ -469,7 +489,7 @@ __device__ __attribute__((always_inline)) void step_down_finish(const StepArgs& 
         if (Ly.bias) rr[c] += bi[c];
         ss += rr[c] * rr[c];
       }
-      const size_t ro = static_cast<size_t>(lw) * D + c0;
+      const size_t ro = static_cast<size_t>(row) * D + c0;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         if (Ly.y_out) Ly.y_out[ro + c] = f32_to_bf16(y[c]);
@@ -485,7 +505,8 @@ __device__ __attribute__((always_inline)) void step_down_finish(const StepArgs& 
 #pragma unroll
       for (int c = 0; c < CPT; ++c)
         __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(rr[c] * inv), rx,
-                                              static_cast<uint32_t>((lw * D + c0 + c) * 2), 0, kCoh);
+                                              static_cast<uint32_t>((row * D + c0 + c) * 2), 0, kCoh);
+      publish(a.xflag + (static_cast<size_t>(l + 1) * kStepTok + row) * 4 + wave);
       if (l + 1 == a.L) {
 #pragma unroll
         for (int c = 0; c < CPT; ++c) a.r[ro + c] = rr[c];
@@ -499,28 +520,24 @@ template <int D, int MS>
 __global__ __launch_bounds__(kStepThreads) void act_step_kernel(StepArgs a) {
   __shared__ float red_a[2][4][2][kStepTok][16];
   __shared__ float red_b[2][4];
-  __shared__ int ctr[2];
-  if (threadIdx.x < 2) ctr[threadIdx.x] = 0;
+  __shared__ int ctr[6];  // per group: barrier counter, -, released wait count
+  if (threadIdx.x < 6) ctr[threadIdx.x] = 0;
   __syncthreads();
   // logical tile of this workgroup: consecutive tiles on one XCD (workgroups
   // are dealt round-robin over the 8 XCDs), so the two token blocks of a
   // neuron block, and the column blocks of one K split, share an L2
   const int b = blockIdx.x;
-  const int lw = (a.G % 8 == 0) ? (b % 8) * (a.G / 8) + b / 8 : b;
+  const int lw = (b % 8) * (a.G / 8) + b / 8;
   if (threadIdx.x < 256) step_gate_up<D>(a, lw, red_a, &ctr[0]);
-  else step_down_finish<D, MS>(a, lw, red_b, &ctr[1]);
+  else step_down_finish<D, MS>(a, lw, red_b, &ctr[3]);
 }
 
-// Sentinel fill of the hand-off buffers (16-byte words) and the abort flag.
-__global__ __launch_bounds__(256) void step_init_kernel(u32x4_t* p0, size_t n0, u32x4_t* p1, size_t n1,
-                                                        u32x4_t* p2, size_t n2, uint32_t* abort_flag,
+// Zero the ready flags and the abort flag of a launch (int32 words).
+__global__ __launch_bounds__(256) void step_init_kernel(int32_t* flags, size_t n, uint32_t* abort_flag,
                                                         int32_t* status_out) {
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-  const u32x4_t s = u32x4_t{kSent, kSent, kSent, kSent};
-  for (size_t j = i; j < n0; j += stride) p0[j] = s;
-  for (size_t j = i; j < n1; j += stride) p1[j] = s;
-  for (size_t j = i; j < n2; j += stride) p2[j] = s;
+  for (size_t j = i; j < n; j += stride) flags[j] = 0;
   if (i == 0) {
     *abort_flag = 0u;
     if (status_out) *status_out = 0;
@@ -578,6 +595,7 @@ struct StepPlan {
   int kpad[kMaxStepLayers];
   size_t dbuf_off[kMaxStepLayers];  // elements
   size_t dbuf_elems, p_elems;
+  size_t nx, na, nb;                // ready flags (int32) of each kind
   size_t bytes;
 };
 
@@ -598,8 +616,12 @@ StepPlan plan_step(int L, int S, int d, const int* K) {
   }
   p.dbuf_elems = off;
   p.p_elems = static_cast<size_t>(2) * kStepSplits * S * d;
+  p.nx = static_cast<size_t>(L + 1) * kStepTok * 4;
+  p.na = static_cast<size_t>(L) * 2 * kStepMaxTiles * 4;
+  p.nb = static_cast<size_t>(L) * 4 * kStepMaxTiles;
   cv.take<uint16_t>(std::max<size_t>(p.dbuf_elems, 8));
   cv.take<float>(p.p_elems);
+  cv.take<int32_t>(p.nx + p.na + p.nb);
   cv.take<uint32_t>(64);
   p.bytes = cv.bytes();
   return p;
@@ -682,7 +704,7 @@ extern "C" int act_denoise_step(const cgs_step_layer* layers, int L, int S, int 
     if (!dma_span_ok(d, std::max(Ly.ldk, 1), 2) || !dma_span_ok(std::max(Ly.K, 1), d, 2)) return CGS_ERR_UNSUPPORTED;
   }
   const int G = step_grid(d);
-  if (G < kStepSplits * (d / kStepCols) || G < S) return CGS_ERR_UNSUPPORTED;
+  if (G % 8 != 0 || G < kStepSplits * (d / kStepCols) || G < 8 * ((S + 7) / 8)) return CGS_ERR_UNSUPPORTED;
   const StepPlan p = plan_step(L, S, d, K);
   if (!ws || ws_bytes < p.bytes) return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -693,10 +715,12 @@ extern "C" int act_denoise_step(const cgs_step_layer* layers, int L, int S, int 
   Carve cv(ws);
   uint16_t* dbuf = cv.take<uint16_t>(std::max<size_t>(p.dbuf_elems, 8));
   float* pbuf = cv.take<float>(p.p_elems);
+  int32_t* flags = cv.take<int32_t>(p.nx + p.na + p.nb);
   uint32_t* abort_flag = cv.take<uint32_t>(64);
   StepArgs a{};
   a.L = L; a.S = S; a.G = G;
   a.r = r; a.x = static_cast<uint16_t*>(x); a.pbuf = pbuf; a.abort_flag = abort_flag;
+  a.xflag = flags; a.aflag = flags + p.nx; a.bflag = flags + p.nx + p.na;
   a.status_out = status_out;
   a.wait_ticks = g_wait_ticks.load();
   for (int l = 0; l < L; ++l) {
@@ -716,12 +740,7 @@ extern "C" int act_denoise_step(const cgs_step_layer* layers, int L, int S, int 
   }
   {
     ProfScope ps("act.step.init", s);
-    const size_t n0 = static_cast<size_t>(L) * S * d * 2 / 16;   // x[1 .. L]
-    const size_t n1 = p.dbuf_elems * 2 / 16;
-    const size_t n2 = p.p_elems * 4 / 16;
-    hipLaunchKernelGGL(step_init_kernel, dim3(256), dim3(256), 0, s,
-                       reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(x) + static_cast<size_t>(S) * d), n0,
-                       reinterpret_cast<u32x4_t*>(dbuf), n1, reinterpret_cast<u32x4_t*>(pbuf), n2, abort_flag,
+    hipLaunchKernelGGL(step_init_kernel, dim3(64), dim3(256), 0, s, flags, p.nx + p.na + p.nb, abort_flag,
                        status_out);
   }
   if (!launch_ok()) return CGS_ERR_LAUNCH;
