@@ -44,8 +44,9 @@
 //
 // Every wait is bounded: past a time limit (or once another wave has given
 // up) a wave sets a device-wide abort flag, records CGS_ERR_TIMEOUT and
-// leaves, so a violated precondition (a sentinel-valued input, too few
-// co-resident workgroups) ends the launch instead of hanging it.
+// leaves, so a violated precondition (too few co-resident workgroups, a
+// concurrent launch on the same workspace) ends the launch instead of
+// hanging it.
 #include <algorithm>
 #include <atomic>
 #include <mutex>

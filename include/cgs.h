@@ -336,12 +336,13 @@ size_t cgs_act_denoise_step_workspace(int L, int S, int d, int K_max);
  *   status_out : device int32 or NULL; 0 on success, CGS_ERR_TIMEOUT if a
  *            wait inside the kernel gave up (then every output is invalid).
  * The kernel keeps one workgroup per CU resident for the whole step and hands
- * data between them through device-coherent memory, polled until it is no
- * longer the all-ones sentinel; every wait is bounded (cgs_set_step_wait_limit).
- * Preconditions: finite inputs and weights (no value may round to the bf16 /
- * fp32 all-ones pattern); no other launch of this kernel may run on the device
- * at the same time (both would need every CU).  CGS_ERR_UNSUPPORTED when the
- * device has fewer than 8 d / 32 or S CUs.  Errors as act_ffn_masked. */
+ * data between them through device-coherent stores and per-wave ready flags
+ * (zeroed by the initialising kernel); every wait is bounded
+ * (cgs_set_step_wait_limit).  Preconditions: no other launch of this kernel
+ * may run on the device at the same time (both would need every CU); the
+ * workspace is not shared with a concurrent launch.  CGS_ERR_UNSUPPORTED when
+ * the device has fewer than 8 d / 32 or S CUs.  Errors as act_ffn_masked.
+ * Steps of several launches (one per call) race if they overlap on a device. */
 int act_denoise_step(const cgs_step_layer* layers, int L, int S, int d, int ff, float* r, void* x,
                      int32_t* status_out, void* ws, size_t ws_bytes, void* stream);
 
