@@ -94,6 +94,7 @@ _SIGS = {
     "cgs_act_ffn_masked_workspace": (_sz, [_i, _i, _i, _i]),
     "act_ffn_masked": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "act_ffn_masked_compact": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "act_ffn_masked_compact_noalloc": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "act_gather_rows": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp]),
     "act_ffn_joint": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cgs_ref_rebuild_dense_workspace": (_sz, [_i, _i, _i, _i, _i]),
@@ -485,6 +486,29 @@ def act_ffn_masked_compact(wc: FFN, x, idx, y_anchor=None, h_anchor=None, y_out=
                                         _ptr(h_anchor), _ptr(y_out), _ptr(y_f32_out), _ptr(h_out),
                                         _glue(glue), _ptr(ws), ws.numel(), _stream(stream)),
            "act_ffn_masked_compact")
+    return y_out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # CGS_NOALLOC_SCRATCH_BYTES
+
+
+def act_ffn_masked_compact_noalloc(wc: FFN, x, idx, y_out, y_anchor=None, h_anchor=None, y_f32_out=None,
+                                   h_out=None, glue=None, stream=None, K=None):
+    """act_ffn_masked_compact for callers that cannot allocate: no workspace,
+    and every output is the caller's (y_out is required).  The library's
+    per-GPU scratch holds the intermediates, so calls that overlap in time on
+    one GPU race; masks whose workspace would exceed NOALLOC_SCRATCH_BYTES are
+    refused (CGS_ERR_WORKSPACE)."""
+    c = wc.cstruct()
+    K = wc.ff if K is None else int(K)
+    _check_act_io(wc, x, y_anchor, h_anchor, y_f32_out, h_out, glue, ff_rows=-1)
+    _expect_index(idx, "idx", K, required=False)
+    S, d = x.shape
+    _expect(y_out, "y_out", wc.dtype, (S, d))
+    _check(lib().act_ffn_masked_compact_noalloc(ctypes.byref(c), _ptr(x), S, _ptr(idx), K, _ptr(y_anchor),
+                                                _ptr(h_anchor), _ptr(y_out), _ptr(y_f32_out), _ptr(h_out),
+                                                _glue(glue), _stream(stream)),
+           "act_ffn_masked_compact_noalloc")
     return y_out
 
 

@@ -22,6 +22,7 @@
 //   act_finish_kernel sums the partials in split order, adds y_a, stores y
 //       (and its fp32 value), and optionally applies the residual/RMSNorm glue.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "gemm.hpp"
@@ -439,6 +440,17 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
   return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
 }
 
+// act_ffn_masked_compact once its arguments are checked.
+int act_compact(const cgs_ffn& wc, const void* x, int S, const int32_t* idx, int K, const float* ya,
+                const float* ha, void* y_out, float* y_f32, float* h_out, const cgs_glue* gl, void* ws,
+                hipStream_t s) {
+  if (wc.dtype == CGS_BF16)
+    return act_t<uint16_t, true>(wc, static_cast<const uint16_t*>(x), S, idx, K, ya, ha,
+                                 static_cast<uint16_t*>(y_out), y_f32, h_out, gl, ws, s, false);
+  return act_t<float, true>(wc, static_cast<const float*>(x), S, idx, K, ya, ha, static_cast<float*>(y_out),
+                            y_f32, h_out, gl, ws, s, false);
+}
+
 }  // namespace
 }  // namespace cgs
 
@@ -498,11 +510,61 @@ extern "C" int act_ffn_masked_compact(const cgs_ffn* wc, const void* x, int S, c
   if (!ws || ws_bytes < cgs_act_ffn_masked_workspace(S, K, wc->d, std::max(K, 1))) return CGS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (const int st = validate_index(idx, K, INT32_MAX, s)) return st;
-  if (wc->dtype == CGS_BF16)
-    return act_t<uint16_t, true>(*wc, static_cast<const uint16_t*>(x), S, idx, K, y_anchor, h_anchor,
-                                 static_cast<uint16_t*>(y_out), y_f32_out, h_out, glue, ws, s, false);
-  return act_t<float, true>(*wc, static_cast<const float*>(x), S, idx, K, y_anchor, h_anchor,
-                            static_cast<float*>(y_out), y_f32_out, h_out, glue, ws, s, false);
+  return act_compact(*wc, x, S, idx, K, y_anchor, h_anchor, y_out, y_f32_out, h_out, glue, ws, s);
+}
+
+// Scratch of act_ffn_masked_compact_noalloc: the deltas and split partials
+// that the caller's workspace holds otherwise.  Each GPU has its own copy;
+// host code uses only the per-device address from hipGetSymbolAddress (the
+// array's name on the host is a stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[CGS_NOALLOC_SCRATCH_BYTES];
+
+namespace cgs {
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+// The scratch array's device address on the current device, looked up once
+// per device with that device current.
+int scratch_address(hipStream_t s, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return CGS_ERR_LAUNCH;
+  if (s) {
+    int sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return CGS_ERR_ARG;
+    if (sdev != dev) return CGS_ERR_ARG;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CGS_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CGS_OK;
+}
+}  // namespace
+}  // namespace cgs
+
+extern "C" int act_ffn_masked_compact_noalloc(const cgs_ffn* wc, const void* x, int S, const int32_t* idx,
+                                              int K, const float* y_anchor, const float* h_anchor,
+                                              void* y_out, float* y_f32_out, float* h_out,
+                                              const cgs_glue* glue, void* stream) {
+  if (!wc || (K > 0 && (!wc->w_gate || !wc->w_up || !wc->w_down)) || !valid_dtype(wc->dtype) ||
+      wc->down_layout != CGS_DOWN_FD || !x || !y_out || !glue_ok(glue) ||
+      (K > 0 && !idx && (h_anchor || h_out)))
+    return CGS_ERR_ARG;
+  if (!act_shape_ok(wc->d, std::max(wc->ff, 1))) return CGS_ERR_UNSUPPORTED;
+  if (S < 0 || K < 0 || K != wc->ff) return CGS_ERR_SHAPE;
+  if (S == 0) return CGS_OK;
+  if (cgs_act_ffn_masked_workspace(S, K, wc->d, std::max(K, 1)) > CGS_NOALLOC_SCRATCH_BYTES)
+    return CGS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (const int st = scratch_address(s, &ws)) return st;
+  // no checked-mode pass here: it synchronises and allocates
+  return act_compact(*wc, x, S, idx, K, y_anchor, h_anchor, y_out, y_f32_out, h_out, glue, ws, s);
 }
 
 extern "C" int act_ffn_joint(const cgs_ffn* wc, const void* x, int S, const int32_t* tok, int k,

@@ -283,6 +283,27 @@ int act_ffn_masked_compact(const cgs_ffn* wc, const void* x, int S, const int32_
                            float* y_f32_out, float* h_out, const cgs_glue* glue, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * act_ffn_masked_compact without a workspace argument.  Its kernels use a
+ * scratch array that the library holds in device memory, one copy per GPU,
+ * kept until the process ends; the call allocates nothing.
+ *   Limit: cgs_act_ffn_masked_workspace(S, K, d, K) <= CGS_NOALLOC_SCRATCH_BYTES
+ *   (8 MiB: it holds e.g. S <= 64 tokens with K <= 4096 neurons at d <= 1024);
+ *   larger calls return CGS_ERR_WORKSPACE before any launch.
+ * The scratch's device address is looked up on the first call on each device
+ * (the current device; `stream` must belong to it, else CGS_ERR_ARG);
+ * CGS_ERR_LAUNCH if that lookup fails.  Nothing in the scratch has to start at
+ * zero: each call writes every scratch element it reads.  All calls on one GPU
+ * share its scratch, so calls that overlap in time on one GPU (on different
+ * streams, or from several threads without ordering) race and give wrong
+ * results.  The checked mode (cgs_set_validate) does not apply to this call.
+ * Arguments, results and other errors as act_ffn_masked_compact. */
+#define CGS_NOALLOC_SCRATCH_BYTES (8u << 20)
+int act_ffn_masked_compact_noalloc(const cgs_ffn* wc, const void* x, int S, const int32_t* idx, int K,
+                                   const float* y_anchor, const float* h_anchor, void* y_out,
+                                   float* y_f32_out, float* h_out, const cgs_glue* glue, void* stream);
+
 /* ---- Action Cache: one whole masked denoising step in one launch -------- */
 
 /* act_gather_rows for the persistent step below: rows idx[0..K) of w_gate and

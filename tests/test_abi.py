@@ -316,3 +316,29 @@ def test_operands_past_32_bit_offsets_are_unsupported():
     rr = cgs._Rerank(4, 14, -1, 0.8)
     assert L.ret_select(buf, buf, 16, (1 << 24) + 8, 0, 4, buf, buf, ctypes.byref(rr), buf, buf, buf, buf, buf,
                         1 << 30, None) == 2
+
+
+def test_noalloc_entry_point_refuses_before_any_device_call():
+    """The no-allocation variant rejects bad arguments and masks whose
+    intermediates exceed its fixed scratch before it touches the device."""
+    L = cgs.lib()
+    buf = ctypes.c_void_p(0x1000)
+    out = ctypes.c_void_p(0x2000)
+    assert cgs.NOALLOC_SCRATCH_BYTES == 8 << 20
+    # the advertised limit: 64 tokens x 4096 neurons at d = 1024 fit
+    assert L.cgs_act_ffn_masked_workspace(64, 4096, 1024, 4096) <= cgs.NOALLOC_SCRATCH_BYTES
+    big_k = 16384                      # 64 tokens x 16384 neurons do not
+    assert L.cgs_act_ffn_masked_workspace(64, big_k, 1024, big_k) > cgs.NOALLOC_SCRATCH_BYTES
+    wc = _ffn(d=1024, ff=big_k, layout=1)
+    assert L.act_ffn_masked_compact_noalloc(ctypes.byref(wc), buf, 64, buf, big_k, None, None, out, None,
+                                            None, None, None) == 3        # CGS_ERR_WORKSPACE
+    w4 = _ffn(d=1024, ff=4096, layout=1)
+    assert L.act_ffn_masked_compact_noalloc(ctypes.byref(w4), buf, 64, buf, 4095, None, None, out, None,
+                                            None, None, None) == 2        # K != wc->ff
+    assert L.act_ffn_masked_compact_noalloc(ctypes.byref(w4), None, 64, buf, 4096, None, None, out, None,
+                                            None, None, None) == 1        # x missing
+    assert L.act_ffn_masked_compact_noalloc(ctypes.byref(w4), buf, 0, buf, 4096, None, None, out, None,
+                                            None, None, None) == 0        # S = 0: nothing to do
+    w_odd = _ffn(d=1000, ff=4096, layout=1)
+    assert L.act_ffn_masked_compact_noalloc(ctypes.byref(w_odd), buf, 64, buf, 4096, None, None, out, None,
+                                            None, None, None) == 4
