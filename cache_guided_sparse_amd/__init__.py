@@ -96,6 +96,10 @@ _SIGS = {
     "act_ffn_masked_compact": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "act_ffn_masked_compact_noalloc": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "act_gather_rows": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp]),
+    "act_mask_indices": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+    "cgs_denoise_schedule": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "cgs_act_masked_layers_workspace": (_sz, [_i, _i, _i]),
+    "act_masked_layers": (_i, [_vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "act_ffn_joint": (_i, [_vp, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "cgs_ref_rebuild_dense_workspace": (_sz, [_i, _i, _i, _i, _i]),
     "ref_rebuild_dense": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _sz, _vp]),
@@ -367,6 +371,29 @@ def act_down_norms(layers, out=None, stream=None):
     return out
 
 
+def act_mask_indices(masks, ff: int, idx_out=None, count_out=None, stream=None):
+    """Stored bit-packed masks [..., ceil(ff/64)] int64 (bit i%64 of word i/64
+    = neuron i) -> (idx [..., ff] int32 ascending then -1, count [...] int32)."""
+    ff = int(ff)
+    words = (ff + 63) // 64
+    _expect(masks, "masks", torch.int64)
+    if masks.dim() < 1 or masks.shape[-1] != words:
+        raise CgsError(f"masks must be [..., {words}] int64 words for ff = {ff}")
+    lead = tuple(masks.shape[:-1])
+    n = 1
+    for v in lead:
+        n *= int(v)
+    if idx_out is None:
+        idx_out = torch.empty(lead + (ff,), dtype=torch.int32, device=masks.device)
+    if count_out is None:
+        count_out = torch.empty(lead, dtype=torch.int32, device=masks.device)
+    _expect(idx_out, "idx_out", torch.int32, lead + (ff,))
+    _expect(count_out, "count_out", torch.int32, lead)
+    _check(lib().act_mask_indices(_ptr(masks), n, ff, _ptr(idx_out), _ptr(count_out), _stream(stream)),
+           "act_mask_indices")
+    return idx_out, count_out
+
+
 def act_build_masks(h_ref, layers, mode: str = "topk", K: int = 0, coverage: float = 0.0,
                     mask_out=None, idx_out=None, count_out=None, ws=None, stream=None, norms=None):
     """Group masks of several layers at once: h_ref [layers][T][ff][S] float32,
@@ -570,6 +597,22 @@ def prep_budget(n_cand: int, m_free: float, m_entry: float, t_avl: float, t_tran
     return n
 
 
+def denoise_schedule(counts, words, ff: int):
+    """The schedule an entry's stored masks imply (cgs_denoise_schedule):
+    counts [L][T] int, words [L][T][ceil(ff/64)] int64/uint64 host arrays.
+    Returns (kind [T]: 0 anchor / 1 update, anchor [T], mask [T]) as lists."""
+    import numpy as np
+    c = np.ascontiguousarray(counts, dtype=np.int32)
+    w = np.ascontiguousarray(words).view(np.uint64)
+    if c.ndim != 2 or w.shape != c.shape + ((int(ff) + 63) // 64,):
+        raise CgsError("denoise_schedule: counts [L][T] and words [L][T][ceil(ff/64)]")
+    L, T = c.shape
+    kind, anc, msk = ((ctypes.c_int32 * T)() for _ in range(3))
+    _check(lib().cgs_denoise_schedule(L, T, int(ff), c.ctypes.data, w.ctypes.data, kind, anc, msk),
+           "cgs_denoise_schedule")
+    return list(kind), list(anc), list(msk)
+
+
 class Window:
     """Sliding GPU working set of `slots` expanded entries (host bookkeeping
     in libcgs; the caller rebuilds the entries an advance admits)."""
@@ -691,6 +734,78 @@ def profile_result(site: str | None = None):
 # --------------------------------------------------------------------------
 # One whole masked denoising step in one persistent launch
 # --------------------------------------------------------------------------
+class _MaskedLayer(ctypes.Structure):
+    _fields_ = [("w", _Ffn), ("idx", ctypes.c_void_p), ("y_anchor", ctypes.c_void_p),
+                ("h_anchor", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("y_out", ctypes.c_void_p),
+                ("y_f32_out", ctypes.c_void_p), ("h_out", ctypes.c_void_p)]
+
+
+@dataclass
+class MaskedLayer:
+    """One layer of act_masked_layers: the compact FFN of its mask (or the full
+    FFN, with idx = 0..ff-1, for a dense anchor layer), the mask's neuron ids,
+    the anchor state, the bias added to r after the layer and optional outputs."""
+    w: FFN
+    idx: torch.Tensor = None
+    y_anchor: torch.Tensor = None
+    h_anchor: torch.Tensor = None
+    bias: torch.Tensor = None
+    y_out: torch.Tensor = None
+    y_f32_out: torch.Tensor = None
+    h_out: torch.Tensor = None
+
+
+class MaskedChain:
+    """A chain of MaskedLayers checked once and kept as the C array, so that
+    replaying it (act_masked_layers) costs one host call.  S: action tokens;
+    ff: neurons of the full FFN (the rows of h_anchor / h_out)."""
+
+    def __init__(self, layers, S: int, ff: int):
+        if not layers:
+            raise CgsError("MaskedChain: no layers")
+        self.n, self.S, self.ff = len(layers), int(S), int(ff)
+        self.d, self.dtype = layers[0].w.d, layers[0].w.dtype
+        self.arr = (_MaskedLayer * self.n)()
+        self.kmax = 0
+        self._refs = []
+        for i, ly in enumerate(layers):
+            w = ly.w
+            if w.layout != "fd" or w.dtype != self.dtype or w.d != self.d:
+                raise CgsError(f"layer {i}: weights must be 'fd' with the chain's d and dtype")
+            K = w.ff
+            self.kmax = max(self.kmax, K)
+            _expect_index(ly.idx, f"layer {i} idx", K, required=False)
+            if ly.idx is None and (ly.h_anchor is not None or ly.h_out is not None):
+                raise CgsError(f"layer {i}: h_anchor / h_out need idx")
+            _expect(ly.y_anchor, f"layer {i} y_anchor", torch.float32, (S, self.d), required=False)
+            _expect(ly.h_anchor, f"layer {i} h_anchor", torch.float32, (ff, S), required=False)
+            _expect(ly.bias, f"layer {i} bias", torch.float32, (self.d,), required=False)
+            _expect(ly.y_out, f"layer {i} y_out", self.dtype, (S, self.d), required=False)
+            _expect(ly.y_f32_out, f"layer {i} y_f32_out", torch.float32, (S, self.d), required=False)
+            _expect(ly.h_out, f"layer {i} h_out", torch.float32, (ff, S), required=False)
+            self.arr[i] = _MaskedLayer(w.cstruct(), _ptr(ly.idx), _ptr(ly.y_anchor), _ptr(ly.h_anchor),
+                                       _ptr(ly.bias), _ptr(ly.y_out), _ptr(ly.y_f32_out), _ptr(ly.h_out))
+            self._refs.append(ly)
+        self.ws_bytes = int(lib().cgs_act_masked_layers_workspace(self.S, self.d, self.kmax))
+        if self.ws_bytes == 0:
+            raise CgsError("MaskedChain: unsupported shape")
+
+
+def act_masked_layers(chain, r, x, ws=None, stream=None, ff: int = None):
+    """Run a chain of masked / dense layers with the residual glue in one host
+    call: x [n+1][S][d] (x[0] read, x[1..n] written), r [S][d] fp32 updated.
+    chain: a MaskedChain, or a list of MaskedLayer (then ff is required)."""
+    if not isinstance(chain, MaskedChain):
+        _expect(r, "r", torch.float32)
+        chain = MaskedChain(chain, r.shape[0], ff)
+    _expect(r, "r", torch.float32, (chain.S, chain.d))
+    _expect(x, "x", chain.dtype, (chain.n + 1, chain.S, chain.d))
+    ws = workspace(chain.ws_bytes, r.device, "act", stream) if ws is None else ws
+    _check(lib().act_masked_layers(chain.arr, chain.n, chain.S, _ptr(r), _ptr(x), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "act_masked_layers")
+    return x
+
+
 class _StepLayer(ctypes.Structure):
     _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down_t", ctypes.c_void_p),
                 ("K", ctypes.c_int32), ("ldk", ctypes.c_int32), ("idx", ctypes.c_void_p),

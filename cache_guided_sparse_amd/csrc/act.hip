@@ -513,6 +513,66 @@ extern "C" int act_ffn_masked_compact(const cgs_ffn* wc, const void* x, int S, c
   return act_compact(*wc, x, S, idx, K, y_anchor, h_anchor, y_out, y_f32_out, h_out, glue, ws, s);
 }
 
+namespace cgs {
+namespace {
+// The checks of act_ffn_masked_compact for one layer of a chain.
+int masked_layer_status(const cgs_masked_layer& L, int d, int dtype) {
+  const cgs_ffn& wc = L.w;
+  const int K = wc.ff;
+  if ((K > 0 && (!wc.w_gate || !wc.w_up || !wc.w_down)) || wc.dtype != dtype ||
+      wc.down_layout != CGS_DOWN_FD || (K > 0 && !L.idx && (L.h_anchor || L.h_out)))
+    return CGS_ERR_ARG;
+  if (wc.d != d) return CGS_ERR_SHAPE;
+  if (!act_shape_ok(wc.d, std::max(wc.ff, 1))) return CGS_ERR_UNSUPPORTED;
+  if (K < 0) return CGS_ERR_SHAPE;
+  return CGS_OK;
+}
+}  // namespace
+}  // namespace cgs
+
+extern "C" size_t cgs_act_masked_layers_workspace(int S, int d, int K_max) {
+  if (S <= 0 || K_max < 0 || d <= 0) return 0;
+  const size_t ffn = cgs_act_ffn_masked_workspace(S, std::max(K_max, 1), d, std::max(K_max, 1));
+  if (ffn == 0) return 0;
+  return ffn + align_up(static_cast<size_t>(S) * d * 4, 256);  // y of layers without y_out
+}
+
+extern "C" int act_masked_layers(const cgs_masked_layer* layers, int n, int S, float* r, void* x, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (n < 0 || S < 0) return CGS_ERR_SHAPE;
+  if (n == 0 || S == 0) return CGS_OK;
+  if (!layers || !r || !x) return CGS_ERR_ARG;
+  const int d = layers[0].w.d, dt = layers[0].w.dtype;
+  if (!valid_dtype(dt)) return CGS_ERR_ARG;
+  int K_max = 0;
+  for (int i = 0; i < n; ++i) {
+    if (const int st = masked_layer_status(layers[i], d, dt)) return st;
+    K_max = std::max(K_max, layers[i].w.ff);
+  }
+  const size_t need = cgs_act_masked_layers_workspace(S, d, K_max);
+  if (need == 0) return CGS_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < need) return CGS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_on())
+    for (int i = 0; i < n; ++i)
+      if (const int st = validate_index(layers[i].idx, layers[i].w.ff, INT32_MAX, s)) return st;
+  const size_t ffn_ws = need - align_up(static_cast<size_t>(S) * d * 4, 256);
+  void* y_scratch = static_cast<char*>(ws) + ffn_ws;
+  const size_t row_bytes = static_cast<size_t>(S) * d * elem_bytes(dt);
+  char* xs = static_cast<char*>(x);
+  for (int i = 0; i < n; ++i) {
+    const cgs_masked_layer& L = layers[i];
+    cgs_glue g{};
+    g.r = r;
+    g.bias = L.bias;
+    g.x_next = xs + (i + 1) * row_bytes;
+    const int st = act_compact(L.w, xs + i * row_bytes, S, L.idx, L.w.ff, L.y_anchor, L.h_anchor,
+                               L.y_out ? L.y_out : y_scratch, L.y_f32_out, L.h_out, &g, ws, s);
+    if (st != CGS_OK) return st;
+  }
+  return CGS_OK;
+}
+
 // Scratch of act_ffn_masked_compact_noalloc: the deltas and split partials
 // that the caller's workspace holds otherwise.  Each GPU has its own copy;
 // host code uses only the per-device address from hipGetSymbolAddress (the

@@ -130,3 +130,48 @@ extern "C" int cgs_window_advance(cgs_window* w, int T, const int32_t* episode, 
   if (n_cand) *n_cand = static_cast<int32_t>(cand.size());
   return CGS_OK;
 }
+
+extern "C" int cgs_denoise_schedule(int L, int T, int ff, const int32_t* counts, const uint64_t* words,
+                                    int32_t* kind_out, int32_t* anchor_out, int32_t* mask_out) {
+  if (L < 1 || L > 64 || T < 1 || T > 64 || ff < 1 || ff > 65536) return CGS_ERR_SHAPE;
+  if (!counts || !words || !kind_out || !anchor_out || !mask_out) return CGS_ERR_ARG;
+  const int nw = (ff + 63) / 64;
+  const uint64_t last = (ff % 64) ? (~0ull >> (64 - ff % 64)) : ~0ull;  // bits of the last word inside ff
+  auto mask_word = [&](int l, int t, int j) {
+    const uint64_t v = words[(static_cast<size_t>(l) * T + t) * nw + j];
+    return j == nw - 1 ? (v & last) : v;
+  };
+  for (int l = 0; l < L; ++l)
+    for (int t = 0; t < T; ++t) {
+      long long bits = 0;
+      for (int j = 0; j < nw; ++j) bits += __builtin_popcountll(mask_word(l, t, j));
+      if (bits != counts[l * T + t]) return CGS_ERR_ARG;
+    }
+  auto same = [&](int t1, int t2) {
+    for (int l = 0; l < L; ++l)
+      for (int j = 0; j < nw; ++j)
+        if (mask_word(l, t1, j) != mask_word(l, t2, j)) return false;
+    return true;
+  };
+  int anchors = 0;
+  for (int t = 0; t < T; ++t) {
+    bool full = true;
+    for (int l = 0; l < L && full; ++l) full = counts[l * T + t] == ff;
+    if (full) {
+      kind_out[t] = 0;
+      anchor_out[t] = anchors++;
+      mask_out[t] = -1;
+      continue;
+    }
+    if (anchors == 0) return CGS_ERR_SHAPE;  // an update needs an anchor before it
+    kind_out[t] = 1;
+    anchor_out[t] = anchors - 1;
+    mask_out[t] = t;
+    for (int u = 0; u < t; ++u)
+      if (kind_out[u] == 1 && mask_out[u] == u && same(u, t)) {
+        mask_out[t] = u;
+        break;
+      }
+  }
+  return CGS_OK;
+}

@@ -336,6 +336,58 @@ MaskWs carve_mask(void* ws, int layers, int T, int ff) {
   return m;
 }
 
+// Stored masks back to index lists: one workgroup per mask; thread t takes
+// kIdxWords consecutive 64-bit words, the block's exclusive prefix sum of the
+// words' populations places each thread's neurons, and positions past the
+// count are filled with -1.  Bits at positions >= ff are ignored.
+constexpr int kIdxThreads = 256;
+constexpr int kIdxWords = 4;  // ff <= 65536: at most 1024 words per mask
+
+__global__ __launch_bounds__(kIdxThreads) void mask_indices_kernel(const uint64_t* __restrict__ masks, int ff,
+                                                                  int32_t* __restrict__ idx_out,
+                                                                  int32_t* __restrict__ count_out) {
+  __shared__ int scan[kIdxThreads];
+  const int tid = threadIdx.x;
+  const int nw = (ff + 63) / 64;
+  const size_t m = blockIdx.x;
+  const uint64_t* w = masks + m * nw;
+  int32_t* out = idx_out + m * ff;
+  uint64_t v[kIdxWords];
+  int pop = 0;
+#pragma unroll
+  for (int j = 0; j < kIdxWords; ++j) {
+    const int wi = tid * kIdxWords + j;
+    uint64_t x = wi < nw ? w[wi] : 0ull;
+    const int valid = ff - wi * 64;  // bits of this word inside [0, ff)
+    if (valid < 64) x &= valid > 0 ? (~0ull >> (64 - valid)) : 0ull;
+    v[j] = x;
+    pop += __popcll(x);
+  }
+  scan[tid] = pop;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the block
+  for (int off = 1; off < kIdxThreads; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const int total = scan[kIdxThreads - 1];
+  int pos = scan[tid] - pop;
+#pragma unroll
+  for (int j = 0; j < kIdxWords; ++j) {
+    uint64_t x = v[j];
+    const int base = (tid * kIdxWords + j) * 64;
+    while (x) {
+      const int b = __builtin_ctzll(x);
+      out[pos++] = base + b;
+      x &= x - 1;
+    }
+  }
+  for (int i = total + tid; i < ff; i += kIdxThreads) out[i] = -1;
+  if (tid == 0 && count_out) count_out[m] = total;
+}
+
 int bit_length(unsigned v) {
   int b = 0;
   while (v) { ++b; v >>= 1; }
@@ -483,4 +535,15 @@ extern "C" int act_build_mask(const float* h_ref, int T, int S, const cgs_ffn* w
                               int32_t* count_out, void* ws, size_t ws_bytes, void* stream) {
   return act_build_masks(h_ref, 1, T, S, w, mode, K, coverage, mask_out, idx_out, count_out, ws, ws_bytes,
                          stream);
+}
+
+extern "C" int act_mask_indices(const uint64_t* masks, int n, int ff, int32_t* idx_out, int32_t* count_out,
+                                void* stream) {
+  if (n < 0 || ff <= 0 || ff > kIdxThreads * kIdxWords * 64) return CGS_ERR_SHAPE;
+  if (n == 0) return CGS_OK;
+  if (!masks || !idx_out) return CGS_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  ProfScope ps("mask.indices", s);
+  hipLaunchKernelGGL(mask_indices_kernel, dim3(n), dim3(kIdxThreads), 0, s, masks, ff, idx_out, count_out);
+  return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
 }

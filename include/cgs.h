@@ -232,6 +232,19 @@ int act_build_masks_normed(const float* h_ref, int layers, int T, int S, const d
                            int mode, int K, double coverage, uint64_t* mask_out, int32_t* idx_out,
                            int32_t* count_out, void* ws, size_t ws_bytes, void* stream);
 
+/* §5 keeps each cache entry's group masks with the entry (bit-packed, the
+ * mask_out format above); §4.1's masked steps read a mask as its list of
+ * neurons.  This turns n stored masks back into those lists.
+ *   masks     : [n][ceil(ff/64)] uint64 (8-byte aligned); bit i%64 of word
+ *               i/64 set iff neuron i is in the mask; bits at positions >= ff
+ *               are ignored.
+ *   idx_out   : [n][ff] int32; row m: the neurons of mask m ascending, then -1
+ *               up to ff (act_build_mask's idx_out layout).
+ *   count_out : [n] int32 (device) or NULL; the number of neurons of mask m.
+ * 1 <= ff <= 65536; n = 0 is a no-op.  No workspace. */
+int act_mask_indices(const uint64_t* masks, int n, int ff, int32_t* idx_out, int32_t* count_out,
+                     void* stream);
+
 /* Workspace bytes for act_ffn_masked with S tokens and K masked neurons. */
 size_t cgs_act_ffn_masked_workspace(int S, int K, int d, int ff);
 
@@ -303,6 +316,44 @@ int act_ffn_masked_compact(const cgs_ffn* wc, const void* x, int S, const int32_
 int act_ffn_masked_compact_noalloc(const cgs_ffn* wc, const void* x, int S, const int32_t* idx, int K,
                                    const float* y_anchor, const float* h_anchor, void* y_out,
                                    float* y_f32_out, float* h_out, const cgs_glue* glue, void* stream);
+
+/* One layer of act_masked_layers: Eq. 4 (§4.1) on the compact weights of the
+ * layer's mask, as one act_ffn_masked_compact call. */
+typedef struct {
+  cgs_ffn w;              /* the mask's compact FFN: w.ff = K rows (act_gather_rows;
+                             the full FFN with K = ff for a dense anchor layer), CGS_DOWN_FD */
+  const int32_t* idx;     /* [K] ascending neuron ids (rows of h_anchor / h_out), or NULL
+                             when both are NULL */
+  const float* y_anchor;  /* [S][d] or NULL (= 0) */
+  const float* h_anchor;  /* [ff][S] over the full FFN's neurons, or NULL (= 0) */
+  const float* bias;      /* [d] added to r after this layer, or NULL */
+  void* y_out;            /* [S][d] dtype, or NULL */
+  float* y_f32_out;       /* [S][d], or NULL */
+  float* h_out;           /* [ff][S]: rows idx receive h^M, or NULL */
+} cgs_masked_layer;
+
+/* Workspace bytes for act_masked_layers with S tokens, width d and masks of
+ * at most K_max neurons. */
+size_t cgs_act_masked_layers_workspace(int S, int d, int K_max);
+
+/* A chain of n stacked layers of the action expert (§4.1 Eq. 4 with the
+ * residual/RMSNorm glue), enqueued by one call: for i = 0 .. n-1
+ *   y_i = Eq. 4 of layers[i] on x[i],  r += round(y_i) (+ bias_i),
+ *   x[i+1] = RMSNorm(r).
+ * Exactly the results of n act_ffn_masked_compact calls with the glue
+ * (r, bias_i, x[i+1]).  The layers of several denoising steps may be chained
+ * (a dense anchor layer is its full FFN with K = ff and the list 0..ff-1), so
+ * a whole denoise whose masks come from a cache entry runs without one host
+ * call per layer.
+ *   layers : HOST array of n layers, equal d and dtype.
+ *   r      : [S][d] fp32 residual stream, updated in place.
+ *   x      : [n+1][S][d] dtype; x[0] is read, x[1..n] are written.
+ * n = 0 or S = 0 is a no-op.  Errors as act_ffn_masked_compact, checked for
+ * every layer before anything is launched (CGS_ERR_WORKSPACE if ws is below
+ * cgs_act_masked_layers_workspace(S, d, max K)).  In checked mode every
+ * layer's idx is checked first. */
+int act_masked_layers(const cgs_masked_layer* layers, int n, int S, float* r, void* x, void* ws,
+                      size_t ws_bytes, void* stream);
 
 /* ---- Action Cache: one whole masked denoising step in one launch -------- */
 
@@ -532,6 +583,28 @@ int cgs_window_advance(cgs_window* w, int T, const int32_t* episode, const int32
                        const int32_t* length, int L, const cgs_budget* budget, int32_t* enter_ep,
                        int32_t* enter_pos, int32_t* enter_slot, int32_t* n_enter, int32_t* leave_slot,
                        int32_t* n_leave, int32_t* n_cand);
+
+/* The denoising schedule a cache entry's stored masks imply (§4.1 "Anchors
+ * with Mask Recomputation"; §5 builds one mask per layer for every step of a
+ * group).  An entry stores one mask per (layer, step): L x T masks of ff
+ * bits.  A step whose masks hold every neuron in all L layers is a dense
+ * anchor step, which refreshes the anchor state; every other step is an Eq. 4
+ * update against the latest anchor with that step's masks.  The one-group
+ * schedule is [all, G, G, G], two groups [all, G1, all, G2].
+ *   counts : [L][T] neurons per mask (host); must equal the masks' bit counts.
+ *   words  : [L][T][ceil(ff/64)] uint64 (host), the masks in act_build_mask's
+ *            format (bits at positions >= ff ignored).
+ *   kind_out   : [T] 0 = anchor, 1 = masked update.
+ *   anchor_out : [T] for an anchor its ordinal among the anchors (0, 1, ..),
+ *                for an update the ordinal of the latest anchor before it.
+ *   mask_out   : [T] for an update the first update step whose L masks are
+ *                the same bits as this step's (whose compact weights it can
+ *                reuse); -1 for an anchor.
+ * CGS_ERR_SHAPE if L, T or ff is out of range (1 .. 64, 1 .. 64, 1 .. 65536)
+ * or step 0 is not an anchor; CGS_ERR_ARG for a NULL pointer or a count that
+ * differs from its mask's bits.  Host logic only. */
+int cgs_denoise_schedule(int L, int T, int ff, const int32_t* counts, const uint64_t* words,
+                         int32_t* kind_out, int32_t* anchor_out, int32_t* mask_out);
 
 #ifdef __cplusplus
 }

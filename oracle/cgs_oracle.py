@@ -43,6 +43,7 @@ __all__ = [
     "score_floor", "ctx_score_keys", "topk_ascending", "ctx_select",
     "gelu_tanh", "ffn_geglu", "ctx_ffn_recompute", "contribution_scores",
     "down_weight_norms", "mask_topk", "coverage_exponent_bits", "mask_coverage", "act_build_mask", "mask_bits",
+    "mask_indices",
     "act_ffn_masked", "act_ffn_joint", "rms_norm", "rebuild_dense", "entry_bytes",
 ]
 
@@ -304,6 +305,19 @@ def mask_bits(idx, ff: int) -> np.ndarray:
     for n in np.asarray(idx, dtype=np.int64):
         words[n // 64] |= np.uint64(1) << np.uint64(n % 64)
     return words
+
+
+def mask_indices(words, ff: int) -> np.ndarray:
+    """A stored bit-packed mask read back as its neuron list (paper §5: the
+    group masks kept with a cache entry; §4.1: a masked step reads the mask's
+    neurons): every n < ff whose bit (n mod 64) of word n // 64 is set,
+    ascending.  Bits at positions >= ff are not neurons and are ignored."""
+    words = [int(w) & ((1 << 64) - 1) for w in np.asarray(words).ravel()]
+    kept = []
+    for n in range(int(ff)):
+        if (words[n // 64] >> (n % 64)) & 1:
+            kept.append(n)
+    return np.array(kept, dtype=np.int32)
 
 
 def act_build_mask(h_ref, w: dict, mode: str, K: int = 0, coverage: float = 0.0):

@@ -61,3 +61,38 @@ class WindowModel:
             self.where[key] = s
             entered.append((key[0], key[1], s))
         return entered, left, len(cands)
+
+
+def denoise_schedule(words, ff: int):
+    """The denoising schedule of a cache entry's stored masks (rMuscle §4.1,
+    "Anchors with Mask Recomputation"; §5 builds a group mask from the
+    group's steps).  words[l][t]: the bit-packed mask of layer l at step t.
+
+    Reading: a step whose masks hold every neuron in all layers is a dense
+    anchor step; any other step updates the latest anchor with its own masks;
+    an update before any anchor is an error.  An update's "mask" is the first
+    update step holding the same masks in every layer.  Returns (kind, anchor,
+    mask) lists as cgs_denoise_schedule defines them."""
+    from .cgs_oracle import mask_indices
+    L, T = len(words), len(words[0])
+    lists = [[tuple(mask_indices(words[l][t], ff).tolist()) for t in range(T)] for l in range(L)]
+    kind, anchor, mask = [], [], []
+    n_anchor = 0
+    for t in range(T):
+        if all(len(lists[l][t]) == ff for l in range(L)):
+            kind.append(0)
+            anchor.append(n_anchor)
+            mask.append(-1)
+            n_anchor += 1
+            continue
+        if n_anchor == 0:
+            raise ValueError("an update step before the first anchor")
+        kind.append(1)
+        anchor.append(n_anchor - 1)
+        first = t
+        for u in range(t):
+            if kind[u] == 1 and all(lists[l][u] == lists[l][t] for l in range(L)):
+                first = u
+                break
+        mask.append(first)
+    return kind, anchor, mask

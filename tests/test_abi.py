@@ -342,3 +342,31 @@ def test_noalloc_entry_point_refuses_before_any_device_call():
     w_odd = _ffn(d=1000, ff=4096, layout=1)
     assert L.act_ffn_masked_compact_noalloc(ctypes.byref(w_odd), buf, 64, buf, 4096, None, None, out, None,
                                             None, None, None) == 4
+
+
+def test_mask_indices_and_masked_layers_validate_before_launch():
+    L = cgs.lib()
+    buf = ctypes.c_void_p(0x1000)
+    assert L.act_mask_indices(buf, 4, 0, buf, None, None) == 2            # ff = 0
+    assert L.act_mask_indices(buf, 4, 65537, buf, None, None) == 2        # ff past 65536
+    assert L.act_mask_indices(buf, -1, 64, buf, None, None) == 2
+    assert L.act_mask_indices(None, 4, 64, buf, None, None) == 1
+    assert L.act_mask_indices(None, 0, 64, None, None, None) == 0         # n = 0: nothing to do
+    r, x = ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    need = L.cgs_act_masked_layers_workspace(50, 1024, 1300)
+    assert need >= L.cgs_act_ffn_masked_workspace(50, 1300, 1024, 1300) + 50 * 1024 * 4
+    arr = (cgs._MaskedLayer * 3)()
+    for i, K in enumerate((4096, 1300, 0)):
+        arr[i].w = _ffn(d=1024, ff=K, layout=1)
+        arr[i].idx = 0x4000
+    assert L.act_masked_layers(arr, 3, 50, r, x, buf, need, None) == 3            # ws sized for K 1300 < 4096
+    assert L.act_masked_layers(arr, 3, 50, None, x, buf, 1 << 40, None) == 1      # r missing
+    assert L.act_masked_layers(arr, 0, 50, None, None, None, 0, None) == 0        # n = 0
+    arr[1].w = _ffn(d=512, ff=1300, layout=1)
+    assert L.act_masked_layers(arr, 3, 50, r, x, buf, 1 << 40, None) == 2         # d differs
+    arr[1].w = _ffn(d=1024, ff=1300, layout=0)
+    assert L.act_masked_layers(arr, 3, 50, r, x, buf, 1 << 40, None) == 1         # not neuron-major
+    arr[1].w = _ffn(d=1024, ff=1300, layout=1)
+    arr[1].idx = None
+    arr[1].h_anchor = 0x5000
+    assert L.act_masked_layers(arr, 3, 50, r, x, buf, 1 << 40, None) == 1         # h_anchor without idx

@@ -203,3 +203,110 @@ def test_denoise_chain_18_layers_4_steps(expert):
                 r_exp = r_exp + expert["dtemb"][t].astype(np.float64)
             assert_close(values(rin[i + 1]), r_exp, f"step {t} layer {l}: residual")
             assert_close(values(xin[i + 1]), O.rms_norm(r_exp), f"step {t} layer {l}: next input", out="bf16")
+
+    # the same denoise as one act_masked_layers chain of 72 layers: the bits of
+    # the per-layer calls above
+    say("configs: the denoise as one chain")
+    y_anc2, h_anc2 = torch.empty_like(y_anc), torch.full_like(h_anc, float("nan"))
+    ych = torch.empty(STEPS * L_EXP, S, DE, dtype=torch.bfloat16, device=dev())
+    chain = []
+    for t in range(STEPS):
+        for l in range(L_EXP):
+            bias = dtemb[t] if l == L_EXP - 1 else None
+            if t == 0:
+                chain.append(cgs.MaskedLayer(W[l], full, bias=bias, y_out=ych[l], y_f32_out=y_anc2[l],
+                                             h_out=h_anc2[l]))
+            else:
+                chain.append(cgs.MaskedLayer(cexp[l], masks[l], y_anchor=y_anc2[l], h_anchor=h_anc2[l],
+                                             bias=bias, y_out=ych[t * L_EXP + l]))
+    xch = torch.empty(STEPS * L_EXP + 1, S, DE, dtype=torch.bfloat16, device=dev())
+    rch = torch.empty(S, DE, dtype=torch.float32, device=dev())
+    cgs.residual_rmsnorm(rch, r_in=_f32(expert["a0"]), bias=temb0, x_out=xch[0])
+    cgs.act_masked_layers(cgs.MaskedChain(chain, S, FFE), rch, xch)
+    torch.cuda.synchronize()
+    assert torch.equal(rch, rin[-1]), "chain: final residual"
+    for i in range(STEPS * L_EXP + 1):
+        assert torch.equal(xch[i], xin[i]), f"chain: input of layer {i}"
+    for i in range(STEPS * L_EXP):
+        assert torch.equal(ych[i], yout[i]), f"chain: y of layer {i}"
+    assert torch.equal(y_anc2, y_anc) and np.array_equal(bits(h_anc2), bits(h_anc)), "chain: anchor state"
+
+
+def test_denoise_two_groups_anchors_at_steps_0_and_2(expert):
+    """The two-group schedule (§4.1, anchors with mask recomputation): steps 0
+    and 2 are dense anchors, step 1 updates the step-0 anchor with the mask of
+    group {0, 1} and step 3 the step-2 anchor with the mask of group {2, 3},
+    each group mask built from its own steps of the reference run.  The whole
+    denoise is one act_masked_layers chain; every layer is checked on its own
+    inputs (teacher forcing), the masks bit for bit."""
+    say("configs: two-group denoise")
+    W, layers = expert["W"], expert["layers"]
+    temb0, dtemb = _f32(expert["temb0"]), [_f32(v) for v in expert["dtemb"]]
+    full = torch.arange(FFE, dtype=torch.int32, device=dev())
+    ra = torch.empty(S, DE, dtype=torch.float32, device=dev())
+    xa = torch.empty(S, DE, dtype=torch.bfloat16, device=dev())
+    ya = torch.empty_like(xa)
+    h_ref = torch.empty(L_EXP, STEPS, FFE, S, dtype=torch.float32, device=dev())
+    cgs.residual_rmsnorm(ra, r_in=_f32(expert["a_ref"]), bias=temb0, x_out=xa)
+    for t in range(STEPS):
+        for l in range(L_EXP):
+            cgs.act_ffn_masked(W[l], xa, full, y_out=ya, h_out=h_ref[l, t])
+            cgs.residual_rmsnorm(ra, y=ya, bias=dtemb[t] if l == L_EXP - 1 else None, x_out=xa)
+    groups = [(0, 2), (2, 4)]
+    gmask = []
+    for g0, g1 in groups:
+        hg = h_ref[:, g0:g1].contiguous()
+        words, midx, cnt = cgs.act_build_masks(hg, W, "coverage", coverage=COVERAGE)
+        torch.cuda.synchronize()
+        hg_h, midx_h, cnt_h = hg.cpu().numpy(), midx.cpu().numpy(), cnt.cpu().numpy()
+        for l in range(L_EXP):
+            idx_o, _ = O.act_build_mask(hg_h[l], layers[l], "coverage", coverage=COVERAGE)
+            assert np.array_equal(midx_h[l][: cnt_h[l]], idx_o), f"group {g0}: layer {l} mask"
+        gmask.append([midx[l, : int(cnt_h[l])].contiguous() for l in range(L_EXP)])
+    cexp = [[cgs.act_gather_rows(W[l], gm[l]) for l in range(L_EXP)] for gm in gmask]
+
+    y_anc = torch.empty(2, L_EXP, S, DE, dtype=torch.float32, device=dev())
+    h_anc = torch.full((2, L_EXP, FFE, S), float("nan"), dtype=torch.float32, device=dev())
+    ych = torch.empty(STEPS * L_EXP, S, DE, dtype=torch.bfloat16, device=dev())
+    yfc = torch.empty(STEPS * L_EXP, S, DE, dtype=torch.float32, device=dev())
+    chain = []
+    for t in range(STEPS):
+        g = t // 2
+        for l in range(L_EXP):
+            i = t * L_EXP + l
+            bias = dtemb[t] if l == L_EXP - 1 else None
+            if t % 2 == 0:
+                chain.append(cgs.MaskedLayer(W[l], full, bias=bias, y_out=ych[i], y_f32_out=y_anc[g, l],
+                                             h_out=h_anc[g, l]))
+            else:
+                chain.append(cgs.MaskedLayer(cexp[g][l], gmask[g][l], y_anchor=y_anc[g, l], h_anchor=h_anc[g, l],
+                                             bias=bias, y_out=ych[i], y_f32_out=yfc[i]))
+    xch = torch.empty(STEPS * L_EXP + 1, S, DE, dtype=torch.bfloat16, device=dev())
+    cgs.residual_rmsnorm(ra, r_in=_f32(expert["a0"]), bias=temb0, x_out=xch[0])
+    cgs.act_masked_layers(cgs.MaskedChain(chain, S, FFE), ra, xch)
+    torch.cuda.synchronize()
+    x_h, y_h, yf_h = bits(xch), bits(ych), yfc.cpu().numpy()
+    y_anc_h, h_anc_h = y_anc.cpu().numpy(), h_anc.cpu().numpy()
+    # the residual stream rebuilt along the chain from the GPU's own outputs
+    # (fp64 here, fp32 on the GPU: 72 additions apart by far less than the bound)
+    r = expert["a0"].astype(np.float32).astype(np.float64) + expert["temb0"].astype(np.float32).astype(np.float64)
+    assert_close(O.decode(x_h[0], "bf16"), O.rms_norm(r), "x_0", out="bf16")
+    for t in range(STEPS):
+        g = t // 2
+        for l in range(L_EXP):
+            i = t * L_EXP + l
+            if t % 2 == 0:
+                y_o, h_o = O.act_ffn_masked(layers[l], x_h[i], np.arange(FFE))
+                assert_close(y_anc_h[g, l], y_o, f"anchor step {t} layer {l}: y_a")
+                assert_close(h_anc_h[g, l], h_o, f"anchor step {t} layer {l}: h_a")
+            else:
+                y_o, _ = O.act_ffn_masked(layers[l], x_h[i], gmask[g][l].cpu().numpy(), y_anc_h[g, l],
+                                          h_anc_h[g, l])
+                assert_close(yf_h[i], y_o, f"step {t} layer {l}: y (fp32)")
+            assert_close(O.decode(y_h[i], "bf16"), y_o, f"step {t} layer {l}: y", out="bf16")
+            r = r + O.decode(y_h[i], "bf16")
+            if l == L_EXP - 1:
+                r = r + expert["dtemb"][t].astype(np.float64)
+            assert_close(O.decode(x_h[i + 1], "bf16"), O.rms_norm(r), f"step {t} layer {l}: next input",
+                         out="bf16")
+

@@ -151,3 +151,42 @@ def test_masks_from_stored_norms_equal_masks_from_weights(mode, K, cov, L, T, ff
         c = int(b[2][l].item())
         assert c == len(oi) and np.array_equal(b[1][l, :c].cpu().numpy(), oi)
         assert np.array_equal(b[0][l].cpu().numpy().view(np.uint64), om)
+
+
+@pytest.mark.parametrize("ff,n", [(4096, 72), (1, 3), (63, 5), (64, 4), (200, 9), (1000, 2), (65536, 3)])
+def test_mask_indices_bit_exact(ff, n):
+    """Stored masks read back as neuron lists (§5 keeps each entry's masks as
+    bits): random words with every bit pattern, including bits past ff, an
+    empty and a full mask; lists, -1 tails and counts equal the oracle's."""
+    say("mask indices", ff, n)
+    nw = (ff + 63) // 64
+    g = rng(47, ff, "misc")
+    words = g.integers(-(2 ** 63), 2 ** 63 - 1, size=(n, nw), dtype=np.int64, endpoint=True)
+    dens = g.uniform(0.05, 0.95, size=n)
+    keep = g.random((n, nw * 64)) < dens[:, None]            # varied densities
+    packed = np.packbits(keep, axis=1, bitorder="little").view("<u8").view(np.int64)
+    words = np.where(g.random((n, 1)) < 0.3, words, packed)   # some rows fully random
+    words[0] = 0
+    if n > 1:
+        words[1] = -1                                         # every bit set, also past ff
+    idx, cnt = cgs.act_mask_indices(torch.from_numpy(words).to(dev()), ff)
+    torch.cuda.synchronize()
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    for m in range(n):
+        want = O.mask_indices(words[m], ff)
+        assert cnt_h[m] == len(want), (m, cnt_h[m], len(want))
+        assert np.array_equal(idx_h[m][: len(want)], want), m
+        assert np.all(idx_h[m][len(want):] == -1), m
+    assert cnt_h[0] == 0 and (n < 2 or cnt_h[1] == ff)
+
+
+def test_mask_indices_read_back_a_built_mask():
+    """The words act_build_masks writes come back as the list it wrote."""
+    say("mask indices of built masks")
+    L, T, S, ff, d = 4, 4, 50, 4096, 256
+    ws = [ffn_weights(48, l, d, ff, down_layout="fd", down_lognormal_sigma=1.5) for l in range(L)]
+    h = np.stack([synthetic_h_ref(48, l, T, ff, S) for l in range(L)]).astype(np.float32)
+    words, idx, cnt = cgs.act_build_masks(to_dev(h, "f32"), [ffn_dev(w) for w in ws], "coverage", coverage=0.844)
+    idx2, cnt2 = cgs.act_mask_indices(words, ff)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)

@@ -150,6 +150,28 @@ def test_mask_bits_layout():
         O.mask_coverage(np.ones(3), 1.5)
 
 
+def test_mask_indices_reads_the_stored_words():
+    """Bit (n mod 64) of word n // 64 is neuron n: a hand-written example, the
+    little-endian byte view through numpy's unpackbits on random words, the
+    empty and full masks, and bits past ff (ignored)."""
+    words = np.array([0b1011, 1 << 63, 0], dtype=np.uint64)
+    assert O.mask_indices(words, 192).tolist() == [0, 1, 3, 127]
+    assert O.mask_indices(words.view(np.int64), 192).tolist() == [0, 1, 3, 127]   # as stored, signed
+    assert O.mask_indices(words, 100).tolist() == [0, 1, 3]                        # 127 is past ff
+    g = np.random.default_rng(5)
+    for ff in (1, 63, 64, 65, 200, 4096):
+        nw = (ff + 63) // 64
+        w = g.integers(0, 2 ** 63, size=nw, dtype=np.int64).view(np.uint64) ^ \
+            (g.integers(0, 2, size=nw, dtype=np.uint64) << np.uint64(63))
+        bits = np.unpackbits(w.astype("<u8").view(np.uint8), bitorder="little")[:ff]
+        assert np.array_equal(O.mask_indices(w, ff), np.flatnonzero(bits).astype(np.int32)), ff
+        full = np.full(nw, np.uint64(2 ** 64 - 1))
+        assert O.mask_indices(full, ff).tolist() == list(range(ff))
+        assert len(O.mask_indices(np.zeros(nw, np.uint64), ff)) == 0
+    idx = np.sort(g.choice(4096, 1251, replace=False))
+    assert np.array_equal(O.mask_indices(O.mask_bits(idx, 4096), 4096), idx)
+
+
 def test_down_weight_norms_against_the_plain_norm_and_closed_forms():
     """||W_n||_2 of Eq. 1 scaled by the fixed point's 2^20: the plain
     Euclidean norm (torch) to rounding; a row of d copies of 2^-5 gives

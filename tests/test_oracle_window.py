@@ -7,7 +7,10 @@ import random
 import pytest
 
 import cache_guided_sparse_amd as cgs
-from oracle.cgs_window import WindowModel, prep_budget, window_entries
+import numpy as np
+
+import oracle as O
+from oracle.cgs_window import WindowModel, denoise_schedule, prep_budget, window_entries
 
 
 def test_window_size_of_the_representative_configuration():
@@ -120,3 +123,50 @@ def test_native_planner_rejects_bad_arguments_without_changing_state():
         cgs.Window(0)
     with pytest.raises(cgs.CgsError):
         cgs.prep_budget(3, 1.0, 1.0, 1.0, 0.0, 0.0)
+
+
+def _words(lists, ff):
+    return np.array([[O.mask_bits(m, ff) for m in row] for row in lists], dtype=np.uint64)
+
+
+def test_denoise_schedule_of_stored_masks():
+    """The schedule of an entry's masks: the one-group [all, G, G, G] and
+    two-group [all, G1, all, G2] layouts by hand, then the native planner
+    against the plain model on random layouts; refusals: an update before any
+    anchor, and counts that disagree with the bits."""
+    ff, L = 200, 3
+    full = list(range(ff))
+    g = np.random.default_rng(7)
+    G = [sorted(g.choice(ff, 50, replace=False)) for _ in range(L)]
+    H = [sorted(g.choice(ff, 70, replace=False)) for _ in range(L)]
+    one = [[full, G[l], G[l], G[l]] for l in range(L)]
+    two = [[full, G[l], full, H[l]] for l in range(L)]
+    assert denoise_schedule(_words(one, ff), ff) == ([0, 1, 1, 1], [0, 0, 0, 0], [-1, 1, 1, 1])
+    assert denoise_schedule(_words(two, ff), ff) == ([0, 1, 0, 1], [0, 0, 1, 1], [-1, 1, -1, 3])
+    # a layer with every neuron does not make an anchor step on its own
+    part = [[full, full if l == 0 else G[l], G[l], G[l]] for l in range(L)]
+    assert denoise_schedule(_words(part, ff), ff) == ([0, 1, 1, 1], [0, 0, 0, 0], [-1, 1, 2, 2])
+    for trial in range(30):
+        T = int(g.integers(1, 7))
+        pool = [[sorted(g.choice(ff, int(g.integers(0, ff)), replace=False)) for _ in range(L)] for _ in range(3)]
+        steps = [None if (t == 0 or g.random() < 0.3) else pool[int(g.integers(0, 3))] for t in range(T)]
+        lists = [[full if steps[t] is None else steps[t][l] for t in range(T)] for l in range(L)]
+        words = _words(lists, ff)
+        counts = np.array([[len(m) for m in row] for row in lists], dtype=np.int32)
+        assert cgs.denoise_schedule(counts, words, ff) == denoise_schedule(words, ff), trial
+    with pytest.raises(ValueError):
+        denoise_schedule(_words([[G[l], full] for l in range(L)], ff), ff)
+    bad = _words([[G[l], full] for l in range(L)], ff)
+    cnt = np.array([[50, ff]] * L, dtype=np.int32)
+    with pytest.raises(cgs.CgsError, match="size or count"):
+        cgs.denoise_schedule(cnt, bad, ff)
+    ok = _words(one, ff)
+    cnt = np.array([[ff, 50, 50, 50]] * L, dtype=np.int32)
+    cnt[1, 2] = 51
+    with pytest.raises(cgs.CgsError, match="invalid argument"):
+        cgs.denoise_schedule(cnt, ok, ff)
+    # bits past ff are ignored by both
+    wpad = ok.copy()
+    wpad[:, :, -1] |= np.uint64(1) << np.uint64(63)
+    cnt = np.array([[ff, 50, 50, 50]] * L, dtype=np.int32)
+    assert cgs.denoise_schedule(cnt, wpad, ff) == denoise_schedule(wpad, ff) == ([0, 1, 1, 1], [0] * 4, [-1, 1, 1, 1])
