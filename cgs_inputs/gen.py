@@ -20,8 +20,10 @@ def rng(seed: int, layer: int, role: str | int) -> np.random.Generator:
 def f32_to_bf16_bits(a) -> np.ndarray:
     """Round float32 values to bf16 (round-to-nearest-even) and return uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    out = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = a.view(np.uint32)
+    # 32-bit sums cannot wrap for finite values (the largest, 0xFF7FFFFF,
+    # plus 0x8000 stays below 2^32); NaN patterns are replaced below
+    out = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
         out[nan] = 0x7FC0

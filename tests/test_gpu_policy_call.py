@@ -72,7 +72,7 @@ def _entry_masks(e, q):
         groups = []
         for gi in range(2 if two else 1):
             g = rng(50 + gi, _entry_id(e, q) * L_EXP + l, "misc")
-            s = np.exp(1.5 * g.standard_normal(FFE)) * np.abs(g.standard_normal(FFE) * g.standard_normal(FFE))
+            s = np.exp(g.standard_normal(FFE)) * np.abs(g.standard_normal(FFE) * g.standard_normal(FFE))
             groups.append(O.mask_coverage(s, COVERAGE))
         steps = [full, groups[0], full, groups[1]] if two else [full, groups[0], groups[0], groups[0]]
         for t, m in enumerate(steps):
@@ -89,14 +89,15 @@ class _Store:
         g = rng(46, 0, "misc")
         self.feats = np.empty((EPISODES, EP_LEN, FEAT), dtype=np.uint16)
         self.hist = np.empty((EPISODES, EP_LEN, HIST_L, JOINTS), dtype=np.float32)
+        self.queries = {}
+        c = np.float32(math.sqrt(1 - 0.98 ** 2))
         for e in range(EPISODES):
-            f = g.standard_normal(FEAT)
+            f = g.standard_normal(FEAT, dtype=np.float32)
             for q in range(EP_LEN):
-                f = 0.98 * f + math.sqrt(1 - 0.98 ** 2) * g.standard_normal(FEAT)
+                f = np.float32(0.98) * f + c * g.standard_normal(FEAT, dtype=np.float32)
                 self.feats[e, q] = O.round_to_bf16_bits(f)
                 if e == 0 and q < CALLS:
-                    self.queries = getattr(self, "queries", {})
-                    self.queries[q] = O.round_to_bf16_bits(f + 0.1 * g.standard_normal(FEAT))
+                    self.queries[q] = O.round_to_bf16_bits(f + np.float32(0.1) * g.standard_normal(FEAT, dtype=np.float32))
             traj = np.cumsum(0.05 * g.standard_normal((EP_LEN + HIST_L, JOINTS)), axis=0)
             self.hist[e] = np.stack([traj[q:q + HIST_L] for q in range(EP_LEN)])
         self.qhist = {q: (self.hist[0, q] + 0.005 * g.standard_normal((HIST_L, JOINTS))).astype(np.float32)
