@@ -4,29 +4,31 @@
 One step is one policy-call slice of rMuscle (Zhou et al.), every row of the
 hot path once, with all inputs resident in HBM:
   * reference retrieval (§4.2, §5): cosine similarity of the call's flattened
-    768 x 1152 ViT features against the 16 prepared entries, top 4, rerank by
+    768 x 1152 ViT features against the 20 prepared entries, top 4, rerank by
     the joint-history distance, fallback below cosine 0.8; the chosen slot
-    drives the prefill (its index is read back to the host);
+    drives the prefill and the denoise (its index is read back to the host);
   * Context Cache prefill (§4.1, Eq. 2/3): 17 VLM FFN layers, 768 visual tokens
     (3 views x 256 patches), d 2048, ff 16384, bf16; per layer the input drift
     score picks ceil(0.3 x 768) = 231 tokens, their FFN rows are recomputed and
     scattered into the cached reference outputs; residual + RMSNorm between
     layers;
   * Action Cache denoise (§4.1, Eq. 4): action expert of 18 layers, d 1024,
-    ff 4096, 50 action tokens, 4 denoising steps in one group: step 0 is the
-    dense anchor, steps 1-3 update it with the group mask (coverage 0.844 of
-    the contribution score), reading the mask's weight rows from compact
-    buffers that a side stream fills beside the anchor step (§4.1, §5; the
-    pages overlap the gathering with the prefill, which is an option here);
-  * group mask construction (§5) for the 18 expert layers from the reference
-    run's activations (offline on the pages, timed here);
-  * one dense rebuild of a reference entry (§4.2): a 16-slot sliding working
-    set over an 800-entry repository of compact entries in pinned host
-    memory advances one position per call (the native window planner,
-    Eq. 5 budget); the entering entry is copied to the device and expanded
-    by the 17-layer prefill into the slot the leaving entry released.
-Prints one JSON line.  Synthetic seeded data of the pages' shapes; the
-weights are random (no trained model is involved).
+    ff 4096, 50 action tokens, 4 denoising steps; the chosen entry's stored
+    masks (one per layer and step, §5) give the schedule: step 0 is the dense
+    anchor, steps 1-3 update it with the entry's group mask (coverage 0.844 of
+    the contribution score), reading that mask's weight rows from compact
+    buffers filled when the entry entered the working set;
+  * preparation of the entries entering the working set (§4.2): the pages'
+    2-D window, 4 candidate episodes x (matched position + 4 next) = 20 slots
+    over an 800-entry repository in pinned host memory (4 episodes x 200
+    positions; each entry a compact input and 18 x 4 bit-packed masks),
+    advances one position per call in every episode (the native window
+    planner, Eq. 5 budget); each entering entry is copied to the device,
+    expanded by the 17-layer dense rebuild, its masks turned into index lists
+    and its update mask's weight rows gathered.
+The group masks themselves are built offline per entry (as on the pages) and
+timed separately.  Prints one JSON line.  Synthetic seeded data of the pages'
+shapes; the weights are random (no trained model is involved).
 """
 from __future__ import annotations
 
@@ -49,7 +51,10 @@ RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
 # workload
 P, D, FF, L_VLM, RHO_P = 768, 2048, 16384, 17, 0.3
 S, DE, FFE, L_EXP, STEPS, COVERAGE = 50, 1024, 4096, 18, 4, 0.844
-STORE, SLOTS, LOOKAHEAD = 800, 16, 15   # repository entries, device slots, window lookahead
+EPISODES, EP_LEN = 4, 200                  # the repository: 4 reference episodes x 200 positions
+STORE = EPISODES * EP_LEN                  # 800 entries
+T_WIN, L_WIN = 4, 4                        # window: T candidate episodes x (matched position + L next)
+SLOTS = T_WIN * (L_WIN + 1)                # 20 device slots
 T_AVL_MS = 500.0                           # a 15-action chunk at 30 Hz (the paper's example)
 FEAT = 768 * 1152                          # ViT layer-15 features of three views, flattened
 HIST_L, JOINTS, TOP_T = 4, 14, 4           # state history, joints (two arms), visual top-T
@@ -112,6 +117,7 @@ class World:
     """Device-resident synthetic state of the benchmark."""
 
     def __init__(self, dev, seed=1234):
+        import numpy as np
         import torch
         import cache_guided_sparse_amd as cgs
         self.cgs = cgs
@@ -127,63 +133,48 @@ class World:
         # VLM FFN layers (Context Cache path, W_down [d][ff])
         self.vlm = [cgs.FFN(randn(FF, D, std=0.02).to(bf), randn(FF, D, std=0.02).to(bf),
                             randn(D, FF, std=0.02).to(bf), "df") for _ in range(L_VLM)]
-        # reference repository: STORE compact entries (the residual stream that
-        # enters layer 0) in pinned host memory, one reference episode of STORE
-        # positions; the current call at position q sees that entry's input
-        # with 231 tokens strongly perturbed (cos ~0.6) and the rest mildly
+        # reference repository: EPISODES x EP_LEN compact entries (the residual
+        # stream that enters layer 0) in pinned host memory, entry e * EP_LEN + q
+        # = position q of episode e; the call at position q of episode 0 sees
+        # that entry's input with 231 tokens strongly perturbed (cos ~0.6) and
+        # the rest mildly (cos ~0.985)
         self.store = torch.empty((STORE, P, D), dtype=bf, pin_memory=True)
-        self.current = torch.empty((STORE, P, D), dtype=torch.float32, device=dev)
+        self.current = torch.empty((EP_LEN, P, D), dtype=torch.float32, device=dev)
         for c0 in range(0, STORE, 64):
             n = min(64, STORE - c0)
             comp = randn(n, P, D)
-            sig = torch.full((n, P, 1), 0.1752, device=dev)
-            for j in range(n):
-                perm = torch.randperm(P, device=dev, generator=g)[: math.ceil(RHO_P * P - 1e-9)]
-                sig[j, perm] = 1.3333
-            self.current[c0:c0 + n] = comp + randn(n, P, D) * sig
             self.store[c0:c0 + n].copy_(comp.to(bf))
+            for j in range(n):
+                e, q = divmod(c0 + j, EP_LEN)
+                if e == 0:
+                    sig = torch.full((P, 1), 0.1752, device=dev)
+                    sig[torch.randperm(P, device=dev, generator=g)[: math.ceil(RHO_P * P - 1e-9)]] = 1.3333
+                    self.current[q] = comp[j] + randn(P, D) * sig
         self.staging = torch.empty((P, D), dtype=bf, device=dev)
-        # retrieval data of every repository position: ViT features that drift
-        # slowly along the episode (consecutive positions cos ~0.98) and the
-        # robot-state history [HIST_L][JOINTS] of a smooth joint trajectory;
-        # the current call's features / history are its position's plus noise
+        # retrieval data of every entry: ViT features that drift slowly along
+        # each episode (consecutive positions cos ~0.98), the robot-state
+        # history [HIST_L][JOINTS] of a smooth joint trajectory per episode; a
+        # call's features / history are its position's plus noise
         self.feat_store = torch.empty((STORE, FEAT), dtype=bf, pin_memory=True)
-        self.qfeat = torch.empty((STORE, FEAT), dtype=bf, device=dev)
-        f = randn(FEAT)
-        for q in range(STORE):
-            f = 0.98 * f + math.sqrt(1 - 0.98 ** 2) * randn(FEAT)
-            self.feat_store[q].copy_(f.to(bf))
-            self.qfeat[q] = (f + 0.1 * randn(FEAT)).to(bf)
-        traj = torch.cumsum(0.05 * randn(STORE + HIST_L, JOINTS), dim=0)
-        hist = torch.stack([traj[q:q + HIST_L] for q in range(STORE)])
+        self.qfeat = torch.empty((EP_LEN, FEAT), dtype=bf, device=dev)
+        hist = []
+        for e in range(EPISODES):
+            f = randn(FEAT)
+            for q in range(EP_LEN):
+                f = 0.98 * f + math.sqrt(1 - 0.98 ** 2) * randn(FEAT)
+                self.feat_store[e * EP_LEN + q].copy_(f.to(bf))
+                if e == 0:
+                    self.qfeat[q] = (f + 0.1 * randn(FEAT)).to(bf)
+            traj = torch.cumsum(0.05 * randn(EP_LEN + HIST_L, JOINTS), dim=0)
+            hist.append(torch.stack([traj[q:q + HIST_L] for q in range(EP_LEN)]))
+        hist = torch.cat(hist)
         self.hist_store = hist.cpu().pin_memory()
-        self.qhist = (hist + 0.005 * randn(STORE, HIST_L, JOINTS)).contiguous()
+        self.qhist = (hist[:EP_LEN] + 0.005 * randn(EP_LEN, HIST_L, JOINTS)).contiguous()
         self.slot_feat = torch.empty((SLOTS, FEAT), dtype=bf, device=dev)
         self.slot_hist = torch.empty((SLOTS, HIST_L, JOINTS), dtype=torch.float32, device=dev)
         self.choice = torch.empty(1, dtype=torch.int32, device=dev)
         self.matches, self.fallbacks, self.calls = 0, 0, 0
-        # expanded working set: SLOTS entries of (xbar, ybar) per layer, managed
-        # as a sliding window (position q .. q + LOOKAHEAD of the episode)
-        self.xbar = torch.empty(SLOTS, L_VLM, P, D, dtype=bf, device=dev)
-        self.ybar = torch.empty_like(self.xbar)
-        self.window = cgs.Window(SLOTS)
-        # initial-position preload, timed to estimate T_rec and T_trans of Eq. 5
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        entered, _, _ = self.window.advance([0], [0], [STORE], LOOKAHEAD)
-        for _, q, slot in entered:
-            self.rebuild_entry(q, slot)
-        torch.cuda.synchronize()
-        self.t_rec_ms = 1e3 * (time.perf_counter() - t1) / len(entered)
-        t1 = time.perf_counter()
-        for _ in range(8):
-            self.staging.copy_(self.store[0], non_blocking=True)
-        torch.cuda.synchronize()
-        self.t_trans_ms = 1e3 * (time.perf_counter() - t1) / 8
-        free, _ = torch.cuda.mem_get_info(dev)
-        self.m_entry = 2 * L_VLM * P * D * 2
-        self.budget = (float(free), float(self.m_entry), T_AVL_MS, self.t_trans_ms, self.t_rec_ms)
-        self.entered = []
+
         # action expert (Action Cache path, neuron-major W_down with log-normal row scale)
         self.exp = []
         for _ in range(L_EXP):
@@ -199,58 +190,106 @@ class World:
             temb.append(torch.cat([torch.sin(ang), torch.cos(ang)]).float())
         self.temb0 = temb[0].contiguous()
         self.dtemb = [(temb[t + 1] - temb[t]).contiguous() for t in range(STEPS)]
-        # buffers
+        self.full = torch.arange(FFE, dtype=torch.int32, device=dev)
+        # denoise buffers: anchor states (two anchors at most), every layer's
+        # input and output of the 4-step chain, the action residual stream
+        self.y_anc = torch.empty(2, L_EXP, S, DE, dtype=torch.float32, device=dev)
+        self.h_anc = torch.empty(2, L_EXP, FFE, S, dtype=torch.float32, device=dev)
+        self.xch = torch.empty(STEPS * L_EXP + 1, S, DE, dtype=bf, device=dev)
+        self.ych = torch.empty(STEPS * L_EXP, S, DE, dtype=bf, device=dev)
+        self.ra = torch.empty(S, DE, dtype=torch.float32, device=dev)
+
+        # every entry's stored masks (§5, offline): a dense reference denoise
+        # from the entry's own start (a_0 perturbed, cosine ~0.95) gives the
+        # activations of the group's four steps; the coverage rule keeps the
+        # top neurons; the entry stores one mask per layer and step, the
+        # one-group schedule [all, G, G, G]
+        self.exp_norms = cgs.act_down_norms(self.exp)
+        self.h_ref = torch.empty(L_EXP, STEPS, FFE, S, dtype=torch.float32, device=dev)
+        ref_layers = [cgs.MaskedLayer(self.exp[l], self.full, bias=self.dtemb[t] if l == L_EXP - 1 else None,
+                                      h_out=self.h_ref[l, t]) for t in range(STEPS) for l in range(L_EXP)]
+        self.ref_chain = cgs.MaskedChain(ref_layers, S, FFE)
+        nw = (FFE + 63) // 64
+        gwords = torch.empty(STORE, L_EXP, nw, dtype=torch.int64, device=dev)
+        gidx = torch.empty(L_EXP, FFE, dtype=torch.int32, device=dev)
+        gcnt = torch.empty(STORE, L_EXP, dtype=torch.int32, device=dev)
+        for j in range(STORE):
+            a_ref = (self.a0 + 0.33 * randn(S, DE)).contiguous()
+            cgs.residual_rmsnorm(self.ra, r_in=a_ref, bias=self.temb0, x_out=self.xch[0])
+            cgs.act_masked_layers(self.ref_chain, self.ra, self.xch)
+            cgs.act_build_masks(self.h_ref, None, "coverage", coverage=COVERAGE, mask_out=gwords[j],
+                                idx_out=gidx, count_out=gcnt[j], norms=self.exp_norms)
+            if j == 0:
+                self.h_ref0 = self.h_ref.clone()   # entry 0's activations, for the sweeps
+        torch.cuda.synchronize()
+        gw = gwords.cpu()
+        self.mask_store = torch.empty((STORE, L_EXP, STEPS, nw), dtype=torch.int64, pin_memory=True)
+        self.mask_store[:, :, 0] = -1                            # step 0: every neuron (the anchor)
+        self.mask_store[:, :, 1:] = gw[:, :, None, :]
+        self.mask_np = self.mask_store.numpy().view(np.uint64)
+        gc = gcnt.cpu().numpy()
+        self.mask_counts = np.empty((STORE, L_EXP, STEPS), dtype=np.int32)
+        self.mask_counts[:, :, 0] = FFE
+        self.mask_counts[:, :, 1:] = gc[:, :, None]
+        self.kmax = [int(self.mask_counts[:, l, 1:].max()) for l in range(L_EXP)]
+        self.K = [float(self.mask_counts[:, l, 1].mean()) for l in range(L_EXP)]   # mean per layer
+        del gwords, gidx, gcnt
+
+        # expanded working set: the pages' 2-D window, SLOTS entries of
+        # (xbar, ybar) per layer, their masks as index lists and the compact
+        # weight rows of each update mask
+        self.xbar = torch.empty(SLOTS, L_VLM, P, D, dtype=bf, device=dev)
+        self.ybar = torch.empty_like(self.xbar)
+        self.slot_words = torch.empty(SLOTS, L_EXP, STEPS, nw, dtype=torch.int64, device=dev)
+        self.slot_idx = torch.empty(SLOTS, L_EXP, STEPS, FFE, dtype=torch.int32, device=dev)
+        self.slot_cnt = torch.empty(SLOTS, L_EXP, STEPS, dtype=torch.int32, device=dev)
+        self.slot_cw = [[None, None] for _ in range(SLOTS)]   # [slot][mask group] -> per-layer buffers
+        self.slot_entry = [-1] * SLOTS
+        self.slot_tail = [None] * SLOTS                       # steps 1.. of the slot's denoise
+        self.slot_plan = [None] * SLOTS                       # its schedule, counts and compact weights
+        self.slot_bytes = [0] * SLOTS                         # algorithmic bytes of those steps
+        self.window = cgs.Window(SLOTS)
+        # the anchor step (step 0) is the same for every stored entry: its
+        # chain is built once
+        head = [cgs.MaskedLayer(self.exp[l], self.full, bias=self.dtemb[0] if l == L_EXP - 1 else None,
+                                y_out=self.ych[l], y_f32_out=self.y_anc[0, l], h_out=self.h_anc[0, l])
+                for l in range(L_EXP)]
+        self.head = cgs.MaskedChain(head, S, FFE)
+        # initial-position preload, timed to estimate T_rec and T_trans of Eq. 5
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        entered, _, _ = self.window.advance(list(range(T_WIN)), [0] * T_WIN, [EP_LEN] * T_WIN, 0)
+        for e, q, slot in entered:
+            self.slot_feat[slot].copy_(self.feat_store[e * EP_LEN + q], non_blocking=True)
+            self.slot_hist[slot].copy_(self.hist_store[e * EP_LEN + q], non_blocking=True)
+            self.rebuild_entry(e, q, slot)
+        torch.cuda.synchronize()
+        self.t_rec_ms = 1e3 * (time.perf_counter() - t1) / len(entered)
+        t1 = time.perf_counter()
+        for _ in range(8):
+            self.staging.copy_(self.store[0], non_blocking=True)
+        torch.cuda.synchronize()
+        self.t_trans_ms = 1e3 * (time.perf_counter() - t1) / 8
+        free, _ = torch.cuda.mem_get_info(dev)
+        self.m_entry = 2 * L_VLM * P * D * 2
+        self.budget = (float(free), float(self.m_entry), T_AVL_MS, self.t_trans_ms, self.t_rec_ms)
+        self.entered = []
+        # the group mask of entry 0 and its compact weights, for the sweeps
+        i0, c0 = cgs.act_mask_indices(self.mask_store[0, :, 1].contiguous().to(dev), FFE)
+        torch.cuda.synchronize()
+        self.K0 = [int(c) for c in c0.tolist()]
+        self.masks = [i0[l, : self.K0[l]].contiguous() for l in range(L_EXP)]
+        self.cexp = [cgs.act_gather_rows(self.exp[l], self.masks[l]) for l in range(L_EXP)]
+        # buffers of the context prefill
         self.k = cgs.ratio_to_count(RHO_P, P)
         self.r = torch.empty(P, D, dtype=torch.float32, device=dev)
         self.x = torch.empty(P, D, dtype=bf, device=dev)
         self.y = torch.empty(P, D, dtype=bf, device=dev)
         self.idx = torch.empty(self.k, dtype=torch.int32, device=dev)
         self.skey = torch.empty(P, dtype=torch.float64, device=dev)
-        self.ra = torch.empty(S, DE, dtype=torch.float32, device=dev)
-        self.xa = torch.empty(S, DE, dtype=bf, device=dev)
-        self.ya = torch.empty(S, DE, dtype=bf, device=dev)
-        self.y_anc = torch.empty(L_EXP, S, DE, dtype=torch.float32, device=dev)
-        self.h_anc = torch.empty(L_EXP, FFE, S, dtype=torch.float32, device=dev)
-        self.full = torch.arange(FFE, dtype=torch.int32, device=dev)
-        # reference denoise run (a0 perturbed, cosine ~0.95) -> h_ref -> group masks
-        self.h_ref = torch.empty(L_EXP, STEPS, FFE, S, dtype=torch.float32, device=dev)
-        a_ref = (self.a0 + 0.33 * randn(S, DE)).contiguous()
-        self._denoise_dense(a_ref, self.h_ref)
-        # Eq. 1's down-projection norms are a property of the weights: computed once
-        self.exp_norms = self.cgs.act_down_norms(self.exp)
-        self.mask_words = torch.empty(L_EXP, (FFE + 63) // 64, dtype=torch.int64, device=dev)
-        self.mask_idx = torch.empty(L_EXP, FFE, dtype=torch.int32, device=dev)
-        self.mask_cnt = torch.empty(L_EXP, dtype=torch.int32, device=dev)
-        self.build_masks(self.mask_words, self.mask_idx, self.mask_cnt)
-        torch.cuda.synchronize()
-        self.K = [int(c) for c in self.mask_cnt.view(-1).tolist()]
-        self.masks = [self.mask_idx[l, : self.K[l]].contiguous() for l in range(L_EXP)]
-        # second set of outputs for the timed mask build
-        self.mw2 = torch.empty_like(self.mask_words)
-        self.mi2 = torch.empty_like(self.mask_idx)
-        self.mc2 = torch.empty_like(self.mask_cnt)
-        # compact weights of the group's masks (§4.1 / §5): the rows each masked
-        # step reads, gathered once per call
-        self.compact_weights = True
-        self.cexp = [cgs.act_gather_rows(self.exp[l], self.masks[l]) for l in range(L_EXP)]
-        self.g_ctx, self.g_anchor, self.g_masked, self.g_mask, self.g_gather = [], None, None, None, None
-        log(f"setup {time.time() - t0:.1f}s; masked neurons per layer {min(self.K)}..{max(self.K)} "
-            f"of {FFE} (mean {sum(self.K) / len(self.K) / FFE:.3f})")
-
-    def _denoise_dense(self, a, h_store):
-        cgs = self.cgs
-        cgs.residual_rmsnorm(self.ra, r_in=a, bias=self.temb0, x_out=self.xa)
-        for t in range(STEPS):
-            for l in range(L_EXP):
-                cgs.act_ffn_masked(self.exp[l], self.xa, self.full, y_out=self.ya, h_out=h_store[l, t])
-                cgs.residual_rmsnorm(self.ra, y=self.ya, bias=self.dtemb[t] if l == L_EXP - 1 else None,
-                                     x_out=self.xa)
-
-    def build_masks(self, words, idx, cnt):
-        # the 18 layers' masks are independent: one batched build, from the
-        # stored weight norms (only the reference activations are read)
-        self.cgs.act_build_masks(self.h_ref, None, "coverage", coverage=COVERAGE,
-                                 mask_out=words, idx_out=idx, count_out=cnt, norms=self.exp_norms)
+        self.g_ctx, self.g_anchor = [], None
+        log(f"setup {time.time() - t0:.1f}s; masked neurons per layer (store mean) "
+            f"{min(self.K):.0f}..{max(self.K):.0f} of {FFE} (mean {sum(self.K) / len(self.K) / FFE:.3f})")
 
     # --- one policy call -------------------------------------------------------
     # Between layers the residual add, the RMSNorm of the next layer's input and
@@ -268,19 +307,25 @@ class World:
 
     @staticmethod
     def position(i):
-        """Matched position of call i: the window advances one entry per call."""
-        return i % (STORE - LOOKAHEAD)
+        """Matched position of call i in every candidate episode: the window
+        advances one position per call."""
+        return i % (EP_LEN - L_WIN)
 
     def advance(self, i):
-        """Slide the window to call i's position; returns (slot of the call's
-        entry, entries to rebuild [(episode, position, slot)])."""
+        """Slide the window to call i's position; the entering entries'
+        retrieval data are copied to their slots at once (the heavy rebuild is
+        the caller's).  Returns the entries to rebuild [(episode, position, slot)]."""
         q = self.position(i)
-        entered, _, _ = self.window.advance([0], [q], [STORE], LOOKAHEAD, self.budget)
+        entered, _, _ = self.window.advance(list(range(T_WIN)), [q] * T_WIN, [EP_LEN] * T_WIN, L_WIN,
+                                            self.budget)
         self.entered.append(len(entered))
-        slot = self.window.slot(0, q)
-        if slot < 0:
+        if self.window.slot(0, q) < 0:
             raise RuntimeError(f"entry {q} is not resident")
-        return slot, entered
+        for e, p, slot in entered:
+            j = e * EP_LEN + p
+            self.slot_feat[slot].copy_(self.feat_store[j], non_blocking=True)
+            self.slot_hist[slot].copy_(self.hist_store[j], non_blocking=True)
+        return entered
 
     def retrieve(self, i):
         """Visual top-T over the prepared slots, joint-history rerank and the
@@ -306,76 +351,103 @@ class World:
             self.ctx_layers(e)
 
     def _anchor(self):
-        cgs = self.cgs
-        cgs.residual_rmsnorm(self.ra, r_in=self.a0, bias=self.temb0, x_out=self.xa)
-        for l in range(L_EXP):
-            cgs.act_ffn_masked(self.exp[l], self.xa, self.full, y_out=self.ya,
-                               y_f32_out=self.y_anc[l], h_out=self.h_anc[l],
-                               glue=(self.ra, self.dtemb[0] if l == L_EXP - 1 else None, self.xa))
-
-    def _masked(self):
-        cgs = self.cgs
-        for t in range(1, STEPS):
-            for l in range(L_EXP):
-                glue = (self.ra, self.dtemb[t] if l == L_EXP - 1 else None, self.xa)
-                if self.compact_weights:
-                    cgs.act_ffn_masked_compact(self.cexp[l], self.xa, self.masks[l], y_anchor=self.y_anc[l],
-                                               h_anchor=self.h_anc[l], y_out=self.ya, glue=glue)
-                else:
-                    cgs.act_ffn_masked(self.exp[l], self.xa, self.masks[l], y_anchor=self.y_anc[l],
-                                       h_anchor=self.h_anc[l], y_out=self.ya, glue=glue)
-
-    def _gather(self):
-        for l in range(L_EXP):
-            self.cgs.act_gather_rows(self.exp[l], self.masks[l], out=self.cexp[l])
-
-    def gather(self):
-        if self.compact_weights:
-            self.g_gather.replay() if self.g_gather else self._gather()
-
-    def _mask_build(self):
-        self.build_masks(self.mw2, self.mi2, self.mc2)
+        self.cgs.residual_rmsnorm(self.ra, r_in=self.a0, bias=self.temb0, x_out=self.xch[0])
+        self.cgs.act_masked_layers(self.head, self.ra, self.xch[: L_EXP + 1])
 
     def act_anchor(self):
         self.g_anchor.replay() if self.g_anchor else self._anchor()
 
-    def act_masked(self):
-        self.g_masked.replay() if self.g_masked else self._masked()
+    def act_masked(self, c):
+        """Steps 1.. of the denoise with slot c's stored masks: one host call
+        (the slot's chain is assembled on its first use, while the GPU runs
+        the prefill and the anchor step)."""
+        if self.slot_tail[c] is None:
+            self.slot_tail[c] = self._tail_chain(c)
+        self.cgs.act_masked_layers(self.slot_tail[c], self.ra, self.xch[L_EXP:])
 
-    def mask_build(self):
-        self.g_mask.replay() if self.g_mask else self._mask_build()
+    def _tail_chain(self, slot):
+        cgs = self.cgs
+        kind, anchor, mask, counts, compact = self.slot_plan[slot]
+        tail = []
+        for t in range(1, STEPS):
+            a = anchor[t]
+            for l in range(L_EXP):
+                i = t * L_EXP + l
+                bias = self.dtemb[t] if l == L_EXP - 1 else None
+                if kind[t] == 0:
+                    tail.append(cgs.MaskedLayer(self.exp[l], self.full, bias=bias, y_out=self.ych[i],
+                                                y_f32_out=self.y_anc[a, l], h_out=self.h_anc[a, l]))
+                else:
+                    m = mask[t]
+                    K = int(counts[l, m])
+                    tail.append(cgs.MaskedLayer(compact[m][l], self.slot_idx[slot, l, m, :K],
+                                                y_anchor=self.y_anc[a, l], h_anchor=self.h_anc[a, l], bias=bias,
+                                                y_out=self.ych[i]))
+        return cgs.MaskedChain(tail, S, FFE)
 
-    def rebuild_entry(self, q, slot):
-        """Transfer compact entry q (and its retrieval features and history) to
-        the device and expand it into `slot` (on the current stream)."""
-        self.slot_feat[slot].copy_(self.feat_store[q], non_blocking=True)
-        self.slot_hist[slot].copy_(self.hist_store[q], non_blocking=True)
-        self.staging.copy_(self.store[q], non_blocking=True)
-        self.cgs.ref_rebuild_dense(self.vlm, self.staging, self.xbar[slot], self.ybar[slot])
+    def rebuild_entry(self, e, q, slot):
+        """Move entry (e, q) to the device and prepare it in `slot` (on the
+        current stream): its compact input is expanded by the 17-layer dense
+        rebuild, its stored masks are copied and turned into index lists, the
+        weight rows of each update mask are gathered into the slot's compact
+        buffers, and the host keeps the slot's denoise chain."""
+        cgs = self.cgs
+        j = e * EP_LEN + q
+        self.staging.copy_(self.store[j], non_blocking=True)
+        self.slot_words[slot].copy_(self.mask_store[j], non_blocking=True)
+        cgs.ref_rebuild_dense(self.vlm, self.staging, self.xbar[slot], self.ybar[slot])
+        cgs.act_mask_indices(self.slot_words[slot], FFE, idx_out=self.slot_idx[slot], count_out=self.slot_cnt[slot])
+        counts = self.mask_counts[j]
+        kind, anchor, mask = cgs.denoise_schedule(counts, self.mask_np[j], FFE)
+        if kind[0] != 0:
+            raise RuntimeError("a stored schedule must start with the anchor step")
+        groups = sorted({mask[t] for t in range(STEPS) if kind[t] == 1})
+        if len(groups) > 2:
+            raise RuntimeError("at most two update masks per entry")
+        compact = {}
+        for gi, t in enumerate(groups):
+            if self.slot_cw[slot][gi] is None:
+                self.slot_cw[slot][gi] = [torch_empty((3, self.kmax[l], DE), self.dev) for l in range(L_EXP)]
+            bufs = self.slot_cw[slot][gi]
+            cw = []
+            for l in range(L_EXP):
+                K = int(counts[l, t])
+                f = cgs.FFN(bufs[l][0, :K], bufs[l][1, :K], bufs[l][2, :K], "fd")
+                cgs.act_gather_rows(self.exp[l], self.slot_idx[slot, l, t, :K], out=f)
+                cw.append(f)
+            compact[t] = cw
+        self.slot_plan[slot] = (kind, anchor, mask, counts, compact)
+        self.slot_tail[slot] = None
+        self.slot_bytes[slot] = sum(masked_layer_bytes(int(counts[l, mask[t]]))
+                                    for t in range(1, STEPS) if kind[t] == 1 for l in range(L_EXP))
+        self.slot_entry[slot] = j
 
     def rebuild(self, entered):
-        for _, q, slot in entered:
-            self.rebuild_entry(q, slot)
+        for e, q, slot in entered:
+            self.rebuild_entry(e, q, slot)
 
     def capture(self):
-        """HIP graphs of the launch-bound phases (fixed buffers): the 17 context
-        layers of each working-set slot, the anchor step, the three masked steps,
-        the mask build and the compact-weight gather.  The rebuild (long kernels)
-        and each call's first RMSNorm stay eager."""
+        """HIP graphs of the launch-bound phases with fixed buffers: the 17
+        context layers of each working-set slot and the anchor step.  The
+        update steps (one host call per call, whose layers depend on the
+        chosen entry), the rebuild (long kernels) and each call's first RMSNorm
+        stay eager."""
         import torch
         torch.cuda.synchronize()
 
         def cap(fn):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
                 fn()
-            return g
+            return gr
         self.g_ctx = [cap(lambda e=e: self.ctx_layers(e)) for e in range(SLOTS)]
         self.g_anchor = cap(self._anchor)
-        self.g_masked = cap(self._masked)
-        self.g_mask = cap(self._mask_build)
-        self.g_gather = cap(self._gather)
         torch.cuda.synchronize()
+
+
+def torch_empty(shape, dev):
+    import torch
+    return torch.empty(shape, dtype=torch.bfloat16, device=dev)
 
 
 def joint_denoise(w, reps: int = 10) -> dict:
@@ -493,7 +565,7 @@ def ctx_sweep(w, reps: int = 8) -> dict:
             ts.append(e0.elapsed_time(e1))
         ms = _median(ts[1:])
         flops = L_VLM * (2.0 * k * D * 2 * FF + 2.0 * k * FF * D)
-        byts = L_VLM * (3 * FF * D * 2 + 2 * k * D * 2 + k * FF * 4 + 2 * P * D * 2)
+        byts = L_VLM * (3 * FF * D * 2 + k * D * 2 + 2 * P * D * 2)
         roof = 1e3 * max(flops / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBPS * 1e9))
         out[f"rho_{rho}"] = {"k": k, "ms": round(ms, 4), "per_layer_us": round(1e3 * ms / L_VLM, 2),
                              "tflops": round(flops / ms / 1e9, 1),
@@ -501,25 +573,98 @@ def ctx_sweep(w, reps: int = 8) -> dict:
                              "bound": "mfma" if flops / byts > RIDGE else "hbm",
                              "frac_of_roofline": round(roof / ms, 4),
                              "mfma_frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
-    out["note"] = ("17 layers per call incl. selection, fused glue and next-layer keys; bytes = weights + "
-                   "gathered rows + h round trip + cached output copy")
+    out["note"] = ("17 layers per call incl. selection, fused glue and next-layer keys; bytes per layer = "
+                   "weights + gathered x rows + cached outputs read + outputs written (no intermediate h)")
     return out
+
+
+def _time_graph(fn, start, flush, reps):
+    """Median (ms) of graph replays of fn, MALL-warm (the same replay just
+    before) and cold (a 512 MB write before each), `start` run before each."""
+    import torch
+    start()
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    res = {}
+    for mode in ("warm", "cold"):
+        ts = []
+        for _ in range(reps + 1):
+            start()
+            if mode == "cold":
+                flush.fill_(1)
+            else:
+                g.replay()
+                start()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[mode] = _median(ts[1:])
+    return res
+
+
+def _time_eager(fn, start, flush, reps):
+    """As _time_graph, with fn launched eagerly each time (its host cost included)."""
+    import torch
+    res = {}
+    for mode in ("warm", "cold"):
+        ts = []
+        for _ in range(reps + 1):
+            start()
+            if mode == "cold":
+                flush.fill_(1)
+            else:
+                fn()
+                start()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[mode] = _median(ts[1:])
+    return res
+
+
+def _rates(res, byts):
+    return {**{f"{m}_ms": round(res[m], 4) for m in res},
+            **{f"{m}_GBps": round(byts / res[m] / 1e6, 1) for m in res},
+            **{f"{m}_hbm_frac": round(byts / res[m] / 1e6 / PEAK_HBM_GBPS, 4) for m in res}}
 
 
 def act_sweep(w, reps: int = 10) -> dict:
     """One masked denoise step (18 expert layers on compact weights, glue
     included) MALL-warm (back-to-back replays) and cold (a 512 MB write before
-    each replay evicts the MALL), with the coverage masks of the run and with
+    each replay evicts the MALL): with the coverage masks of entry 0 and with
     top-K masks at neuron ratios 0.2 / 0.3 / 0.4 built from the same reference
-    activations (§5's rule)."""
+    activations (§5's rule), graph-replayed; the coverage step also as one
+    eager act_masked_layers call (how the policy call runs it) and as the
+    persistent one-launch step (act_denoise_step)."""
     import torch
     cgs = w.cgs
     flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=w.dev)
+    w._anchor()                      # anchor state of step 0 in y_anc[0], h_anc[0]
+    torch.cuda.synchronize()
+    ra = torch.empty(S, DE, dtype=torch.float32, device=w.dev)
+    xa = torch.empty(S, DE, dtype=torch.bfloat16, device=w.dev)
+    ya = torch.empty_like(xa)
+    xs = torch.empty(L_EXP + 1, S, DE, dtype=torch.bfloat16, device=w.dev)
+
+    def start():
+        cgs.residual_rmsnorm(ra, r_in=w.a0, bias=w.temb0, x_out=xa)
+        xs[0].copy_(xa)
+
     out = {}
     cases = [("coverage_0.844", w.masks, w.cexp)]
     for rho in (0.2, 0.3, 0.4):
         K = cgs.ratio_to_count(rho, FFE)
-        _, mi, mc = cgs.act_build_masks(w.h_ref, None, "topk", K=K, norms=w.exp_norms)
+        _, mi, mc = cgs.act_build_masks(w.h_ref0, None, "topk", K=K, norms=w.exp_norms)
         torch.cuda.synchronize()
         cnt = [int(c) for c in mc.tolist()]
         masks = [mi[l, : cnt[l]].contiguous() for l in range(L_EXP)]
@@ -527,54 +672,127 @@ def act_sweep(w, reps: int = 10) -> dict:
     for name, masks, cexp in cases:
         def step(masks=masks, cexp=cexp):
             for l in range(L_EXP):
-                cgs.act_ffn_masked_compact(cexp[l], w.xa, masks[l], y_anchor=w.y_anc[l], h_anchor=w.h_anc[l],
-                                           y_out=w.ya, glue=(w.ra, w.dtemb[1] if l == L_EXP - 1 else None, w.xa))
-
-        def start():
-            cgs.residual_rmsnorm(w.ra, r_in=w.a0, bias=w.temb0, x_out=w.xa)
-
-        start()
-        step()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        res = {}
-        for mode in ("warm", "cold"):
-            ts = []
-            for _ in range(reps + 1):
-                start()
-                if mode == "cold":
-                    flush.fill_(1)
-                else:
-                    g.replay()
-                    start()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                g.replay()
-                e1.record()
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1))
-            res[mode] = _median(ts[1:])
+                cgs.act_ffn_masked_compact(cexp[l], xa, masks[l], y_anchor=w.y_anc[0, l], h_anchor=w.h_anc[0, l],
+                                           y_out=ya, glue=(ra, w.dtemb[1] if l == L_EXP - 1 else None, xa))
+        res = _time_graph(step, start, flush, reps)
         Ks = [int(m.numel()) for m in masks]
         byts = sum(masked_layer_bytes(K) for K in Ks)
-        out[name] = {"neurons_mean": round(sum(Ks) / len(Ks), 1), "bytes": byts,
-                     **{f"{m}_ms": round(res[m], 4) for m in res},
-                     **{f"{m}_GBps": round(byts / res[m] / 1e6, 1) for m in res},
-                     **{f"{m}_hbm_frac": round(byts / res[m] / 1e6 / PEAK_HBM_GBPS, 4) for m in res}}
-    out["note"] = "one masked step (18 layers); cold = MALL evicted by a 512 MB write before the step"
+        out[name] = {"neurons_mean": round(sum(Ks) / len(Ks), 1), "bytes": byts, **_rates(res, byts)}
+    # the coverage step as the policy call runs it: one eager chain call
+    chain = cgs.MaskedChain([cgs.MaskedLayer(w.cexp[l], w.masks[l], y_anchor=w.y_anc[0, l], h_anchor=w.h_anc[0, l],
+                                             bias=w.dtemb[1] if l == L_EXP - 1 else None) for l in range(L_EXP)],
+                            S, FFE)
+    byts = out["coverage_0.844"]["bytes"]
+    res = _time_eager(lambda: cgs.act_masked_layers(chain, ra, xs), start, flush, reps)
+    out["coverage_0.844_eager_chain"] = _rates(res, byts)
+    # the persistent one-launch step on the same masks (transposed down weights)
+    st = [cgs.StepLayer(cgs.act_gather_rows_t(w.exp[l], w.masks[l]), idx=w.masks[l], y_anchor=w.y_anc[0, l],
+                        h_anchor=w.h_anc[0, l], bias=w.dtemb[1] if l == L_EXP - 1 else None) for l in range(L_EXP)]
+    status = torch.zeros(1, dtype=torch.int32, device=w.dev)
+    res = _time_graph(lambda: cgs.act_denoise_step(st, ra, xs, FFE, status=status), start, flush, reps)
+    torch.cuda.synchronize()
+    out["coverage_0.844_persistent"] = {**_rates(res, byts), "status": int(status.item())}
+    out["note"] = ("one masked step (18 layers); cold = MALL evicted by a 512 MB write before the step; "
+                   "graph-replayed unless named eager")
     return out
 
 
-def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
+def act_schedules(w, reps: int = 10) -> dict:
+    """The whole 4-step denoise under the two anchor schedules of §4.1,
+    graph-replayed, warm and cold: one group (anchor at step 0, steps 1-3
+    updated with the group mask of steps 0-3) and two groups (anchors at steps
+    0 and 2; step 1 updated with the mask of steps {0, 1}, step 3 with that of
+    steps {2, 3}); masks from entry 0's reference activations (coverage 0.844)."""
+    import torch
+    cgs = w.cgs
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=w.dev)
+    ra = torch.empty(S, DE, dtype=torch.float32, device=w.dev)
+    xs = torch.empty(STEPS * L_EXP + 1, S, DE, dtype=torch.bfloat16, device=w.dev)
+    anchor_bytes = L_EXP * (3 * FFE * DE * 2 + S * DE * 2 + S * DE * 4 + FFE * S * 4 + S * DE * 2)
+
+    def group_masks(t0, t1):
+        hg = w.h_ref0[:, t0:t1].contiguous()
+        _, mi, mc = cgs.act_build_masks(hg, None, "coverage", coverage=COVERAGE, norms=w.exp_norms)
+        torch.cuda.synchronize()
+        cnt = [int(c) for c in mc.tolist()]
+        masks = [mi[l, : cnt[l]].contiguous() for l in range(L_EXP)]
+        return masks, [cgs.act_gather_rows(w.exp[l], masks[l]) for l in range(L_EXP)]
+
+    def chain_of(kinds):
+        layers, byts = [], 0
+        a = -1
+        for t, kind in enumerate(kinds):
+            if kind is None:
+                a += 1
+                byts += anchor_bytes
+            for l in range(L_EXP):
+                bias = w.dtemb[t] if l == L_EXP - 1 else None
+                if kind is None:
+                    layers.append(cgs.MaskedLayer(w.exp[l], w.full, bias=bias, y_f32_out=w.y_anc[a, l],
+                                                  h_out=w.h_anc[a, l]))
+                else:
+                    masks, cexp = kind
+                    layers.append(cgs.MaskedLayer(cexp[l], masks[l], y_anchor=w.y_anc[a, l], h_anchor=w.h_anc[a, l],
+                                                  bias=bias))
+                    byts += masked_layer_bytes(int(masks[l].numel()))
+        return cgs.MaskedChain(layers, S, FFE), byts
+
+    def start():
+        cgs.residual_rmsnorm(ra, r_in=w.a0, bias=w.temb0, x_out=xs[0])
+
+    g1 = (w.masks, w.cexp)
+    ga, gb = group_masks(0, 2), group_masks(2, 4)
+    out = {}
+    for name, kinds in (("one_group", [None, g1, g1, g1]), ("two_groups", [None, ga, None, gb])):
+        chain, byts = chain_of(kinds)
+        res = _time_graph(lambda chain=chain: cgs.act_masked_layers(chain, ra, xs), start, flush, reps)
+        upd = [k for k in kinds if k is not None]
+        nm = [sum(int(m.numel()) for m in k[0]) / L_EXP for k in upd]
+        out[name] = {"anchor_steps": sum(k is None for k in kinds), "update_neurons_mean": round(sum(nm) / len(nm), 1),
+                     "bytes": byts, **_rates(res, byts)}
+    out["note"] = "4 denoise steps of 18 layers as one chain, glue included; bytes = anchors' dense + updates' masked"
+    return out
+
+
+def mask_build_timing(w, reps: int = 20) -> dict:
+    """The 18-layer group mask build from one entry's reference activations
+    (stored weight norms; offline per entry on the pages), graph-replayed."""
+    import torch
+    cgs = w.cgs
+    nw = (FFE + 63) // 64
+    words = torch.empty(L_EXP, nw, dtype=torch.int64, device=w.dev)
+    idx = torch.empty(L_EXP, FFE, dtype=torch.int32, device=w.dev)
+    cnt = torch.empty(L_EXP, dtype=torch.int32, device=w.dev)
+
+    def build():
+        cgs.act_build_masks(w.h_ref0, None, "coverage", coverage=COVERAGE, mask_out=words, idx_out=idx,
+                            count_out=cnt, norms=w.exp_norms)
+    build()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        build()
+    ts = []
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return {"ms": round(_median(ts[1:]), 4), "layers": L_EXP,
+            "note": "per entry, offline (the store holds the result); not part of the call"}
+
+
+def cpu_baseline(k_masked_mean: int, rebuilds: float, reps: int = 6) -> dict:
     """The oracle, timed on the host cores over a bounded sample of the step:
     one context layer (select + recompute of 231 rows), one dense anchor
-    layer, one masked layer, one mask build, one dense rebuild layer and one
-    retrieval over the 16 prepared entries, each timed `reps` times (mean),
-    scaled to the step's 17 / 18 / 54 / 18 / 17 / 1 counts."""
+    layer, one masked layer, one dense rebuild layer and one retrieval over
+    the 20 prepared entries, each timed `reps` times (mean), scaled to the
+    step's 17 / 18 / 54 / 17 x rebuilds / 1 counts."""
     import numpy as np
     import oracle as O
-    from cgs_inputs import act_tokens, ctx_layer_inputs, ffn_weights, random_bf16, synthetic_h_ref
+    from cgs_inputs import act_tokens, ctx_layer_inputs, ffn_weights, random_bf16
     threads = None
     try:
         from threadpoolctl import threadpool_info
@@ -587,7 +805,6 @@ def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
     y_ref = random_bf16(7, 0, "y_ref", (P, D))
     we = ffn_weights(7, 1, DE, FFE, down_layout="fd", down_lognormal_sigma=1.5)
     t_ = act_tokens(7, 1, S, DE, noise_sigma=0.33)
-    h = synthetic_h_ref(7, 1, STEPS, FFE, S)
     r0 = random_bf16(7, 0, "r0", (P, D))
     k = O.ratio_to_count(RHO_P, P)
     m = np.sort(np.random.default_rng(0).permutation(FFE)[:k_masked_mean]).astype(np.int32)
@@ -595,8 +812,7 @@ def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
     g = np.random.default_rng(7)
     feats = O.round_to_bf16_bits(g.standard_normal((SLOTS + 1, FEAT)))
     hists = g.standard_normal((SLOTS, HIST_L, JOINTS))
-    tm = {"ctx_layer": 0.0, "anchor_layer": 0.0, "masked_layer": 0.0, "mask_layer": 0.0,
-          "rebuild_layer": 0.0, "retrieval": 0.0}
+    tm = {"ctx_layer": 0.0, "anchor_layer": 0.0, "masked_layer": 0.0, "rebuild_layer": 0.0, "retrieval": 0.0}
     for _ in range(reps):
         t0 = time.perf_counter()
         idx, _ = O.ctx_select(inp["x"], inp["x_ref"], k)
@@ -609,9 +825,6 @@ def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
         O.act_ffn_masked(we, t_["x"], m, ya.astype(np.float32), ha.astype(np.float32))
         tm["masked_layer"] += time.perf_counter() - t0
         t0 = time.perf_counter()
-        O.act_build_mask(h, we, "coverage", coverage=COVERAGE)
-        tm["mask_layer"] += time.perf_counter() - t0
-        t0 = time.perf_counter()
         O.rebuild_dense([w], r0)
         tm["rebuild_layer"] += time.perf_counter() - t0
         t0 = time.perf_counter()
@@ -620,12 +833,12 @@ def cpu_baseline(k_masked_mean: int, reps: int = 6) -> dict:
     total = sum(tm.values())
     tm = {k_: v / reps for k_, v in tm.items()}
     per_step = (L_VLM * tm["ctx_layer"] + L_EXP * tm["anchor_layer"]
-                + (STEPS - 1) * L_EXP * tm["masked_layer"] + L_EXP * tm["mask_layer"]
-                + L_VLM * tm["rebuild_layer"] + tm["retrieval"])
+                + (STEPS - 1) * L_EXP * tm["masked_layer"] + rebuilds * L_VLM * tm["rebuild_layer"]
+                + tm["retrieval"])
     return {"value": round(per_step * 1e3, 1), "unit": "ms", "cores": cores, "kind": "oracle",
             "sample": (f"one layer of each row, timed {reps} times on the host (mean) and scaled to the step: "
-                       "17 x (ctx select + 231-row recompute) + 18 x dense anchor + 54 x masked "
-                       "+ 18 x mask build + 17 x dense rebuild layer + one retrieval over 16 entries; "
+                       f"17 x (ctx select + 231-row recompute) + 18 x dense anchor + 54 x masked "
+                       f"+ {rebuilds:g} x 17 dense rebuild layers + one retrieval over {SLOTS} entries; "
                        "NumPy float64"),
             "sample_seconds": round(total, 2),
             "per_layer_ms": {k_: round(v * 1e3, 2) for k_, v in tm.items()}}
@@ -640,19 +853,13 @@ def main():
     ap.add_argument("--no-graphs", action="store_true",
                     help="launch every kernel eagerly instead of replaying HIP graphs")
     ap.add_argument("--rebuild-stream", choices=("side", "overlap", "main"), default="main",
-                    help="run the entry rebuild in line (main), on a side stream as soon as its slot is free "
-                         "(side), or on a side stream after the call's context prefill with the next call's "
-                         "prefill waiting for it (overlap: the rebuild shares the GPU with the action path only)")
+                    help="prepare the entering entries in line after the call (main), on a side stream as soon "
+                         "as their slots are free (side), or on a side stream after the call's context prefill "
+                         "with the next call's prefill waiting for it (overlap)")
     ap.add_argument("--no-joint", action="store_true",
                     help="skip the separate joint token + neuron sparsity measurement")
     ap.add_argument("--no-sweeps", action="store_true",
-                    help="skip the recompute-ratio and neuron-ratio sweeps (reported beside the step)")
-    ap.add_argument("--gather-during", choices=("prefill", "anchor"), default="anchor",
-                    help="run the compact-weight gather beside the anchor step, after the context prefill "
-                         "(default: the rows are then still in the MALL when the masked steps read them), "
-                         "or beside the prefill, as the pages overlap it")
-    ap.add_argument("--no-compact", action="store_true",
-                    help="masked steps gather the mask's weight rows in place (no compact buffers)")
+                    help="skip the ratio sweeps, the schedule comparison and the mask-build timing")
     ap.add_argument("--serial-steps", type=int, default=8,
                     help="calls timed with everything on one stream, for comparison")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
@@ -663,6 +870,9 @@ def main():
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         sys.exit("steps must be >= 1 and warmup >= 0")
+    if args.warmup + args.steps + args.serial_steps + 4 > EP_LEN - L_WIN:
+        sys.exit(f"at most {EP_LEN - L_WIN - args.serial_steps - 4} warmup + timed steps: every call must "
+                 "find its position inside the episodes")
 
     import torch
     import cache_guided_sparse_amd as cgs
@@ -670,70 +880,54 @@ def main():
     dev = torch.device("cuda:0")
     w = World(dev)
 
-    phases = ["ctx_prefill", "act_anchor", "act_masked", "mask_build", "rebuild", "gather", "retrieval"]
-    # The compact weights of the group's masks are gathered on a side stream
-    # beside the anchor step, after the context prefill (or beside the
-    # prefill); the masked steps wait for them, and the gather waits until the
-    # previous call's masked steps are done with the buffers.  The rebuild of the entry 16 calls ahead runs in line after the
-    # call, or on a second side stream (then `serial` steps put it back in
-    # line for comparison): it waits for the call's context prefill to release
-    # the slot, and the prefill that next uses the slot waits for the rebuild.
-    # In the overlap schedule the rebuild starts after the call's prefill and
-    # the next call's prefill waits for it, so it shares the GPU with the
-    # latency-bound action path only.
+    phases = ["ctx_prefill", "act_anchor", "act_masked", "rebuild", "retrieval"]
+    # The entries entering the window (one per candidate episode and call)
+    # are prepared in line after the call, or on a side stream (then `serial`
+    # steps put them back in line for comparison): a slot's preparation waits
+    # until the last call that chose the slot is done with it, and the call
+    # that next chooses it waits for the preparation.  In the overlap schedule
+    # the preparation starts after the call's prefill and the next call's
+    # prefill waits for it, so it shares the GPU with the action path only.
     # All streams have the default priority.
-    w.compact_weights = not args.no_compact
     main_s = torch.cuda.current_stream()
-    gather_s = torch.cuda.Stream(device=dev)
     side = torch.cuda.Stream(device=dev) if args.rebuild_stream in ("side", "overlap") else None
     overlap = args.rebuild_stream == "overlap"
-    rebuild_done = torch.cuda.Event()
-    ctx_done = [torch.cuda.Event() for _ in range(SLOTS)]
+    rebuild_done, ctx_done = torch.cuda.Event(), torch.cuda.Event()
+    used = [torch.cuda.Event() for _ in range(SLOTS)]
     rebuilt = [torch.cuda.Event() for _ in range(SLOTS)]
     pending = [False] * SLOTS
-    gathered, masked_done = torch.cuda.Event(), torch.cuda.Event()
-    gather_after_prefill = args.gather_during == "anchor"
+    call_bytes = []
 
     def step(i, ev=None, serial=False):
-        """One call.  ev: 11 timing events; 9-10 the retrieval, 0-4 the other
-        main-stream phases, 5-6 the rebuild and 7-8 the gather on the streams
-        that run them."""
-        _, entered = w.advance(i)
+        """One call.  ev: 11 timing events; 9-10 the retrieval, 0-3 the other
+        main-stream phases, 5-6 the preparation of the entering entries on the
+        stream that runs it."""
+        entered = w.advance(i)
         rec = (lambda q: ev[q].record()) if ev is not None else (lambda q: None)
-
-        def launch_gather(after=None):
-            gather_s.wait_event(masked_done)
-            if after is not None:
-                gather_s.wait_event(after)
-            with torch.cuda.stream(gather_s):
-                rec(7)
-                w.gather()
-                rec(8)
-                gathered.record(gather_s)
-        if not gather_after_prefill:
-            launch_gather()
         rec(9)
-        e = w.retrieve(i)   # the slot the retrieval picks drives the prefill
+        e = w.retrieve(i)   # the slot the retrieval picks drives the prefill and the denoise
         rec(10)
         if pending[e]:
             main_s.wait_event(rebuilt[e])
             pending[e] = False
         if overlap and not serial:
-            main_s.wait_event(rebuild_done)   # the previous call's rebuild ends before this prefill
+            main_s.wait_event(rebuild_done)   # the previous call's preparation ends before this prefill
         rec(0)
         w.ctx_prefill(i, e)
         rec(1)
-        ctx_done[e].record(main_s)
-        if gather_after_prefill:
-            launch_gather(ctx_done[e])
+        ctx_done.record(main_s)
+        w.act_anchor()
+        rec(2)
+        w.act_masked(e)
+        rec(3)
+        used[e].record(main_s)
+        call_bytes.append(w.slot_bytes[e])
         if side is not None and not serial:
-            # a slot taken by an entering entry was last read by an earlier
-            # call's prefill; the next prefill that reads it waits for this
             with torch.cuda.stream(side):
                 for _, _, s_ in entered:
-                    side.wait_event(ctx_done[s_])
+                    side.wait_event(used[s_])
                 if overlap:
-                    side.wait_event(ctx_done[e])   # start once this call's prefill is done
+                    side.wait_event(ctx_done)   # start once this call's prefill is done
                 rec(5)
                 w.rebuild(entered)
                 rec(6)
@@ -742,15 +936,7 @@ def main():
                     pending[s_] = True
                 if overlap:
                     rebuild_done.record(side)
-        w.act_anchor()
-        rec(2)
-        main_s.wait_event(gathered)
-        w.act_masked()
-        masked_done.record(main_s)
-        rec(3)
-        w.mask_build()
-        rec(4)
-        if side is None or serial:
+        else:
             rec(5)
             w.rebuild(entered)
             rec(6)
@@ -763,10 +949,10 @@ def main():
             step(first + j, evs[j], serial)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / n
-        bounds = [(0, 1), (1, 2), (2, 3), (3, 4), (5, 6), (7, 8), (9, 10)]
+        bounds = [(0, 1), (1, 2), (2, 3), (5, 6), (9, 10)]
         ph = {p: sum(evs[j][a].elapsed_time(evs[j][b]) for j in range(n)) / n
               for p, (a, b) in zip(phases, bounds)}
-        crit = sorted(evs[j][9].elapsed_time(evs[j][4]) for j in range(n))
+        crit = sorted(evs[j][9].elapsed_time(evs[j][3]) for j in range(n))
         return 1e3 * wall, ph, crit
 
     # warmup; after one step that loads every kernel, the first half also times
@@ -774,7 +960,7 @@ def main():
     step(0, serial=True)
     torch.cuda.synchronize()
     n_prof = max(1, args.warmup // 2)
-    cgs.profile_start("", 800 * n_prof + 64)
+    cgs.profile_start("", 1200 * n_prof + 64)
     for i in range(1, n_prof + 1):
         step(i, serial=True)
     cgs.profile_stop()
@@ -782,15 +968,17 @@ def main():
     sites = {}
     for s in ("ctx.score", "ctx.topk", "ctx.glu", "ctx.down", "ctx.finish", "rebuild.norm",
               "rebuild.glu", "rebuild.down", "rebuild.finish", "act.glu.dense", "act.down.dense",
-              "act.glu.masked", "act.down.masked", "act.finish", "act.gather", "mask.contrib",
-              "mask.select", "ret.dot", "ret.select", "glue.rmsnorm"):
+              "act.glu.masked", "act.down.masked", "act.finish", "act.gather", "mask.indices",
+              "ret.dot", "ret.select", "glue.rmsnorm"):
         t, n = cgs.profile_result(s)
         if n:
             sites[s] = {"launches_per_step": n / n_prof, "mean_us": round(1e3 * t / n, 2),
                         "ms_per_step": round(t / n_prof, 4)}
     # The dominant kernel is timed per launch in the timed region, which needs
-    # its launches to be eager: with HIP graphs only the rebuild's are.
-    eager = (lambda s: True) if args.no_graphs else (lambda s: s.startswith("rebuild."))
+    # its launches to be eager: with HIP graphs the context prefill and the
+    # anchor step are replayed.
+    eager = (lambda s: True) if args.no_graphs else \
+        (lambda s: s.startswith("rebuild.") or s.endswith(".masked") or s in ("act.finish", "act.gather"))
     dom_all = max((s for s in sites if site_work(s, w.k, w.K)), key=lambda s: sites[s]["ms_per_step"])
     dom = max((s for s in sites if site_work(s, w.k, w.K) and eager(s)), key=lambda s: sites[s]["ms_per_step"])
     if dom != dom_all:
@@ -816,7 +1004,8 @@ def main():
         torch.cuda.synchronize()
 
     # timed region: K steps, the dominant kernel bracketed by HIP events
-    cgs.profile_start(dom, args.steps * 64 + 64)
+    first_bytes = len(call_bytes)
+    cgs.profile_start(dom, args.steps * 128 + 64)
     ms_per_step, ph, crit = timed(i, args.steps)
     cgs.profile_stop()
     dom_ms, dom_n = cgs.profile_result(dom)
@@ -837,62 +1026,67 @@ def main():
                 "traffic_source": traffic_src,
                 "traffic_over_algorithmic": round(traffic / byts, 3) if traffic else None}
 
-    # Action Cache masked step: algorithmic bytes over its measured time (FFN + glue)
-    Km = w.K
-    masked_bytes = sum(masked_layer_bytes(K) for K in Km)
+    # Action Cache update steps inside the call: algorithmic bytes of the
+    # chosen entries' masks over the measured time (FFN + glue)
+    masked_bytes = sum(call_bytes[first_bytes:]) / max(1, len(call_bytes) - first_bytes)
     masked_step_ms = ph["act_masked"] / (STEPS - 1)
-    k_ffn_ms = (sites.get("act.glu.masked", {}).get("ms_per_step", 0)
-                + sites.get("act.down.masked", {}).get("ms_per_step", 0)
-                + sites.get("act.finish", {}).get("ms_per_step", 0) * (STEPS - 1) / STEPS) / (STEPS - 1)
+    step_bytes = masked_bytes / (STEPS - 1)
+    # context prefill against the per-layer algorithmic work: the weights once,
+    # the gathered rows, the cached outputs read and the outputs written
     ctx_flops = L_VLM * (2.0 * w.k * D * 2 * FF + 2.0 * w.k * FF * D)
-    ctx_bytes = L_VLM * (3 * FF * D * 2 + 2 * w.k * D * 2 + w.k * FF * 4 + 2 * P * D * 2)
+    ctx_bytes = L_VLM * (3 * FF * D * 2 + w.k * D * 2 + 2 * P * D * 2)
     ctx_roof_ms = 1e3 * max(ctx_flops / (PEAK_BF16_TFLOPS * 1e12), ctx_bytes / (PEAK_HBM_GBPS * 1e9))
+    entered_per_call = sum(w.entered[-args.steps:]) / args.steps
+    workload = ("policy-call slice: retrieval over the 20 prepared entries (cosine of 768x1152 ViT features, "
+                "top-4, joint-history rerank, fallback) + 17-layer Context Cache prefill (768 tokens, d 2048, "
+                "ff 16384, rho_p 0.3) against the chosen entry + its 4-step Action Cache denoise (18 layers, "
+                "d 1024, ff 4096, 50 tokens; the entry's stored masks, coverage 0.844, one group: anchor step 0, "
+                "steps 1-3 updated) + the preparation of the entries entering the window (host-to-device "
+                "transfer of the compact entry and its 18x4 bit-packed masks, 17-layer dense rebuild, mask "
+                "index lists, compact weight rows of its update mask). Working set: the pages' 2-D window, "
+                f"{T_WIN} candidate episodes x (matched position + {L_WIN} next) = {SLOTS} slots over an "
+                f"{STORE}-entry pinned host repository ({EPISODES} episodes x {EP_LEN} positions), so "
+                f"{T_WIN} entries enter per call. Deviations from the workload as specified: {SLOTS} slots "
+                "(it names 16), entries prepared " +
+                ("in line on the main stream after the call (it names a side stream)"
+                 if args.rebuild_stream == "main" else f"on a side stream ({args.rebuild_stream})") +
+                ", group masks built offline per entry (not timed in the call)")
     out = {
         "metric": METRIC, "value": round(ms_per_step, 4), "unit": "ms", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": ("policy-call slice: retrieval over the 16 prepared entries (cosine of "
-                                "768x1152 ViT features, top-4, joint-history rerank, fallback) + "
-                                "17-layer Context Cache prefill (768 tokens, d 2048, "
-                                "ff 16384, rho_p 0.3) + 4-step Action Cache denoise (18 layers, d 1024, "
-                                "ff 4096, 50 tokens, coverage 0.844, anchor step 0) + group mask build "
-                                "+ one 17-layer dense entry rebuild (host-to-device transfer of the compact "
-                                "entry included) for a 16-slot sliding window over an 800-entry pinned host "
-                                "repository; the masks' weight rows gathered into compact buffers on a side "
-                                "stream beside the " + args.gather_during + " step"),
+        "config": {"workload": workload,
                    "tokens": P, "rho_p": RHO_P, "k": w.k, "coverage": COVERAGE,
-                   "hip_graphs": not args.no_graphs, "compact_weights": not args.no_compact,
-                   "rebuild_stream": args.rebuild_stream, "gather_during": args.gather_during,
-                   "masked_neurons_mean": round(sum(Km) / len(Km), 1)},
+                   "hip_graphs": not args.no_graphs, "rebuild_stream": args.rebuild_stream,
+                   "window": {"episodes": T_WIN, "lookahead": L_WIN, "slots": SLOTS},
+                   "masked_neurons_mean": round(sum(w.K) / len(w.K), 1)},
         "roofline": roofline,
         "breakdown_ms": {p: round(v, 4) for p, v in ph.items()},
         "ctx_prefill": {"ms": round(ph["ctx_prefill"], 4), "tflops": round(ctx_flops / ph["ctx_prefill"] / 1e9, 1),
-                        "roofline_ms": round(ctx_roof_ms, 4),
+                        "bytes": ctx_bytes, "roofline_ms": round(ctx_roof_ms, 4),
                         "frac_of_roofline": round(ctx_roof_ms / ph["ctx_prefill"], 4),
-                        "mfma_frac": round(ctx_flops / ph["ctx_prefill"] / 1e9 / PEAK_BF16_TFLOPS, 4)},
-        "act_masked_step": {"ms": round(masked_step_ms, 4), "bytes": masked_bytes,
-                            "GBps": round(masked_bytes / masked_step_ms / 1e6, 1),
-                            "hbm_frac": round(masked_bytes / masked_step_ms / 1e6 / PEAK_HBM_GBPS, 4),
-                            "ffn_kernels_ms": round(k_ffn_ms, 4),
-                            "note": "18 masked layers incl. residual/RMSNorm glue, inside the call: "
-                                    + ("the compact weights were gathered beside the anchor step, so the "
-                                       "masked steps find them in the MALL"
-                                       if args.gather_during == "anchor" else
-                                       "the first masked step finds its compact weights evicted by the "
-                                       "prefill's weight stream, the next two MALL-warm")
-                                    + " (act_sweep has cold and warm apart)"},
-        "rebuild_ms_per_entry": round(ph["rebuild"] / max(1e-9, sum(w.entered[-args.steps:]) / args.steps), 4),
-        "working_set": {"repository_entries": STORE, "repository_bytes": STORE * P * D * 2,
-                        "slots": SLOTS, "window": {"episodes": 1, "lookahead": LOOKAHEAD},
-                        "entered_per_call": round(sum(w.entered[-args.steps:]) / args.steps, 3),
+                        "mfma_frac": round(ctx_flops / ph["ctx_prefill"] / 1e9 / PEAK_BF16_TFLOPS, 4),
+                        "note": "bytes per layer: weights + gathered x rows + cached outputs read + outputs "
+                                "written (no intermediate h)"},
+        "act_masked_step": {"ms": round(masked_step_ms, 4), "bytes": round(step_bytes),
+                            "GBps": round(step_bytes / masked_step_ms / 1e6, 1),
+                            "hbm_frac": round(step_bytes / masked_step_ms / 1e6 / PEAK_HBM_GBPS, 4),
+                            "note": "one update step of 18 masked layers incl. residual/RMSNorm glue, inside the "
+                                    "call, one eager act_masked_layers call for steps 1-3; the chosen entry's "
+                                    "compact weights were gathered when it entered the window, calls earlier, "
+                                    "so they stream from HBM (cold); act_sweep has warm and cold apart"},
+        "rebuild_ms_per_entry": round(ph["rebuild"] / max(1e-9, entered_per_call), 4),
+        "working_set": {"repository_entries": STORE, "repository_bytes": STORE * (P * D * 2 + L_EXP * STEPS * FFE // 8),
+                        "slots": SLOTS, "window": {"episodes": T_WIN, "lookahead": L_WIN},
+                        "entered_per_call": round(entered_per_call, 3),
                         "eq5": {"m_free": w.budget[0], "m_entry": w.budget[1], "t_avl_ms": T_AVL_MS,
                                 "t_trans_ms": round(w.t_trans_ms, 4), "t_rec_ms": round(w.t_rec_ms, 4),
                                 "n_prep_bound": cgs.prep_budget(10 ** 6, *w.budget)}},
         "critical_path_ms": {"median": round(crit[len(crit) // 2], 4),
                              "p95": round(crit[min(len(crit) - 1, int(math.ceil(0.95 * len(crit))) - 1)], 4),
-                             "what": "retrieval + context prefill + anchor + 3 masked steps + mask build "
-                                     "of one call (retrieval includes its host read-back)"},
+                             "what": "retrieval + context prefill + anchor + 3 update steps of one call "
+                                     "(retrieval includes its host read-back)"},
         "retrieval": {"ms": round(ph["retrieval"], 4), "top_t": TOP_T, "features": FEAT,
                       "history": [HIST_L, JOINTS], "calls": w.calls,
                       "chose_matched_entry": round(w.matches / max(1, w.calls), 4), "fallbacks": w.fallbacks},
@@ -903,12 +1097,14 @@ def main():
     if not args.no_joint:
         out["joint_denoise"] = joint_denoise(w)
     if not args.no_sweeps:
-        log("ratio sweeps ...")
+        log("sweeps ...")
         out["ctx_sweep"] = ctx_sweep(w)
         out["act_sweep"] = act_sweep(w)
+        out["act_schedules"] = act_schedules(w)
+        out["mask_build"] = mask_build_timing(w)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
-        out["cpu_baseline"] = cpu_baseline(int(round(sum(Km) / len(Km))))
+        out["cpu_baseline"] = cpu_baseline(int(round(sum(w.K) / len(w.K))), entered_per_call)
     line = json.dumps(out)
     print(line, flush=True)
     if args.out:

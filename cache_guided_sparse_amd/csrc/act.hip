@@ -441,14 +441,15 @@ int act_t(const cgs_ffn& w, const T* x, int S, const int32_t* idx, int K, const 
 }
 
 // act_ffn_masked_compact once its arguments are checked.
+// dense: profiling site names only (a layer without anchor state in a chain).
 int act_compact(const cgs_ffn& wc, const void* x, int S, const int32_t* idx, int K, const float* ya,
                 const float* ha, void* y_out, float* y_f32, float* h_out, const cgs_glue* gl, void* ws,
-                hipStream_t s) {
+                hipStream_t s, bool dense = false) {
   if (wc.dtype == CGS_BF16)
     return act_t<uint16_t, true>(wc, static_cast<const uint16_t*>(x), S, idx, K, ya, ha,
-                                 static_cast<uint16_t*>(y_out), y_f32, h_out, gl, ws, s, false);
+                                 static_cast<uint16_t*>(y_out), y_f32, h_out, gl, ws, s, dense);
   return act_t<float, true>(wc, static_cast<const float*>(x), S, idx, K, ya, ha, static_cast<float*>(y_out),
-                            y_f32, h_out, gl, ws, s, false);
+                            y_f32, h_out, gl, ws, s, dense);
 }
 
 }  // namespace
@@ -567,7 +568,8 @@ extern "C" int act_masked_layers(const cgs_masked_layer* layers, int n, int S, f
     g.bias = L.bias;
     g.x_next = xs + (i + 1) * row_bytes;
     const int st = act_compact(L.w, xs + i * row_bytes, S, L.idx, L.w.ff, L.y_anchor, L.h_anchor,
-                               L.y_out ? L.y_out : y_scratch, L.y_f32_out, L.h_out, &g, ws, s);
+                               L.y_out ? L.y_out : y_scratch, L.y_f32_out, L.h_out, &g, ws, s,
+                               !L.y_anchor && !L.h_anchor);
     if (st != CGS_OK) return st;
   }
   return CGS_OK;
