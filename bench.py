@@ -55,6 +55,7 @@ EPISODES, EP_LEN = 4, 200                  # the repository: 4 reference episode
 STORE = EPISODES * EP_LEN                  # 800 entries
 T_WIN, L_WIN = 4, 4                        # window: T candidate episodes x (matched position + L next)
 SLOTS = T_WIN * (L_WIN + 1)                # 20 device slots
+NSTAGE = 4                                 # staging buffers of entering entries
 T_AVL_MS = 500.0                           # a 15-action chunk at 30 Hz (the paper's example)
 FEAT = 768 * 1152                          # ViT layer-15 features of three views, flattened
 HIST_L, JOINTS, TOP_T = 4, 14, 4           # state history, joints (two arms), visual top-T
@@ -150,7 +151,15 @@ class World:
                     sig = torch.full((P, 1), 0.1752, device=dev)
                     sig[torch.randperm(P, device=dev, generator=g)[: math.ceil(RHO_P * P - 1e-9)]] = 1.3333
                     self.current[q] = comp[j] + randn(P, D) * sig
-        self.staging = torch.empty((P, D), dtype=bf, device=dev)
+        # host-to-device transfers of entering entries run on a copy stream
+        # through a ring of staging buffers (an entry's rebuild reads its
+        # compact input from one)
+        self.staging = torch.empty((NSTAGE, P, D), dtype=bf, device=dev)
+        self.copy_s = torch.cuda.Stream(device=dev)
+        self.stage_free = [torch.cuda.Event() for _ in range(NSTAGE)]
+        self.stage_next = 0
+        self.feat_ready = torch.cuda.Event()
+        self.slot_ready = [torch.cuda.Event() for _ in range(SLOTS)]   # a slot's last preparation done
         # retrieval data of every entry: ViT features that drift slowly along
         # each episode (consecutive positions cos ~0.98), the robot-state
         # history [HIST_L][JOINTS] of a smooth joint trajectory per episode; a
@@ -258,16 +267,13 @@ class World:
         # initial-position preload, timed to estimate T_rec and T_trans of Eq. 5
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        entered, _, _ = self.window.advance(list(range(T_WIN)), [0] * T_WIN, [EP_LEN] * T_WIN, 0)
-        for e, q, slot in entered:
-            self.slot_feat[slot].copy_(self.feat_store[e * EP_LEN + q], non_blocking=True)
-            self.slot_hist[slot].copy_(self.hist_store[e * EP_LEN + q], non_blocking=True)
-            self.rebuild_entry(e, q, slot)
+        entered, _, _ = self.window.advance(list(range(T_WIN)), [0] * T_WIN, [EP_LEN] * T_WIN, L_WIN)
+        self.prepare(entered, torch.cuda.current_stream())
         torch.cuda.synchronize()
         self.t_rec_ms = 1e3 * (time.perf_counter() - t1) / len(entered)
         t1 = time.perf_counter()
         for _ in range(8):
-            self.staging.copy_(self.store[0], non_blocking=True)
+            self.staging[0].copy_(self.store[0], non_blocking=True)
         torch.cuda.synchronize()
         self.t_trans_ms = 1e3 * (time.perf_counter() - t1) / 8
         free, _ = torch.cuda.mem_get_info(dev)
@@ -311,27 +317,53 @@ class World:
         advances one position per call."""
         return i % (EP_LEN - L_WIN)
 
-    def advance(self, i):
-        """Slide the window to call i's position; the entering entries'
-        retrieval data are copied to their slots at once (the heavy rebuild is
-        the caller's).  Returns the entries to rebuild [(episode, position, slot)]."""
+    def slide(self, i):
+        """Slide the window to call i's position (host bookkeeping); returns
+        the entries to prepare [(episode, position, slot)]."""
         q = self.position(i)
         entered, _, _ = self.window.advance(list(range(T_WIN)), [q] * T_WIN, [EP_LEN] * T_WIN, L_WIN,
                                             self.budget)
         self.entered.append(len(entered))
-        if self.window.slot(0, q) < 0:
-            raise RuntimeError(f"entry {q} is not resident")
-        for e, p, slot in entered:
-            j = e * EP_LEN + p
-            self.slot_feat[slot].copy_(self.feat_store[j], non_blocking=True)
-            self.slot_hist[slot].copy_(self.hist_store[j], non_blocking=True)
         return entered
+
+    def prepare(self, entered, stream):
+        """Prepare the entering entries: their compact inputs, masks and
+        retrieval data go host-to-device on the copy stream; each entry's
+        rebuild, mask lists and compact rows follow on `stream` once its
+        transfer is done."""
+        import torch
+        jobs = []
+        with torch.cuda.stream(self.copy_s):
+            for e, q, slot in entered:
+                j = e * EP_LEN + q
+                k = self.stage_next
+                self.stage_next = (k + 1) % NSTAGE
+                self.copy_s.wait_event(self.stage_free[k])
+                self.copy_s.wait_event(self.slot_ready[slot])   # its mask words were last read there
+                self.staging[k].copy_(self.store[j], non_blocking=True)
+                self.slot_words[slot].copy_(self.mask_store[j], non_blocking=True)
+                self.slot_feat[slot].copy_(self.feat_store[j], non_blocking=True)
+                self.slot_hist[slot].copy_(self.hist_store[j], non_blocking=True)
+                done = torch.cuda.Event()
+                done.record(self.copy_s)
+                jobs.append((e, q, slot, k, done))
+            self.feat_ready.record(self.copy_s)
+        with torch.cuda.stream(stream):
+            for e, q, slot, k, done in jobs:
+                stream.wait_event(done)
+                self.rebuild_entry(e, q, slot, k)
+                self.stage_free[k].record(stream)
+                self.slot_ready[slot].record(stream)
 
     def retrieve(self, i):
         """Visual top-T over the prepared slots, joint-history rerank and the
         fallback test for call i; returns the chosen slot (host sync), or the
         window's slot for the matched position when retrieval falls back."""
+        import torch
         q = self.position(i)
+        if self.window.slot(0, q) < 0:
+            raise RuntimeError(f"entry {q} is not resident")
+        torch.cuda.current_stream().wait_event(self.feat_ready)   # the entries prepared last
         self.cgs.ret_select(self.qfeat[q], self.slot_feat, TOP_T, self.qhist[q], self.slot_hist, arm=-1,
                             min_cos=0.8, choice_out=self.choice)
         c = int(self.choice.item())
@@ -385,17 +417,16 @@ class World:
                                                 y_out=self.ych[i]))
         return cgs.MaskedChain(tail, S, FFE)
 
-    def rebuild_entry(self, e, q, slot):
-        """Move entry (e, q) to the device and prepare it in `slot` (on the
-        current stream): its compact input is expanded by the 17-layer dense
-        rebuild, its stored masks are copied and turned into index lists, the
-        weight rows of each update mask are gathered into the slot's compact
-        buffers, and the host keeps the slot's denoise chain."""
+    def rebuild_entry(self, e, q, slot, k):
+        """Prepare entry (e, q), transferred to staging buffer k and its
+        slot's mask words, in `slot` (on the current stream): its compact input
+        is expanded by the 17-layer dense rebuild, its stored masks are turned
+        into index lists, the weight rows of each update mask are gathered
+        into the slot's compact buffers (one launch per mask), and the host
+        keeps the slot's denoise plan."""
         cgs = self.cgs
         j = e * EP_LEN + q
-        self.staging.copy_(self.store[j], non_blocking=True)
-        self.slot_words[slot].copy_(self.mask_store[j], non_blocking=True)
-        cgs.ref_rebuild_dense(self.vlm, self.staging, self.xbar[slot], self.ybar[slot])
+        cgs.ref_rebuild_dense(self.vlm, self.staging[k], self.xbar[slot], self.ybar[slot])
         cgs.act_mask_indices(self.slot_words[slot], FFE, idx_out=self.slot_idx[slot], count_out=self.slot_cnt[slot])
         counts = self.mask_counts[j]
         kind, anchor, mask = cgs.denoise_schedule(counts, self.mask_np[j], FFE)
@@ -409,12 +440,10 @@ class World:
             if self.slot_cw[slot][gi] is None:
                 self.slot_cw[slot][gi] = [torch_empty((3, self.kmax[l], DE), self.dev) for l in range(L_EXP)]
             bufs = self.slot_cw[slot][gi]
-            cw = []
-            for l in range(L_EXP):
-                K = int(counts[l, t])
-                f = cgs.FFN(bufs[l][0, :K], bufs[l][1, :K], bufs[l][2, :K], "fd")
-                cgs.act_gather_rows(self.exp[l], self.slot_idx[slot, l, t, :K], out=f)
-                cw.append(f)
+            cw = [cgs.FFN(bufs[l][0, :int(counts[l, t])], bufs[l][1, :int(counts[l, t])],
+                          bufs[l][2, :int(counts[l, t])], "fd") for l in range(L_EXP)]
+            cgs.act_gather_rows_layers(self.exp, [self.slot_idx[slot, l, t, :int(counts[l, t])] for l in range(L_EXP)],
+                                       cw)
             compact[t] = cw
         self.slot_plan[slot] = (kind, anchor, mask, counts, compact)
         self.slot_tail[slot] = None
@@ -422,9 +451,6 @@ class World:
                                     for t in range(1, STEPS) if kind[t] == 1 for l in range(L_EXP))
         self.slot_entry[slot] = j
 
-    def rebuild(self, entered):
-        for e, q, slot in entered:
-            self.rebuild_entry(e, q, slot)
 
     def capture(self):
         """HIP graphs of the launch-bound phases with fixed buffers: the 17
@@ -901,8 +927,9 @@ def main():
     def step(i, ev=None, serial=False):
         """One call.  ev: 11 timing events; 9-10 the retrieval, 0-3 the other
         main-stream phases, 5-6 the preparation of the entering entries on the
-        stream that runs it."""
-        entered = w.advance(i)
+        stream that runs it.  After the call the window slides to the next
+        call's position and the entering entries are prepared (the pages
+        rebuild them while the robot executes the action chunk)."""
         rec = (lambda q: ev[q].record()) if ev is not None else (lambda q: None)
         rec(9)
         e = w.retrieve(i)   # the slot the retrieval picks drives the prefill and the denoise
@@ -922,6 +949,7 @@ def main():
         rec(3)
         used[e].record(main_s)
         call_bytes.append(w.slot_bytes[e])
+        entered = w.slide(i + 1)
         if side is not None and not serial:
             with torch.cuda.stream(side):
                 for _, _, s_ in entered:
@@ -929,7 +957,7 @@ def main():
                 if overlap:
                     side.wait_event(ctx_done)   # start once this call's prefill is done
                 rec(5)
-                w.rebuild(entered)
+                w.prepare(entered, side)
                 rec(6)
                 for _, _, s_ in entered:
                     rebuilt[s_].record(side)
@@ -938,7 +966,7 @@ def main():
                     rebuild_done.record(side)
         else:
             rec(5)
-            w.rebuild(entered)
+            w.prepare(entered, main_s)
             rec(6)
 
     def timed(first, n, serial=False):

@@ -96,6 +96,7 @@ _SIGS = {
     "act_ffn_masked_compact": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "act_ffn_masked_compact_noalloc": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "act_gather_rows": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp]),
+    "act_gather_rows_layers": (_i, [_vp, _i, _vp]),
     "act_mask_indices": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "cgs_denoise_schedule": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "cgs_act_masked_layers_workspace": (_sz, [_i, _i, _i]),
@@ -734,6 +735,30 @@ def profile_result(site: str | None = None):
 # --------------------------------------------------------------------------
 # One whole masked denoising step in one persistent launch
 # --------------------------------------------------------------------------
+class _GatherLayer(ctypes.Structure):
+    _fields_ = [("w", _Ffn), ("idx", ctypes.c_void_p), ("K", ctypes.c_int32), ("wg_out", ctypes.c_void_p),
+                ("wu_out", ctypes.c_void_p), ("wd_out", ctypes.c_void_p)]
+
+
+def act_gather_rows_layers(ws, idxs, outs, stream=None):
+    """act_gather_rows for several layers in one launch: ws (full FFNs, 'fd'),
+    idxs (int32 lists), outs (compact FFNs [K][d] to fill), one of each per layer."""
+    n = len(ws)
+    if not (len(idxs) == len(outs) == n) or n == 0:
+        raise CgsError("act_gather_rows_layers: one weight set, index list and output per layer")
+    arr = (_GatherLayer * n)()
+    for i, (w, idx, out) in enumerate(zip(ws, idxs, outs)):
+        if w.layout != "fd" or out.layout != "fd":
+            raise CgsError("act_gather_rows_layers: neuron-major ('fd') weights")
+        _expect_index(idx, f"layer {i} idx")
+        K = int(idx.numel())
+        for t, name in ((out.w_gate, "w_gate"), (out.w_up, "w_up"), (out.w_down, "w_down")):
+            _expect(t, f"layer {i} out.{name}", w.dtype, (K, w.d))
+        arr[i] = _GatherLayer(w.cstruct(), _ptr(idx), K, _ptr(out.w_gate), _ptr(out.w_up), _ptr(out.w_down))
+    _check(lib().act_gather_rows_layers(arr, n, _stream(stream)), "act_gather_rows_layers")
+    return outs
+
+
 class _MaskedLayer(ctypes.Structure):
     _fields_ = [("w", _Ffn), ("idx", ctypes.c_void_p), ("y_anchor", ctypes.c_void_p),
                 ("h_anchor", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("y_out", ctypes.c_void_p),

@@ -354,6 +354,35 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const T* __restri
     *reinterpret_cast<u32x4_t*>(dst + e) = *reinterpret_cast<const u32x4_t*>(src + e);
 }
 
+// act_gather_rows over several layers in one launch: global row r of the
+// launch is row (r - first[l]) of layer l's three matrices, one wavefront
+// per row (matrix-major within a layer, as gather_rows_kernel).
+constexpr int kGatherMaxLayers = 32;  // the table travels as a kernel argument (about 2 KB)
+template <typename T> struct GatherTable {
+  const T* src[kGatherMaxLayers][3];
+  T* dst[kGatherMaxLayers][3];
+  const int32_t* idx[kGatherMaxLayers];
+  int first[kGatherMaxLayers + 1];  // prefix of 3 K per layer
+  int K[kGatherMaxLayers];
+  int n, d;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void gather_layers_kernel(GatherTable<T> tab) {
+  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= tab.first[tab.n]) return;
+  int l = 0;
+  while (l + 1 < tab.n && row >= tab.first[l + 1]) ++l;
+  const int r = row - tab.first[l];
+  const int K = tab.K[l];
+  const int m = r / K, i = r - m * K;
+  const T* src = tab.src[l][m] + static_cast<size_t>(tab.idx[l][i]) * tab.d;
+  T* dst = tab.dst[l][m] + static_cast<size_t>(i) * tab.d;
+  constexpr int V = 16 / static_cast<int>(sizeof(T));
+  for (int e = (threadIdx.x & 63) * V; e < tab.d; e += 64 * V)
+    *reinterpret_cast<u32x4_t*>(dst + e) = *reinterpret_cast<const u32x4_t*>(src + e);
+}
+
 struct ActPlan {
   int K_pad, S_pad, tt, splits, steps_per_split;
   size_t d_elems, part_elems;
@@ -652,6 +681,61 @@ extern "C" int act_ffn_joint(const cgs_ffn* wc, const void* x, int S, const int3
                                  static_cast<uint16_t*>(y_out), y_f32_out, nullptr, glue, ws, s, false, tok, S);
   return act_t<float, true>(*wc, static_cast<const float*>(x), k, idx, K, y_anchor, h_anchor,
                             static_cast<float*>(y_out), y_f32_out, nullptr, glue, ws, s, false, tok, S);
+}
+
+namespace {
+template <typename T>
+int gather_layers_t(const cgs_gather_layer* layers, int n, hipStream_t s) {
+  GatherTable<T> tab{};
+  tab.n = 0;
+  tab.d = layers[0].w.d;
+  int rows = 0;
+  for (int i = 0; i < n; ++i) {
+    const cgs_gather_layer& L = layers[i];
+    if (L.K == 0) continue;
+    const int l = tab.n++;
+    tab.src[l][0] = static_cast<const T*>(L.w.w_gate);
+    tab.src[l][1] = static_cast<const T*>(L.w.w_up);
+    tab.src[l][2] = static_cast<const T*>(L.w.w_down);
+    tab.dst[l][0] = static_cast<T*>(L.wg_out);
+    tab.dst[l][1] = static_cast<T*>(L.wu_out);
+    tab.dst[l][2] = static_cast<T*>(L.wd_out);
+    tab.idx[l] = L.idx;
+    tab.K[l] = L.K;
+    tab.first[l] = rows;
+    rows += 3 * L.K;
+  }
+  tab.first[tab.n] = rows;
+  if (rows == 0) return CGS_OK;
+  ProfScope ps("act.gather", s);
+  const dim3 grid((rows + kThreads / 64 - 1) / (kThreads / 64));
+  hipLaunchKernelGGL((gather_layers_kernel<T>), grid, dim3(kThreads), 0, s, tab);
+  return launch_ok() ? CGS_OK : CGS_ERR_LAUNCH;
+}
+}  // namespace
+
+extern "C" int act_gather_rows_layers(const cgs_gather_layer* layers, int n, void* stream) {
+  if (n < 1 || n > kGatherMaxLayers) return CGS_ERR_SHAPE;
+  if (!layers) return CGS_ERR_ARG;
+  const int d = layers[0].w.d, dt = layers[0].w.dtype;
+  if (!valid_dtype(dt)) return CGS_ERR_ARG;
+  long long rows = 0;
+  for (int i = 0; i < n; ++i) {
+    const cgs_gather_layer& L = layers[i];
+    if (!L.w.w_gate || !L.w.w_up || !L.w.w_down || L.w.dtype != dt || L.w.down_layout != CGS_DOWN_FD)
+      return CGS_ERR_ARG;
+    if (L.w.d != d) return CGS_ERR_SHAPE;
+    if (!act_shape_ok(L.w.d, L.w.ff)) return CGS_ERR_UNSUPPORTED;
+    if (L.K < 0 || L.K > L.w.ff) return CGS_ERR_SHAPE;
+    if (L.K > 0 && (!L.idx || !L.wg_out || !L.wu_out || !L.wd_out)) return CGS_ERR_ARG;
+    rows += 3ll * L.K;
+  }
+  if (rows > INT32_MAX - 64) return CGS_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_on())
+    for (int i = 0; i < n; ++i)
+      if (const int st = validate_index(layers[i].idx, layers[i].K, layers[i].w.ff, s)) return st;
+  return dt == CGS_BF16 ? gather_layers_t<uint16_t>(layers, n, s) : gather_layers_t<float>(layers, n, s);
 }
 
 extern "C" int act_gather_rows(const cgs_ffn* w, const int32_t* idx, int K, void* wg_out, void* wu_out,

@@ -283,6 +283,23 @@ int act_ffn_masked(const cgs_ffn* w, const void* x, int S, const int32_t* idx, i
 int act_gather_rows(const cgs_ffn* w, const int32_t* idx, int K, void* wg_out, void* wu_out,
                     void* wd_out, void* stream);
 
+/* One layer of act_gather_rows_layers. */
+typedef struct {
+  cgs_ffn w;              /* the full FFN, CGS_DOWN_FD */
+  const int32_t* idx;     /* [K] int32 in [0, w.ff) (device) */
+  int32_t K;              /* rows to copy, 0 <= K <= w.ff */
+  void* wg_out;           /* [K][d] each (device, caller-owned, not overlapping the weights) */
+  void* wu_out;
+  void* wd_out;
+} cgs_gather_layer;
+
+/* act_gather_rows for n layers (1 .. 32, equal d and dtype) in one launch:
+ * the compact weights of a whole mask group at once (§4.1, §5), e.g. when a
+ * cache entry's masks enter the working set.  Each layer's results are
+ * exactly act_gather_rows's.  In checked mode every idx is checked first.
+ * No workspace. */
+int act_gather_rows_layers(const cgs_gather_layer* layers, int n, void* stream);
+
 /* §4.1, Eq. 4 on compact weights: as act_ffn_masked for the full FFN and the
  * mask idx, but wc holds only the mask's rows (wc->ff == K; row i is neuron
  * idx[i], as act_gather_rows writes them), so no weight address depends on

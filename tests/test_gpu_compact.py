@@ -153,3 +153,22 @@ def test_joint_no_rows_and_glue():
     r_exp = r0.astype(np.float64) + values(y)
     assert_close(values(r), r_exp, "residual")
     assert_close(values(xn), O.rms_norm(r_exp), "x_next", out="bf16")
+
+
+@pytest.mark.parametrize("dtype,d,ff", [("bf16", 1024, 4096), ("f32", 256, 1024)])
+def test_gather_rows_layers_bit_exact(dtype, d, ff):
+    """All layers of a mask group gathered in one launch: every layer's rows
+    are the weights' rows idx, bit for bit (a layer with an empty mask and one
+    with every neuron included)."""
+    say("gather rows layers", dtype, d, ff)
+    Ks = [ff * 3 // 10, 0, 37, ff, 1]
+    ws = [ffn_weights(43, l, d, ff, dtype=dtype, down_layout="fd") for l in range(len(Ks))]
+    idxs = [_idx(ff, K, 43 + l) for l, K in enumerate(Ks)]
+    W = [ffn_dev(w) for w in ws]
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    outs = [cgs.FFN(*(torch.full((K, d), 7, dtype=dt, device=dev()) for _ in range(3)), layout="fd") for K in Ks]
+    cgs.act_gather_rows_layers(W, [torch.from_numpy(i).to(dev()) for i in idxs], outs)
+    torch.cuda.synchronize()
+    for l, (w, idx, out) in enumerate(zip(ws, idxs, outs)):
+        for name, t in (("w_gate", out.w_gate), ("w_up", out.w_up), ("w_down", out.w_down)):
+            assert np.array_equal(bits(t), np.asarray(w[name])[idx]), (l, name)
