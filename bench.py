@@ -230,6 +230,9 @@ class World:
                                 idx_out=gidx, count_out=gcnt[j], norms=self.exp_norms)
             if j == 0:
                 self.h_ref0 = self.h_ref.clone()   # entry 0's activations, for the sweeps
+            if (j + 1) % 200 == 0:
+                torch.cuda.synchronize()
+                log(f"setup: masks of {j + 1} of {STORE} entries built")
         torch.cuda.synchronize()
         gw = gwords.cpu()
         self.mask_store = torch.empty((STORE, L_EXP, STEPS, nw), dtype=torch.int64, pin_memory=True)
