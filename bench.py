@@ -257,7 +257,7 @@ class World:
         self.slot_cnt = torch.empty(SLOTS, L_EXP, STEPS, dtype=torch.int32, device=dev)
         self.slot_cw = [[None, None] for _ in range(SLOTS)]   # [slot][mask group] -> per-layer buffers
         self.slot_entry = [-1] * SLOTS
-        self.slot_tail = [None] * SLOTS                       # steps 1.. of the slot's denoise
+        self.slot_tail = [None] * SLOTS                       # steps 1.. of the slot's denoise, a chain each
         self.slot_plan = [None] * SLOTS                       # its schedule, counts and compact weights
         self.slot_bytes = [0] * SLOTS                         # algorithmic bytes of those steps
         self.window = cgs.Window(SLOTS)
@@ -392,19 +392,24 @@ class World:
     def act_anchor(self):
         self.g_anchor.replay() if self.g_anchor else self._anchor()
 
-    def act_masked(self, c):
+    def act_masked(self, c, marks=None):
         """Steps 1.. of the denoise with slot c's stored masks: one host call
-        (the slot's chain is assembled on its first use, while the GPU runs
-        the prefill and the anchor step)."""
+        per step (the slot's chains are assembled on their first use, while
+        the GPU runs the prefill and the anchor step); marks[t - 1] is
+        recorded after step t."""
         if self.slot_tail[c] is None:
             self.slot_tail[c] = self._tail_chain(c)
-        self.cgs.act_masked_layers(self.slot_tail[c], self.ra, self.xch[L_EXP:])
+        for t, chain in enumerate(self.slot_tail[c], start=1):
+            self.cgs.act_masked_layers(chain, self.ra, self.xch[t * L_EXP:(t + 1) * L_EXP + 1])
+            if marks is not None and t < STEPS - 1:
+                marks[t - 1]()
 
     def _tail_chain(self, slot):
         cgs = self.cgs
         kind, anchor, mask, counts, compact = self.slot_plan[slot]
-        tail = []
+        chains = []
         for t in range(1, STEPS):
+            tail = []
             a = anchor[t]
             for l in range(L_EXP):
                 i = t * L_EXP + l
@@ -418,7 +423,8 @@ class World:
                     tail.append(cgs.MaskedLayer(compact[m][l], self.slot_idx[slot, l, m, :K],
                                                 y_anchor=self.y_anc[a, l], h_anchor=self.h_anc[a, l], bias=bias,
                                                 y_out=self.ych[i]))
-        return cgs.MaskedChain(tail, S, FFE)
+            chains.append(cgs.MaskedChain(tail, S, FFE))
+        return chains
 
     def rebuild_entry(self, e, q, slot, k):
         """Prepare entry (e, q), transferred to staging buffer k and its
@@ -928,8 +934,9 @@ def main():
     call_bytes = []
 
     def step(i, ev=None, serial=False):
-        """One call.  ev: 11 timing events; 9-10 the retrieval, 0-3 the other
-        main-stream phases, 5-6 the preparation of the entering entries on the
+        """One call.  ev: 13 timing events; 9-10 the retrieval, 0-3 the other
+        main-stream phases (11 and 12 between the update steps), 5-6 the
+        preparation of the entering entries on the
         stream that runs it.  After the call the window slides to the next
         call's position and the entering entries are prepared (the pages
         rebuild them while the robot executes the action chunk)."""
@@ -948,7 +955,7 @@ def main():
         ctx_done.record(main_s)
         w.act_anchor()
         rec(2)
-        w.act_masked(e)
+        w.act_masked(e, [lambda: rec(11), lambda: rec(12)])
         rec(3)
         used[e].record(main_s)
         call_bytes.append(w.slot_bytes[e])
@@ -973,7 +980,7 @@ def main():
             rec(6)
 
     def timed(first, n, serial=False):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(11)] for _ in range(n)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(13)] for _ in range(n)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for j in range(n):
@@ -983,6 +990,8 @@ def main():
         bounds = [(0, 1), (1, 2), (2, 3), (5, 6), (9, 10)]
         ph = {p: sum(evs[j][a].elapsed_time(evs[j][b]) for j in range(n)) / n
               for p, (a, b) in zip(phases, bounds)}
+        ph["update_steps"] = [sum(evs[j][a].elapsed_time(evs[j][b]) for j in range(n)) / n
+                              for a, b in ((2, 11), (11, 12), (12, 3))]
         crit = sorted(evs[j][9].elapsed_time(evs[j][3]) for j in range(n))
         return 1e3 * wall, ph, crit
 
@@ -1026,6 +1035,7 @@ def main():
     serial = None
     if side is not None and args.serial_steps > 0:
         s_ms, s_ph, s_crit = timed(i, args.serial_steps, serial=True)
+        s_ph.pop("update_steps")
         i += args.serial_steps
         serial = {"ms_per_step": round(s_ms, 4), "breakdown_ms": {p: round(v, 4) for p, v in s_ph.items()},
                   "critical_path_ms_median": round(s_crit[len(s_crit) // 2], 4)}
@@ -1038,6 +1048,7 @@ def main():
     first_bytes = len(call_bytes)
     cgs.profile_start(dom, args.steps * 128 + 64)
     ms_per_step, ph, crit = timed(i, args.steps)
+    upd = ph.pop("update_steps")
     cgs.profile_stop()
     dom_ms, dom_n = cgs.profile_result(dom)
 
@@ -1100,13 +1111,15 @@ def main():
                         "mfma_frac": round(ctx_flops / ph["ctx_prefill"] / 1e9 / PEAK_BF16_TFLOPS, 4),
                         "note": "bytes per layer: weights + gathered x rows + cached outputs read + outputs "
                                 "written (no intermediate h)"},
-        "act_masked_step": {"ms": round(masked_step_ms, 4), "bytes": round(step_bytes),
-                            "GBps": round(step_bytes / masked_step_ms / 1e6, 1),
-                            "hbm_frac": round(step_bytes / masked_step_ms / 1e6 / PEAK_HBM_GBPS, 4),
-                            "note": "one update step of 18 masked layers incl. residual/RMSNorm glue, inside the "
-                                    "call, one eager act_masked_layers call for steps 1-3; the chosen entry's "
-                                    "compact weights were gathered when it entered the window, calls earlier, "
-                                    "so they stream from HBM (cold); act_sweep has warm and cold apart"},
+        "act_masked_step": {"ms": round(upd[0], 4), "bytes": round(step_bytes),
+                            "GBps": round(step_bytes / upd[0] / 1e6, 1),
+                            "hbm_frac": round(step_bytes / upd[0] / 1e6 / PEAK_HBM_GBPS, 4),
+                            "steps_ms": [round(v, 4) for v in upd], "mean_ms": round(masked_step_ms, 4),
+                            "note": "the first update step of the call (18 masked layers incl. residual/RMSNorm "
+                                    "glue, one eager act_masked_layers call per step): the chosen entry's compact "
+                                    "rows were gathered when it entered the window, calls earlier, and stream "
+                                    "from HBM (cold); steps_ms has the three steps, the later two finding the rows "
+                                    "in the MALL; act_sweep has graph-replayed warm and cold figures"},
         "rebuild_ms_per_entry": round(ph["rebuild"] / max(1e-9, entered_per_call), 4),
         "working_set": {"repository_entries": STORE, "repository_bytes": STORE * (P * D * 2 + L_EXP * STEPS * FFE // 8),
                         "slots": SLOTS, "window": {"episodes": T_WIN, "lookahead": L_WIN},
