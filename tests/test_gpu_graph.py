@@ -96,3 +96,85 @@ def test_ctx_chain_graph(fused_score):
 
     _replays_match(run, reset, [y, r, x, idx])
     assert np.all(np.diff(idx.cpu().numpy()) > 0)
+
+
+def test_act_masked_layers_graph():
+    """A whole two-group denoise (dense anchor, update, dense anchor, update;
+    3 layers a step) enqueued by one act_masked_layers call inside a graph:
+    every replay reproduces the eager chain bit for bit, anchor state included."""
+    say("graph act_masked_layers")
+    S, d, ff, L = 50, 1024, 4096, 3
+    ws = [ffn_weights(31, l, d, ff, down_layout="fd", down_lognormal_sigma=1.5) for l in range(L)]
+    W = [ffn_dev(w) for w in ws]
+    a0 = to_dev(act_tokens(31, 0, S, d)["x"]).float().contiguous()
+    full = torch.arange(ff, dtype=torch.int32, device=dev())
+    masks = [torch.arange(o, ff, 3, dtype=torch.int32, device=dev()) for o in (0, 1)]
+    cw = [[cgs.act_gather_rows(W[l], m) for l in range(L)] for m in masks]
+    ya = torch.empty(2, L, S, d, dtype=torch.float32, device=dev())
+    ha = torch.empty(2, L, ff, S, dtype=torch.float32, device=dev())
+    ych = torch.empty(4 * L, S, d, dtype=torch.bfloat16, device=dev())
+    bias = torch.linspace(-1, 1, d, device=dev())
+    layers = []
+    for t in range(4):
+        g = t // 2
+        for l in range(L):
+            b = bias if l == L - 1 else None
+            if t % 2 == 0:
+                layers.append(cgs.MaskedLayer(W[l], full, bias=b, y_out=ych[t * L + l], y_f32_out=ya[g, l],
+                                              h_out=ha[g, l]))
+            else:
+                layers.append(cgs.MaskedLayer(cw[g][l], masks[g], y_anchor=ya[g, l], h_anchor=ha[g, l], bias=b,
+                                              y_out=ych[t * L + l]))
+    chain = cgs.MaskedChain(layers, S, ff)
+    r = torch.empty(S, d, dtype=torch.float32, device=dev())
+    x = torch.empty(4 * L + 1, S, d, dtype=torch.bfloat16, device=dev())
+
+    def reset():
+        cgs.residual_rmsnorm(r, r_in=a0, x_out=x[0])
+
+    def run():
+        cgs.act_masked_layers(chain, r, x)
+
+    _replays_match(run, reset, [x, ych, r, ya, ha])
+
+
+def test_act_masked_layers_fp32_and_empty_masks():
+    """fp32 weights and activations through act_masked_layers, with an empty
+    mask (K = 0: y = y_a) among the layers: every layer's bits equal the
+    per-layer act_ffn_masked_compact calls'."""
+    say("act_masked_layers fp32")
+    S, d, ff, L = 16, 256, 1024, 3
+    ws = [ffn_weights(32, l, d, ff, dtype="f32", down_layout="fd") for l in range(L)]
+    W = [ffn_dev(w) for w in ws]
+    a0 = to_dev(act_tokens(32, 0, S, d, dtype="f32")["x"], "f32")
+    full = torch.arange(ff, dtype=torch.int32, device=dev())
+    masks = [torch.arange(0, ff, 4, dtype=torch.int32, device=dev()),
+             torch.empty(0, dtype=torch.int32, device=dev()),
+             torch.arange(5, ff, 7, dtype=torch.int32, device=dev())]
+    cw = [cgs.act_gather_rows(W[l], masks[l]) for l in range(L)]
+    ya = torch.empty(L, S, d, dtype=torch.float32, device=dev())
+    ha = torch.empty(L, ff, S, dtype=torch.float32, device=dev())
+    outs = []
+    for mode in ("chain", "calls"):
+        r = torch.empty(S, d, dtype=torch.float32, device=dev())
+        x = torch.empty(2 * L + 1, S, d, dtype=torch.float32, device=dev())
+        y = torch.empty(2 * L, S, d, dtype=torch.float32, device=dev())
+        cgs.residual_rmsnorm(r, r_in=a0, x_out=x[0])
+        if mode == "chain":
+            layers = [cgs.MaskedLayer(W[l], full, y_out=y[l], y_f32_out=ya[l], h_out=ha[l]) for l in range(L)]
+            layers += [cgs.MaskedLayer(cw[l], masks[l], y_anchor=ya[l], h_anchor=ha[l], y_out=y[L + l])
+                       for l in range(L)]
+            cgs.act_masked_layers(cgs.MaskedChain(layers, S, ff), r, x)
+        else:
+            for l in range(L):
+                cgs.act_ffn_masked_compact(W[l], x[l], full, y_out=y[l], y_f32_out=ya[l], h_out=ha[l],
+                                           glue=(r, None, x[l + 1]))
+            for l in range(L):
+                cgs.act_ffn_masked_compact(cw[l], x[L + l], masks[l], y_anchor=ya[l], h_anchor=ha[l],
+                                           y_out=y[L + l], glue=(r, None, x[L + l + 1]))
+        torch.cuda.synchronize()
+        outs.append((x.clone(), y.clone(), r.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    # the empty mask's layer is the anchor output rounded to the dtype (fp32: itself)
+    assert torch.equal(outs[0][1][L + 1], ya[1])
