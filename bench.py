@@ -23,9 +23,10 @@ hot path once, with all inputs resident in HBM:
     over an 800-entry repository in pinned host memory (4 episodes x 200
     positions; each entry a compact input and 18 x 4 bit-packed masks),
     advances one position per call in every episode (the native window
-    planner, Eq. 5 budget); each entering entry is copied to the device,
-    expanded by the 17-layer dense rebuild, its masks turned into index lists
-    and its update mask's weight rows gathered.
+    planner, Eq. 5 budget); the 4 entering entries are copied to the device
+    and expanded together by one 17-layer dense rebuild over their 4 x 768
+    rows, then each entry's masks are turned into index lists and its update
+    mask's weight rows gathered.
 The group masks themselves are built offline per entry (as on the pages) and
 timed separately.  Prints one JSON line.  Synthetic seeded data of the pages'
 shapes; the weights are random (no trained model is involved).
@@ -91,16 +92,19 @@ def stored_traffic(site: str):
     return None, None
 
 
-def site_work(site: str, k: int, K_masked: list) -> tuple:
-    """Algorithmic (flops, bytes) of one launch of a timing site."""
+def site_work(site: str, k: int, K_masked: list, rebuild_rows: int = P * T_WIN) -> tuple:
+    """Algorithmic (flops, bytes) of one launch of a timing site; a rebuild
+    launch covers rebuild_rows rows (the entries prepared together: one batch of
+    T_WIN entries per call)."""
+    M = rebuild_rows
     if site == "ctx.glu":
         return 2.0 * k * D * 2 * FF, 2 * FF * D * 2 + k * D * 2 + k * FF * 2
     if site == "ctx.down":
         return 2.0 * k * FF * D, D * FF * 2 + k * FF * 2 + k * D * 2
     if site == "rebuild.glu":
-        return 2.0 * P * D * 2 * FF, 2 * FF * D * 2 + P * D * 2 + P * FF * 2
+        return 2.0 * M * D * 2 * FF, 2 * FF * D * 2 + M * D * 2 + M * FF * 2
     if site == "rebuild.down":
-        return 2.0 * P * FF * D, D * FF * 2 + P * FF * 2 + P * D * 2
+        return 2.0 * M * FF * D, D * FF * 2 + M * FF * 2 + M * D * 2
     if site == "act.glu.dense":
         return 2.0 * S * DE * 2 * FFE, 2 * FFE * DE * 2 + S * DE * 2 + FFE * S * 4
     if site == "act.down.dense":
@@ -156,8 +160,7 @@ class World:
         # compact input from one)
         self.staging = torch.empty((NSTAGE, P, D), dtype=bf, device=dev)
         self.copy_s = torch.cuda.Stream(device=dev)
-        self.stage_free = [torch.cuda.Event() for _ in range(NSTAGE)]
-        self.stage_next = 0
+        self.stage_free = torch.cuda.Event()
         self.feat_ready = torch.cuda.Event()
         self.slot_ready = [torch.cuda.Event() for _ in range(SLOTS)]   # a slot's last preparation done
         # retrieval data of every entry: ViT features that drift slowly along
@@ -330,33 +333,35 @@ class World:
         return entered
 
     def prepare(self, entered, stream):
-        """Prepare the entering entries: their compact inputs, masks and
-        retrieval data go host-to-device on the copy stream; each entry's
-        rebuild, mask lists and compact rows follow on `stream` once its
-        transfer is done."""
+        """Prepare the entering entries, up to NSTAGE at a time: their compact
+        inputs, masks and retrieval data go host-to-device on the copy stream;
+        on `stream` the batch is expanded by one dense rebuild over all its
+        rows (ref_rebuild_dense_batch), then each entry's masks become index
+        lists and its update masks' weight rows are gathered."""
         import torch
-        jobs = []
-        with torch.cuda.stream(self.copy_s):
-            for e, q, slot in entered:
-                j = e * EP_LEN + q
-                k = self.stage_next
-                self.stage_next = (k + 1) % NSTAGE
-                self.copy_s.wait_event(self.stage_free[k])
-                self.copy_s.wait_event(self.slot_ready[slot])   # its mask words were last read there
-                self.staging[k].copy_(self.store[j], non_blocking=True)
-                self.slot_words[slot].copy_(self.mask_store[j], non_blocking=True)
-                self.slot_feat[slot].copy_(self.feat_store[j], non_blocking=True)
-                self.slot_hist[slot].copy_(self.hist_store[j], non_blocking=True)
+        for b0 in range(0, len(entered), NSTAGE):
+            batch = entered[b0:b0 + NSTAGE]
+            with torch.cuda.stream(self.copy_s):
+                self.copy_s.wait_event(self.stage_free)       # the previous batch has read the staging rows
+                for k, (e, q, slot) in enumerate(batch):
+                    j = e * EP_LEN + q
+                    self.copy_s.wait_event(self.slot_ready[slot])   # its mask words were last read there
+                    self.staging[k].copy_(self.store[j], non_blocking=True)
+                    self.slot_words[slot].copy_(self.mask_store[j], non_blocking=True)
+                    self.slot_feat[slot].copy_(self.feat_store[j], non_blocking=True)
+                    self.slot_hist[slot].copy_(self.hist_store[j], non_blocking=True)
                 done = torch.cuda.Event()
                 done.record(self.copy_s)
-                jobs.append((e, q, slot, k, done))
-            self.feat_ready.record(self.copy_s)
-        with torch.cuda.stream(stream):
-            for e, q, slot, k, done in jobs:
+                self.feat_ready.record(self.copy_s)
+            with torch.cuda.stream(stream):
                 stream.wait_event(done)
-                self.rebuild_entry(e, q, slot, k)
-                self.stage_free[k].record(stream)
-                self.slot_ready[slot].record(stream)
+                n = len(batch)
+                self.cgs.ref_rebuild_dense_batch(self.vlm, self.staging[:n], [self.xbar[s_] for _, _, s_ in batch],
+                                                 [self.ybar[s_] for _, _, s_ in batch])
+                self.stage_free.record(stream)
+                for e, q, slot in batch:
+                    self.finish_entry(e, q, slot)
+                    self.slot_ready[slot].record(stream)
 
     def retrieve(self, i):
         """Visual top-T over the prepared slots, joint-history rerank and the
@@ -426,16 +431,14 @@ class World:
             chains.append(cgs.MaskedChain(tail, S, FFE))
         return chains
 
-    def rebuild_entry(self, e, q, slot, k):
-        """Prepare entry (e, q), transferred to staging buffer k and its
-        slot's mask words, in `slot` (on the current stream): its compact input
-        is expanded by the 17-layer dense rebuild, its stored masks are turned
-        into index lists, the weight rows of each update mask are gathered
-        into the slot's compact buffers (one launch per mask), and the host
-        keeps the slot's denoise plan."""
+    def finish_entry(self, e, q, slot):
+        """The rest of entry (e, q)'s preparation in `slot` (on the current
+        stream), after its rebuild: its stored masks are turned into index
+        lists, the weight rows of each update mask are gathered into the
+        slot's compact buffers (one launch per mask), and the host keeps the
+        slot's denoise plan."""
         cgs = self.cgs
         j = e * EP_LEN + q
-        cgs.ref_rebuild_dense(self.vlm, self.staging[k], self.xbar[slot], self.ybar[slot])
         cgs.act_mask_indices(self.slot_words[slot], FFE, idx_out=self.slot_idx[slot], count_out=self.slot_cnt[slot])
         counts = self.mask_counts[j]
         kind, anchor, mask = cgs.denoise_schedule(counts, self.mask_np[j], FFE)
@@ -1052,6 +1055,8 @@ def main():
     cgs.profile_stop()
     dom_ms, dom_n = cgs.profile_result(dom)
 
+    if dom.startswith("rebuild.") and any(n_ != T_WIN for n_ in w.entered[-args.steps:]):
+        sys.exit("the rebuild roofline assumes one batch of T_WIN entries per timed call")
     flops, byts = site_work(dom, w.k, w.K)
     if dom_n == 0:
         sys.exit(f"no timed launches of {dom}")
@@ -1084,8 +1089,9 @@ def main():
                 "ff 16384, rho_p 0.3) against the chosen entry + its 4-step Action Cache denoise (18 layers, "
                 "d 1024, ff 4096, 50 tokens; the entry's stored masks, coverage 0.844, one group: anchor step 0, "
                 "steps 1-3 updated) + the preparation of the entries entering the window (host-to-device "
-                "transfer of the compact entry and its 18x4 bit-packed masks, 17-layer dense rebuild, mask "
-                "index lists, compact weight rows of its update mask). Working set: the pages' 2-D window, "
+                "transfer of the compact entries and their 18x4 bit-packed masks, one 17-layer dense rebuild "
+                "over the entering entries' rows together, mask index lists, compact weight rows of each "
+                "entry's update mask). Working set: the pages' 2-D window, "
                 f"{T_WIN} candidate episodes x (matched position + {L_WIN} next) = {SLOTS} slots over an "
                 f"{STORE}-entry pinned host repository ({EPISODES} episodes x {EP_LEN} positions), so "
                 f"{T_WIN} entries enter per call. Deviations from the workload as specified: {SLOTS} slots "

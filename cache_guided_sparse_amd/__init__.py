@@ -97,6 +97,8 @@ _SIGS = {
     "act_ffn_masked_compact_noalloc": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "act_gather_rows": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp]),
     "act_gather_rows_layers": (_i, [_vp, _i, _vp]),
+    "cgs_ref_rebuild_dense_batch_workspace": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "ref_rebuild_dense_batch": (_i, [_vp, _i, _vp, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "act_mask_indices": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "cgs_denoise_schedule": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "cgs_act_masked_layers_workspace": (_sz, [_i, _i, _i]),
@@ -695,6 +697,33 @@ def ref_rebuild_dense(layers, r0, x_ref_out=None, y_ref_out=None, ws=None, strea
                                    _ptr(ws), ws.numel(), _stream(stream)), "ref_rebuild_dense")
     return x_ref_out, y_ref_out
 
+
+
+def ref_rebuild_dense_batch(layers, r0, x_ref_outs, y_ref_outs, ws=None, stream=None):
+    """Dense rebuild of n entries in one prefill over their n P rows: r0
+    [n][P][d]; x_ref_outs / y_ref_outs: n tensors [L][P][d] each (entry e's
+    outputs, as ref_rebuild_dense writes them)."""
+    L = len(layers)
+    arr = (_Ffn * L)(*[w.cstruct() for w in layers])
+    _expect(r0, "r0", layers[0].dtype)
+    if r0.dim() != 3 or r0.shape[2] != layers[0].d:
+        raise CgsError(f"r0 must be [n][P][{layers[0].d}]")
+    n, P, d = r0.shape
+    if len(x_ref_outs) != n or len(y_ref_outs) != n:
+        raise CgsError("one x_ref and one y_ref output per entry")
+    for e in range(n):
+        _expect(x_ref_outs[e], f"x_ref_outs[{e}]", r0.dtype, (L, P, d))
+        _expect(y_ref_outs[e], f"y_ref_outs[{e}]", r0.dtype, (L, P, d))
+    xs = (ctypes.c_void_p * n)(*[_ptr(t) for t in x_ref_outs])
+    ys = (ctypes.c_void_p * n)(*[_ptr(t) for t in y_ref_outs])
+    c0 = arr[0]
+    nbytes = lib().cgs_ref_rebuild_dense_batch_workspace(L, n, P, d, c0.ff, c0.dtype)
+    if nbytes == 0:
+        raise CgsError("ref_rebuild_dense_batch: unsupported shape")
+    ws = workspace(nbytes, r0.device, "rebuild", stream) if ws is None else ws
+    _check(lib().ref_rebuild_dense_batch(arr, L, _ptr(r0), n, P, xs, ys, _ptr(ws), ws.numel(), _stream(stream)),
+           "ref_rebuild_dense_batch")
+    return x_ref_outs, y_ref_outs
 
 def residual_rmsnorm(r, y=None, bias=None, x_out=None, r_in=None, stream=None):
     """r = (r_in or r) + y + bias (fp32); x_out = RMSNorm(r) (eps 1e-6, no scale)."""

@@ -424,6 +424,80 @@ int rebuild_t(const cgs_ffn* layers, int L, const T* r0, int P, T* xo, T* yo, vo
   return CGS_OK;
 }
 
+// Several entries rebuilt as one prefill over n P rows: the GEMMs and the
+// row finish run on contiguous work rows, and after each layer one launch
+// copies the layer's rows out to every entry's own x_ref / y_ref.
+constexpr int kBatchMax = 16;
+template <typename T> struct RowDist {
+  T* y[kBatchMax];
+  T* x[kBatchMax];
+};
+
+// Row blockIdx.x of the work buffers (entry row / P, position row % P):
+// y row to y[e] + yoff, x row (when x_off >= 0) to x[e] + x_off.
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void distribute_rows_kernel(const T* __restrict__ yw,
+                                                                      const T* __restrict__ xw, int P, int d,
+                                                                      RowDist<T> dst, long long y_off,
+                                                                      long long x_off) {
+  const int row = blockIdx.x;
+  const int e = row / P, p = row - e * P;
+  const size_t src = static_cast<size_t>(row) * d, pos = static_cast<size_t>(p) * d;
+  constexpr int V = 16 / static_cast<int>(sizeof(T));
+  for (int c = threadIdx.x * V; c < d; c += kRowThreads * V) {
+    if (y_off >= 0)
+      *reinterpret_cast<u32x4_t*>(dst.y[e] + y_off + pos + c) = *reinterpret_cast<const u32x4_t*>(yw + src + c);
+    if (x_off >= 0)
+      *reinterpret_cast<u32x4_t*>(dst.x[e] + x_off + pos + c) = *reinterpret_cast<const u32x4_t*>(xw + src + c);
+  }
+}
+
+template <typename T>
+int rebuild_batch_t(const cgs_ffn* layers, int L, const T* r0, int n, int P, T* const* xo, T* const* yo,
+                    void* ws, hipStream_t s) {
+  const cgs_ffn& w0 = layers[0];
+  const int M = n * P;
+  const int d = w0.d;
+  const FfnPlan p = plan_ffn(M, d, w0.ff, w0.dtype);
+  Carve cv(ws);
+  float* r = cv.take<float>(static_cast<size_t>(M) * d);
+  T* xw = cv.take<T>(static_cast<size_t>(M) * d);
+  T* yw = cv.take<T>(static_cast<size_t>(M) * d);
+  T* H = cv.take<T>(p.h_elems);
+  float* part = cv.take<float>(p.part_elems);
+  const long long lay = static_cast<long long>(P) * d;
+  RowDist<T> dst{};
+  for (int e = 0; e < n; ++e) {
+    dst.y[e] = yo[e];
+    dst.x[e] = xo[e];
+  }
+  {
+    ProfScope ps("rebuild.norm", s);
+    hipLaunchKernelGGL((residual_rmsnorm_kernel<T, T, T>), dim3(M), dim3(kRowThreads), 0, s, r0, r,
+                       static_cast<const T*>(nullptr), static_cast<const float*>(nullptr), d, xw);
+    hipLaunchKernelGGL((distribute_rows_kernel<T>), dim3(M), dim3(kRowThreads), 0, s, yw, xw, P, d, dst, -1ll,
+                       0ll);
+  }
+  if (!launch_ok()) return CGS_ERR_LAUNCH;
+  for (int l = 0; l < L; ++l) {
+    launch_ffn_core<T>(layers[l], xw, nullptr, M, p, H, part, "rebuild.glu", "rebuild.down", s);
+    ProfScope ps("rebuild.finish", s);
+    const bool more = l + 1 < L;
+    const GlueArgs<T> ga{r, nullptr, more ? xw : static_cast<T*>(nullptr), nullptr, nullptr, 0, 0};
+    const size_t split_stride = static_cast<size_t>(M) * d;
+    if (d == 8 * kRowThreads)
+      launch_finish1<T>(dim3(M), s, part, p.splits, split_stride, d, false, static_cast<const int32_t*>(nullptr),
+                        M, static_cast<const T*>(nullptr), yw, ga);
+    else
+      hipLaunchKernelGGL((row_finish_kernel<T>), dim3(M), dim3(kRowThreads), 0, s, part, p.splits, split_stride,
+                         d, false, static_cast<const int32_t*>(nullptr), M, static_cast<const T*>(nullptr), yw, ga);
+    hipLaunchKernelGGL((distribute_rows_kernel<T>), dim3(M), dim3(kRowThreads), 0, s, yw, xw, P, d, dst,
+                       l * lay, more ? (l + 1) * lay : -1ll);
+    if (!launch_ok()) return CGS_ERR_LAUNCH;
+  }
+  return CGS_OK;
+}
+
 }  // namespace
 }  // namespace cgs
 
@@ -500,6 +574,47 @@ extern "C" int ref_rebuild_dense(const cgs_ffn* layers, int L, const void* r0, i
                                static_cast<uint16_t*>(x_ref_out), static_cast<uint16_t*>(y_ref_out), ws, s);
   return rebuild_t<float>(layers, L, static_cast<const float*>(r0), P, static_cast<float*>(x_ref_out),
                           static_cast<float*>(y_ref_out), ws, s);
+}
+
+extern "C" size_t cgs_ref_rebuild_dense_batch_workspace(int L, int n, int P, int d, int ff, int dtype) {
+  (void)L;
+  if (n < 1 || n > kBatchMax || P <= 0 || !valid_dtype(dtype) || !ffn_shape_ok(d, ff, dtype)) return 0;
+  const long long M = static_cast<long long>(n) * P;
+  if (M > INT32_MAX || !ffn_span_ok(M, M, d, ff, dtype)) return 0;
+  const FfnPlan p = plan_ffn(static_cast<int>(M), d, ff, dtype);
+  Carve cv(nullptr);
+  cv.take<float>(static_cast<size_t>(M) * d);
+  cv.take<char>(static_cast<size_t>(M) * d * elem_bytes(dtype));
+  cv.take<char>(static_cast<size_t>(M) * d * elem_bytes(dtype));
+  cv.take<char>(p.h_elems * elem_bytes(dtype));
+  cv.take<float>(p.part_elems);
+  return cv.bytes();
+}
+
+extern "C" int ref_rebuild_dense_batch(const cgs_ffn* layers, int L, const void* r0, int n, int P,
+                                       void* const* x_ref_out, void* const* y_ref_out, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  if (!layers || !r0 || !x_ref_out || !y_ref_out) return CGS_ERR_ARG;
+  if (L <= 0 || P <= 0 || n < 1 || n > kBatchMax) return CGS_ERR_SHAPE;
+  for (int e = 0; e < n; ++e)
+    if (!x_ref_out[e] || !y_ref_out[e]) return CGS_ERR_ARG;
+  for (int l = 0; l < L; ++l) {
+    if (!ffn_ok(&layers[l], CGS_DOWN_DF)) return CGS_ERR_ARG;
+    if (layers[l].d != layers[0].d || layers[l].ff != layers[0].ff || layers[l].dtype != layers[0].dtype)
+      return CGS_ERR_SHAPE;
+  }
+  const cgs_ffn& w0 = layers[0];
+  const size_t need = cgs_ref_rebuild_dense_batch_workspace(L, n, P, w0.d, w0.ff, w0.dtype);
+  if (need == 0) return CGS_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < need) return CGS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w0.dtype == CGS_BF16)
+    return rebuild_batch_t<uint16_t>(layers, L, static_cast<const uint16_t*>(r0), n, P,
+                                     reinterpret_cast<uint16_t* const*>(x_ref_out),
+                                     reinterpret_cast<uint16_t* const*>(y_ref_out), ws, s);
+  return rebuild_batch_t<float>(layers, L, static_cast<const float*>(r0), n, P,
+                                reinterpret_cast<float* const*>(x_ref_out), reinterpret_cast<float* const*>(y_ref_out),
+                                ws, s);
 }
 
 extern "C" int cgs_residual_rmsnorm(float* r, const float* r_in, const void* y, int y_dtype,

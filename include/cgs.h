@@ -457,6 +457,26 @@ size_t cgs_ref_rebuild_dense_workspace(int L, int P, int d, int ff, int dtype);
 int ref_rebuild_dense(const cgs_ffn* layers, int L, const void* r0, int P, void* x_ref_out,
                       void* y_ref_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes for ref_rebuild_dense_batch (0 if unsupported). */
+size_t cgs_ref_rebuild_dense_batch_workspace(int L, int n, int P, int d, int ff, int dtype);
+
+/* ref_rebuild_dense for n entries at once (§4.2: every position entering the
+ * working set is reconstructed; with T candidate episodes T of them enter
+ * together): one dense prefill over n P rows, so each layer's weights are
+ * streamed once for all n entries and the GEMMs run n times the rows.
+ *   r0        : [n][P][d] dtype (device), the entries' compact inputs.
+ *   x_ref_out, y_ref_out : HOST arrays of n device pointers, entry e's
+ *               [L][P][d] outputs as ref_rebuild_dense writes them (16-byte
+ *               aligned, caller-owned, not overlapping each other or r0).
+ * Each entry's results are those of ref_rebuild_dense on that entry alone up to
+ * the fp32 summation order of the down projection's K splits (which depends on
+ * the rows in the launch).  1 <= n <= 16; CGS_ERR_UNSUPPORTED if n*P*d, ff*d or
+ * n*P*ff elements span 2^32 bytes or more.  Errors otherwise as
+ * ref_rebuild_dense. */
+int ref_rebuild_dense_batch(const cgs_ffn* layers, int L, const void* r0, int n, int P,
+                            void* const* x_ref_out, void* const* y_ref_out, void* ws, size_t ws_bytes,
+                            void* stream);
+
 /* ---- Inter-layer glue (standalone) -------------------------------------- */
 
 /* Residual add and RMSNorm between FFN layers (the glue of a layer stack,

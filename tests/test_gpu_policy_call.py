@@ -16,7 +16,8 @@ matched position and the next L = 4 of each, 20 slots.
 
 Per call: the window advances every episode by one position (native planner
 against the plain model); the entering entries are moved to the device (input,
-features, history, masks), expanded by the 17-layer dense rebuild, their masks
+features, history, masks), expanded by the 17-layer dense rebuild (up to four
+entries in one prefill over their rows), their masks
 turned back into index lists on the GPU and their update steps' weight rows
 gathered into compact buffers.  Retrieval among the 20 slots picks the call's
 entry; the 17-layer selective prefill (rho_p 0.3) runs against it, then the
@@ -141,12 +142,19 @@ def calls():
     r_act = torch.empty(S, DE, dtype=torch.float32, device=dev())
     slot_entry, slot_chain, slot_sched = [None] * SLOTS, [None] * SLOTS, [None] * SLOTS
 
+    def admit_batch(batch):
+        """The entering entries, up to 4 at a time: one dense rebuild over all
+        their rows, then each entry's own preparation."""
+        r0 = torch.stack([to_dev(store.entry(e, q)[0]["x"]) for e, q, _ in batch]).contiguous()
+        cgs.ref_rebuild_dense_batch(W, r0, [xbar[s_] for _, _, s_ in batch], [ybar[s_] for _, _, s_ in batch])
+        for e, q, slot in batch:
+            admit(e, q, slot)
+
     def admit(e, q, slot):
         entry, (words, counts) = store.entry(e, q)
         slot_feat[slot] = to_dev(store.feats[e, q])
         slot_hist[slot] = to_dev(store.hist[e, q], "f32")
         slot_words[slot] = torch.from_numpy(words.view(np.int64)).to(dev())
-        cgs.ref_rebuild_dense(W, to_dev(entry["x"]), x_ref_out=xbar[slot], y_ref_out=ybar[slot])
         cgs.act_mask_indices(slot_words[slot], FFE, idx_out=slot_idx[slot], count_out=slot_cnt[slot])
         kind, anchor, mask = cgs.denoise_schedule(counts, words, FFE)
         compact = {}
@@ -184,8 +192,8 @@ def calls():
         rec = {"q": q}
         entered, left, ncand = window.advance(eps, [q] * EPISODES, lens, LOOKAHEAD)
         rec["window"] = ((entered, left, ncand), model.advance(eps, [q] * EPISODES, lens, LOOKAHEAD))
-        for e, pos, slot in entered:
-            admit(e, pos, slot)
+        for b0 in range(0, len(entered), 4):
+            admit_batch(entered[b0:b0 + 4])
         cos, top, dist, choice = cgs.ret_select(to_dev(store.queries[q]), slot_feat, TOP_T,
                                                 to_dev(store.qhist[q], "f32"), slot_hist, arm=-1, min_cos=0.8)
         torch.cuda.synchronize()

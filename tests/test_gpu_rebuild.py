@@ -63,3 +63,38 @@ def test_residual_rmsnorm_glue():
     r_o = r.astype(np.float64) + O.decode(yb, "bf16") + bias
     assert_close(values(rt), r_o, "residual", tol=1e-6)
     assert_close(values(xo), O.rms_norm(r_o), "rmsnorm", out="bf16")
+
+
+@pytest.mark.parametrize("dtype,n,L,P,d,ff", [("bf16", 4, 3, 100, 256, 512), ("f32", 3, 2, 64, 256, 1024),
+                                              ("bf16", 1, 2, 40, 128, 256), ("bf16", 4, 2, 768, 2048, 16384)])
+def test_batched_rebuild_teacher_forced(dtype, n, L, P, d, ff):
+    """n entries rebuilt as one prefill over n P rows (ref_rebuild_dense_batch):
+    every entry's outputs land in its own buffers and pass the teacher-forced
+    check on their own; the gate/up rows equal the single-entry rebuild's
+    within the bound (the down projection's split order differs with the row
+    count), and the buffers around each entry's outputs are untouched."""
+    say("batched rebuild", dtype, n, L, P, d, ff)
+    layers = [ffn_weights(33, l, d, ff, dtype=dtype) for l in range(L)]
+    r0s = [random_bf16(33, 1 + e, "r0", (P, d), std=2.0, dtype=dtype) for e in range(n)]
+    W = [ffn_dev(w) for w in layers]
+    r0 = torch.stack([to_dev(r, dtype) for r in r0s]).contiguous()
+    dt = r0.dtype
+    # each entry's outputs inside a larger buffer with guard rows around them
+    big_x = torch.full((n, L + 2, P, d), 3.0, dtype=dt, device=dev())
+    big_y = torch.full((n, L + 2, P, d), 3.0, dtype=dt, device=dev())
+    xs = [big_x[e, 1:L + 1] for e in range(n)]
+    ys = [big_y[e, 1:L + 1] for e in range(n)]
+    cgs.ref_rebuild_dense_batch(W, r0, xs, ys)
+    torch.cuda.synchronize()
+    rows = None if P * d <= 256 * 1024 else np.linspace(0, P - 1, 12).astype(int)
+    for e in range(n):
+        check_rebuild_teacher_forced(layers, r0s[e], xs[e], ys[e], dtype, rows=rows)
+        assert bool((big_x[e, 0] == 3.0).all() and (big_x[e, L + 1] == 3.0).all()), "x guard rows"
+        assert bool((big_y[e, 0] == 3.0).all() and (big_y[e, L + 1] == 3.0).all()), "y guard rows"
+    if n > 1 and P * d <= 256 * 1024:
+        x1, y1 = cgs.ref_rebuild_dense(W, r0[1])
+        torch.cuda.synchronize()
+        assert torch.equal(x1[0], xs[1][0]), "x_ref of layer 0 is one RMSNorm of the same input"
+        for l in range(L):
+            assert_close(values(ys[1][l]), values(y1[l]).astype(np.float64), f"layer {l}: single-entry rebuild",
+                         out=dtype)
