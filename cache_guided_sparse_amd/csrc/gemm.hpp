@@ -23,6 +23,7 @@
 namespace cgs {
 
 constexpr int kXcds = 8;
+constexpr int kMGroup = 4;  // row tiles per group in the workgroup order
 
 template <typename T> struct GemmArgs {
   const T* A;              // [*][lda]; row r of the tile is a_rows[m0+r] or m0+r
@@ -127,13 +128,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> g) {
 
   // Workgroups are dealt round-robin over the 8 XCDs; renumber them so that
   // consecutive logical tiles (same B tile, neighbouring A tiles) share an XCD
-  // and its L2.
+  // and its L2.  With many row tiles (a batched rebuild) they go in groups of
+  // kMGroup: within an XCD the workgroups running together cover kMGroup row
+  // tiles of several weight tiles, instead of every row tile of a few weight
+  // tiles, so each XCD streams fewer distinct A rows per round.
   const int nb = g.n_tiles * g.m_tiles * g.splits;
   int logical = blockIdx.x;
   if (nb % kXcds == 0) logical = (blockIdx.x % kXcds) * (nb / kXcds) + blockIdx.x / kXcds;
-  const int mtile = logical % g.m_tiles;
-  const int ntile = (logical / g.m_tiles) % g.n_tiles;
   const int split = logical / (g.m_tiles * g.n_tiles);
+  const int lt = logical - split * (g.m_tiles * g.n_tiles);
+  const int gm = (g.m_tiles > kMGroup && g.m_tiles % kMGroup == 0) ? kMGroup : g.m_tiles;
+  const int mtile = (lt / (gm * g.n_tiles)) * gm + lt % gm;
+  const int ntile = (lt / gm) % g.n_tiles;
   const int m0 = mtile * BM;
   const int k_begin = split * g.k_per_split;
   const int k_end = min(g.K, k_begin + g.k_per_split);
