@@ -822,6 +822,48 @@ def mask_build_timing(w, reps: int = 20) -> dict:
             "note": "per entry, offline (the store holds the result); not part of the call"}
 
 
+def vendor_gemm(w, reps: int = 20) -> dict:
+    """Context for the dominant kernel: the vendor GEMM library (torch's
+    F.linear, hipBLASLt) on the batched rebuild's two shapes, against this
+    library's rebuild GEMMs timed in the same way (median of `reps` launches,
+    HIP events, weights of one layer).  The library's gate/up call is the plain
+    GEMM: it writes both projections, [rows][2 ff] bf16, and leaves the GeGLU
+    to another pass; the down call reads the same h and writes bf16."""
+    import torch
+    import torch.nn.functional as F
+    cgs = w.cgs
+    rows = T_WIN * P
+    f = w.vlm[0]
+    x = w.staging[:T_WIN].reshape(rows, D)
+    w_gu = torch.cat([f.w_gate, f.w_up], 0)
+    h = torch.randn(rows, FF, dtype=x.dtype, device=w.dev)
+
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return _median([a.elapsed_time(b) for a, b in ts]) * 1e3
+
+    glu_us = med(lambda: F.linear(x, w_gu))
+    down_us = med(lambda: F.linear(h, f.w_down))
+    del w_gu
+    out = {"rows": rows, "vendor_glu_unfused_us": round(glu_us, 1), "vendor_down_us": round(down_us, 1)}
+    for site, us in (("glu", glu_us), ("down", down_us)):
+        fl, _ = site_work(f"rebuild.{site}", w.k, w.K)
+        out[f"vendor_{site}_tflops"] = round(fl / (us * 1e-6) / 1e12, 1)
+    out["note"] = ("torch F.linear (hipBLASLt) on the rebuild's shapes, for context: its gate/up GEMM "
+                   "writes [rows][2 ff] without the GeGLU epilogue; compare roofline.mean_us and "
+                   "kernel_sites['rebuild.down'] for this library's fused kernels")
+    return out
+
+
 def cpu_baseline(k_masked_mean: int, rebuilds: float, reps: int = 6) -> dict:
     """The oracle, timed on the host cores over a bounded sample of the step:
     one context layer (select + recompute of 231 rows), one dense anchor
@@ -1152,6 +1194,7 @@ def main():
         out["act_sweep"] = act_sweep(w)
         out["act_schedules"] = act_schedules(w)
         out["mask_build"] = mask_build_timing(w)
+        out["vendor_gemm"] = vendor_gemm(w)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(int(round(sum(w.K) / len(w.K))), entered_per_call)

@@ -29,6 +29,8 @@
 //             4 x 128 gate/up tiles and 4 x 8 x 8 down tiles, two and one
 //             rounds of 256 workgroups); else 256 x 128.
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "common.hpp"
 #include "gemm.hpp"
@@ -57,11 +59,47 @@ enum TileId { kTileS = 0, kTileM = 1, kTileL = 2, kTileX = 3, kTileG = 4, kTileW
 // and enough row tiles that the grid fills whole rounds of workgroups.
 constexpr int kWideRows = 2048;
 
+constexpr int kLdsPerCu = 160 * 1024;
+
+// Compute units of the current device, cached per device (0 if the query fails).
+int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  if (static_cast<int>(cache.size()) <= dev) cache.resize(dev + 1, -1);
+  if (cache[dev] < 0) {
+    int cus = 0;
+    cache[dev] = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? cus : 0;
+  }
+  return cache[dev];
+}
+
+// A tile configuration whose LDS rings leave room for one workgroup per CU
+// runs persistently when the launch has more tiles than CUs: one workgroup per
+// CU (a multiple of 8, so that each keeps its tiles on its XCD) takes every
+// gridDim-th tile, and its rings run on from one tile into the next.  The
+// kernel needs the same K range length for every tile, at least as many K
+// tiles as ring stages, and no ragged row tile; gathered rows keep one tile
+// per workgroup.
 template <typename Cfg, typename T, bool GLU, bool GATHER>
 void launch_cfg(const GemmArgs<T>& g, const char* site, hipStream_t s) {
   ProfScope ps(site, s);
+  const int nb = g.n_tiles * g.m_tiles * g.splits;
+  if constexpr (!GATHER && 2 * Cfg::kLds > kLdsPerCu) {
+    constexpr int bk = 128 / static_cast<int>(sizeof(T));
+    const int cus = device_cus() / kXcds * kXcds;
+    if (cus > 0 && nb > cus && g.M % Cfg::kBM == 0 && g.K % g.k_per_split == 0 &&
+        g.k_per_split % bk == 0 && g.k_per_split / bk >= std::max(Cfg::kSA, Cfg::kSB)) {
+      hipLaunchKernelGGL(
+          (gemm_kernel_persist<T, Cfg::kBM, Cfg::kWM, Cfg::kWN, Cfg::kNT, Cfg::kSA, Cfg::kSB, GLU>),
+          dim3(cus), dim3(Cfg::kThreads), 0, s, g);
+      return;
+    }
+  }
   hipLaunchKernelGGL((gemm_kernel<T, Cfg::kBM, Cfg::kWM, Cfg::kWN, Cfg::kNT, Cfg::kSA, Cfg::kSB, GLU, GATHER>),
-                     dim3(g.n_tiles * g.m_tiles * g.splits), dim3(Cfg::kThreads), 0, s, g);
+                     dim3(nb), dim3(Cfg::kThreads), 0, s, g);
 }
 
 template <typename T, bool GLU, bool GATHER>

@@ -11,7 +11,11 @@
 // Data movement (gfx950): K tiles of 128 bytes per row travel global -> LDS
 // by LDS DMA (global_load_lds_dwordx4, 1 KB per wavefront instruction) into
 // two rings (A tiles SA deep, B tiles SB deep; half of the waves load each
-// operand), one workgroup barrier per K tile.  A tile row is 8 chunks
+// operand), one workgroup barrier per K tile.  gemm_kernel_persist runs the
+// same tiles with fewer workgroups than tiles: each workgroup takes the tiles
+// blockIdx.x, blockIdx.x + gridDim.x, ... and its rings run on across them,
+// so the first K tiles of the next tile are in flight while the current one
+// finishes and stores its epilogue.  A tile row is 8 chunks
 // of 16 bytes; chunk c of row r sits at physical chunk c ^ (r & 7), so the
 // 16-byte MFMA fragment reads of 8 consecutive rows fall in 8 distinct bank
 // groups.  The waves form a WM x WN grid; each owns (BM/WM) x 16 NT of the tile.
@@ -93,6 +97,79 @@ struct GemmCfg {
   static constexpr int kBM = BM, kWM = WM, kWN = WN, kNT = NT, kSA = SA, kSB = SB;
 };
 
+// Output tile of logical workgroup v.  Workgroups are dealt round-robin over
+// the 8 XCDs; renumber them so that consecutive logical tiles (same B tile,
+// neighbouring A tiles) share an XCD and its L2.  With many row tiles (a
+// batched rebuild) they go in groups of kMGroup: within an XCD the workgroups
+// running together cover kMGroup row tiles of several weight tiles, instead of
+// every row tile of a few weight tiles, so each XCD streams fewer distinct A
+// rows per round.
+struct GemmTile {
+  int m0, ntile, split;
+};
+template <typename T>
+__device__ __forceinline__ GemmTile gemm_tile(const GemmArgs<T>& g, int bm, int v) {
+  const int nb = g.n_tiles * g.m_tiles * g.splits;
+  int logical = v;
+  if (nb % kXcds == 0) logical = (v % kXcds) * (nb / kXcds) + v / kXcds;
+  const int split = logical / (g.m_tiles * g.n_tiles);
+  const int lt = logical - split * (g.m_tiles * g.n_tiles);
+  const int gm = (g.m_tiles > kMGroup && g.m_tiles % kMGroup == 0) ? kMGroup : g.m_tiles;
+  const int mtile = (lt / (gm * g.n_tiles)) * gm + lt % gm;
+  return GemmTile{mtile * bm, (lt / gm) % g.n_tiles, split};
+}
+
+// Epilogue of one tile: lane holds rows 4 (lane >> 4) + v of column lane & 15
+// of each 16 x 16 accumulator tile.  bf16 h goes out in rows of 4 columns (8
+// bytes per lane) after a quad transpose; fp32 h and the partial sums element
+// by element.  Rows at or past M are dropped (CHECK; a launch of full row
+// tiles has none).
+template <typename T, int MT, int NT, int WTM, int BN, bool GLU, bool CHECK>
+__device__ __forceinline__ void gemm_store(const GemmArgs<T>& g, const f32x4_t (&acc)[MT][NT], const GemmTile& t,
+                                           int lane, int wm, int wn) {
+  if constexpr (GLU && sizeof(T) == 2) {
+    const QuadTranspose qt(lane);
+    const int rq = 4 * (lane >> 4) + (lane & 3);
+    const int cq = 4 * ((lane & 15) >> 2);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = t.m0 + wm * WTM + mt * 16 + rq;
+#pragma unroll
+      for (int nt = 0; nt < NT / 2; ++nt) {
+        float h[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) h[v] = gelu_tanh(acc[mt][nt][v]) * acc[mt][nt + NT / 2][v];
+        const uint2 w = qt(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+        const int col = t.ntile * (BN / 2) + wn * 8 * NT + nt * 16 + cq;
+        if (!CHECK || row < g.M) *reinterpret_cast<uint2*>(g.H + static_cast<size_t>(row) * g.ldh + col) = w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = t.m0 + wm * WTM + mt * 16 + 4 * (lane >> 4) + v;
+        if (CHECK && row >= g.M) continue;
+        if (GLU) {
+#pragma unroll
+          for (int nt = 0; nt < NT / 2; ++nt) {
+            const int col = t.ntile * (BN / 2) + wn * 8 * NT + nt * 16 + (lane & 15);
+            const float h = gelu_tanh(acc[mt][nt][v]) * acc[mt][nt + NT / 2][v];
+            g.H[static_cast<size_t>(row) * g.ldh + col] = Elem<T>::from_f32(h);
+          }
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const int col = t.ntile * BN + wn * 16 * NT + nt * 16 + (lane & 15);
+            g.C[t.split * g.split_stride + static_cast<size_t>(row) * g.ldc + col] = acc[mt][nt][v];
+          }
+        }
+      }
+    }
+  }
+}
+
 // Loader roles: waves 0 .. NW/2-1 move A tiles, waves NW/2 .. NW-1 move B
 // tiles.  Each wave's vmcnt then counts transfers of one operand only, so the
 // B (weight) ring can run SB-1 tiles ahead while the A ring runs SA-1 ahead:
@@ -126,21 +203,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> g) {
   const bool role_a = wave < HW;
   const int wr = role_a ? wave : wave - HW;  // index within the role
 
-  // Workgroups are dealt round-robin over the 8 XCDs; renumber them so that
-  // consecutive logical tiles (same B tile, neighbouring A tiles) share an XCD
-  // and its L2.  With many row tiles (a batched rebuild) they go in groups of
-  // kMGroup: within an XCD the workgroups running together cover kMGroup row
-  // tiles of several weight tiles, instead of every row tile of a few weight
-  // tiles, so each XCD streams fewer distinct A rows per round.
-  const int nb = g.n_tiles * g.m_tiles * g.splits;
-  int logical = blockIdx.x;
-  if (nb % kXcds == 0) logical = (blockIdx.x % kXcds) * (nb / kXcds) + blockIdx.x / kXcds;
-  const int split = logical / (g.m_tiles * g.n_tiles);
-  const int lt = logical - split * (g.m_tiles * g.n_tiles);
-  const int gm = (g.m_tiles > kMGroup && g.m_tiles % kMGroup == 0) ? kMGroup : g.m_tiles;
-  const int mtile = (lt / (gm * g.n_tiles)) * gm + lt % gm;
-  const int ntile = (lt / gm) % g.n_tiles;
-  const int m0 = mtile * BM;
+  const GemmTile tile = gemm_tile(g, BM, blockIdx.x);
+  const int m0 = tile.m0, ntile = tile.ntile, split = tile.split;
   const int k_begin = split * g.k_per_split;
   const int k_end = min(g.K, k_begin + g.k_per_split);
   const int nk = (k_end - k_begin) / BK;
@@ -291,30 +355,217 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> g) {
     }
   }
 
-  // Epilogue: lane holds rows 4 (lane >> 4) + v of column lane & 15 of each
-  // 16 x 16 tile.
+  gemm_store<T, MT, NT, WTM, BN, GLU, true>(g, acc, tile, lane, wm, wn);
+}
+
+// Persistent form of gemm_kernel for launches with more tiles than CUs: a
+// grid of one workgroup per CU (a multiple of 8, so that each keeps its
+// tiles on its XCD) takes every gridDim-th tile.  The host launches it only
+// when every tile is full (M % BM == 0), A rows are not gathered, and every
+// tile's K range has the same length of at least SA and SB K tiles.  Same
+// pipeline and epilogue as gemm_kernel; the rings run on across the
+// workgroup's tiles (the current tile's last K steps issue the next tile's
+// first K tiles), and a tile's row and K offsets enter through the scalar
+// base address of its transfers.
+template <typename T, int BM, int WM, int WN, int NT, int SA, int SB, bool GLU>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel_persist(GemmArgs<T> g) {
+  using Cfg = GemmCfg<BM, WM, WN, NT, SA, SB>;
+  static_assert(!GLU || NT % 2 == 0, "GLU pairs gate and up tiles");
+  static_assert(SA >= 2 && SB >= 2 && SA <= 6 && SB <= 6, "ring depth");
+  constexpr int NW = Cfg::kWaves;
+  static_assert(NW % 2 == 0, "two loader roles");
+  constexpr int HW = NW / 2;
+  constexpr int BN = Cfg::kBN;
+  constexpr int BK = 128 / static_cast<int>(sizeof(T));
+  constexpr int KS = BK / 32;
+  constexpr int FC = Frag<T>::kBytes / 16;
+  constexpr int WTM = BM / WM;
+  constexpr int MT = WTM / 16;
+  constexpr int A_DMA = BM / 8, B_DMA = BN / 8;
+  static_assert(A_DMA % HW == 0 && B_DMA % HW == 0, "transfers must split evenly");
+  constexpr int LPW_A = A_DMA / HW, LPW_B = B_DMA / HW;
+  static_assert(!GLU || LPW_B % 2 == 0, "gate and up transfers split evenly");
+  constexpr int A_RING = 0, B_RING = SA * BM * 128;
+  __shared__ __attribute__((aligned(1024))) char lds[Cfg::kLds];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const bool role_a = wave < HW;
+  const int wr = role_a ? wave : wave - HW;
+  const int nb = g.n_tiles * g.m_tiles * g.splits;
+  auto tile_of = [&](int v) { return gemm_tile(g, BM, v); };
+  // byte offset of a tile's operand rows and K range
+  auto a_toff = [&](const GemmTile& t) {
+    return static_cast<size_t>(t.m0) * g.lda * sizeof(T) + static_cast<size_t>(t.split) * g.k_per_split * sizeof(T);
+  };
+  auto b_toff = [&](const GemmTile& t) {
+    return static_cast<size_t>(t.ntile) * (GLU ? BN / 2 : BN) * g.ldb * sizeof(T) +
+           static_cast<size_t>(t.split) * g.k_per_split * sizeof(T);
+  };
+  GemmTile cur = tile_of(blockIdx.x);
+  const int nk = (min(g.K, cur.split * g.k_per_split + g.k_per_split) - cur.split * g.k_per_split) / BK;
+
+  // Transfer i of a loader wave covers tile rows 8 (wr + HW i) .. + 7 (as in
+  // gemm_kernel): the lane's offset in transfer 0 plus i steps of 8 HW rows,
+  // all within the tile.  In GLU mode a B loader's first LPW_B / 2 transfers
+  // read gate rows and the rest the same rows of up.
+  const int sub = lane >> 3;
+  const uint32_t cbyte = static_cast<uint32_t>(((lane & 7) ^ sub) * 16);
+  uint32_t off0 = 0;
+  if (role_a) {
+    // the row clamp of gemm_kernel, although every tile here is full (m - m0 =
+    // 8 wr + sub): the 256 x 256 tile sits at the 256-VGPR limit, and this form
+    // measured to keep its allocation free of scratch spills
+    const int m = min(cur.m0 + 8 * wr + sub, g.M - 1);
+    off0 = static_cast<uint32_t>(m - cur.m0) * static_cast<uint32_t>(g.lda) * sizeof(T) + cbyte;
+  } else {
+    const int r = 8 * wr + sub;
+    off0 = static_cast<uint32_t>(GLU ? r % (BN / 2) : r) * static_cast<uint32_t>(g.ldb) * sizeof(T) + cbyte;
+  }
+  const uint32_t step = static_cast<uint32_t>(8 * HW) * static_cast<uint32_t>(role_a ? g.lda : g.ldb) * sizeof(T);
+  const char* const ptr0 = reinterpret_cast<const char*>(role_a ? g.A : g.B0);
+  const char* const ptr1 = reinterpret_cast<const char*>(role_a ? g.A : (GLU ? g.B1 : g.B0));
+  const uint32_t lds0 = lds_addr(lds);
+
+  // Transfers of this wave's operand for K tile kt of the tile at toff, into
+  // stage q of its ring.
+  auto issue = [&](size_t toff, int kt, int q) {
+    const uint32_t kb = static_cast<uint32_t>(kt) * 128u;
+    const char* const p0 = ptr0 + toff;
+    const char* const p1 = ptr1 + toff;
+    if (role_a) {
+      const uint32_t st = lds0 + A_RING + q * (BM * 128);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+      for (int i = 0; i < LPW_A; ++i) dma_1k(st + (wr + HW * i) * 1024, p0, off0 + kb + i * step);
+    } else {
+      constexpr int kHalf = GLU ? LPW_B / 2 : LPW_B;
+      const uint32_t st = lds0 + B_RING + q * (BN * 128);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = m0 + wm * WTM + mt * 16 + 4 * (lane >> 4) + v;
-      if (row >= g.M) continue;
-      if (GLU) {
+      for (int i = 0; i < LPW_B; ++i)
+        dma_1k(st + (wr + HW * i) * 1024, i < LPW_B / 2 ? p0 : p1, off0 + kb + (i % kHalf) * step);
+    }
+  };
+  auto wait_for = [&](int t, int last_a, int last_b) {
+    if (role_a) wait_tile<LPW_A, SA - 1>(max(0, last_a - t));
+    else wait_tile<LPW_B, SB - 1>(max(0, last_b - t));
+  };
+
+  f32x4_t acc[MT][NT];
+  int brow[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT / 2; ++nt) {
-          const int col = ntile * (BN / 2) + wn * 8 * NT + nt * 16 + (lane & 15);
-          const float h = gelu_tanh(acc[mt][nt][v]) * acc[mt][nt + NT / 2][v];
-          g.H[static_cast<size_t>(row) * g.ldh + col] = Elem<T>::from_f32(h);
-        }
+  for (int nt = 0; nt < NT; ++nt)
+    brow[nt] = GLU ? ((nt < NT / 2) ? wn * 8 * NT + nt * 16 : BN / 2 + wn * 8 * NT + (nt - NT / 2) * 16)
+                   : wn * 16 * NT + nt * 16;
+  const int arow0 = wm * WTM + (lane & 15);
+  const int swz = lane & 7;
+  const int grp = lane >> 4;
+
+  // Ring stages of the K tile being computed: K tile kt + S of a tile (or
+  // the next tile's K tile kt + S - nk) takes the stage of K tile kt.
+  int qa = 0, qb = 0;
+  auto advance = [&]() {
+    qa = qa + 1 == SA ? 0 : qa + 1;
+    qb = qb + 1 == SB ? 0 : qb + 1;
+  };
+  auto load = [&](int ks, Frag<T> (&af)[MT], Frag<T> (&bf)[NT]) {
+    const char* as = lds + A_RING + qa * (BM * 128);
+    const char* bs = lds + B_RING + qb * (BN * 128);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const char* rowp = bs + (brow[nt] + (lane & 15)) * 128;
+#pragma unroll
+      for (int q = 0; q < FC; ++q)
+        bf[nt].chunk(q) = *reinterpret_cast<const u32x4_t*>(rowp + (((ks * 4 + grp) * FC + q) ^ swz) * 16);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const char* rowp = as + (arow0 + mt * 16) * 128;
+#pragma unroll
+      for (int q = 0; q < FC; ++q)
+        af[mt].chunk(q) = *reinterpret_cast<const u32x4_t*>(rowp + (((ks * 4 + grp) * FC + q) ^ swz) * 16);
+    }
+  };
+  auto mfmas = [&](const Frag<T> (&a)[MT], const Frag<T> (&b)[NT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mma(a[mt], b[nt], acc[mt][nt]);
+  };
+
+  const int S_own = role_a ? SA : SB;
+  auto run_tile = [&](int vt) {
+    const int vn = vt + static_cast<int>(gridDim.x);
+    const bool has_next = vn < nb;
+    const GemmTile nxt = has_next ? tile_of(vn) : cur;
+    const size_t toff = role_a ? a_toff(cur) : b_toff(cur);
+    const size_t toff_n = role_a ? a_toff(nxt) : b_toff(nxt);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // K tiles 0 .. S-2 are in flight: issued here for the first tile, by the
+    // previous tile's last K steps otherwise.  Loads and stores share the
+    // vector memory counter and may complete out of order with each other, so
+    // a counted wait proves nothing while the previous tile's epilogue stores
+    // are outstanding: after them the first wait is for every transfer and
+    // store.
+    if (nk > 0) {
+      if (vt == static_cast<int>(blockIdx.x)) {
+        for (int p = 0; p < S_own - 1 && p < nk; ++p) issue(toff, p, p);
+        wait_for(0, min(SA - 2, nk - 1), min(SB - 2, nk - 1));
       } else {
+        wait_vm_barrier<0>();
+      }
+      const int qo = role_a ? qa : qb;  // K tile S - 1 takes the stage before K tile 0's
+      if (S_own - 1 < nk) issue(toff, S_own - 1, qo == 0 ? S_own - 1 : qo - 1);
+    }
+    Frag<T> ca[MT], cb[NT];
+    if (nk > 0) {
+      load(0, ca, cb);
+      for (int kt = 0; kt + 1 < nk; ++kt) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int col = ntile * BN + wn * 16 * NT + nt * 16 + (lane & 15);
-          g.C[split * g.split_stride + static_cast<size_t>(row) * g.ldc + col] = acc[mt][nt][v];
+        for (int ks = 0; ks < KS; ++ks) {
+          Frag<T> na[MT], nb_[NT];
+          if (ks + 1 < KS) {
+            load(ks + 1, na, nb_);
+          } else {
+            const int la = has_next ? kt + SA - 1 : min(kt + SA - 1, nk - 1);
+            const int lb = has_next ? kt + SB - 1 : min(kt + SB - 1, nk - 1);
+            wait_for(kt + 1, la, lb);
+            const int q = role_a ? qa : qb;  // the stage of K tile kt, read by every wave by now
+            if (kt + S_own < nk) issue(toff, kt + S_own, q);
+            else if (has_next) issue(toff_n, kt + S_own - nk, q);
+            advance();
+            load(0, na, nb_);
+          }
+          mfmas(ca, cb);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) ca[mt] = na[mt];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) cb[nt] = nb_[nt];
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        Frag<T> na[MT], nb_[NT];
+        if (ks + 1 < KS) load(ks + 1, na, nb_);
+        mfmas(ca, cb);
+        if (ks + 1 < KS) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) ca[mt] = na[mt];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) cb[nt] = nb_[nt];
         }
       }
     }
-  }
+    gemm_store<T, MT, NT, WTM, BN, GLU, false>(g, acc, cur, lane, wm, wn);
+    advance();
+    cur = nxt;
+  };
+  for (int vt = blockIdx.x; vt < nb; vt += gridDim.x) run_tile(vt);
 }
 
 }  // namespace cgs

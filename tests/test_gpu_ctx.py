@@ -75,10 +75,14 @@ def test_index_list_longer_than_the_staged_search(d):
     assert_close(O.decode(y[sample], "bf16"), y_o, "sampled recomputed rows", out="bf16")
 
 
-def test_dense_equals_rebuild_layer():
-    """k = P is the dense FFN: equal to one rebuild layer's output at the same input."""
-    say("ctx dense vs rebuild")
-    P, d, ff = 96, 256, 512
+@pytest.mark.parametrize("P,d,ff", [(96, 256, 512), (768, 2048, 16384), (3072, 2048, 16384)])
+def test_dense_equals_rebuild_layer(P, d, ff):
+    """k = P is the dense FFN: equal to one rebuild layer's output at the same
+    input, bit for bit.  The gathered rows of the Context Cache path always run
+    one tile per workgroup; at 768 and 3072 rows the rebuild's gate/up
+    projection has more tiles than CUs and runs persistently (2 and 6 tiles per
+    workgroup, 192 x 256 and 256 x 256 tiles), with the same sums."""
+    say("ctx dense vs rebuild", P, d, ff)
     w = ffn_weights(2, 0, d, ff)
     r0 = random_bf16(2, 0, "r0", (P, d))
     W = ffn_dev(w)
