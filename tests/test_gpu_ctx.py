@@ -75,22 +75,33 @@ def test_index_list_longer_than_the_staged_search(d):
     assert_close(O.decode(y[sample], "bf16"), y_o, "sampled recomputed rows", out="bf16")
 
 
-@pytest.mark.parametrize("P,d,ff", [(96, 256, 512), (768, 2048, 16384), (3072, 2048, 16384)])
-def test_dense_equals_rebuild_layer(P, d, ff):
+@pytest.mark.parametrize("P,d,ff,dtype", [(96, 256, 512, "bf16"), (768, 2048, 16384, "bf16"),
+                                          (3072, 2048, 16384, "bf16"), (12288, 2048, 16384, "bf16"),
+                                          (768, 1024, 16384, "f32")])
+def test_dense_equals_rebuild_layer(P, d, ff, dtype):
     """k = P is the dense FFN: equal to one rebuild layer's output at the same
     input, bit for bit.  The gathered rows of the Context Cache path always run
-    one tile per workgroup; at 768 and 3072 rows the rebuild's gate/up
-    projection has more tiles than CUs and runs persistently (2 and 6 tiles per
-    workgroup, 192 x 256 and 256 x 256 tiles), with the same sums."""
-    say("ctx dense vs rebuild", P, d, ff)
-    w = ffn_weights(2, 0, d, ff)
-    r0 = random_bf16(2, 0, "r0", (P, d))
+    one tile per workgroup; with more tiles than CUs the rebuild runs them
+    persistently, with the same sums: the gate/up projection at 768, 3072 and
+    12288 rows (2, 6 and 24 tiles per workgroup; 192 x 256 and 256 x 256
+    tiles) and in fp32 (256 x 128 tiles, 3 per workgroup), the down
+    projection at 12288 rows (one K split, 2 tiles per workgroup)."""
+    say("ctx dense vs rebuild", P, d, ff, dtype)
+    w = ffn_weights(2, 0, d, ff, dtype=dtype)
+    r0 = random_bf16(2, 0, "r0", (P, d), dtype=dtype)
     W = ffn_dev(w)
-    xo, yo = cgs.ref_rebuild_dense([W], to_dev(r0))
+    xo, yo = cgs.ref_rebuild_dense([W], to_dev(r0, dtype))
     y = cgs.ctx_ffn_recompute(W, xo[0], torch.zeros_like(xo[0]),
                               torch.arange(P, dtype=torch.int32, device=dev()))
     torch.cuda.synchronize()
-    assert np.array_equal(bits(y), bits(yo[0]))
+    raw = np.uint32 if dtype == "f32" else np.uint16
+    assert np.array_equal(bits(y).view(raw), bits(yo[0]).view(raw))
+    if P > 4096:
+        # both paths run the 12288-row down projection persistently: sampled
+        # rows against the oracle, teacher-forced on the GPU's own layer input
+        sample = np.linspace(0, P - 1, 16).astype(int)
+        y_o = O.ffn_geglu(O.decode(bits(xo[0])[sample], dtype), w)
+        assert_close(O.decode(bits(yo[0])[sample], dtype), y_o, "sampled rows", out=dtype)
 
 
 @pytest.mark.parametrize("rho", [0.1, 0.3, 1.0])
