@@ -66,13 +66,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_text(text: str) -> str:
+    """C++ source without its comments, whitespace collapsed."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split())
+
+
 def _source_hash(files) -> str:
-    """First 16 hex digits of the sha256 of the kernel's source files, in order."""
+    """First 16 hex digits of the sha256 of the kernel's source files, in order,
+    comments and layout left out: counters stay tied to the code they measured
+    through edits of comments alone."""
     import hashlib
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "cache_guided_sparse_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "cache_guided_sparse_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

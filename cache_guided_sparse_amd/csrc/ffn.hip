@@ -26,8 +26,11 @@
 //             one round of 256 workgroups), 256 x 128 otherwise; the down
 //             projection keeps 128 x 128 tiles (2 x 16 tiles x 8 K splits)
 //   M > 256   192 x 256 (bf16 with d % 256 == 0: the 768-row rebuild is
-//             4 x 128 gate/up tiles and 4 x 8 x 8 down tiles, two and one
-//             rounds of 256 workgroups); else 256 x 128.
+//             4 x 128 gate/up tiles and 4 x 8 x 8 down tiles); gate/up at
+//             2048 rows or more (a batched rebuild) 256 x 256; else 256 x 128.
+// A launch with more tiles than CUs, full row tiles and no gathered rows
+// runs persistently (launch_cfg): the 768-row gate/up projection as 256
+// workgroups of 2 tiles, the 3072-row one (4 entries) of 6.
 #include <algorithm>
 #include <mutex>
 #include <vector>
@@ -52,11 +55,11 @@ using CfgM = GemmCfg<128, 4, 2, 4, 2, 4>;   // 128 x 128, 8 waves,  96 KB
 using CfgL = GemmCfg<256, 4, 2, 4, 2, 5>;   // 256 x 128, 8 waves, 144 KB
 using CfgX = GemmCfg<192, 2, 4, 4, 2, 3>;   // 192 x 256, 8 waves, 144 KB
 using CfgG = GemmCfg<128, 4, 2, 8, 2, 4>;   // 128 x 256, 8 waves, 160 KB (32 x 128 wave tiles)
-using CfgW = GemmCfg<256, 2, 4, 4, 2, 3>;   // 256 x 256, 8 waves, 160 KB (128 x 64 wave tiles, 230 VGPRs)
+using CfgW = GemmCfg<256, 2, 4, 4, 2, 3>;   // 256 x 256, 8 waves, 160 KB (128 x 64 wave tiles)
 enum TileId { kTileS = 0, kTileM = 1, kTileL = 2, kTileX = 3, kTileG = 4, kTileW = 5 };
 // Rows from which the gate/up projection takes 256 x 256 tiles (a batched
-// rebuild): 10% fewer fragment reads and transfers per MFMA than 192 x 256,
-// and enough row tiles that the grid fills whole rounds of workgroups.
+// rebuild): a third more MFMA work per K tile's barrier and transfers than
+// 192 x 256, and enough row tiles that the tiles divide evenly over the CUs.
 constexpr int kWideRows = 2048;
 
 constexpr int kLdsPerCu = 160 * 1024;
