@@ -477,32 +477,63 @@ int rebuild_t(const cgs_ffn* layers, int L, const T* r0, int P, T* xo, T* yo, vo
   return CGS_OK;
 }
 
-// Several entries rebuilt as one prefill over n P rows: the GEMMs and the
-// row finish run on contiguous work rows, and after each layer one launch
-// copies the layer's rows out to every entry's own x_ref / y_ref.
+// Several entries rebuilt as one prefill over n P rows: the GEMMs run on
+// contiguous work rows, and each layer's row finish writes its rows' outputs
+// straight into every entry's own y_ref / x_ref.
 constexpr int kBatchMax = 16;
 template <typename T> struct RowDist {
   T* y[kBatchMax];
   T* x[kBatchMax];
 };
 
-// Row blockIdx.x of the work buffers (entry row / P, position row % P):
-// y row to y[e] + yoff, x row (when x_off >= 0) to x[e] + x_off.
+// Row blockIdx.x of the work rows (entry row / P, position row % P) to
+// x[e] + x_off: the first layer's input of every entry.
 template <typename T>
-__global__ __launch_bounds__(kRowThreads) void distribute_rows_kernel(const T* __restrict__ yw,
-                                                                      const T* __restrict__ xw, int P, int d,
-                                                                      RowDist<T> dst, long long y_off,
-                                                                      long long x_off) {
+__global__ __launch_bounds__(kRowThreads) void distribute_rows_kernel(const T* __restrict__ xw, int P, int d,
+                                                                      RowDist<T> dst, long long x_off) {
   const int row = blockIdx.x;
   const int e = row / P, p = row - e * P;
   const size_t src = static_cast<size_t>(row) * d, pos = static_cast<size_t>(p) * d;
   constexpr int V = 16 / static_cast<int>(sizeof(T));
-  for (int c = threadIdx.x * V; c < d; c += kRowThreads * V) {
-    if (y_off >= 0)
-      *reinterpret_cast<u32x4_t*>(dst.y[e] + y_off + pos + c) = *reinterpret_cast<const u32x4_t*>(yw + src + c);
-    if (x_off >= 0)
-      *reinterpret_cast<u32x4_t*>(dst.x[e] + x_off + pos + c) = *reinterpret_cast<const u32x4_t*>(xw + src + c);
+  for (int c = threadIdx.x * V; c < d; c += kRowThreads * V)
+    *reinterpret_cast<u32x4_t*>(dst.x[e] + x_off + pos + c) = *reinterpret_cast<const u32x4_t*>(xw + src + c);
+}
+
+// Row finish of a batched rebuild, row p of the n P work rows (entry p / P,
+// position p % P): y = the split sum of the partials, stored in the entry's
+// y_ref of this layer (y_off); r += round(y); x_next = RMSNorm(r) into the
+// work rows (the next layer's input) and the entry's x_ref of the next layer
+// (x_off).  The same arithmetic as the single-entry finish.  RUNS: runs of 8
+// a thread keeps between the residual update and the normalisation (1 when
+// d = 8 kRowThreads, one run per thread; kGlueKeep otherwise).
+template <typename T, int RUNS>
+__global__ __launch_bounds__(kRowThreads) void rebuild_finish_kernel(const float* __restrict__ part, int splits,
+                                                                     size_t split_stride, int d, int P,
+                                                                     RowDist<T> dst, long long y_off,
+                                                                     long long x_off, GlueArgs<T> glue) {
+  __shared__ float red[kRowThreads / 64];
+  const int p = blockIdx.x;
+  const int e = p / P;
+  const size_t ro = static_cast<size_t>(p) * d;
+  const size_t qo = static_cast<size_t>(p - e * P) * d;
+  T* const y_row = dst.y[e] + y_off + qo;
+  if (glue.x_next) glue.x_copy = dst.x[e] + x_off + qo;
+  float ss = 0.f;
+  float keep[RUNS][8];
+  int j = 0;
+  for (int c = threadIdx.x * 8; c < d; c += kRowThreads * 8, ++j) {
+    float v[8], rr[8], b[8];
+    glue_prefetch(glue, ro, c, rr, b);
+    Row8<float>::load(part + ro + c, v);
+    add_splits(part + split_stride + ro + c, split_stride, splits - 1, v);
+    Row8<T>::store(y_row + c, v);
+    ss += glue_add(glue, ro, c, v, rr, b);
+    if (j < RUNS) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) keep[j][q] = rr[q];
+    }
   }
+  if (glue.x_next) glue_norm_t<T, kRowThreads>(glue, ro, d, ss, red, keep);
 }
 
 template <typename T>
@@ -515,7 +546,6 @@ int rebuild_batch_t(const cgs_ffn* layers, int L, const T* r0, int n, int P, T* 
   Carve cv(ws);
   float* r = cv.take<float>(static_cast<size_t>(M) * d);
   T* xw = cv.take<T>(static_cast<size_t>(M) * d);
-  T* yw = cv.take<T>(static_cast<size_t>(M) * d);
   T* H = cv.take<T>(p.h_elems);
   float* part = cv.take<float>(p.part_elems);
   const long long lay = static_cast<long long>(P) * d;
@@ -528,24 +558,22 @@ int rebuild_batch_t(const cgs_ffn* layers, int L, const T* r0, int n, int P, T* 
     ProfScope ps("rebuild.norm", s);
     hipLaunchKernelGGL((residual_rmsnorm_kernel<T, T, T>), dim3(M), dim3(kRowThreads), 0, s, r0, r,
                        static_cast<const T*>(nullptr), static_cast<const float*>(nullptr), d, xw);
-    hipLaunchKernelGGL((distribute_rows_kernel<T>), dim3(M), dim3(kRowThreads), 0, s, yw, xw, P, d, dst, -1ll,
-                       0ll);
+    hipLaunchKernelGGL((distribute_rows_kernel<T>), dim3(M), dim3(kRowThreads), 0, s, xw, P, d, dst, 0ll);
   }
   if (!launch_ok()) return CGS_ERR_LAUNCH;
   for (int l = 0; l < L; ++l) {
     launch_ffn_core<T>(layers[l], xw, nullptr, M, p, H, part, "rebuild.glu", "rebuild.down", s);
     ProfScope ps("rebuild.finish", s);
     const bool more = l + 1 < L;
-    const GlueArgs<T> ga{r, nullptr, more ? xw : static_cast<T*>(nullptr), nullptr, nullptr, 0, 0};
+    const GlueArgs<T> ga{r, nullptr, more ? xw : static_cast<T*>(nullptr), nullptr, nullptr, 0, 0, nullptr};
     const size_t split_stride = static_cast<size_t>(M) * d;
+    const long long y_off = l * lay, x_off = more ? (l + 1) * lay : -1ll;
     if (d == 8 * kRowThreads)
-      launch_finish1<T>(dim3(M), s, part, p.splits, split_stride, d, false, static_cast<const int32_t*>(nullptr),
-                        M, static_cast<const T*>(nullptr), yw, ga);
+      hipLaunchKernelGGL((rebuild_finish_kernel<T, 1>), dim3(M), dim3(kRowThreads), 0, s, part, p.splits,
+                         split_stride, d, P, dst, y_off, x_off, ga);
     else
-      hipLaunchKernelGGL((row_finish_kernel<T>), dim3(M), dim3(kRowThreads), 0, s, part, p.splits, split_stride,
-                         d, false, static_cast<const int32_t*>(nullptr), M, static_cast<const T*>(nullptr), yw, ga);
-    hipLaunchKernelGGL((distribute_rows_kernel<T>), dim3(M), dim3(kRowThreads), 0, s, yw, xw, P, d, dst,
-                       l * lay, more ? (l + 1) * lay : -1ll);
+      hipLaunchKernelGGL((rebuild_finish_kernel<T, kGlueKeep>), dim3(M), dim3(kRowThreads), 0, s, part, p.splits,
+                         split_stride, d, P, dst, y_off, x_off, ga);
     if (!launch_ok()) return CGS_ERR_LAUNCH;
   }
   return CGS_OK;
@@ -637,7 +665,6 @@ extern "C" size_t cgs_ref_rebuild_dense_batch_workspace(int L, int n, int P, int
   const FfnPlan p = plan_ffn(static_cast<int>(M), d, ff, dtype);
   Carve cv(nullptr);
   cv.take<float>(static_cast<size_t>(M) * d);
-  cv.take<char>(static_cast<size_t>(M) * d * elem_bytes(dtype));
   cv.take<char>(static_cast<size_t>(M) * d * elem_bytes(dtype));
   cv.take<char>(p.h_elems * elem_bytes(dtype));
   cv.take<float>(p.part_elems);

@@ -115,6 +115,7 @@ template <typename T> struct GlueArgs {
   double* score_key;    // [rows]
   int score_kind;       // cgs_score_kind
   long long score_floor;
+  T* x_copy;            // this row's second x_next destination (row-relative) or NULL
 };
 
 inline bool glue_ok(const cgs_glue* g) {
@@ -209,6 +210,7 @@ __device__ __forceinline__ void glue_norm_t(const GlueArgs<T>& g, size_t ro, int
 #pragma unroll
     for (int e = 0; e < 8; ++e) rr[e] *= inv;
     Row8<T>::store(g.x_next + ro + c, rr);
+    if (g.x_copy) Row8<T>::store(g.x_copy + c, rr);
     if (g.score_key) {
       float xr[8];
       Row8<T>::round(rr);
