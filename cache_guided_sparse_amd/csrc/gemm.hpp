@@ -11,14 +11,16 @@
 // Data movement (gfx950): K tiles of 128 bytes per row travel global -> LDS
 // by LDS DMA (global_load_lds_dwordx4, 1 KB per wavefront instruction) into
 // two rings (A tiles SA deep, B tiles SB deep; half of the waves load each
-// operand), one workgroup barrier per K tile.  gemm_kernel_persist runs the
-// same tiles with fewer workgroups than tiles: each workgroup takes the tiles
+// operand), one workgroup barrier per K tile.  A tile row is 8 chunks of 16
+// bytes; chunk c of row r sits at physical chunk c ^ (r & 7), so the 16-byte
+// MFMA fragment reads of 8 consecutive rows fall in 8 distinct bank groups.
+// The waves form a WM x WN grid; each owns (BM/WM) x 16 NT of the tile.
+//
+// gemm_kernel runs one tile per workgroup; gemm_kernel_persist runs the same
+// tiles with fewer workgroups than tiles: each workgroup takes the tiles
 // blockIdx.x, blockIdx.x + gridDim.x, ... and its rings run on across them,
 // so the first K tiles of the next tile are in flight while the current one
-// finishes and stores its epilogue.  A tile row is 8 chunks
-// of 16 bytes; chunk c of row r sits at physical chunk c ^ (r & 7), so the
-// 16-byte MFMA fragment reads of 8 consecutive rows fall in 8 distinct bank
-// groups.  The waves form a WM x WN grid; each owns (BM/WM) x 16 NT of the tile.
+// finishes and stores its epilogue.
 #pragma once
 
 #include "common.hpp"
