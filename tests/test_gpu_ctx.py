@@ -77,7 +77,8 @@ def test_index_list_longer_than_the_staged_search(d):
 
 @pytest.mark.parametrize("P,d,ff,dtype", [(96, 256, 512, "bf16"), (768, 2048, 16384, "bf16"),
                                           (3072, 2048, 16384, "bf16"), (12288, 2048, 16384, "bf16"),
-                                          (768, 1024, 16384, "f32")])
+                                          (768, 1024, 16384, "f32"), (1152, 2048, 8320, "bf16"),
+                                          (2304, 2048, 16384, "bf16")])
 def test_dense_equals_rebuild_layer(P, d, ff, dtype):
     """k = P is the dense FFN: equal to one rebuild layer's output at the same
     input, bit for bit.  The gathered rows of the Context Cache path always run
@@ -85,7 +86,10 @@ def test_dense_equals_rebuild_layer(P, d, ff, dtype):
     persistently, with the same sums: the gate/up projection at 768, 3072 and
     12288 rows (2, 6 and 24 tiles per workgroup; 192 x 256 and 256 x 256
     tiles) and in fp32 (256 x 128 tiles, 3 per workgroup), the down
-    projection at 12288 rows (one K split, 2 tiles per workgroup)."""
+    projection at 12288 rows (one K split, 2 tiles per workgroup).  Uneven
+    shares: 390 tiles (1152 rows, ff 8320; not a multiple of 8, so without the
+    XCD renumbering) and 1152 tiles (2304 rows: 9 row tiles in one group), 1 or
+    2 and 4 or 5 tiles per workgroup."""
     say("ctx dense vs rebuild", P, d, ff, dtype)
     w = ffn_weights(2, 0, d, ff, dtype=dtype)
     r0 = random_bf16(2, 0, "r0", (P, d), dtype=dtype)
