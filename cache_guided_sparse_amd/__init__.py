@@ -25,8 +25,8 @@ CGS_BF16, CGS_F32 = 0, 1
 CGS_SCORE_REL_RMS, CGS_SCORE_COSINE = 0, 1
 CGS_MASK_TOPK, CGS_MASK_COVERAGE = 0, 1
 CGS_DOWN_DF, CGS_DOWN_FD = 0, 1
-CGS_ERR_DATA = 6
-CGS_ERR_TIMEOUT = 7
+CGS_OK, CGS_ERR_ARG, CGS_ERR_SHAPE, CGS_ERR_WORKSPACE = 0, 1, 2, 3
+CGS_ERR_UNSUPPORTED, CGS_ERR_LAUNCH, CGS_ERR_DATA, CGS_ERR_TIMEOUT = 4, 5, 6, 7
 
 _KIND = {"rel_rms": CGS_SCORE_REL_RMS, "cosine": CGS_SCORE_COSINE}
 _MODE = {"topk": CGS_MASK_TOPK, "coverage": CGS_MASK_COVERAGE}
@@ -270,7 +270,9 @@ class FFN:
 def set_validate(on: bool) -> bool:
     """Checked mode (debugging): calls first verify their documented device-data
     preconditions and raise CgsError (status CGS_ERR_DATA) on a violation;
-    synchronises streams, so never while capturing.  Returns the previous setting."""
+    synchronises streams, so a checked call on a stream under graph capture
+    raises CgsError (CGS_ERR_UNSUPPORTED) before enqueuing anything.  Returns
+    the previous setting."""
     return bool(lib().cgs_set_validate(1 if on else 0))
 
 

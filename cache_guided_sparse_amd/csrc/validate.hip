@@ -66,6 +66,12 @@ int* device_flag() {
 
 template <typename Launch>
 int run_check(hipStream_t s, Launch launch) {
+  // A check reads its verdict back to the host, which a stream under graph
+  // capture cannot do: refuse before enqueuing anything, so that the caller's
+  // capture stays valid.
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return CGS_ERR_LAUNCH;
+  if (cs != hipStreamCaptureStatusNone) return CGS_ERR_UNSUPPORTED;
   int* flag = device_flag();
   if (!flag) return CGS_ERR_LAUNCH;
   hipLaunchKernelGGL(zero_flag_kernel, dim3(1), dim3(1), 0, s, flag);

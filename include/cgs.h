@@ -120,8 +120,10 @@ const char* cgs_status_str(int status);
  * |h| < 2^24 and |w| < 2^5 for contribution scores; finite keys), wait for
  * the check on their stream and return CGS_ERR_DATA before launching
  * anything else.  The mode synchronises streams and allocates one int per
- * device on first use, so it must not be on while a stream is captured.
- * Returns the previous setting. */
+ * device on first use, so it cannot work on a stream under graph capture: a
+ * checked call on a capturing stream returns CGS_ERR_UNSUPPORTED without
+ * enqueuing anything (the capture stays valid).  Returns the previous
+ * setting. */
 int cgs_set_validate(int on);
 
 /* ABI version (major*100 + minor). */

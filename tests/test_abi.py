@@ -370,3 +370,13 @@ def test_mask_indices_and_masked_layers_validate_before_launch():
     arr[1].idx = None
     arr[1].h_anchor = 0x5000
     assert L.act_masked_layers(arr, 3, 50, r, x, buf, 1 << 40, None) == 1         # h_anchor without idx
+
+
+def test_binding_status_codes_match_the_header():
+    """The binding's CGS_* status constants are the header's cgs_status values."""
+    import re
+    text = open(cgs.HEADER_PATH).read()
+    enum = dict((m.group(1), int(m.group(2))) for m in re.finditer(r"\b(CGS_(?:OK|ERR_[A-Z]+))\s*=\s*(\d+)", text))
+    assert enum, "no cgs_status values found in the header"
+    for name, value in enum.items():
+        assert getattr(cgs, name) == value, name

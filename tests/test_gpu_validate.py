@@ -129,3 +129,28 @@ def test_stored_norms_must_be_finite_and_non_negative(checked):
     bad[0, 9] = float("inf")
     _data_error(lambda: cgs.act_build_masks(h, None, "topk", K=32, norms=bad))
     torch.cuda.synchronize()
+
+
+def test_checked_call_refused_under_graph_capture(checked):
+    """A checked call reads its verdict back to the host, which a stream under
+    graph capture cannot do: it refuses (CGS_ERR_UNSUPPORTED) before enqueuing
+    anything, and the capture stays valid (the graph replays what else was
+    captured)."""
+    say("validate under capture")
+    keys = torch.arange(64, dtype=torch.float64, device=dev())
+    idx = torch.zeros(8, dtype=torch.int32, device=dev())
+    out = torch.zeros(4, device=dev())
+    cgs.ctx_select_from_keys(keys, 8, idx_out=idx)  # checked, outside capture: fine
+    torch.cuda.synchronize()
+    assert idx.cpu().tolist() == list(range(56, 64))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            out.add_(1.0)
+            with pytest.raises(cgs.CgsError) as e:
+                cgs.ctx_select_from_keys(keys, 8, idx_out=idx)
+            assert e.value.status == cgs.CGS_ERR_UNSUPPORTED, str(e.value)
+    g.replay()
+    torch.cuda.synchronize()
+    assert out.cpu().tolist() == [1.0] * 4
