@@ -431,7 +431,9 @@ size_t cgs_act_denoise_step_workspace(int L, int S, int d, int K_max);
  * (zeroed by the initialising kernel); every wait is bounded
  * (cgs_set_step_wait_limit).  Preconditions: no other launch of this kernel
  * may run on the device at the same time (both would need every CU); the
- * workspace is not shared with a concurrent launch.  CGS_ERR_UNSUPPORTED when
+ * workspace is not shared with a concurrent launch.  Kernels of other
+ * streams that hold CUs only delay the step (its remaining workgroups start
+ * as CUs free up); a delay past the wait limit ends it with CGS_ERR_TIMEOUT.  CGS_ERR_UNSUPPORTED when
  * the device has fewer than 8 d / 32 or S CUs.  Errors as act_ffn_masked.
  * Steps of several launches (one per call) race if they overlap on a device. */
 int act_denoise_step(const cgs_step_layer* layers, int L, int S, int d, int ff, float* r, void* x,
