@@ -429,7 +429,10 @@ int ctx_recompute_t(const cgs_ffn& w, const T* x, const T* y_ref, const int32_t*
   T* H = cv.take<T>(p.h_elems);
   float* part = cv.take<float>(p.part_elems);
   if (k > 0) {
-    launch_ffn_core<T>(w, x, idx, k, p, H, part, "ctx.glu", "ctx.down", s);
+    // k == P: an ascending, duplicate-free list of P positions in [0, P) is
+    // 0 .. P-1, so the rows are read in place (no gather), which lets a
+    // launch with more tiles than CUs run persistently.
+    launch_ffn_core<T>(w, x, k == P ? nullptr : idx, k, p, H, part, "ctx.glu", "ctx.down", s);
     if (!launch_ok()) return CGS_ERR_LAUNCH;
   }
   {
