@@ -434,9 +434,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel_persist(GemmArgs<T> 
   // Transfers of this wave's operand for K tile kt of the tile at toff, into
   // stage q of its ring.  Everything but the lane's own offset off0 (the
   // tile, the K tile and the transfer's rows) goes into the scalar base
-  // address, so a lane holds one offset register for all of its transfers
-  // (with the per-transfer sums in vector registers the 256 x 256 tile needed
-  // 253 of them, now 243, and ran 2% slower).
+  // address, so a lane holds one offset register for all of its transfers.
+  // Per-transfer sums in vector registers would cost one register each (253
+  // instead of 243 on the 256 x 256 tile) and 2% of its time.
   auto issue = [&](size_t toff, int kt, int q) {
     const size_t kb = static_cast<size_t>(kt) * 128u;
     const char* const p0 = ptr0 + toff + kb;
