@@ -29,7 +29,7 @@
 namespace cgs {
 
 constexpr int kXcds = 8;
-constexpr int kMGroup = 4;  // row tiles per group in the workgroup order
+constexpr int kMGroup = 4;  // default row tiles per group in the workgroup order
 
 template <typename T> struct GemmArgs {
   const T* A;              // [*][lda]; row r of the tile is a_rows[m0+r] or m0+r
@@ -47,6 +47,7 @@ template <typename T> struct GemmArgs {
   float* C;                // partial output [splits][M][ldc]
   int ldc;
   size_t split_stride;
+  int m_group;             // row tiles per group of the workgroup order (0 = kMGroup)
 };
 
 // LDS byte address (M0 / ds offset) of a __shared__ location.
@@ -102,10 +103,10 @@ struct GemmCfg {
 // Output tile of logical workgroup v.  Workgroups are dealt round-robin over
 // the 8 XCDs; renumber them so that consecutive logical tiles (same B tile,
 // neighbouring A tiles) share an XCD and its L2.  With many row tiles (a
-// batched rebuild) they go in groups of kMGroup: within an XCD the workgroups
-// running together cover kMGroup row tiles of several weight tiles, instead of
+// batched rebuild) they go in groups of m_group: within an XCD the workgroups
+// running together cover m_group row tiles of several weight tiles, instead of
 // every row tile of a few weight tiles, so each XCD streams fewer distinct A
-// rows per round.
+// rows per round.  The best group balances the A and B bytes an XCD fetches.
 struct GemmTile {
   int m0, ntile, split;
 };
@@ -116,7 +117,8 @@ __device__ __forceinline__ GemmTile gemm_tile(const GemmArgs<T>& g, int bm, int 
   if (nb % kXcds == 0) logical = (v % kXcds) * (nb / kXcds) + v / kXcds;
   const int split = logical / (g.m_tiles * g.n_tiles);
   const int lt = logical - split * (g.m_tiles * g.n_tiles);
-  const int gm = (g.m_tiles > kMGroup && g.m_tiles % kMGroup == 0) ? kMGroup : g.m_tiles;
+  const int mg = g.m_group > 0 ? g.m_group : kMGroup;
+  const int gm = (g.m_tiles > mg && g.m_tiles % mg == 0) ? mg : g.m_tiles;
   const int mtile = (lt / (gm * g.n_tiles)) * gm + lt % gm;
   return GemmTile{mtile * bm, (lt / gm) % g.n_tiles, split};
 }
