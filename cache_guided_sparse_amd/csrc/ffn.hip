@@ -53,11 +53,15 @@ constexpr int kFinishIdxLds = 4096;  // index lists up to this length are search
 // tile of a batched rebuild is the exception: its x rows come back from the
 // MALL (each XCD's L2 cannot hold a round's operands) while its weight tiles
 // are shared by the XCD's workgroups, so its A ring is the deeper one
-// (3 + 2 stages measured 3% faster than 2 + 3, bit-identical).
+// (3 + 2 stages measured 3% faster than 2 + 3, bit-identical), and so is that
+// of the 192 x 256 tile of a dense gate/up projection (768 and 1536 rows: 5%
+// and 3% faster).  The down projection keeps 2 + 3 (1536 rows: 2.5% slower
+// with 3 + 2).
 using CfgS = GemmCfg<64, 2, 2, 4, 2, 4>;    //  64 x 128, 4 waves,  80 KB LDS
 using CfgM = GemmCfg<128, 4, 2, 4, 2, 4>;   // 128 x 128, 8 waves,  96 KB
 using CfgL = GemmCfg<256, 4, 2, 4, 2, 5>;   // 256 x 128, 8 waves, 144 KB
 using CfgX = GemmCfg<192, 2, 4, 4, 2, 3>;   // 192 x 256, 8 waves, 144 KB
+using CfgXG = GemmCfg<192, 2, 4, 4, 3, 2>;  // the same tile for a dense gate/up projection, 136 KB
 using CfgG = GemmCfg<128, 4, 2, 8, 2, 4>;   // 128 x 256, 8 waves, 160 KB (32 x 128 wave tiles)
 using CfgW = GemmCfg<256, 2, 4, 4, 3, 2>;   // 256 x 256, 8 waves, 160 KB (128 x 64 wave tiles)
 enum TileId { kTileS = 0, kTileM = 1, kTileL = 2, kTileX = 3, kTileG = 4, kTileW = 5 };
@@ -122,7 +126,10 @@ void launch_tile(int tile, const GemmArgs<T>& g, const char* site, hipStream_t s
       if constexpr (sizeof(T) == 2) launch_cfg<CfgW, T, GLU, GATHER>(g, site, s);
       break;
     default:
-      if constexpr (sizeof(T) == 2) launch_cfg<CfgX, T, GLU, GATHER>(g, site, s);
+      if constexpr (sizeof(T) == 2) {
+        if constexpr (GLU && !GATHER) launch_cfg<CfgXG, T, GLU, GATHER>(g, site, s);
+        else launch_cfg<CfgX, T, GLU, GATHER>(g, site, s);
+      }
       break;
   }
 }
